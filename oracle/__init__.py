@@ -1,0 +1,261 @@
+"""CPU oracle for the decoder block (TEST INFRASTRUCTURE ONLY).
+
+Only tests/, the smoke check and the benchmark's cpu_baseline leg may import
+this package.  It wraps liboracle.so (plain C, fp64, built from oracle.c with
+gcc) through ctypes.  It never imports the HIP package: configurations are
+passed as plain attributes (duck typing) and arrays as numpy.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from types import SimpleNamespace
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+NORM = {"rms": 0, "rms_nogamma": 1, "layer": 2}
+MLP = {"swiglu": 0, "relu": 1, "gelu_tanh": 2}
+ROPE = {"none": 0, "neox": 1}
+
+_DP = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (-O2 -fopenmp, no fast-math)."""
+    if force or not os.path.exists(_SO):
+        src = os.path.join(_HERE, "oracle.c")
+        tmp = _SO + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", "-Wall",
+               "-o", tmp, src, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+class _Cfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "T", "C", "NH", "NKV", "H", "norm", "mlp", "rope")] + [
+        ("rope_base", ctypes.c_double), ("eps", ctypes.c_double),
+        ("qkv_bias", ctypes.c_int), ("o_bias", ctypes.c_int), ("mlp_bias", ctypes.c_int)]
+
+
+_WNAMES = ("g1", "b1", "wqkv", "bqkv", "wo", "bo", "g2", "b2", "w_up", "b_up", "w_down", "b_down")
+_SNAMES = ("n1", "r1", "mu1", "qkv", "o", "lse", "x2", "n2", "r2", "mu2", "up", "h")
+
+
+class _W(ctypes.Structure):
+    _fields_ = [(n, _DP) for n in _WNAMES]
+
+
+class _S(ctypes.Structure):
+    _fields_ = [(n, _DP) for n in _SNAMES]
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        _lib = ctypes.CDLL(_SO)
+        _lib.orc_num_threads.restype = ctypes.c_int
+    return _lib
+
+
+def _d(a):
+    """Contiguous float64 copy/view of a."""
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _p(a):
+    if a is None:
+        return _DP()
+    assert a.dtype == np.float64 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_DP)
+
+
+def num_threads() -> int:
+    return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().orc_set_num_threads(int(n))
+
+
+# ---------------------------------------------------------------------------
+# per-op wrappers
+# ---------------------------------------------------------------------------
+def norm_forward(mode: str, x, g=None, b=None, eps=1e-5):
+    x = _d(x)
+    C = x.shape[-1]
+    R = x.size // C
+    out = np.empty_like(x)
+    rstd = np.empty(R)
+    mean = np.empty(R)
+    lib().orc_norm_forward(NORM[mode], _p(x), _p(None if g is None else _d(g)),
+                           _p(None if b is None else _d(b)), ctypes.c_double(eps),
+                           ctypes.c_long(R), C, _p(out), _p(rstd), _p(mean))
+    return out, rstd, mean
+
+
+def norm_backward(mode: str, dy, x, g, rstd, mean):
+    dy, x = _d(dy), _d(x)
+    C = x.shape[-1]
+    R = x.size // C
+    dx = np.zeros_like(x)
+    dg = np.zeros(C)
+    db = np.zeros(C)
+    lib().orc_norm_backward(NORM[mode], _p(dy), _p(x), _p(None if g is None else _d(g)),
+                            _p(_d(rstd)), _p(_d(mean)), ctypes.c_long(R), C,
+                            _p(dx), _p(dg), _p(db))
+    return dx, dg, db
+
+
+def linear_forward(inp, w, bias=None):
+    inp, w = _d(inp), _d(w)
+    N, K = w.shape
+    R = inp.size // K
+    out = np.empty(inp.shape[:-1] + (N,))
+    lib().orc_linear_forward(_p(inp), _p(w), _p(None if bias is None else _d(bias)),
+                             ctypes.c_long(R), K, N, _p(out))
+    return out
+
+
+def linear_backward(dout, inp, w):
+    dout, inp, w = _d(dout), _d(inp), _d(w)
+    N, K = w.shape
+    R = inp.size // K
+    dinp = np.zeros_like(inp)
+    dw = np.zeros_like(w)
+    db = np.zeros(N)
+    lib().orc_linear_backward(_p(dout), _p(inp), _p(w), ctypes.c_long(R), K, N,
+                              _p(dinp), _p(dw), _p(db))
+    return dinp, dw, db
+
+
+def rope(buf, B, T, stride, off, nheads, hd, base, inverse=False):
+    """Returns a rotated copy of buf ([B*T, stride])."""
+    out = _d(buf).copy()
+    lib().orc_rope(_p(out), B, T, stride, off, nheads, hd, ctypes.c_double(base), int(inverse))
+    return out
+
+
+def attn_forward(qkv, B, T, C, NH, NKV):
+    qkv = _d(qkv)
+    out = np.empty((B, T, C))
+    lse = np.empty((B, NH, T))
+    lib().orc_attn_forward(_p(qkv), B, T, C, NH, NKV, _p(out), _p(lse))
+    return out, lse
+
+
+def attn_backward(qkv, dout, B, T, C, NH, NKV):
+    qkv, dout = _d(qkv), _d(dout)
+    dqkv = np.empty_like(qkv)
+    lib().orc_attn_backward(_p(qkv), _p(dout), B, T, C, NH, NKV, _p(dqkv))
+    return dqkv
+
+
+def attn_forward_materialized(qkv, B, T, C, NH, NKV):
+    qkv = _d(qkv)
+    out = np.empty((B, T, C))
+    att = np.empty((B, NH, T, T))
+    lib().orc_attn_forward_materialized(_p(qkv), B, T, C, NH, NKV, _p(out), _p(att))
+    return out, att
+
+
+def attn_backward_materialized(qkv, att, dout, B, T, C, NH, NKV):
+    qkv, att, dout = _d(qkv), _d(att), _d(dout)
+    dqkv = np.empty_like(qkv)
+    lib().orc_attn_backward_materialized(_p(qkv), _p(att), _p(dout), B, T, C, NH, NKV, _p(dqkv))
+    return dqkv
+
+
+def act_forward(mlp: str, up, H):
+    up = _d(up)
+    W = up.shape[-1]
+    R = up.size // W
+    h = np.empty(up.shape[:-1] + (H,))
+    lib().orc_act_forward(MLP[mlp], _p(up), ctypes.c_long(R), H, _p(h))
+    return h
+
+
+def act_backward(mlp: str, dh, up, H):
+    dh, up = _d(dh), _d(up)
+    W = up.shape[-1]
+    R = up.size // W
+    dup = np.zeros_like(up)
+    lib().orc_act_backward(MLP[mlp], _p(dh), _p(up), ctypes.c_long(R), H, _p(dup))
+    return dup
+
+
+# ---------------------------------------------------------------------------
+# the block
+# ---------------------------------------------------------------------------
+def _cfg(cfg, B=None, T=None) -> _Cfg:
+    return _Cfg(B=cfg.B if B is None else B, T=cfg.T if T is None else T, C=cfg.C, NH=cfg.NH,
+                NKV=cfg.NKV, H=cfg.H, norm=NORM[cfg.norm], mlp=MLP[cfg.mlp], rope=ROPE[cfg.rope],
+                rope_base=float(cfg.rope_base), eps=float(cfg.eps), qkv_bias=int(cfg.qkv_bias),
+                o_bias=int(cfg.o_bias), mlp_bias=int(cfg.mlp_bias))
+
+
+def _dims(cfg):
+    hd = cfg.C // cfg.NH
+    QKV = cfg.C + 2 * cfg.NKV * hd
+    W = 2 * cfg.H if cfg.mlp == "swiglu" else cfg.H
+    return hd, QKV, W
+
+
+def block_forward(cfg, weights: dict, x):
+    """Returns (y [B,T,C], saved namespace of float64 arrays)."""
+    B, T, C = cfg.B, cfg.T, cfg.C
+    BT = B * T
+    hd, QKV, W = _dims(cfg)
+    x = _d(x).reshape(B, T, C)
+    wd = {k: _d(v) for k, v in weights.items() if v is not None}
+    cw = _W(**{n: _p(wd.get(n)) for n in _WNAMES})
+    sv = SimpleNamespace(n1=np.empty((BT, C)), r1=np.empty(BT), mu1=np.empty(BT),
+                         qkv=np.empty((BT, QKV)), o=np.empty((BT, C)), lse=np.empty((B, cfg.NH, T)),
+                         x2=np.empty((BT, C)), n2=np.empty((BT, C)), r2=np.empty(BT),
+                         mu2=np.empty(BT), up=np.empty((BT, W)), h=np.empty((BT, cfg.H)))
+    cs = _S(**{n: _p(getattr(sv, n)) for n in _SNAMES})
+    y = np.empty((B, T, C))
+    c = _cfg(cfg)
+    lib().orc_block_forward(ctypes.byref(c), ctypes.byref(cw), _p(x), _p(y), ctypes.byref(cs))
+    return y, sv
+
+
+def block_backward(cfg, weights: dict, x, saved, dy):
+    """Returns (dx [B,T,C], grads dict).  Gradients start at zero."""
+    B, T, C = cfg.B, cfg.T, cfg.C
+    x = _d(x).reshape(B, T, C)
+    dy = _d(dy).reshape(B, T, C)
+    wd = {k: _d(v) for k, v in weights.items() if v is not None}
+    cw = _W(**{n: _p(wd.get(n)) for n in _WNAMES})
+    grads = {n: np.zeros_like(v) for n, v in wd.items()}
+    cg = _W(**{n: _p(grads.get(n)) for n in _WNAMES})
+    cs = _S(**{n: _p(getattr(saved, n)) for n in _SNAMES})
+    dx = np.empty((B, T, C))
+    c = _cfg(cfg)
+    lib().orc_block_backward(ctypes.byref(c), ctypes.byref(cw), _p(x), ctypes.byref(cs),
+                             _p(dy), _p(dx), ctypes.byref(cg))
+    return dx, grads
+
+
+def block_stack(cfg, layer_weights, x, dy):
+    """Forward through all layers, then backward.  Returns (y, dx, grads per
+    layer, saved per layer)."""
+    saved, xs = [], []
+    h = _d(x)
+    for w in layer_weights:
+        xs.append(h)
+        h, sv = block_forward(cfg, w, h)
+        saved.append(sv)
+    y = h
+    g = _d(dy)
+    grads = [None] * len(layer_weights)
+    for i in reversed(range(len(layer_weights))):
+        g, grads[i] = block_backward(cfg, layer_weights[i], xs[i], saved[i], g)
+    return y, g, grads, saved
