@@ -1,0 +1,176 @@
+"""ctypes binding of libdtb.so.  Argument marshalling only: every step of the
+block runs in the library's HIP kernels; torch supplies device memory and the
+current stream.  The library must be built (python -m
+decoder_only_transformer_block_amd.build); nothing here falls back to another
+implementation."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libdtb.so")
+
+DTB_OK = 0
+ERRORS = {-1: "DTB_EINVAL_SHAPE", -2: "DTB_EINVAL_PTR", -3: "DTB_EDTYPE", -4: "DTB_EINVAL_ENUM",
+          -5: "DTB_ELAUNCH"}
+DTYPE = {"f32": 0, "bf16": 1}
+NORM = {"rms": 0, "rms_nogamma": 1, "layer": 2}
+MLP = {"swiglu": 0, "relu": 1, "gelu_tanh": 2}
+ROPE = {"none": 0, "neox": 1}
+
+_VP = ctypes.c_void_p
+_WNAMES = ("g1", "b1", "wqkv", "bqkv", "wo", "bo", "g2", "b2", "w_up", "b_up", "w_down", "b_down")
+
+
+class BlockCfg(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in ("B", "T", "C", "NH", "NKV", "H", "norm", "mlp", "rope")] + [
+        ("rope_base", ctypes.c_float), ("eps", ctypes.c_float),
+        ("qkv_bias", ctypes.c_int), ("o_bias", ctypes.c_int), ("mlp_bias", ctypes.c_int),
+        ("dtype", ctypes.c_int)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in _WNAMES]
+
+
+class BlockGrads(ctypes.Structure):
+    _fields_ = [(n, _VP) for n in _WNAMES]
+
+
+class SavedLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_longlong) for n in
+                ("n1", "r1", "mu1", "qkv", "o", "lse", "x2", "n2", "r2", "mu2", "up", "h", "total")]
+
+
+class Timing(ctypes.Structure):
+    _fields_ = [("ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("launches", ctypes.c_longlong)]
+
+
+class DtbError(RuntimeError):
+    pass
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdtb.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise DtbError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decoder_only_transformer_block_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        i, v, f, z = ctypes.c_int, _VP, ctypes.c_float, ctypes.c_size_t
+        L.attn_forward.argtypes = [v, v, v, i, i, i, i, i, i, v]
+        L.attn_backward.argtypes = [v, v, v, v, v, i, i, i, i, i, i, v, v]
+        L.attn_workspace_bytes.argtypes = [i, i, i]
+        L.attn_workspace_bytes.restype = z
+        cp = ctypes.POINTER(BlockCfg)
+        L.block_saved_bytes.argtypes = [cp]
+        L.block_saved_bytes.restype = z
+        L.block_workspace_bytes.argtypes = [cp]
+        L.block_workspace_bytes.restype = z
+        L.block_saved_layout.argtypes = [cp, ctypes.POINTER(SavedLayout)]
+        L.block_forward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, v]
+        L.block_backward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, ctypes.POINTER(BlockGrads), v, v]
+        L.dtb_strerror.argtypes = [i]
+        L.dtb_strerror.restype = ctypes.c_char_p
+        L.dtb_version.restype = ctypes.c_char_p
+        L.dtb_timing_enable.argtypes = [i]
+        L.dtb_timing_collect.argtypes = [ctypes.POINTER(Timing), i]
+        _lib = L
+    return _lib
+
+
+def check(rc: int, what: str = "") -> None:
+    if rc != DTB_OK:
+        msg = lib().dtb_strerror(rc).decode()
+        raise DtbError(f"{what}: {ERRORS.get(rc, rc)}: {msg}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def make_cfg(c, B=None, T=None) -> BlockCfg:
+    """BlockCfg from any object with the workload attributes."""
+    return BlockCfg(B=c.B if B is None else B, T=c.T if T is None else T, C=c.C, NH=c.NH, NKV=c.NKV, H=c.H,
+                    norm=NORM[c.norm], mlp=MLP[c.mlp], rope=ROPE[c.rope], rope_base=float(c.rope_base),
+                    eps=float(c.eps), qkv_bias=int(c.qkv_bias), o_bias=int(c.o_bias),
+                    mlp_bias=int(c.mlp_bias), dtype=DTYPE[c.dtype])
+
+
+def weights_struct(w: dict) -> BlockWeights:
+    return BlockWeights(**{n: _ptr(w.get(n)) for n in _WNAMES})
+
+
+def grads_struct(g: dict) -> BlockGrads:
+    return BlockGrads(**{n: _ptr(g.get(n)) for n in _WNAMES})
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+def attn_forward(out, lse, qkv, B, T, C, NH, NKV, dtype, stream=None):
+    check(lib().attn_forward(_ptr(out), _ptr(lse), _ptr(qkv), B, T, C, NH, NKV, DTYPE[dtype], _stream(stream)),
+          "attn_forward")
+
+
+def attn_workspace_bytes(B, T, NH) -> int:
+    return lib().attn_workspace_bytes(B, T, NH)
+
+
+def attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, workspace, stream=None):
+    check(lib().attn_backward(_ptr(dqkv), _ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, T, C, NH, NKV,
+                              DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_backward")
+
+
+def block_saved_bytes(cfg: BlockCfg) -> int:
+    return lib().block_saved_bytes(ctypes.byref(cfg))
+
+
+def block_workspace_bytes(cfg: BlockCfg) -> int:
+    return lib().block_workspace_bytes(ctypes.byref(cfg))
+
+
+def block_saved_layout(cfg: BlockCfg) -> SavedLayout:
+    L = SavedLayout()
+    check(lib().block_saved_layout(ctypes.byref(cfg), ctypes.byref(L)), "block_saved_layout")
+    return L
+
+
+def block_forward(cfg: BlockCfg, weights: dict, x_in, x_out, saved, workspace, stream=None):
+    w = weights_struct(weights)
+    check(lib().block_forward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_in), _ptr(x_out), _ptr(saved),
+                              _ptr(workspace), _stream(stream)), "block_forward")
+
+
+def block_backward(cfg: BlockCfg, weights: dict, x_in, saved, dx_out, dx_in, grads: dict, workspace, stream=None):
+    w = weights_struct(weights)
+    g = grads_struct(grads)
+    check(lib().block_backward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_in), _ptr(saved), _ptr(dx_out),
+                               _ptr(dx_in), ctypes.byref(g), _ptr(workspace), _stream(stream)), "block_backward")
+
+
+def timing_enable(on: bool) -> None:
+    lib().dtb_timing_enable(int(on))
+
+
+def timing_collect():
+    arr = (Timing * 4)()
+    n = lib().dtb_timing_collect(arr, 4)
+    names = ["gemm", "attn_fwd", "attn_bwd", "elementwise"]
+    return {names[i]: {"ms": arr[i].ms, "flops": arr[i].flops, "bytes": arr[i].bytes,
+                       "launches": arr[i].launches} for i in range(n)}

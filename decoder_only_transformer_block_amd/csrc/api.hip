@@ -1,0 +1,435 @@
+// C ABI of libdtb: argument validation, buffer layouts and the launch
+// sequences of block_forward / block_backward / attn_forward / attn_backward.
+// Nothing here allocates device memory or synchronises the host (except the
+// opt-in measurement helper dtb_timing_collect).
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "common.h"
+
+namespace dtb {
+
+// ---------------------------------------------------------------- errors ---
+static thread_local char g_msg[256];
+
+int set_launch_error(hipError_t e, const char *what) {
+    snprintf(g_msg, sizeof g_msg, "kernel launch failed in %s: %s", what, hipGetErrorString(e));
+    return DTB_ELAUNCH;
+}
+
+// ---------------------------------------------------------------- timing ---
+bool g_timing_on = false;
+struct TRec {
+    hipEvent_t a, b;
+    int cls;
+    double flops, bytes;
+};
+static std::mutex g_tmu;
+static std::vector<TRec> g_trec;
+static std::vector<hipEvent_t> g_pool;
+static hipEvent_t g_pending = nullptr;
+static dtb_timing g_tot[K_NCLASS];
+
+static hipEvent_t ev_get() {
+    if (!g_pool.empty()) {
+        hipEvent_t e = g_pool.back();
+        g_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+void timing_begin(hipStream_t s) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_pending = ev_get();
+    if (g_pending) (void)hipEventRecord(g_pending, s);
+}
+
+void timing_end(hipStream_t s, int cls, double flops, double bytes) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (!g_pending) return;
+    hipEvent_t b = ev_get();
+    if (!b) return;
+    (void)hipEventRecord(b, s);
+    g_trec.push_back(TRec{g_pending, b, cls, flops, bytes});
+    g_pending = nullptr;
+}
+
+}  // namespace dtb
+
+using namespace dtb;
+
+extern "C" {
+
+const char *dtb_version(void) { return "dtb 0.1 gfx950"; }
+
+const char *dtb_strerror(int code) {
+    switch (code) {
+    case DTB_OK: return "ok";
+    case DTB_EINVAL_SHAPE: return "invalid shape (C % NH, NH % NKV, unsupported head width, C or H not a multiple of 8, negative size or overflow)";
+    case DTB_EINVAL_PTR: return "a required pointer is NULL or not 16-byte aligned";
+    case DTB_EDTYPE: return "dtype must be DTB_F32 or DTB_BF16";
+    case DTB_EINVAL_ENUM: return "unknown norm / mlp / rope selector";
+    case DTB_ELAUNCH: return g_msg[0] ? g_msg : "kernel launch failed";
+    default: return "unknown error code";
+    }
+}
+
+int dtb_timing_enable(int on) {
+    g_timing_on = on != 0;
+    return DTB_OK;
+}
+
+int dtb_timing_collect(dtb_timing *out, int max_classes) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    for (auto &r : g_trec) {
+        float ms = 0.f;
+        if (hipEventSynchronize(r.b) == hipSuccess && hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+            dtb_timing &t = g_tot[r.cls];
+            t.ms += ms;
+            t.flops += r.flops;
+            t.bytes += r.bytes;
+            t.launches += 1;
+        }
+        g_pool.push_back(r.a);
+        g_pool.push_back(r.b);
+    }
+    g_trec.clear();
+    int n = max_classes < K_NCLASS ? max_classes : K_NCLASS;
+    for (int i = 0; i < n; i++) out[i] = g_tot[i];
+    for (int i = 0; i < K_NCLASS; i++) g_tot[i] = dtb_timing{0, 0, 0, 0};
+    return n;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ validation ---
+static bool hd_ok(int hd, int dtype) {
+    if (dtype == DTB_BF16) return hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128;
+    return hd == 4 || hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128;
+}
+static bool aligned(const void *p) { return ((uintptr_t)p & 15) == 0; }
+static bool ptr_ok(const void *p) { return p && aligned(p); }
+
+static int check_attn_shape(int B, int T, int C, int NH, int NKV, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (B < 0 || T < 0 || C <= 0 || NH <= 0 || NKV <= 0) return DTB_EINVAL_SHAPE;
+    if (C % NH || NH % NKV) return DTB_EINVAL_SHAPE;
+    if (!hd_ok(C / NH, dtype)) return DTB_EINVAL_SHAPE;
+    long long QKV = (long long)C + 2LL * NKV * (C / NH);
+    if ((long long)B * T * QKV >= (1LL << 40) || (long long)B * T >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+struct Dims {
+    long long BT;
+    int hd, QKV, W, es;
+};
+
+static int check_cfg(const dtb_block_cfg *c, Dims *d) {
+    if (!c) return DTB_EINVAL_PTR;
+    int e = check_attn_shape(c->B, c->T, c->C, c->NH, c->NKV, c->dtype);
+    if (e) return e;
+    if (c->norm < 0 || c->norm > 2 || c->mlp < 0 || c->mlp > 2 || c->rope < 0 || c->rope > 1)
+        return DTB_EINVAL_ENUM;
+    if (c->H <= 0 || c->H % 8 || c->C % 8) return DTB_EINVAL_SHAPE;
+    if (c->C > (c->dtype == DTB_BF16 ? 8192 : 4096)) return DTB_EINVAL_SHAPE;
+    if (!(c->eps > 0.f)) return DTB_EINVAL_SHAPE;
+    if (c->rope == DTB_ROPE_NEOX && !(c->rope_base > 0.f)) return DTB_EINVAL_SHAPE;
+    d->BT = (long long)c->B * c->T;
+    d->hd = c->C / c->NH;
+    d->QKV = c->C + 2 * c->NKV * d->hd;
+    d->W = c->mlp == DTB_MLP_SWIGLU ? 2 * c->H : c->H;
+    d->es = c->dtype == DTB_BF16 ? 2 : 4;
+    if (d->BT * (long long)(d->W > d->QKV ? d->W : d->QKV) >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+static size_t al(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static void saved_layout(const dtb_block_cfg *c, const Dims &d, dtb_saved_layout *L) {
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        long long r = (long long)o;
+        o += al(bytes);
+        return r;
+    };
+    bool ln = c->norm == DTB_NORM_LAYER;
+    L->n1 = take((size_t)d.BT * c->C * d.es);
+    L->r1 = take((size_t)d.BT * 4);
+    L->mu1 = ln ? take((size_t)d.BT * 4) : -1;
+    L->qkv = take((size_t)d.BT * d.QKV * d.es);
+    L->o = take((size_t)d.BT * c->C * d.es);
+    L->lse = take((size_t)c->B * c->NH * c->T * 4);
+    L->x2 = take((size_t)d.BT * c->C * d.es);
+    L->n2 = take((size_t)d.BT * c->C * d.es);
+    L->r2 = take((size_t)d.BT * 4);
+    L->mu2 = ln ? take((size_t)d.BT * 4) : -1;
+    L->up = take((size_t)d.BT * d.W * d.es);
+    L->h = take((size_t)d.BT * c->H * d.es);
+    L->total = (long long)o;
+}
+
+struct WsLayout {
+    size_t cs, dh, dup, dn2, dx2, dO, dqkv, dn1, D, npart, bpart, gemm, total;
+    int nparts, bparts;
+    size_t gemm_bytes;
+};
+
+static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t r = o;
+        o += al(bytes);
+        return r;
+    };
+    W->cs = take((size_t)c->T * (d.hd / 2) * 8);
+    W->dh = take((size_t)d.BT * c->H * d.es);
+    W->dup = take((size_t)d.BT * d.W * d.es);
+    W->dn2 = take((size_t)d.BT * c->C * d.es);
+    W->dx2 = take((size_t)d.BT * c->C * d.es);
+    W->dO = take((size_t)d.BT * c->C * d.es);
+    W->dqkv = take((size_t)d.BT * d.QKV * d.es);
+    W->dn1 = take((size_t)d.BT * c->C * d.es);
+    W->D = take((size_t)c->B * c->NH * c->T * 4);
+    W->nparts = norm_backward_parts(d.BT);
+    W->npart = take((size_t)W->nparts * 2 * c->C * 4);
+    W->bparts = bias_grad_parts(d.BT);
+    int maxn = d.QKV > d.W ? d.QKV : d.W;
+    if (c->C > maxn) maxn = c->C;
+    W->bpart = take((size_t)W->bparts * maxn * 4);
+    int BT = (int)d.BT;
+    size_t g = 0, t;
+    t = gemm_ws_bytes(c->C, c->H, BT, c->dtype); if (t > g) g = t;
+    t = gemm_ws_bytes(d.W, c->C, BT, c->dtype); if (t > g) g = t;
+    t = gemm_ws_bytes(c->C, c->C, BT, c->dtype); if (t > g) g = t;
+    t = gemm_ws_bytes(d.QKV, c->C, BT, c->dtype); if (t > g) g = t;
+    W->gemm_bytes = g;
+    W->gemm = take(g);
+    W->total = o;
+}
+
+extern "C" {
+
+size_t block_saved_bytes(const dtb_block_cfg *cfg) {
+    Dims d;
+    if (check_cfg(cfg, &d)) return 0;
+    dtb_saved_layout L;
+    saved_layout(cfg, d, &L);
+    return (size_t)L.total;
+}
+
+int block_saved_layout(const dtb_block_cfg *cfg, dtb_saved_layout *layout) {
+    Dims d;
+    int e = check_cfg(cfg, &d);
+    if (e) return e;
+    if (!layout) return DTB_EINVAL_PTR;
+    saved_layout(cfg, d, layout);
+    return DTB_OK;
+}
+
+size_t block_workspace_bytes(const dtb_block_cfg *cfg) {
+    Dims d;
+    if (check_cfg(cfg, &d)) return 0;
+    WsLayout W;
+    ws_layout(cfg, d, &W);
+    return W.total;
+}
+
+size_t attn_workspace_bytes(int B, int T, int NH) {
+    if (B < 0 || T < 0 || NH <= 0) return 0;
+    size_t n = (size_t)B * T * NH * 4;
+    return n ? al(n) : 256;
+}
+
+int attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV, int dtype,
+                 void *stream) {
+    int e = check_attn_shape(B, T, C, NH, NKV, dtype);
+    if (e) return e;
+    if ((long long)B * T == 0) return DTB_OK;
+    if (!ptr_ok(out) || !ptr_ok(lse) || !ptr_ok(qkv)) return DTB_EINVAL_PTR;
+    return launch_attn_forward(out, lse, qkv, B, T, C, NH, NKV, dtype, (hipStream_t)stream);
+}
+
+int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout, const float *lse, int B, int T,
+                  int C, int NH, int NKV, int dtype, void *workspace, void *stream) {
+    int e = check_attn_shape(B, T, C, NH, NKV, dtype);
+    if (e) return e;
+    if ((long long)B * T == 0) return DTB_OK;
+    if (!ptr_ok(dqkv) || !ptr_ok(qkv) || !ptr_ok(out) || !ptr_ok(dout) || !ptr_ok(lse) || !ptr_ok(workspace))
+        return DTB_EINVAL_PTR;
+    return launch_attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, (float *)workspace,
+                                (hipStream_t)stream);
+}
+
+static int check_weights(const dtb_block_cfg *c, const dtb_block_weights *w) {
+    if (!w) return DTB_EINVAL_PTR;
+    if (!ptr_ok(w->wqkv) || !ptr_ok(w->wo) || !ptr_ok(w->w_up) || !ptr_ok(w->w_down)) return DTB_EINVAL_PTR;
+    if (c->norm != DTB_NORM_RMS_NOGAMMA && (!ptr_ok(w->g1) || !ptr_ok(w->g2))) return DTB_EINVAL_PTR;
+    if (c->norm == DTB_NORM_LAYER && (!ptr_ok(w->b1) || !ptr_ok(w->b2))) return DTB_EINVAL_PTR;
+    if (c->qkv_bias && !ptr_ok(w->bqkv)) return DTB_EINVAL_PTR;
+    if (c->o_bias && !ptr_ok(w->bo)) return DTB_EINVAL_PTR;
+    if (c->mlp_bias && (!ptr_ok(w->b_up) || !ptr_ok(w->b_down))) return DTB_EINVAL_PTR;
+    return DTB_OK;
+}
+
+static int check_grads(const dtb_block_cfg *c, const dtb_block_grads *g) {
+    if (!g) return DTB_EINVAL_PTR;
+    if (!ptr_ok(g->wqkv) || !ptr_ok(g->wo) || !ptr_ok(g->w_up) || !ptr_ok(g->w_down)) return DTB_EINVAL_PTR;
+    if (c->norm != DTB_NORM_RMS_NOGAMMA && (!ptr_ok(g->g1) || !ptr_ok(g->g2))) return DTB_EINVAL_PTR;
+    if (c->norm == DTB_NORM_LAYER && (!ptr_ok(g->b1) || !ptr_ok(g->b2))) return DTB_EINVAL_PTR;
+    if (c->qkv_bias && !ptr_ok(g->bqkv)) return DTB_EINVAL_PTR;
+    if (c->o_bias && !ptr_ok(g->bo)) return DTB_EINVAL_PTR;
+    if (c->mlp_bias && (!ptr_ok(g->b_up) || !ptr_ok(g->b_down))) return DTB_EINVAL_PTR;
+    return DTB_OK;
+}
+
+#define TRY(x)                  \
+    do {                        \
+        int _r = (x);           \
+        if (_r) return _r;      \
+    } while (0)
+
+int block_forward(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in, void *x_out, void *saved,
+                  void *workspace, void *stream) {
+    Dims d;
+    TRY(check_cfg(c, &d));
+    if (d.BT == 0) return DTB_OK;
+    TRY(check_weights(c, w));
+    if (!ptr_ok(x_in) || !ptr_ok(x_out) || !ptr_ok(saved) || !ptr_ok(workspace)) return DTB_EINVAL_PTR;
+    hipStream_t s = (hipStream_t)stream;
+    dtb_saved_layout L;
+    saved_layout(c, d, &L);
+    WsLayout W;
+    ws_layout(c, d, &W);
+    char *sv = (char *)saved, *ws = (char *)workspace;
+    const int C = c->C, H = c->H, BT = (int)d.BT, dt = c->dtype;
+    void *n1 = sv + L.n1, *qkv = sv + L.qkv, *o = sv + L.o, *x2 = sv + L.x2, *n2 = sv + L.n2, *up = sv + L.up,
+         *h = sv + L.h;
+    float *r1 = (float *)(sv + L.r1), *r2 = (float *)(sv + L.r2);
+    float *mu1 = L.mu1 >= 0 ? (float *)(sv + L.mu1) : nullptr, *mu2 = L.mu2 >= 0 ? (float *)(sv + L.mu2) : nullptr;
+    float *lse = (float *)(sv + L.lse);
+
+    TRY(norm_forward(c->norm, dt, x_in, w->g1, w->b1, c->eps, BT, C, n1, r1, mu1, s));
+    GemmArgs g{};
+    g.dtype = dt;
+    g.a_kmajor = g.b_kmajor = true;
+    // qkv = n1 Wqkv^T + bqkv
+    g.A = n1; g.lda = C; g.B = w->wqkv; g.ldb = C; g.M = BT; g.N = d.QKV; g.K = C;
+    g.out = qkv; g.ldo = d.QKV; g.bias = c->qkv_bias ? w->bqkv : nullptr; g.res = nullptr;
+    TRY(gemm(g, nullptr, 0, s));
+    if (c->rope == DTB_ROPE_NEOX) {
+        float *cs = (float *)(ws + W.cs);
+        TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
+        TRY(rope_apply(dt, qkv, cs, c->B, c->T, d.QKV, c->NH, c->NKV, d.hd, 0, s));
+    }
+    TRY(launch_attn_forward(o, lse, qkv, c->B, c->T, C, c->NH, c->NKV, dt, s));
+    // x2 = x + o Wo^T + bo
+    g.A = o; g.lda = C; g.B = w->wo; g.ldb = C; g.M = BT; g.N = C; g.K = C;
+    g.out = x2; g.ldo = C; g.bias = c->o_bias ? w->bo : nullptr; g.res = x_in; g.ldr = C;
+    TRY(gemm(g, nullptr, 0, s));
+    TRY(norm_forward(c->norm, dt, x2, w->g2, w->b2, c->eps, BT, C, n2, r2, mu2, s));
+    // up = n2 Wup^T + bup
+    g.A = n2; g.lda = C; g.B = w->w_up; g.ldb = C; g.M = BT; g.N = d.W; g.K = C;
+    g.out = up; g.ldo = d.W; g.bias = c->mlp_bias ? w->b_up : nullptr; g.res = nullptr;
+    TRY(gemm(g, nullptr, 0, s));
+    TRY(act_forward(c->mlp, dt, up, BT, H, h, s));
+    // x_out = x2 + h Wdown^T + bdown
+    g.A = h; g.lda = H; g.B = w->w_down; g.ldb = H; g.M = BT; g.N = C; g.K = H;
+    g.out = x_out; g.ldo = C; g.bias = c->mlp_bias ? w->b_down : nullptr; g.res = x2; g.ldr = C;
+    TRY(gemm(g, nullptr, 0, s));
+    return DTB_OK;
+}
+
+int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in, const void *saved,
+                   const void *dx_out, void *dx_in, const dtb_block_grads *gr, void *workspace, void *stream) {
+    Dims d;
+    TRY(check_cfg(c, &d));
+    if (d.BT == 0) return DTB_OK;
+    TRY(check_weights(c, w));
+    TRY(check_grads(c, gr));
+    if (!ptr_ok(x_in) || !ptr_ok(saved) || !ptr_ok(dx_out) || !ptr_ok(dx_in) || !ptr_ok(workspace))
+        return DTB_EINVAL_PTR;
+    hipStream_t s = (hipStream_t)stream;
+    dtb_saved_layout L;
+    saved_layout(c, d, &L);
+    WsLayout W;
+    ws_layout(c, d, &W);
+    const char *sv = (const char *)saved;
+    char *ws = (char *)workspace;
+    const int C = c->C, H = c->H, BT = (int)d.BT, dt = c->dtype;
+    const void *n1 = sv + L.n1, *qkv = sv + L.qkv, *o = sv + L.o, *x2 = sv + L.x2, *n2 = sv + L.n2,
+               *up = sv + L.up, *h = sv + L.h;
+    const float *r1 = (const float *)(sv + L.r1), *r2 = (const float *)(sv + L.r2);
+    const float *mu1 = L.mu1 >= 0 ? (const float *)(sv + L.mu1) : nullptr;
+    const float *mu2 = L.mu2 >= 0 ? (const float *)(sv + L.mu2) : nullptr;
+    const float *lse = (const float *)(sv + L.lse);
+    void *dh = ws + W.dh, *dup = ws + W.dup, *dn2 = ws + W.dn2, *dx2 = ws + W.dx2, *dO = ws + W.dO,
+         *dqkv = ws + W.dqkv, *dn1 = ws + W.dn1;
+    float *Dbuf = (float *)(ws + W.D), *npart = (float *)(ws + W.npart), *bpart = (float *)(ws + W.bpart);
+    void *gws = ws + W.gemm;
+    const void *dy = dx_out;
+
+    GemmArgs dinp{};
+    dinp.dtype = dt;
+    dinp.a_kmajor = true;
+    dinp.b_kmajor = false;
+    GemmArgs dw{};
+    dw.dtype = dt;
+    dw.a_kmajor = false;
+    dw.b_kmajor = false;
+    dw.out_f32 = true;
+    dw.accumulate = true;
+
+    // down projection: dh = dy Wdown; dWdown += dy^T h; db_down
+    dinp.A = dy; dinp.lda = C; dinp.B = w->w_down; dinp.ldb = H; dinp.M = BT; dinp.N = H; dinp.K = C;
+    dinp.out = dh; dinp.ldo = H;
+    TRY(gemm(dinp, nullptr, 0, s));
+    dw.A = dy; dw.lda = C; dw.B = h; dw.ldb = H; dw.M = C; dw.N = H; dw.K = BT; dw.out = gr->w_down; dw.ldo = H;
+    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    if (c->mlp_bias) TRY(bias_grad(dt, dy, BT, C, gr->b_down, bpart, W.bparts, s));
+    // activation
+    TRY(act_backward(c->mlp, dt, dh, up, BT, H, dup, s));
+    // up projection: dn2 = dup Wup; dWup += dup^T n2
+    dinp.A = dup; dinp.lda = d.W; dinp.B = w->w_up; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.W;
+    dinp.out = dn2; dinp.ldo = C;
+    TRY(gemm(dinp, nullptr, 0, s));
+    dw.A = dup; dw.lda = d.W; dw.B = n2; dw.ldb = C; dw.M = d.W; dw.N = C; dw.K = BT; dw.out = gr->w_up; dw.ldo = C;
+    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    if (c->mlp_bias) TRY(bias_grad(dt, dup, BT, d.W, gr->b_up, bpart, W.bparts, s));
+    // norm2 backward + residual: dx2 = dy + Norm2^T(dn2)
+    TRY(norm_backward(c->norm, dt, dn2, x2, w->g2, r2, mu2, dy, BT, C, dx2, gr->g2, gr->b2, npart, W.nparts, s));
+    // output projection: dO = dx2 Wo; dWo += dx2^T o
+    dinp.A = dx2; dinp.lda = C; dinp.B = w->wo; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = C;
+    dinp.out = dO; dinp.ldo = C;
+    TRY(gemm(dinp, nullptr, 0, s));
+    dw.A = dx2; dw.lda = C; dw.B = o; dw.ldb = C; dw.M = C; dw.N = C; dw.K = BT; dw.out = gr->wo; dw.ldo = C;
+    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    if (c->o_bias) TRY(bias_grad(dt, dx2, BT, C, gr->bo, bpart, W.bparts, s));
+    // attention
+    TRY(launch_attn_backward(dqkv, qkv, o, dO, lse, c->B, c->T, C, c->NH, c->NKV, dt, Dbuf, s));
+    if (c->rope == DTB_ROPE_NEOX) {
+        float *cs = (float *)(ws + W.cs);
+        TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
+        TRY(rope_apply(dt, dqkv, cs, c->B, c->T, d.QKV, c->NH, c->NKV, d.hd, 1, s));
+    }
+    // qkv projection: dn1 = dqkv Wqkv; dWqkv += dqkv^T n1
+    dinp.A = dqkv; dinp.lda = d.QKV; dinp.B = w->wqkv; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.QKV;
+    dinp.out = dn1; dinp.ldo = C;
+    TRY(gemm(dinp, nullptr, 0, s));
+    dw.A = dqkv; dw.lda = d.QKV; dw.B = n1; dw.ldb = C; dw.M = d.QKV; dw.N = C; dw.K = BT; dw.out = gr->wqkv;
+    dw.ldo = C;
+    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    if (c->qkv_bias) TRY(bias_grad(dt, dqkv, BT, d.QKV, gr->bqkv, bpart, W.bparts, s));
+    // norm1 backward + residual: dx_in = dx2 + Norm1^T(dn1)
+    TRY(norm_backward(c->norm, dt, dn1, x_in, w->g1, r1, mu1, dx2, BT, C, dx_in, gr->g1, gr->b1, npart, W.nparts,
+                      s));
+    return DTB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,806 @@
+// Causal grouped-query flash attention, forward and backward, for gfx950.
+//
+// What is computed ("nanoeuler — CUDA kernels": the flash_attn_forward_kernel /
+// flash_attn_backward_kernel declarations and the attention_cpu_fwd/bwd
+// definitions; "microgpt.cu": attention_backward's dS = P (dP - sum P dP)):
+//   s_tj = q_t.k_j / sqrt(hd) (j <= t), o_t = softmax(s_t) V, lse_t = logsumexp_j s_tj,
+//   backward with P_tj = exp(s_tj - lse_t), D_t = dO_t.o_t, dS = P (dO V^T - D).
+// Query head h reads kv head h / (NH/NKV).
+//
+// Design (CDNA4, wave64, 32x32 MFMA blocks):
+// * Scores are computed transposed, S^T = K Q^T, so a lane owns one query
+//   (column l%32) and 16 keys (rows) of each 32x32 block: the running max and
+//   sum of the online softmax are in-register reductions plus one exchange
+//   with the partner lane l^32.  The same layout makes P^T (and dS^T) usable
+//   directly as the B operand of the next product: the k order of an MFMA is
+//   ours to choose as long as both operands use it, so lane half g feeds the
+//   keys its accumulators hold (8*(r/4) + 4g + r%4).
+// * The A operand of those products needs several keys of one head dimension
+//   per lane (V^T, K^T, Q^T, dO^T).  For bf16 the tile is staged a second time
+//   transposed in LDS (8x8 register transposes during staging, 8-byte slots
+//   XOR-swizzled with the row); for fp32 one element per lane is read from the
+//   natural tile.
+// * Natural tiles are rows of hd elements in 16-byte chunks, XOR-swizzled
+//   with (row & 7).  Two LDS stages; the next tile's global loads are issued
+//   before the current tile's MFMAs (one barrier per tile).  Half of the
+//   threads stage one tensor, the other half the other.
+// * forward: one workgroup = 4 waves x 32 queries of one (b, h), key tiles of
+//   64, last query blocks launched first (causal load balance).
+// * backward: D = rowsum(dO o) by a small kernel; dQ by a query-owning kernel
+//   (like the forward: S^T, dP^T = V dO^T, dQ^T += K^T dS^T); dK and dV by a
+//   key-owning kernel (4 waves x 32 keys of one (b, kv head)) that loops over
+//   the group's query heads and the query tiles at or after its keys
+//   (S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS), so dK/dV are
+//   summed over the group in registers -- no atomics, deterministic.
+#include <type_traits>
+
+#include "common.h"
+
+namespace dtb {
+
+template <typename T, int HD> struct AT {
+    static constexpr int ES = sizeof(T);
+    static constexpr int EPC = 16 / ES;                 // elements per 16-byte chunk
+    static constexpr int NCH = HD * ES / 16;            // chunks per natural row
+    static constexpr int NC = NCH / 2;                  // chunk pairs (MFMA steps)
+    static constexpr int RB = HD * ES;                  // natural row bytes
+    static constexpr int XM = (NCH < 8 ? NCH : 8) - 1;  // swizzle mask
+    static constexpr int ND = HD >= 32 ? HD / 32 : 1;   // 32-row blocks over hd
+};
+static constexpr bool is_bf16(int) { return false; }
+
+template <typename T, int HD> __device__ __forceinline__ int nat_off(int row, int chunk) {
+    return row * AT<T, HD>::RB + ((chunk ^ (row & AT<T, HD>::XM)) << 4);
+}
+// transposed bf16 tile: HD rows (head dim) x ROWS columns (keys or queries),
+// 8-byte slots of 4 columns, slot index XOR (row & (ROWS/4 - 1))
+template <int ROWS> __device__ __forceinline__ int tr_off(int d, int slot) {
+    return d * (ROWS * 2) + ((slot ^ (d & (ROWS / 4 - 1))) << 3);
+}
+
+// ---------------------------------------------------------------------------
+// staging helpers (a subset of NT threads, local id tl)
+// ---------------------------------------------------------------------------
+// natural [ROWS][HD] tile: chunk items
+template <typename T, int HD, int ROWS, int NT> struct Nat {
+    static constexpr int ITEMS = ROWS * AT<T, HD>::NCH;
+    static constexpr int P = (ITEMS + NT - 1) / NT;
+    __device__ static __forceinline__ void load(u32x4 *reg, const T *g, long long stride, int row0, int nrows,
+                                                int hd, int tl) {
+        constexpr int NCH = AT<T, HD>::NCH, EPC = AT<T, HD>::EPC;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int idx = tl + NT * p;
+            int r = idx / NCH, c = idx % NCH;
+            if (idx < ITEMS && row0 + r < nrows && c * EPC < hd)
+                reg[p] = ld16(g + (long long)(row0 + r) * stride + c * EPC);
+            else
+                reg[p] = u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ static __forceinline__ void store(const u32x4 *reg, char *lds, int tl) {
+        constexpr int NCH = AT<T, HD>::NCH;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int idx = tl + NT * p;
+            if (idx < ITEMS) *reinterpret_cast<u32x4 *>(lds + nat_off<T, HD>(idx / NCH, idx % NCH)) = reg[p];
+        }
+    }
+};
+
+// bf16 8x8 blocks of a [ROWS][HD] tile, stored natural and/or transposed
+template <int HD, int ROWS, int NT> struct Blk {
+    static constexpr int NBD = HD / 8, NBR = ROWS / 8;
+    static constexpr int ITEMS = NBD * NBR;
+    static constexpr int P = (ITEMS + NT - 1) / NT;
+    __device__ static __forceinline__ void load(u32x4 (*reg)[8], const bf16 *g, long long stride, int row0,
+                                                int nrows, int hd, int tl) {
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int idx = tl + NT * p;
+            int db = idx % NBD, rb = idx / NBD;
+            bool live = idx < ITEMS && db * 8 < hd;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                int row = row0 + rb * 8 + i;
+                if (live && row < nrows) reg[p][i] = ld16(g + (long long)row * stride + db * 8);
+                else reg[p][i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+    template <bool NAT, bool TR>
+    __device__ static __forceinline__ void store(const u32x4 (*reg)[8], char *nat, char *tr, int tl) {
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int idx = tl + NT * p;
+            if (idx >= ITEMS) continue;
+            int db = idx % NBD, rb = idx / NBD;
+            if constexpr (NAT) {
+#pragma unroll
+                for (int i = 0; i < 8; i++)
+                    *reinterpret_cast<u32x4 *>(nat + nat_off<bf16, HD>(rb * 8 + i, db)) = reg[p][i];
+            }
+            if constexpr (TR) {
+                u32x4 o[8];
+                transpose8x8(reg[p], o);
+#pragma unroll
+                for (int j = 0; j < 8; j++) {
+                    int d = db * 8 + j;
+                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS>(d, 2 * rb)) = u32x2{o[j][0], o[j][1]};
+                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS>(d, 2 * rb + 1)) = u32x2{o[j][2], o[j][3]};
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// fragment helpers
+// ---------------------------------------------------------------------------
+// A operand "transposed": lane (d = l%32 + 32*db, half g) supplies the keys that
+// accumulator registers r0..r0+7 (bf16) / r (fp32) of an S^T-layout block hold.
+// bf16: keys koff + {0..3} and koff + 8 + {0..3}, koff = j*32 + 16*hh + 4g, read
+// from the transposed tile; zero for d >= HD.
+template <int HD, int ROWS>
+__device__ __forceinline__ bf16x8 tr_frag(const char *tr, int d, int koff) {
+    if (HD < 32 && d >= HD) return bf16x8{};
+    u32x2 a = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS>(d, koff >> 2));
+    u32x2 b = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS>(d, (koff >> 2) + 2));
+    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+// fp32: element (row, d) of a natural tile
+template <int HD> __device__ __forceinline__ float nat_elem(const char *nat, int row, int d) {
+    if (HD < 32 && d >= HD) return 0.f;
+    return *reinterpret_cast<const float *>(nat + nat_off<float, HD>(row, d >> 2) + ((d & 3) << 2));
+}
+
+// acc_o (ND blocks over head dim, columns = the lane's query/key) +=
+//   A^T (HD x 32 positions of block j) * X (32 positions x 32 columns), with X in
+// S^T-layout registers x (one 32x32 block) and A^T read from LDS.
+template <typename T, int HD, int ROWS>
+__device__ __forceinline__ void mma_trans(f32x16 *acc, const f32x16 &x, const char *tile, int j, int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+    if constexpr (std::is_same<T, bf16>::value) {
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++) {
+            bf16x8 xb;
+#pragma unroll
+            for (int e = 0; e < 8; e++) xb[e] = (bf16)x[8 * hh + e];
+            const int koff = j * 32 + 16 * hh + 4 * g;
+#pragma unroll
+            for (int db = 0; db < AT<T, HD>::ND; db++)
+                acc[db] = mfma32(tr_frag<HD, ROWS>(tile, db * 32 + l32, koff), xb, acc[db]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; r++) {
+            const int row = j * 32 + acc_row(r, lane);
+#pragma unroll
+            for (int db = 0; db < AT<T, HD>::ND; db++)
+                acc[db] = mfma32(nat_elem<HD>(tile, row, db * 32 + l32), x[r], acc[db]);
+        }
+    }
+}
+
+// S-block (32 rows of `tile` x 32 columns given by per-lane fragments frag[c]):
+// acc += tile[rows j*32 .. +32] . frag^T over the head dimension
+template <typename T, int HD>
+__device__ __forceinline__ void mma_rows(f32x16 &acc, const char *tile, int rowbase, const u32x4 *frag, int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int c = 0; c < AT<T, HD>::NC; c++) {
+        u32x4 a = *reinterpret_cast<const u32x4 *>(tile + nat_off<T, HD>(rowbase + l32, 2 * c + g));
+        mma_chunk(acc, a, frag[c], T());
+    }
+}
+
+// per-lane fragments of one row: chunks 2c+g
+template <typename T, int HD>
+__device__ __forceinline__ void load_row_frag(u32x4 *f, const T *row, bool valid, int hd, int g) {
+#pragma unroll
+    for (int c = 0; c < AT<T, HD>::NC; c++) {
+        int ch = 2 * c + g;
+        f[c] = (valid && ch * AT<T, HD>::EPC < hd) ? ld16(row + ch * AT<T, HD>::EPC) : u32x4{0, 0, 0, 0};
+    }
+}
+
+// write ND accumulator blocks (lane = row position, regs = head dim) scaled by s
+template <typename T, int HD>
+__device__ __forceinline__ void store_rows(T *row, const f32x16 *acc, float s, int hd, int lane) {
+#pragma unroll
+    for (int db = 0; db < AT<T, HD>::ND; db++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+            int d = db * 32 + 8 * r4 + 4 * (lane >> 5);
+            if (d < hd) {
+                if constexpr (std::is_same<T, bf16>::value) {
+                    u32x2 v{pack_bf16x2(acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s),
+                            pack_bf16x2(acc[db][4 * r4 + 2] * s, acc[db][4 * r4 + 3] * s)};
+                    *reinterpret_cast<u32x2 *>(row + d) = v;
+                } else {
+                    f32x4 v{acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s, acc[db][4 * r4 + 2] * s,
+                            acc[db][4 * r4 + 3] * s};
+                    *reinterpret_cast<f32x4 *>(row + d) = v;
+                }
+            }
+        }
+}
+
+struct AttnP {
+    const void *qkv;
+    const void *out;
+    const void *dout;
+    void *o;        // forward output / dqkv for the backward
+    float *lse;     // forward output
+    const float *lse_in;
+    const float *D;
+    int B, T, C, NH, NKV, hd, QKV;
+    float sl2;      // log2(e) / sqrt(hd)
+    float scale;    // 1 / sqrt(hd)
+};
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+// ---------------------------------------------------------------------------
+// forward
+// ---------------------------------------------------------------------------
+template <typename T, int HD> struct FwdCfg {
+    static constexpr int BQ = 128, BKV = 64;
+    static constexpr int KB = BKV * HD * (int)sizeof(T);  // K natural tile bytes (= V tile bytes)
+    static constexpr int STAGE = 2 * KB;
+    // staging: K natural by threads [128, 256); V by [0, 128) (transposed bf16 / natural fp32)
+    static constexpr int PK = Nat<T, HD, BKV, 128>::P;
+    static constexpr int PV = std::is_same<T, bf16>::value ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
+    static constexpr int PREG = PK > PV ? PK : PV;
+};
+
+template <typename T, int HD>
+__device__ __forceinline__ void fwd_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
+                                               int T_, int hd) {
+    const int t = threadIdx.x;
+    if (t >= 128) {
+        Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t - 128);
+    } else {
+        if constexpr (std::is_same<T, bf16>::value)
+            Blk<HD, 64, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), vb, stride, kv0, T_, hd, t);
+        else
+            Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t);
+    }
+}
+template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(const u32x4 *reg, char *st) {
+    const int t = threadIdx.x;
+    constexpr int KB = FwdCfg<T, HD>::KB;
+    if (t >= 128) {
+        Nat<T, HD, 64, 128>::store(reg, st, t - 128);
+    } else {
+        if constexpr (std::is_same<T, bf16>::value)
+            Blk<HD, 64, 128>::template store<false, true>(reinterpret_cast<const u32x4(*)[8]>(reg), nullptr,
+                                                         st + KB, t);
+        else
+            Nat<T, HD, 64, 128>::store(reg, st + KB, t);
+    }
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
+    using A = AT<T, HD>;
+    using FC = FwdCfg<T, HD>;
+    constexpr int BQ = FC::BQ, BKV = FC::BKV;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int nqb = (p.T + BQ - 1) / BQ;
+    const int BH = p.B * p.NH;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+    const int bh = blockIdx.x % BH;
+    const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+    const long long stride = p.QKV;
+    const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
+    const T *kbase = base + p.C + kh * p.hd;
+    const T *vbase = kbase + p.NKV * p.hd;
+
+    u32x4 qf[A::NC];
+    load_row_frag<T, HD>(qf, base + (long long)qi * stride + h * p.hd, qi < p.T, p.hd, g);
+
+    f32x16 O[A::ND];
+#pragma unroll
+    for (int d = 0; d < A::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) O[d][r] = 0.f;
+    float m = -1e30f, lsum = 0.f;
+
+    const int kv_end = min(p.T, q0 + BQ);
+    const int ntiles = (kv_end + BKV - 1) / BKV;
+    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
+
+    u32x4 reg[FC::PREG];
+    fwd_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
+    fwd_stage_store<T, HD>(reg, smem);
+    __syncthreads();
+
+    for (int kt = 0; kt < ntiles; kt++) {
+        const bool more = kt + 1 < ntiles;
+        if (more) fwd_stage_load<T, HD>(reg, kbase, vbase, stride, (kt + 1) * BKV, p.T, p.hd);
+        const char *Ks = smem + (kt & 1) * FC::STAGE;
+        const char *Vs = Ks + FC::KB;
+        if (kt < wtiles) {
+            const int kv0 = kt * BKV;
+            f32x16 S[2];
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+#pragma unroll
+                for (int r = 0; r < 16; r++) S[j][r] = 0.f;
+                mma_rows<T, HD>(S[j], Ks, j * 32, qf, lane);
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    int key = kv0 + j * 32 + acc_row(r, lane);
+                    float x = key <= qi ? S[j][r] * p.sl2 : -INFINITY;
+                    S[j][r] = x;
+                    mt = fmaxf(mt, x);
+                }
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+            const float mn = fmaxf(m, mt);
+            const float alpha = exp2f(m - mn);
+            m = mn;
+            lsum *= alpha;
+#pragma unroll
+            for (int d = 0; d < A::ND; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) O[d][r] *= alpha;
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    float e = exp2f(S[j][r] - mn);
+                    S[j][r] = e;
+                    lsum += e;
+                }
+#pragma unroll
+            for (int j = 0; j < 2; j++) mma_trans<T, HD, BKV>(O, S[j], Vs, j, lane);
+        }
+        if (more) fwd_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
+        __syncthreads();
+    }
+
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (qi < p.T) {
+        T *orow = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + qi) * p.C + h * p.hd;
+        store_rows<T, HD>(orow, O, 1.f / ltot, p.hd, lane);
+        if (g == 0) p.lse[((long long)b * p.NH + h) * p.T + qi] = (m + log2f(ltot)) * LN2;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward: D = rowsum(dO * O)   [B][NH][T] fp32, one wave per (b, t) row
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
+    const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= (long long)p.B * p.T) return;
+    const int b = (int)(row / p.T), tq = (int)(row % p.T);
+    const T *o = reinterpret_cast<const T *>(p.out) + row * p.C;
+    const T *d = reinterpret_cast<const T *>(p.dout) + row * p.C;
+    constexpr int EPC = 16 / sizeof(T);
+    const int hd = p.hd;
+    // lanes sweep the row in 16-byte chunks; a head spans hd/EPC chunks
+    const int nch = p.C / EPC, hch = hd / EPC;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+        int c = c0 + lane;
+        float s = 0.f;
+        if (c < nch) {
+            float fo[EPC], fd[EPC];
+            unpack16<T>(ld16(o + c * EPC), fo);
+            unpack16<T>(ld16(d + c * EPC), fd);
+#pragma unroll
+            for (int e = 0; e < EPC; e++) s += fo[e] * fd[e];
+        }
+        // reduce over the hch consecutive lanes of each head (hch is a power of 2)
+        for (int off = 1; off < hch && off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+        if (hch > 64) {
+            // head wider than one sweep: not reached for hd <= 128 (hch <= 32)
+        }
+        if (c < nch && (c % hch) == 0) {
+            int h = c / hch;
+            D[((long long)b * p.NH + h) * p.T + tq] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward: dQ (query-owning)
+// ---------------------------------------------------------------------------
+template <typename T, int HD> struct DqCfg {
+    static constexpr int BQ = 128, BKV = 64;
+    static constexpr int KB = BKV * HD * (int)sizeof(T);
+    static constexpr bool BF = std::is_same<T, bf16>::value;
+    // LDS stage: K natural, V natural, (bf16) K transposed
+    static constexpr int STAGE = (BF ? 3 : 2) * KB;
+    static constexpr int PK = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
+    static constexpr int PV = Nat<T, HD, BKV, 128>::P;
+    static constexpr int PREG = PK > PV ? PK : PV;
+};
+
+template <typename T, int HD>
+__device__ __forceinline__ void dq_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
+                                              int T_, int hd) {
+    const int t = threadIdx.x;
+    if (t < 128) {
+        if constexpr (std::is_same<T, bf16>::value)
+            Blk<HD, 64, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), kb, stride, kv0, T_, hd, t);
+        else
+            Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t);
+    } else {
+        Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t - 128);
+    }
+}
+template <typename T, int HD> __device__ __forceinline__ void dq_stage_store(const u32x4 *reg, char *st) {
+    const int t = threadIdx.x;
+    constexpr int KB = DqCfg<T, HD>::KB;
+    if (t < 128) {
+        if constexpr (std::is_same<T, bf16>::value)
+            Blk<HD, 64, 128>::template store<true, true>(reinterpret_cast<const u32x4(*)[8]>(reg), st,
+                                                        st + 2 * KB, t);
+        else
+            Nat<T, HD, 64, 128>::store(reg, st, t);
+    } else {
+        Nat<T, HD, 64, 128>::store(reg, st + KB, t - 128);
+    }
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
+    using A = AT<T, HD>;
+    using FC = DqCfg<T, HD>;
+    constexpr int BQ = FC::BQ, BKV = FC::BKV;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int nqb = (p.T + BQ - 1) / BQ;
+    const int BH = p.B * p.NH;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH);
+    const int bh = blockIdx.x % BH;
+    const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+
+    const long long stride = p.QKV;
+    const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
+    const T *kbase = base + p.C + kh * p.hd;
+    const T *vbase = kbase + p.NKV * p.hd;
+
+    u32x4 qf[A::NC], df[A::NC];
+    load_row_frag<T, HD>(qf, base + (long long)qi * stride + h * p.hd, qi < p.T, p.hd, g);
+    load_row_frag<T, HD>(df, reinterpret_cast<const T *>(p.dout) + ((long long)b * p.T + qi) * p.C + h * p.hd,
+                         qi < p.T, p.hd, g);
+    const long long li = ((long long)b * p.NH + h) * p.T + qi;
+    const float lse2 = qi < p.T ? p.lse_in[li] * LOG2E : INFINITY;
+    const float Dq = qi < p.T ? p.D[li] : 0.f;
+
+    f32x16 dQ[A::ND];
+#pragma unroll
+    for (int d = 0; d < A::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) dQ[d][r] = 0.f;
+
+    const int kv_end = min(p.T, q0 + BQ);
+    const int ntiles = (kv_end + BKV - 1) / BKV;
+    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
+
+    u32x4 reg[FC::PREG];
+    dq_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
+    dq_stage_store<T, HD>(reg, smem);
+    __syncthreads();
+
+    for (int kt = 0; kt < ntiles; kt++) {
+        const bool more = kt + 1 < ntiles;
+        if (more) dq_stage_load<T, HD>(reg, kbase, vbase, stride, (kt + 1) * BKV, p.T, p.hd);
+        const char *Ks = smem + (kt & 1) * FC::STAGE;
+        const char *Vs = Ks + FC::KB;
+        const char *Kt = FC::BF ? Ks + 2 * FC::KB : Ks;
+        if (kt < wtiles) {
+            const int kv0 = kt * BKV;
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                f32x16 S, dP;
+#pragma unroll
+                for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+                mma_rows<T, HD>(S, Ks, j * 32, qf, lane);
+                mma_rows<T, HD>(dP, Vs, j * 32, df, lane);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    int key = kv0 + j * 32 + acc_row(r, lane);
+                    float pr = key <= qi ? exp2f(S[r] * p.sl2 - lse2) : 0.f;
+                    S[r] = pr * (dP[r] - Dq);
+                }
+                mma_trans<T, HD, BKV>(dQ, S, Kt, j, lane);
+            }
+        }
+        if (more) dq_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
+        __syncthreads();
+    }
+    if (qi < p.T) {
+        T *row = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + qi) * p.QKV + h * p.hd;
+        store_rows<T, HD>(row, dQ, p.scale, p.hd, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward: dK, dV (key-owning, summed over the query heads of the group)
+// ---------------------------------------------------------------------------
+template <typename T, int HD> struct DkvCfg {
+    static constexpr int BK = 128;   // keys per workgroup (4 waves x 32)
+    static constexpr int BQ = 64;    // queries per tile
+    static constexpr bool BF = std::is_same<T, bf16>::value;
+    static constexpr int QB = BQ * HD * (int)sizeof(T);
+    // LDS stage: Q natural, dO natural, (bf16) Q transposed, dO transposed, then lse2[BQ], D[BQ]
+    static constexpr int STAGE = (BF ? 4 : 2) * QB + 2 * BQ * 4;
+    static constexpr int PQ = BF ? 8 * Blk<HD, BQ, 128>::P : Nat<T, HD, BQ, 128>::P;
+    static constexpr int PREG = PQ;
+};
+
+template <typename T, int HD>
+__device__ __forceinline__ void dkv_stage_load(u32x4 *reg, float &aux, const T *qb, const T *db, long long qstride,
+                                               long long dstride, const float *lse, const float *D, int q0, int T_,
+                                               int hd) {
+    const int t = threadIdx.x;
+    constexpr int BQ = DkvCfg<T, HD>::BQ;
+    const T *g = t < 128 ? qb : db;
+    const long long st = t < 128 ? qstride : dstride;
+    const int tl = t & 127;
+    if constexpr (std::is_same<T, bf16>::value)
+        Blk<HD, BQ, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), g, st, q0, T_, hd, tl);
+    else
+        Nat<T, HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
+    // threads 0..BQ-1: lse*log2e of query q0+t; threads 128..128+BQ-1: D
+    if (tl < BQ) {
+        int q = q0 + tl;
+        if (t < 128) aux = q < T_ ? lse[q] * LOG2E : INFINITY;
+        else aux = q < T_ ? D[q] : 0.f;
+    }
+}
+template <typename T, int HD>
+__device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, char *st) {
+    using FC = DkvCfg<T, HD>;
+    const int t = threadIdx.x, tl = t & 127;
+    char *nat = st + (t < 128 ? 0 : FC::QB);
+    if constexpr (std::is_same<T, bf16>::value) {
+        char *tr = st + (t < 128 ? 2 : 3) * FC::QB;
+        Blk<HD, FC::BQ, 128>::template store<true, true>(reinterpret_cast<const u32x4(*)[8]>(reg), nat, tr, tl);
+    } else {
+        Nat<T, HD, FC::BQ, 128>::store(reg, nat, tl);
+    }
+    float *f = reinterpret_cast<float *>(st + (FC::BF ? 4 : 2) * FC::QB);
+    if (tl < FC::BQ) f[(t < 128 ? 0 : FC::BQ) + tl] = aux;
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
+    using A = AT<T, HD>;
+    using FC = DkvCfg<T, HD>;
+    constexpr int BK = FC::BK, BQ = FC::BQ;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int nkb = (p.T + BK - 1) / BK;
+    const int BKVH = p.B * p.NKV;
+    const int kb = (int)(blockIdx.x / BKVH);   // low key blocks (most work) first
+    const int bk = blockIdx.x % BKVH;
+    const int b = bk / p.NKV, kh = bk % p.NKV;
+    const int grp = p.NH / p.NKV;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
+    const int k0 = kb * BK, kw0 = k0 + wave * 32, ki = kw0 + l32;
+    (void)nkb;
+
+    const long long stride = p.QKV;
+    const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
+    const T *krow = base + (long long)ki * stride + p.C + kh * p.hd;
+    const T *vrow = krow + p.NKV * p.hd;
+
+    u32x4 kf[A::NC], vf[A::NC];
+    load_row_frag<T, HD>(kf, krow, ki < p.T, p.hd, g);
+    load_row_frag<T, HD>(vf, vrow, ki < p.T, p.hd, g);
+
+    f32x16 dK[A::ND], dV[A::ND];
+#pragma unroll
+    for (int d = 0; d < A::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) dK[d][r] = dV[d][r] = 0.f;
+
+    const int qt0 = k0 / BQ;                       // first query tile touching these keys
+    const int nqt = (p.T + BQ - 1) / BQ - qt0;     // query tiles per head
+    const int niter = nqt * grp;
+
+    auto srcs = [&](int it, const T *&qb, const T *&db, const float *&lse, const float *&D, int &q0) {
+        int hh = it / nqt, qt = qt0 + it % nqt;
+        int h = kh * grp + hh;
+        q0 = qt * BQ;
+        qb = base + h * p.hd;
+        db = reinterpret_cast<const T *>(p.dout) + (long long)b * p.T * p.C + h * p.hd;
+        lse = p.lse_in + ((long long)b * p.NH + h) * p.T;
+        D = p.D + ((long long)b * p.NH + h) * p.T;
+    };
+
+    u32x4 reg[FC::PREG];
+    float aux = 0.f;
+    if (niter > 0) {
+        const T *qb, *db;
+        const float *lse, *D;
+        int q0;
+        srcs(0, qb, db, lse, D, q0);
+        dkv_stage_load<T, HD>(reg, aux, qb, db, stride, p.C, lse, D, q0, p.T, p.hd);
+        dkv_stage_store<T, HD>(reg, aux, smem);
+    }
+    __syncthreads();
+
+    for (int it = 0; it < niter; it++) {
+        const bool more = it + 1 < niter;
+        if (more) {
+            const T *qb, *db;
+            const float *lse, *D;
+            int q0;
+            srcs(it + 1, qb, db, lse, D, q0);
+            dkv_stage_load<T, HD>(reg, aux, qb, db, stride, p.C, lse, D, q0, p.T, p.hd);
+        }
+        const char *st = smem + (it & 1) * FC::STAGE;
+        const char *Qs = st, *dOs = st + FC::QB;
+        const char *Qt = FC::BF ? st + 2 * FC::QB : Qs;
+        const char *dOt = FC::BF ? st + 3 * FC::QB : dOs;
+        const float *lse2 = reinterpret_cast<const float *>(st + (FC::BF ? 4 : 2) * FC::QB);
+        const float *Dt = lse2 + BQ;
+        const int q0 = (qt0 + it % nqt) * BQ;
+        if (q0 + BQ - 1 >= kw0 && kw0 < p.T) {
+#pragma unroll
+            for (int j = 0; j < BQ / 32; j++) {
+                f32x16 S, dP;
+#pragma unroll
+                for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+                mma_rows<T, HD>(S, Qs, j * 32, kf, lane);
+                mma_rows<T, HD>(dP, dOs, j * 32, vf, lane);
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    int ql = j * 32 + acc_row(r, lane);
+                    int q = q0 + ql;
+                    float pr = q >= ki ? exp2f(S[r] * p.sl2 - lse2[ql]) : 0.f;
+                    S[r] = pr;
+                    dP[r] = pr * (dP[r] - Dt[ql]);
+                }
+                mma_trans<T, HD, BQ>(dV, S, dOt, j, lane);
+                mma_trans<T, HD, BQ>(dK, dP, Qt, j, lane);
+            }
+        }
+        if (more) dkv_stage_store<T, HD>(reg, aux, smem + ((it + 1) & 1) * FC::STAGE);
+        __syncthreads();
+    }
+    if (ki < p.T) {
+        T *row = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + ki) * p.QKV + p.C + kh * p.hd;
+        store_rows<T, HD>(row, dK, p.scale, p.hd, lane);
+        store_rows<T, HD>(row + p.NKV * p.hd, dV, 1.f, p.hd, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <typename K> static hipError_t set_lds(K kernel, int bytes) {
+    return hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+static int pad_hd(int hd, int dtype) {
+    int m = dtype == DTB_BF16 ? 16 : 8;
+    int p = m;
+    while (p < hd) p <<= 1;
+    return p;
+}
+
+template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_t s) {
+    using FC = FwdCfg<T, HD>;
+    static bool init = false;
+    if (!init) {
+        hipError_t e = set_lds(attn_fwd_kernel<T, HD>, 2 * FC::STAGE);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    int nqb = (p.T + FC::BQ - 1) / FC::BQ;
+    hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, hipStream_t s) {
+    using QC = DqCfg<T, HD>;
+    using KC = DkvCfg<T, HD>;
+    static bool init = false;
+    if (!init) {
+        hipError_t e = set_lds(attn_bwd_dq_kernel<T, HD>, 2 * QC::STAGE);
+        if (e != hipSuccess) return e;
+        e = set_lds(attn_bwd_dkv_kernel<T, HD>, 2 * KC::STAGE);
+        if (e != hipSuccess) return e;
+        init = true;
+    }
+    long long rows = (long long)p.B * p.T;
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnP q = p;
+    q.D = D;
+    int nqb = (p.T + QC::BQ - 1) / QC::BQ;
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * QC::STAGE, s, q);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    int nkb = (p.T + KC::BK - 1) / KC::BK;
+    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
+    return hipGetLastError();
+}
+
+static AttnP make_params(const void *qkv, int B, int T, int C, int NH, int NKV) {
+    AttnP p{};
+    p.qkv = qkv;
+    p.B = B; p.T = T; p.C = C; p.NH = NH; p.NKV = NKV;
+    p.hd = C / NH;
+    p.QKV = C + 2 * NKV * p.hd;
+    p.scale = 1.f / sqrtf((float)p.hd);
+    p.sl2 = p.scale * LOG2E;
+    return p;
+}
+
+#define DTB_HD_DISPATCH(FN, T, hdp, ...)                 \
+    (hdp == 8     ? FN<T, 8>(__VA_ARGS__)                \
+     : hdp == 16  ? FN<T, 16>(__VA_ARGS__)               \
+     : hdp == 32  ? FN<T, 32>(__VA_ARGS__)               \
+     : hdp == 64  ? FN<T, 64>(__VA_ARGS__)               \
+                  : FN<T, 128>(__VA_ARGS__))
+
+int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV, int dtype,
+                        hipStream_t s) {
+    if (B == 0 || T == 0) return DTB_OK;
+    AttnP p = make_params(qkv, B, T, C, NH, NKV);
+    p.o = out;
+    p.lse = lse;
+    int hdp = pad_hd(p.hd, dtype);
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16 ? (hdp == 16   ? fwd_t<bf16, 16>(p, s)
+                                        : hdp == 32 ? fwd_t<bf16, 32>(p, s)
+                                        : hdp == 64 ? fwd_t<bf16, 64>(p, s)
+                                                    : fwd_t<bf16, 128>(p, s))
+                                     : DTB_HD_DISPATCH(fwd_t, float, hdp, p, s);
+    if (e != hipSuccess) return set_launch_error(e, "attn_forward");
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        double flops = 4.0 * p.hd * (double)NH * B * (double)T * (T + 1) / 2;
+        double bytes = es * (double)B * T * (p.QKV + C) + 4.0 * B * NH * T;
+        timing_end(s, K_ATTN_FWD, flops, bytes);
+    }
+    return DTB_OK;
+}
+
+int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout, const float *lse, int B,
+                         int T, int C, int NH, int NKV, int dtype, float *D, hipStream_t s) {
+    if (B == 0 || T == 0) return DTB_OK;
+    AttnP p = make_params(qkv, B, T, C, NH, NKV);
+    p.o = dqkv;
+    p.out = out;
+    p.dout = dout;
+    p.lse_in = lse;
+    int hdp = pad_hd(p.hd, dtype);
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16 ? (hdp == 16   ? bwd_t<bf16, 16>(p, D, s)
+                                        : hdp == 32 ? bwd_t<bf16, 32>(p, D, s)
+                                        : hdp == 64 ? bwd_t<bf16, 64>(p, D, s)
+                                                    : bwd_t<bf16, 128>(p, D, s))
+                                     : DTB_HD_DISPATCH(bwd_t, float, hdp, p, D, s);
+    if (e != hipSuccess) return set_launch_error(e, "attn_backward");
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        double flops = 2.5 * 4.0 * p.hd * (double)NH * B * (double)T * (T + 1) / 2;
+        double bytes = es * (double)B * T * (2.0 * p.QKV + 2.0 * C) + 4.0 * B * NH * T;
+        timing_end(s, K_ATTN_BWD, flops, bytes);
+    }
+    return DTB_OK;
+}
+
+}  // namespace dtb

@@ -1,0 +1,198 @@
+// Internal header of libdtb: element types, vector loads, MFMA wrappers and
+// the launch bookkeeping shared by the kernel files.  gfx950 (CDNA4) only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/dtb.h"
+
+namespace dtb {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr int WAVE = 64;
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }
+
+// 16-byte vector of T: 4 floats or 8 bf16
+template <typename T> struct Vec;
+template <> struct Vec<float> {
+    static constexpr int N = 4;
+    typedef f32x4 type;
+};
+template <> struct Vec<bf16> {
+    static constexpr int N = 8;
+    typedef bf16x8 type;
+};
+
+template <typename T> __device__ __forceinline__ u32x4 ld16(const T *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+template <typename T> __device__ __forceinline__ void st16(T *p, u32x4 v) {
+    *reinterpret_cast<u32x4 *>(p) = v;
+}
+
+// unpack / pack a 16-byte vector into floats
+template <typename T> __device__ __forceinline__ void unpack16(u32x4 v, float *f);
+template <> __device__ __forceinline__ void unpack16<float>(u32x4 v, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) f[i] = __uint_as_float(v[i]);
+}
+template <> __device__ __forceinline__ void unpack16<bf16>(u32x4 v, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        f[2 * i] = __uint_as_float(v[i] << 16);
+        f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16 a = (bf16)lo, b = (bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+template <typename T> __device__ __forceinline__ u32x4 pack16(const float *f);
+template <> __device__ __forceinline__ u32x4 pack16<float>(const float *f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = __float_as_uint(f[i]);
+    return v;
+}
+template <> __device__ __forceinline__ u32x4 pack16<bf16>(const float *f) {
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; i++) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+}
+
+// wave-wide reductions (64 lanes)
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+
+// ---------------------------------------------------------------- MFMA ---
+// 32x32 output block: lane l, accumulator r holds row 8*(r/4) + 4*(l/32) + r%4,
+// column l%32.  The A operand lane l supplies row l%32, the B operand lane l
+// column l%32; both supply the same k positions for the same lane half l/32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
+
+// ---- MFMA on one 16-byte chunk of A and B ---------------------------------
+__device__ __forceinline__ void mma_chunk(f32x16 &acc, u32x4 a, u32x4 b, bf16) {
+    acc = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc);
+}
+__device__ __forceinline__ void mma_chunk(f32x16 &acc, u32x4 a, u32x4 b, float) {
+#pragma unroll
+    for (int e = 0; e < 4; e++) acc = mfma32(__uint_as_float(a[e]), __uint_as_float(b[e]), acc);
+}
+
+// ---- transposes of register blocks ---------------------------------------
+// bf16 8x8: in[i] holds row k=i (8 consecutive m); out[j] holds m=j (8 consecutive k)
+__device__ __forceinline__ void transpose8x8(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            uint32_t a = in[2 * p][j >> 1], b = in[2 * p + 1][j >> 1];
+            out[j][p] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+        }
+    }
+}
+// fp32 4x4
+__device__ __forceinline__ void transpose4x4(const u32x4 *in, u32x4 *out) {
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int p = 0; p < 4; p++) out[j][p] = in[p][j];
+}
+
+// ----------------------------------------------------------- host side ---
+struct Launch {
+    hipStream_t stream;
+};
+
+// per-kernel-class timing (measurement only)
+enum KClass { K_GEMM = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_NCLASS = 4 };
+void timing_begin(hipStream_t s);
+void timing_end(hipStream_t s, int cls, double flops, double bytes);
+extern bool g_timing_on;
+
+int set_launch_error(hipError_t e, const char *what);
+
+#define DTB_LAUNCH_CHECK(what)                                           \
+    do {                                                                  \
+        hipError_t _e = hipGetLastError();                                \
+        if (_e != hipSuccess) return ::dtb::set_launch_error(_e, what);   \
+    } while (0)
+
+// ---------------------------------------------------------- internal ops ---
+// GEMM: C[m, n] = sum_k A(m, k) B(n, k) over a K range, with
+//   A(m, k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B(n, k) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+// Epilogue: out = acc (+ bias[n]) (+ res[m*ldr + n]) stored as out_dtype, or
+// (accumulate) out_f32 += acc.
+struct GemmArgs {
+    const void *A, *B;
+    long long lda, ldb;
+    int M, N, K;
+    bool a_kmajor, b_kmajor;
+    int dtype;            // operand dtype
+    void *out;            // dtype (or fp32 when out_f32)
+    long long ldo;
+    bool out_f32;         // out is fp32
+    bool accumulate;      // out_f32 += acc
+    const void *bias;     // [N] dtype, may be NULL
+    const void *res;      // [M, ldr] dtype, may be NULL (may alias out)
+    long long ldr;
+};
+// ws: fp32 scratch for split-K partials (may be NULL -> no split)
+int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s);
+size_t gemm_ws_bytes(int M, int N, int K, int dtype);
+
+int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV,
+                        int dtype, hipStream_t s);
+// D: fp32 scratch [B][NH][T]
+int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout,
+                         const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
+                         float *D, hipStream_t s);
+
+// elementwise / reductions
+int norm_forward(int mode, int dtype, const void *x, const void *g, const void *b, float eps, long R, int C,
+                 void *out, float *rstd, float *mean, hipStream_t s);
+// dx = dres + Norm^T(dy); partial sums of dgamma/dbeta into part[npart][2][C]
+int norm_backward(int mode, int dtype, const void *dy, const void *x, const void *g, const float *rstd,
+                  const float *mean, const void *dres, long R, int C, void *dx, float *dg, float *db,
+                  float *part, int npart, hipStream_t s);
+int norm_backward_parts(long R);
+int rope_table(float *cs, int T, int hd, float base, hipStream_t s);
+int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int NH, int NKV, int hd,
+               int inverse, hipStream_t s);
+int act_forward(int mlp, int dtype, const void *up, long R, int H, void *h, hipStream_t s);
+int act_backward(int mlp, int dtype, const void *dh, const void *up, long R, int H, void *dup,
+                 hipStream_t s);
+// db[n] += sum_r dy[r*N + n]
+int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, int npart, hipStream_t s);
+int bias_grad_parts(long R);
+
+}  // namespace dtb

@@ -1,0 +1,508 @@
+// Bandwidth-bound kernels of the block: RMSNorm / LayerNorm forward and
+// backward, NeoX RoPE, the MLP activations and the bias-gradient reductions.
+//
+// Sources (page title, section):
+//   "nanoeuler — CUDA kernels": rmsnorm_forward_kernel / rmsnorm_backward_kernel
+//     (r = (mean x^2 + eps)^-1/2; dx += g dy r - x (sum dy g x) r^3 / C),
+//     swiglu_forward_kernel / swiglu_backward_kernel, residual_add_kernel.
+//   "microgpt.cu": RMSNorm without gamma, relu_forward/backward_kernel.
+//   llm.c train_gpt2.c: layernorm_forward / layernorm_backward, gelu_forward /
+//     gelu_backward (tanh approximation), matmul_backward's bias gradient.
+//   "nx_f32_qwen2_train_gate.nx source": build_rope (NeoX half-split pairs,
+//     theta_i = base^(-2i/hd)).
+//
+// Layout and design: one wave64 per row for the norms, 16-byte vector loads
+// and stores, the row held in registers between the reduction and the write;
+// gamma/beta/bias gradients are reduced deterministically (per-workgroup
+// partial sums in fp32, then a second kernel adds them into the gradient).
+#include <type_traits>
+
+#include "common.h"
+
+namespace dtb {
+
+// ---------------------------------------------------------------- norms ---
+// NPL: 16-byte chunks per lane (row width C <= 64 * NPL * EPC)
+template <typename T, int NPL, int MODE>
+__global__ __launch_bounds__(256) void norm_fwd_kernel(const T *x, const T *g, const T *bta, float eps, long R,
+                                                        int C, T *out, float *rstd, float *mean) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (row >= R) return;
+    const int nch = C / EPC;
+    const T *xr = x + row * C;
+    float v[NPL][EPC];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        int c = lane + 64 * k;
+        if (c < nch) {
+            unpack16<T>(ld16(xr + c * EPC), v[k]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPC; e++) v[k][e] = 0.f;
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; e++) s += (MODE == DTB_NORM_LAYER) ? v[k][e] : v[k][e] * v[k][e];
+    }
+    float mu = 0.f, ms;
+    if (MODE == DTB_NORM_LAYER) {
+        mu = wave_sum(s) / C;
+        float q = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            int c = lane + 64 * k;
+            if (c < nch)
+#pragma unroll
+                for (int e = 0; e < EPC; e++) {
+                    float d = v[k][e] - mu;
+                    q += d * d;
+                }
+        }
+        ms = wave_sum(q) / C;
+    } else {
+        ms = wave_sum(s) / C;
+    }
+    const float r = rsqrtf(ms + eps);
+    T *orow = out + row * C;
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        int c = lane + 64 * k;
+        if (c >= nch) continue;
+        float gv[EPC], bv[EPC], o[EPC];
+        if (MODE != DTB_NORM_RMS_NOGAMMA) unpack16<T>(ld16(g + c * EPC), gv);
+        if (MODE == DTB_NORM_LAYER) unpack16<T>(ld16(bta + c * EPC), bv);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            float n = (v[k][e] - mu) * r;
+            if (MODE != DTB_NORM_RMS_NOGAMMA) n *= gv[e];
+            if (MODE == DTB_NORM_LAYER) n += bv[e];
+            o[e] = n;
+        }
+        st16(orow + c * EPC, pack16<T>(o));
+    }
+    if (lane == 0) {
+        rstd[row] = r;
+        if (MODE == DTB_NORM_LAYER) mean[row] = mu;
+    }
+}
+
+// dx = dres + Norm^T(dy).  Each wave handles rows wave_id, wave_id + nwaves, ...;
+// gamma/beta partials per workgroup -> part[blockIdx.x][0..C) and [C..2C).
+template <typename T, int NPL, int MODE>
+__global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, const T *g, const float *rstd,
+                                                        const float *mean, const T *dres, long R, int C, T *dx,
+                                                        float *part) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr bool HAS_G = MODE != DTB_NORM_RMS_NOGAMMA;
+    constexpr bool LN = MODE == DTB_NORM_LAYER;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int nch = C / EPC;
+    const long nwaves = (long)gridDim.x * 4;
+    float ag[NPL][EPC], ab[NPL][EPC];
+#pragma unroll
+    for (int k = 0; k < NPL; k++)
+#pragma unroll
+        for (int e = 0; e < EPC; e++) ag[k][e] = ab[k][e] = 0.f;
+    float gv[NPL][EPC];
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        int c = lane + 64 * k;
+#pragma unroll
+        for (int e = 0; e < EPC; e++) gv[k][e] = 1.f;
+        if (HAS_G && c < nch) unpack16<T>(ld16(g + c * EPC), gv[k]);
+    }
+    for (long row = (long)blockIdx.x * 4 + wave; row < R; row += nwaves) {
+        const float r = rstd[row];
+        const float mu = LN ? mean[row] : 0.f;
+        float xh[NPL][EPC], d[NPL][EPC];
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            int c = lane + 64 * k;
+            if (c < nch) {
+                unpack16<T>(ld16(x + row * C + c * EPC), xh[k]);
+                unpack16<T>(ld16(dy + row * C + c * EPC), d[k]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < EPC; e++) xh[k][e] = d[k][e] = 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < EPC; e++) {
+                xh[k][e] = (xh[k][e] - mu) * r;        // normalised input
+                float dn = d[k][e] * gv[k][e];
+                s1 += dn;
+                s2 += dn * xh[k][e];
+            }
+        }
+        s2 = wave_sum(s2) / C;
+        if (LN) s1 = wave_sum(s1) / C;
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            int c = lane + 64 * k;
+            if (c >= nch) continue;
+            float rs[EPC], o[EPC];
+            unpack16<T>(ld16(dres + row * C + c * EPC), rs);
+#pragma unroll
+            for (int e = 0; e < EPC; e++) {
+                float dn = d[k][e] * gv[k][e];
+                // RMS: r (dn - xhat * mean(dn xhat));  LN: r (dn - mean(dn) - xhat mean(dn xhat))
+                float v = r * (dn - (LN ? s1 : 0.f) - xh[k][e] * s2);
+                o[e] = rs[e] + v;
+                ag[k][e] += d[k][e] * xh[k][e];
+                ab[k][e] += d[k][e];
+            }
+            st16(dx + row * C + c * EPC, pack16<T>(o));
+        }
+    }
+    if (!HAS_G) return;
+    // combine the 4 waves through LDS, chunk by chunk, then write the partial
+    __shared__ float buf[4][64 * 4];
+#pragma unroll
+    for (int k = 0; k < NPL; k++) {
+        for (int half = 0; half < (LN ? 2 : 1); half++) {
+#pragma unroll
+            for (int e0 = 0; e0 < EPC; e0 += 4) {
+                __syncthreads();
+#pragma unroll
+                for (int e = 0; e < 4; e++) buf[wave][lane * 4 + e] = half ? ab[k][e0 + e] : ag[k][e0 + e];
+                __syncthreads();
+                // thread i (of 256) owns element i of the 64*4 slice
+                int i = threadIdx.x;
+                float sum = buf[0][i] + buf[1][i] + buf[2][i] + buf[3][i];
+                int ln = i >> 2, e = i & 3;
+                int c = ln + 64 * k;
+                if (c < nch) part[(long)blockIdx.x * 2 * C + half * C + c * EPC + e0 + e] = sum;
+            }
+        }
+    }
+}
+
+// dst[i] += sum_p part[p][i] for i < n (part row stride ld)
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst) {
+    int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= n) return;
+    float s = 0.f;
+    for (int p = 0; p < np; p++) s += part[(long)p * ld + i];
+    dst[i] += s;
+}
+
+static int npl_for(int C, int dtype) {
+    int epc = dtype == DTB_BF16 ? 8 : 4;
+    int nch = C / epc;
+    int npl = 1;
+    while (64 * npl < nch) npl <<= 1;
+    return npl;
+}
+
+template <typename T, int NPL>
+static hipError_t norm_fwd_t(int mode, const void *x, const void *g, const void *b, float eps, long R, int C,
+                             void *out, float *rstd, float *mean, hipStream_t s) {
+    dim3 grid((unsigned)((R + 3) / 4));
+    const T *xx = (const T *)x, *gg = (const T *)g, *bb = (const T *)b;
+    T *oo = (T *)out;
+    if (mode == DTB_NORM_RMS)
+        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C, oo,
+                           rstd, mean);
+    else if (mode == DTB_NORM_RMS_NOGAMMA)
+        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, xx, gg, bb, eps,
+                           R, C, oo, rstd, mean);
+    else
+        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C,
+                           oo, rstd, mean);
+    return hipGetLastError();
+}
+
+#define NPL_DISPATCH(FN, T, npl, ...)                                                   \
+    (npl == 1   ? FN<T, 1>(__VA_ARGS__)                                                \
+     : npl == 2 ? FN<T, 2>(__VA_ARGS__)                                                \
+     : npl == 4 ? FN<T, 4>(__VA_ARGS__)                                                \
+     : npl == 8 ? FN<T, 8>(__VA_ARGS__)                                                \
+                : FN<T, 16>(__VA_ARGS__))
+
+int norm_forward(int mode, int dtype, const void *x, const void *g, const void *b, float eps, long R, int C,
+                 void *out, float *rstd, float *mean, hipStream_t s) {
+    if (R <= 0) return DTB_OK;
+    int npl = npl_for(C, dtype);
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16 ? NPL_DISPATCH(norm_fwd_t, bf16, npl, mode, x, g, b, eps, R, C, out, rstd, mean, s)
+                                     : NPL_DISPATCH(norm_fwd_t, float, npl, mode, x, g, b, eps, R, C, out, rstd, mean, s);
+    if (e != hipSuccess) return set_launch_error(e, "norm_forward");
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, (double)R * (2 * es * C + (mode == DTB_NORM_LAYER ? 8 : 4)));
+    }
+    return DTB_OK;
+}
+
+int norm_backward_parts(long R) {
+    long waves = (R + 3) / 4;
+    return (int)(waves < 512 ? (waves > 0 ? waves : 1) : 512);
+}
+
+template <typename T, int NPL>
+static hipError_t norm_bwd_t(int mode, const void *dy, const void *x, const void *g, const float *rstd,
+                             const float *mean, const void *dres, long R, int C, void *dx, float *part, int np,
+                             hipStream_t s) {
+    dim3 grid(np);
+    const T *a = (const T *)dy, *xx = (const T *)x, *gg = (const T *)g, *rr = (const T *)dres;
+    T *o = (T *)dx;
+    if (mode == DTB_NORM_RMS)
+        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean, rr,
+                           R, C, o, part);
+    else if (mode == DTB_NORM_RMS_NOGAMMA)
+        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, a, xx, gg, rstd,
+                           mean, rr, R, C, o, part);
+    else
+        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean,
+                           rr, R, C, o, part);
+    return hipGetLastError();
+}
+
+int norm_backward(int mode, int dtype, const void *dy, const void *x, const void *g, const float *rstd,
+                  const float *mean, const void *dres, long R, int C, void *dx, float *dg, float *db, float *part,
+                  int npart, hipStream_t s) {
+    if (R <= 0) return DTB_OK;
+    int npl = npl_for(C, dtype);
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16
+                       ? NPL_DISPATCH(norm_bwd_t, bf16, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s)
+                       : NPL_DISPATCH(norm_bwd_t, float, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s);
+    if (e != hipSuccess) return set_launch_error(e, "norm_backward");
+    if (mode != DTB_NORM_RMS_NOGAMMA) {
+        hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part, npart, 2L * C, C, dg);
+        if (mode == DTB_NORM_LAYER)
+            hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part + C, npart, 2L * C,
+                               C, db);
+        e = hipGetLastError();
+        if (e != hipSuccess) return set_launch_error(e, "norm_backward reduce");
+    }
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, (double)R * (4 * es * C + (mode == DTB_NORM_LAYER ? 8 : 4)));
+    }
+    return DTB_OK;
+}
+
+// ------------------------------------------------------------------ RoPE ---
+// cs[t][i] = (cos(t theta_i), sin(t theta_i)), theta_i = base^(-2i/hd), computed
+// in double and rounded to fp32 (fp32 angles lose ~1e-4 rad at t ~ 1e3-1e4)
+__global__ void rope_table_kernel(float2 *cs, int T, int half, int hd, double base) {
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)T * half) return;
+    int t = (int)(i / half), k = (int)(i % half);
+    double theta = pow(base, -2.0 * k / hd);
+    double a = t * theta;
+    cs[i] = make_float2((float)cos(a), (float)sin(a));
+}
+
+int rope_table(float *cs, int T, int hd, float base, hipStream_t s) {
+    int half = hd / 2;
+    long n = (long)T * half;
+    if (n <= 0) return DTB_OK;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float2 *)cs, T, half,
+                       hd, (double)base);
+    DTB_LAUNCH_CHECK("rope_table");
+    return DTB_OK;
+}
+
+// one thread per (row, head, pair i); heads 0..NH-1 are q (offset 0), NH.. are k (offset C)
+template <typename T>
+__global__ __launch_bounds__(256) void rope_kernel(T *qkv, const float2 *cs, long BT, int T_, int QKV, int NH,
+                                                    int NKV, int hd, int inverse) {
+    const int half = hd / 2;
+    const int nheads = NH + NKV;
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    long total = BT * nheads * half;
+    if (i >= total) return;
+    int k = (int)(i % half);
+    long rh = i / half;
+    int head = (int)(rh % nheads);
+    long row = rh / nheads;
+    int t = (int)(row % T_);
+    T *v = qkv + row * QKV + (long)head * hd;   // k heads follow the q heads contiguously
+    float2 c = cs[(long)t * half + k];
+    float x = to_f32(v[k]), y = to_f32(v[k + half]);
+    float sn = inverse ? -c.y : c.y;
+    v[k] = from_f32<T>(x * c.x - y * sn);
+    v[k + half] = from_f32<T>(y * c.x + x * sn);
+}
+
+int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int NH, int NKV, int hd, int inverse,
+               hipStream_t s) {
+    long BT = (long)B * T;
+    long total = BT * (NH + NKV) * (hd / 2);
+    if (total <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    dim3 grid((unsigned)((total + 255) / 256));
+    if (dtype == DTB_BF16)
+        hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, s, (bf16 *)qkv, (const float2 *)cs, BT, T, QKV, NH,
+                           NKV, hd, inverse);
+    else
+        hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, (float *)qkv, (const float2 *)cs, BT, T, QKV,
+                           NH, NKV, hd, inverse);
+    DTB_LAUNCH_CHECK("rope");
+    if (g_timing_on) timing_end(s, K_ELEM, 0, 2.0 * (dtype == DTB_BF16 ? 2 : 4) * total * 2);
+    return DTB_OK;
+}
+
+// ------------------------------------------------------------ activations ---
+__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+constexpr float GELU_K = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float GELU_C = 0.044715f;
+
+template <typename T, int MLP>
+__global__ __launch_bounds__(256) void act_fwd_kernel(const T *up, long R, int H, T *h) {
+    constexpr int EPC = 16 / sizeof(T);
+    const int W = MLP == DTB_MLP_SWIGLU ? 2 * H : H;
+    const int hc = H / EPC;
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= R * hc) return;
+    long r = i / hc;
+    int c = (int)(i % hc);
+    float a[EPC], o[EPC];
+    unpack16<T>(ld16(up + r * W + c * EPC), a);
+    if (MLP == DTB_MLP_SWIGLU) {
+        float u[EPC];
+        unpack16<T>(ld16(up + r * W + H + c * EPC), u);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) o[e] = a[e] * sigm(a[e]) * u[e];
+    } else if (MLP == DTB_MLP_RELU) {
+#pragma unroll
+        for (int e = 0; e < EPC; e++) o[e] = a[e] > 0.f ? a[e] : 0.f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            float f = a[e];
+            o[e] = 0.5f * f * (1.f + tanhf(GELU_K * (f + GELU_C * f * f * f)));
+        }
+    }
+    st16(h + r * H + c * EPC, pack16<T>(o));
+}
+
+template <typename T, int MLP>
+__global__ __launch_bounds__(256) void act_bwd_kernel(const T *dh, const T *up, long R, int H, T *dup) {
+    constexpr int EPC = 16 / sizeof(T);
+    const int W = MLP == DTB_MLP_SWIGLU ? 2 * H : H;
+    const int hc = H / EPC;
+    long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= R * hc) return;
+    long r = i / hc;
+    int c = (int)(i % hc);
+    float d[EPC], a[EPC], o[EPC];
+    unpack16<T>(ld16(dh + r * H + c * EPC), d);
+    unpack16<T>(ld16(up + r * W + c * EPC), a);
+    if (MLP == DTB_MLP_SWIGLU) {
+        float u[EPC], du[EPC];
+        unpack16<T>(ld16(up + r * W + H + c * EPC), u);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            float sg = sigm(a[e]);
+            o[e] = d[e] * u[e] * sg * (1.f + a[e] * (1.f - sg));
+            du[e] = d[e] * a[e] * sg;
+        }
+        st16(dup + r * W + H + c * EPC, pack16<T>(du));
+    } else if (MLP == DTB_MLP_RELU) {
+#pragma unroll
+        for (int e = 0; e < EPC; e++) o[e] = a[e] > 0.f ? d[e] : 0.f;
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            float f = a[e];
+            float u = GELU_K * (f + GELU_C * f * f * f);
+            float th = tanhf(u);
+            o[e] = d[e] * (0.5f * (1.f + th) + 0.5f * f * (1.f - th * th) * GELU_K * (1.f + 3.f * GELU_C * f * f));
+        }
+    }
+    st16(dup + r * W + c * EPC, pack16<T>(o));
+}
+
+template <typename T>
+static hipError_t act_fwd_t(int mlp, const void *up, long R, int H, void *h, hipStream_t s) {
+    constexpr int EPC = 16 / sizeof(T);
+    long n = R * (H / EPC);
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (mlp == DTB_MLP_SWIGLU)
+        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+    else if (mlp == DTB_MLP_RELU)
+        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+    else
+        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+    return hipGetLastError();
+}
+template <typename T>
+static hipError_t act_bwd_t(int mlp, const void *dh, const void *up, long R, int H, void *dup, hipStream_t s) {
+    constexpr int EPC = 16 / sizeof(T);
+    long n = R * (H / EPC);
+    dim3 grid((unsigned)((n + 255) / 256));
+    if (mlp == DTB_MLP_SWIGLU)
+        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R,
+                           H, (T *)dup);
+    else if (mlp == DTB_MLP_RELU)
+        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R, H,
+                           (T *)dup);
+    else
+        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)dh,
+                           (const T *)up, R, H, (T *)dup);
+    return hipGetLastError();
+}
+
+int act_forward(int mlp, int dtype, const void *up, long R, int H, void *h, hipStream_t s) {
+    if (R <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16 ? act_fwd_t<bf16>(mlp, up, R, H, h, s) : act_fwd_t<float>(mlp, up, R, H, h, s);
+    if (e != hipSuccess) return set_launch_error(e, "act_forward");
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, es * R * H * (mlp == DTB_MLP_SWIGLU ? 3 : 2));
+    }
+    return DTB_OK;
+}
+
+int act_backward(int mlp, int dtype, const void *dh, const void *up, long R, int H, void *dup, hipStream_t s) {
+    if (R <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    hipError_t e = dtype == DTB_BF16 ? act_bwd_t<bf16>(mlp, dh, up, R, H, dup, s)
+                                     : act_bwd_t<float>(mlp, dh, up, R, H, dup, s);
+    if (e != hipSuccess) return set_launch_error(e, "act_backward");
+    if (g_timing_on) {
+        double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, es * R * H * (mlp == DTB_MLP_SWIGLU ? 5 : 3));
+    }
+    return DTB_OK;
+}
+
+// --------------------------------------------------------- bias gradient ---
+// part[p][n] = sum over the p-th row range of dy[r][n]
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(const T *dy, long R, int N, long rows_per, float *part) {
+    int n = blockIdx.x * 256 + threadIdx.x;
+    if (n >= N) return;
+    long r0 = (long)blockIdx.y * rows_per, r1 = min(R, r0 + rows_per);
+    float s = 0.f;
+    for (long r = r0; r < r1; r++) s += to_f32(dy[r * N + n]);
+    part[(long)blockIdx.y * N + n] = s;
+}
+
+int bias_grad_parts(long R) {
+    long p = (R + 63) / 64;
+    return (int)(p < 256 ? (p > 0 ? p : 1) : 256);
+}
+
+int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, int npart, hipStream_t s) {
+    if (R <= 0 || N <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    long rows_per = (R + npart - 1) / npart;
+    dim3 grid((N + 255) / 256, npart);
+    if (dtype == DTB_BF16)
+        hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
+    else
+        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3((N + 255) / 256), dim3(256), 0, s, part, npart, (long)N, N, db);
+    DTB_LAUNCH_CHECK("bias_grad");
+    if (g_timing_on) timing_end(s, K_ELEM, 0, (double)R * N * (dtype == DTB_BF16 ? 2 : 4));
+    return DTB_OK;
+}
+
+}  // namespace dtb

@@ -1,0 +1,399 @@
+// MFMA GEMM for gfx950: the linear layers of the block and their backward
+// products ("nanoeuler — CUDA kernels": matmul_forward_cuda, out = inp w^T;
+// matmul_backward_dinp_cuda, dinp += dout w; matmul_backward_dw_cuda,
+// dw += dout^T inp; llm.c matmul_forward / matmul_backward with bias).
+//
+// One kernel template computes C[m, n] = sum_k A(m, k) B(n, k) for any of the
+// three operand layouts:
+//   forward  out = x W^T      A = x    [M][K] (k-major)  B = W  [N][K] (k-major)
+//   dinp     dx  = dy W       A = dy   [M][K] (k-major)  B = W  [K][N] (n-major)
+//   dW       dW += dy^T x     A = dy   [K][M] (m-major)  B = x  [K][N] (n-major)
+//
+// Design (CDNA4):
+// * 256 threads = 4 wave64s in a 2 x 2 grid; each wave owns a (BM/2) x (BN/2)
+//   sub-tile made of 32 x 32 MFMA blocks (v_mfma_f32_32x32x16_bf16 for bf16,
+//   v_mfma_f32_32x32x2_f32 for fp32) accumulated in fp32.
+// * A K-slab of the A and B tiles is staged in LDS as rows of 128 bytes
+//   (64 bf16 or 32 fp32 along k) split into eight 16-byte chunks whose
+//   position is XOR-swizzled with (row & 7), so the 16-byte fragment reads of
+//   32 consecutive rows are spread over all banks.  Two LDS stages: the global
+//   loads of slab k+1 are issued before the MFMAs of slab k and written to the
+//   other stage afterwards, one barrier per slab.
+// * k-major operands are copied with 16-byte loads; m/n-major operands are
+//   loaded as 8x8 (bf16) or 4x4 (fp32) blocks and transposed in registers so
+//   that LDS always holds k-contiguous rows.
+// * Lane half g = lane/32 of both operands reads chunk 2c+g of a slab for
+//   c = 0..3; that fixes one common k order for A and B, which is all the MFMA
+//   contraction needs.
+// * Weight gradients accumulate into fp32 (+=).  When there are too few output
+//   tiles to fill 256 CUs, K is split over gridDim.z into fp32 partials that a
+//   second kernel adds into the gradient (deterministic, no atomics).
+// * Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
+//   the 8 XCDs) works on a contiguous, row-grouped range of tiles and shares
+//   operand panels in its own L2.
+#include "common.h"
+
+namespace dtb {
+
+template <typename T> struct GT;
+template <> struct GT<bf16> {
+    static constexpr int EPC = 8;   // elements per 16-byte chunk
+    static constexpr int BK = 64;   // k per slab (8 chunks)
+};
+template <> struct GT<float> {
+    static constexpr int EPC = 4;
+    static constexpr int BK = 32;
+};
+
+struct KParams {
+    const void *A, *B;
+    long long lda, ldb;
+    int M, N, K;
+    int kchunk;  // k range per split (multiple of BK)
+    void *out;
+    long long ldo;
+    int out_mode;  // 0 store dtype, 1 store fp32, 2 accumulate fp32, 3 split partial fp32
+    const void *bias;
+    const void *res;
+    long long ldr;
+    float *part;   // split partials [splits][M][N]
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+// ---- slab loaders ---------------------------------------------------------
+// rows R of an operand tile starting at row0 (< nrows valid), k in [k0, kend)
+template <typename T, int R, bool KMAJOR> struct Loader;
+
+template <typename T, int R> struct Loader<T, R, true> {
+    static constexpr int P = R / 32;  // rows per thread
+    u32x4 reg[P];
+    __device__ __forceinline__ void load(const T *base, long long ld, int row0, int nrows, int k0, int kend) {
+        const int t = threadIdx.x, c = t & 7;
+        const int kk = k0 + c * GT<T>::EPC;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int r = (t >> 3) + 32 * p, gr = row0 + r;
+            if (gr < nrows && kk < kend) reg[p] = ld16(base + (long long)gr * ld + kk);
+            else reg[p] = u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const {
+        const int t = threadIdx.x, c = t & 7;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int r = (t >> 3) + 32 * p;
+            *reinterpret_cast<u32x4 *>(lds + swz(r, c)) = reg[p];
+        }
+    }
+};
+
+// m/n-major: global element (k, r) at base[k*ld + r]
+template <int R> struct Loader<bf16, R, false> {
+    static constexpr int NB = R;                  // (64/8) * (R/8) 8x8 blocks
+    static constexpr int P = (NB + 255) / 256;
+    u32x4 reg[P][8];
+    __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int blk = t + 256 * p;
+            int rb = blk % (R / 8), kb = blk / (R / 8);
+            int gr = row0 + rb * 8;
+            bool live = blk < NB && gr < nrows;
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                int k = k0 + kb * 8 + i;
+                if (live && k < kend) reg[p][i] = ld16(base + (long long)k * ld + gr);
+                else reg[p][i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int blk = t + 256 * p;
+            if (blk >= NB) continue;
+            int rb = blk % (R / 8), kb = blk / (R / 8);
+            u32x4 o[8];
+            transpose8x8(reg[p], o);
+#pragma unroll
+            for (int j = 0; j < 8; j++) {
+                int r = rb * 8 + j;
+                *reinterpret_cast<u32x4 *>(lds + swz(r, kb)) = o[j];
+            }
+        }
+    }
+};
+
+template <int R> struct Loader<float, R, false> {
+    static constexpr int NB = 2 * R;              // (32/4) * (R/4) 4x4 blocks
+    static constexpr int P = (NB + 255) / 256;
+    u32x4 reg[P][4];
+    __device__ __forceinline__ void load(const float *base, long long ld, int row0, int nrows, int k0, int kend) {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int blk = t + 256 * p;
+            int rb = blk % (R / 4), kb = blk / (R / 4);
+            int gr = row0 + rb * 4;
+            bool live = blk < NB && gr < nrows;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                int k = k0 + kb * 4 + i;
+                if (live && k < kend) reg[p][i] = ld16(base + (long long)k * ld + gr);
+                else reg[p][i] = u32x4{0, 0, 0, 0};
+            }
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const {
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            int blk = t + 256 * p;
+            if (blk >= NB) continue;
+            int rb = blk % (R / 4), kb = blk / (R / 4);
+            u32x4 o[4];
+            transpose4x4(reg[p], o);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                int r = rb * 4 + j;
+                *reinterpret_cast<u32x4 *>(lds + swz(r, kb)) = o[j];
+            }
+        }
+    }
+};
+
+// ---- tile id remap ---------------------------------------------------------
+__device__ __forceinline__ void tile_coords(int nm, int nn, int &tm, int &tn) {
+    int nt = nm * nn;
+    int pid = blockIdx.x;
+    if ((nt & 7) == 0) pid = (pid & 7) * (nt >> 3) + (pid >> 3);  // contiguous range per XCD
+    const int GM = 8;
+    int per_group = GM * nn;
+    int group = pid / per_group;
+    int first_m = group * GM;
+    int gsize = min(nm - first_m, GM);
+    int in_group = pid - group * per_group;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+template <typename T, int BM, int BN, bool AK, bool BKM>
+__global__ __launch_bounds__(256) void gemm_kernel(KParams p) {
+    constexpr int BK = GT<T>::BK;
+    constexpr int MI = BM / 64, NI = BN / 64;
+    constexpr int STAGE = (BM + BN) * 128;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(nm, nn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = blockIdx.z * p.kchunk;
+    const int kend = min(p.K, kbeg + p.kchunk);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
+
+    const T *A = reinterpret_cast<const T *>(p.A);
+    const T *B = reinterpret_cast<const T *>(p.B);
+    Loader<T, BM, AK> la;
+    Loader<T, BN, BKM> lb;
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; i++)
+#pragma unroll
+        for (int j = 0; j < NI; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    if (nk > 0) {
+        la.load(A, p.lda, m0, p.M, kbeg, kend);
+        lb.load(B, p.ldb, n0, p.N, kbeg, kend);
+        la.store(smem);
+        lb.store(smem + BM * 128);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; kt++) {
+        const bool more = kt + 1 < nk;
+        if (more) {
+            int k0 = kbeg + (kt + 1) * BK;
+            la.load(A, p.lda, m0, p.M, k0, kend);
+            lb.load(B, p.ldb, n0, p.N, k0, kend);
+        }
+        const char *As = smem + (kt & 1) * STAGE;
+        const char *Bs = As + BM * 128;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            u32x4 af[MI], bfr[NI];
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+                af[i] = *reinterpret_cast<const u32x4 *>(As + swz(wm * (BM / 2) + i * 32 + l32, 2 * c + g));
+#pragma unroll
+            for (int j = 0; j < NI; j++)
+                bfr[j] = *reinterpret_cast<const u32x4 *>(Bs + swz(wn * (BN / 2) + j * 32 + l32, 2 * c + g));
+#pragma unroll
+            for (int i = 0; i < MI; i++)
+#pragma unroll
+                for (int j = 0; j < NI; j++) mma_chunk(acc[i][j], af[i], bfr[j], T());
+        }
+        if (more) {
+            char *nx = smem + ((kt + 1) & 1) * STAGE;
+            la.store(nx);
+            lb.store(nx + BM * 128);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue ----
+    const T *bias = reinterpret_cast<const T *>(p.bias);
+    const T *res = reinterpret_cast<const T *>(p.res);
+#pragma unroll
+    for (int j = 0; j < NI; j++) {
+        const int n = n0 + wn * (BN / 2) + j * 32 + l32;
+        if (n >= p.N) continue;
+        const float bv = bias ? to_f32(bias[n]) : 0.f;
+#pragma unroll
+        for (int i = 0; i < MI; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * (BM / 2) + i * 32 + acc_row(r, lane);
+                if (m >= p.M) continue;
+                float v = acc[i][j][r];
+                if (p.out_mode == 0) {
+                    v += bv;
+                    if (res) v += to_f32(res[(long long)m * p.ldr + n]);
+                    reinterpret_cast<T *>(p.out)[(long long)m * p.ldo + n] = from_f32<T>(v);
+                } else if (p.out_mode == 1) {
+                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] = v + bv;
+                } else if (p.out_mode == 2) {
+                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] += v;
+                } else {
+                    p.part[((long long)blockIdx.z * p.M + m) * p.N + n] = v;
+                }
+            }
+        }
+    }
+}
+
+// out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0)
+__global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *out, long long ldo, int M, int N,
+                                                      int splits) {
+    long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
+    long long total4 = (long long)M * N / 4;
+    if (i4 >= total4) return;
+    long long e = i4 * 4;
+    int m = (int)(e / N), n = (int)(e % N);
+    f32x4 s = *reinterpret_cast<const f32x4 *>(part + e);
+    for (int z = 1; z < splits; z++) s += *reinterpret_cast<const f32x4 *>(part + (long long)z * M * N + e);
+    f32x4 *o = reinterpret_cast<f32x4 *>(out + (long long)m * ldo + n);
+    *o = *o + s;
+}
+
+// ---- host side ---------------------------------------------------------------
+template <typename T, int BM, int BN, bool AK, bool BKM>
+static hipError_t launch_t(const KParams &p, int splits, hipStream_t s) {
+    constexpr int STAGE = (BM + BN) * 128;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<T, BM, BN, AK, BKM>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
+    dim3 grid(nm * nn, 1, splits);
+    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AK, BKM>), grid, dim3(256), 2 * STAGE, s, p);
+    return hipGetLastError();
+}
+
+template <typename T, int BM, int BN>
+static hipError_t launch_layout(const KParams &p, bool ak, bool bk, int splits, hipStream_t s) {
+    if (ak && bk) return launch_t<T, BM, BN, true, true>(p, splits, s);
+    if (ak && !bk) return launch_t<T, BM, BN, true, false>(p, splits, s);
+    if (!ak && !bk) return launch_t<T, BM, BN, false, false>(p, splits, s);
+    return launch_t<T, BM, BN, false, true>(p, splits, s);
+}
+
+struct TileChoice {
+    int bm, bn;
+};
+static TileChoice choose_tile(int M, int N, int dtype) {
+    auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (dtype == DTB_BF16) {
+        if (tiles(256, 128) >= 512) return {256, 128};
+        if (tiles(128, 128) >= 256) return {128, 128};
+        return {64, 64};
+    }
+    if (tiles(128, 128) >= 256) return {128, 128};
+    return {64, 64};
+}
+
+static int choose_splits(const GemmArgs &g, TileChoice tc) {
+    if (!(g.out_f32 && g.accumulate) || g.bias || g.res) return 1;
+    const int BK = g.dtype == DTB_BF16 ? 64 : 32;
+    long long tiles = (long long)((g.M + tc.bm - 1) / tc.bm) * ((g.N + tc.bn - 1) / tc.bn);
+    int splits = 1;
+    while (tiles * splits < 512 && (long long)g.K / (splits * 2) >= 8 * BK && splits < 16) splits *= 2;
+    return splits;
+}
+
+size_t gemm_ws_bytes(int M, int N, int K, int dtype) {
+    GemmArgs g{};
+    g.M = M; g.N = N; g.K = K; g.dtype = dtype; g.out_f32 = true; g.accumulate = true;
+    TileChoice tc = choose_tile(M, N, dtype);
+    int sp = choose_splits(g, tc);
+    return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+}
+
+int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
+    if (g.M <= 0 || g.N <= 0) return DTB_OK;
+    TileChoice tc = choose_tile(g.M, g.N, g.dtype);
+    int splits = choose_splits(g, tc);
+    if (splits > 1 && (!ws || ws_bytes < (size_t)splits * g.M * g.N * sizeof(float))) splits = 1;
+    const int BK = g.dtype == DTB_BF16 ? 64 : 32;
+    KParams p{};
+    p.A = g.A; p.B = g.B; p.lda = g.lda; p.ldb = g.ldb;
+    p.M = g.M; p.N = g.N; p.K = g.K;
+    int kchunk = (g.K + splits - 1) / splits;
+    kchunk = (kchunk + BK - 1) / BK * BK;
+    p.kchunk = kchunk > 0 ? kchunk : BK;
+    p.out = g.out; p.ldo = g.ldo;
+    p.out_mode = splits > 1 ? 3 : (g.out_f32 ? (g.accumulate ? 2 : 1) : 0);
+    p.bias = g.bias; p.res = g.res; p.ldr = g.ldr;
+    p.part = splits > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+    double flops = 2.0 * g.M * g.N * (double)g.K;
+    if (g_timing_on) timing_begin(s);
+    hipError_t e;
+    if (g.dtype == DTB_BF16) {
+        if (tc.bm == 256) e = launch_layout<bf16, 256, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
+        else if (tc.bm == 128) e = launch_layout<bf16, 128, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
+        else e = launch_layout<bf16, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
+    } else {
+        if (tc.bm == 128) e = launch_layout<float, 128, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
+        else e = launch_layout<float, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
+    }
+    if (e != hipSuccess) return set_launch_error(e, "gemm");
+    if (splits > 1) {
+        long long total4 = (long long)g.M * g.N / 4;
+        hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s,
+                           reinterpret_cast<const float *>(ws), reinterpret_cast<float *>(g.out), g.ldo, g.M,
+                           g.N, splits);
+        e = hipGetLastError();
+        if (e != hipSuccess) return set_launch_error(e, "splitk_reduce");
+    }
+    if (g_timing_on) {
+        const double es = g.dtype == DTB_BF16 ? 2.0 : 4.0;
+        double bytes = es * ((double)g.M * g.K + (double)g.N * g.K) +
+                       (g.out_f32 ? 4.0 * (g.accumulate ? 2.0 : 1.0) : es) * g.M * g.N;
+        timing_end(s, K_GEMM, flops, bytes);
+    }
+    return DTB_OK;
+}
+
+}  // namespace dtb

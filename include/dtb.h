@@ -1,0 +1,203 @@
+/*
+ * dtb.h -- C ABI of libdtb.so: one pre-norm decoder-only transformer block,
+ * forward and backward, and causal grouped-query flash attention, as
+ * hand-written HIP kernels for AMD gfx950 (MI355X).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Problem statement (B, T, C, NH, NKV) as in the flash_attn_forward_kernel /
+ *   flash_attn_backward_kernel declarations of the "nanoeuler — CUDA kernels"
+ *   page: B sequences of T tokens, model width C, NH query heads of width
+ *   hd = C / NH, NKV key/value heads; query head h reads kv head h / (NH/NKV).
+ * - Activations are row-major [B, T, width].  The packed qkv row of token
+ *   (b, t) is [q heads (NH*hd) | k heads (NKV*hd) | v heads (NKV*hd)], width
+ *   QKV = C + 2*NKV*hd (that page's `qkvd`).
+ * - Weights are row-major [out, in] (that page's parameter layout `W`, and
+ *   llm.c's ParameterTensors): a linear layer computes y = x W^T + b.
+ * - dtype DTB_F32: every activation, weight, gamma and bias is fp32.
+ *   dtype DTB_BF16: they are bf16 (raw 16-bit storage, round-to-nearest-even
+ *   on store); accumulation is fp32.  In both cases lse, the saved norm
+ *   statistics and every parameter gradient are fp32.
+ * - All pointers are DEVICE pointers (hipMalloc'd or torch CUDA tensors) except
+ *   the cfg / weights / grads structs themselves, which are read on the host
+ *   during the call.  Buffers must be 16-byte aligned.
+ * - The caller owns every buffer.  The library never allocates, frees or
+ *   synchronises: each call validates its arguments on the host, enqueues
+ *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ * - Errors: 0 on success, a negative DTB_E* code otherwise (no kernel is
+ *   enqueued when validation fails; the library never calls exit()).
+ *   dtb_strerror() gives a message; for DTB_ELAUNCH it includes the HIP error.
+ * - Calls on the same stream are ordered; calls on different streams that
+ *   touch the same buffers race.
+ */
+#ifndef DTB_H
+#define DTB_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- codes ------------------------------------------------------------- */
+#define DTB_OK 0
+#define DTB_EINVAL_SHAPE (-1) /* C % NH, NH % NKV, hd unsupported, odd hd with RoPE,
+                                 C or H not a multiple of 8, negative sizes, overflow */
+#define DTB_EINVAL_PTR (-2)   /* a required pointer is NULL or misaligned */
+#define DTB_EDTYPE (-3)       /* dtype not DTB_F32 / DTB_BF16 */
+#define DTB_EINVAL_ENUM (-4)  /* unknown norm / mlp / rope selector */
+#define DTB_ELAUNCH (-5)      /* a kernel launch failed; see dtb_strerror */
+
+#define DTB_F32 0
+#define DTB_BF16 1
+
+#define DTB_NORM_RMS 0         /* RMSNorm with gamma */
+#define DTB_NORM_RMS_NOGAMMA 1 /* RMSNorm without gamma */
+#define DTB_NORM_LAYER 2       /* LayerNorm with gamma and beta */
+
+#define DTB_MLP_SWIGLU 0       /* h = silu(x Wg^T) * (x Wu^T) */
+#define DTB_MLP_RELU 1         /* h = relu(x W1^T + b1) */
+#define DTB_MLP_GELU_TANH 2    /* h = gelu_tanh(x W1^T + b1) */
+
+#define DTB_ROPE_NONE 0
+#define DTB_ROPE_NEOX 1        /* half-split pairs (i, i + hd/2) */
+
+/* Supported head widths: hd in {4, 8, 16, 32, 64, 128} for DTB_F32 and
+ * {8, 16, 32, 64, 128} for DTB_BF16 (hd * element size a multiple of 16 bytes). */
+
+/* ---- causal GQA flash attention ----------------------------------------
+ * attn_forward: "nanoeuler — CUDA kernels", flash_attn_forward_kernel
+ * declaration (packed qkv in; out and lse out), with the softmax of
+ * attention_cpu_fwd on the same page:
+ *   s_tj = (q_t . k_j) / sqrt(hd) for j <= t, o_t = sum_j softmax_j(s_t) v_j,
+ *   lse_t = max_j s_tj + ln sum_j exp(s_tj - max_j s_tj)  (natural log).
+ *   qkv  [B, T, QKV]  input, dtype
+ *   out  [B, T, C]    output, dtype; head h at columns h*hd .. h*hd+hd-1
+ *   lse  [B, NH, T]   output, fp32
+ * B == 0 or T == 0 is a no-op.  No workspace. */
+int attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV,
+                 int dtype, void *stream);
+
+/* attn_backward: the same page's flash_attn_backward_kernel declaration
+ * (dqkv from qkv, out, dout, lse); the gradient is the softmax backward of
+ * attention_cpu_bwd there and of attention_backward on the "microgpt.cu" page:
+ *   P_tj = exp(s_tj - lse_t), D_t = sum_d dO_td O_td, dS_tj = P_tj (dO_t.v_j - D_t),
+ *   dq_t = sum_j dS_tj k_j / sqrt(hd), dk_j = sum_{t, h in group} dS_tj q_t / sqrt(hd),
+ *   dv_j = sum_{t, h in group} P_tj dO_t.
+ *   dqkv [B, T, QKV]  output, dtype, OVERWRITTEN (every element written)
+ *   qkv, out, dout    inputs as in attn_forward (out and lse from attn_forward)
+ *   workspace attn_workspace_bytes(B, T, NH) bytes of device scratch (holds
+ *             D [B, NH, T] fp32); contents on entry are ignored
+ * Deterministic (no atomics). */
+int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout,
+                  const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
+                  void *workspace, void *stream);
+size_t attn_workspace_bytes(int B, int T, int NH);
+
+/* ---- the block --------------------------------------------------------- */
+typedef struct {
+    int B, T, C, NH, NKV, H; /* H = MLP hidden width */
+    int norm;                /* DTB_NORM_* (both norms of the block) */
+    int mlp;                 /* DTB_MLP_* */
+    int rope;                /* DTB_ROPE_* */
+    float rope_base;         /* theta_i = rope_base^(-2i/hd) */
+    float eps;               /* inside the square root of both norms */
+    int qkv_bias, o_bias, mlp_bias; /* 0/1: which linear layers carry a bias */
+    int dtype;               /* DTB_F32 / DTB_BF16 */
+} dtb_block_cfg;
+
+/* Block parameters (dtype storage).  Unused entries may be NULL.
+ *   g1, b1   [C]      norm1 gamma / beta (beta: LayerNorm only)
+ *   wqkv     [QKV, C] packed q, k, v projection; bqkv [QKV]
+ *   wo       [C, C]   output projection; bo [C]
+ *   g2, b2   [C]      norm2 gamma / beta
+ *   w_up     SwiGLU: [2H, C], rows 0..H-1 the gate, rows H..2H-1 the up
+ *            projection; ReLU / GELU: [H, C].  b_up [2H] or [H]
+ *   w_down   [C, H];  b_down [C] */
+typedef struct {
+    const void *g1, *b1, *wqkv, *bqkv, *wo, *bo, *g2, *b2, *w_up, *b_up, *w_down, *b_down;
+} dtb_block_weights;
+
+/* Parameter gradients, fp32, same shapes as dtb_block_weights, ACCUMULATED
+ * (+=): the caller zeroes them before the first backward of a step (cuBLAS
+ * beta = 1 in nanoeuler's matmul_backward_*_cuda; += in llm.c's backward).
+ * Entries for parameters the config does not use are ignored. */
+typedef struct {
+    float *g1, *b1, *wqkv, *bqkv, *wo, *bo, *g2, *b2, *w_up, *b_up, *w_down, *b_down;
+} dtb_block_grads;
+
+/* Byte offsets of the activations block_forward stores in `saved` (each
+ * 256-byte aligned; -1 where the config has no such tensor).
+ *   n1 [BT, C] dtype        norm1 output
+ *   r1, mu1 [BT] fp32       norm1 rstd and mean (mean: LayerNorm only)
+ *   qkv [BT, QKV] dtype     projection + bias, after RoPE on q and k
+ *   o [BT, C] dtype         attention output;  lse [B, NH, T] fp32
+ *   x2 [BT, C] dtype        x + attention branch
+ *   n2, r2, mu2             as n1, r1, mu1 for norm2
+ *   up [BT, 2H or H] dtype  MLP pre-activation ([gate | up] for SwiGLU)
+ *   h [BT, H] dtype         MLP activation output */
+typedef struct {
+    long long n1, r1, mu1, qkv, o, lse, x2, n2, r2, mu2, up, h, total;
+} dtb_saved_layout;
+
+/* Sizes (bytes) of the caller-provided `saved` and `workspace` buffers for a
+ * config; 0 if the config is invalid.  One workspace serves both calls. */
+size_t block_saved_bytes(const dtb_block_cfg *cfg);
+size_t block_workspace_bytes(const dtb_block_cfg *cfg);
+int block_saved_layout(const dtb_block_cfg *cfg, dtb_saved_layout *layout);
+
+/* block_forward: the pre-norm block of "nanoeuler — CUDA kernels" run_train /
+ * forward_gpu (RMSNorm, QKV GEMM, RoPE, flash attention, O GEMM + residual,
+ * RMSNorm, MLP GEMMs, down GEMM + residual), generalised by the mini-Qwen2
+ * trainer (QKV bias before NeoX RoPE), llm.c's gpt2_forward (LayerNorm, GELU,
+ * biases) and microgpt.cu's forward_position (RMSNorm without gamma, ReLU):
+ *   n1 = Norm1(x); qkv = n1 Wqkv^T + bqkv; RoPE(q, k); o, lse = attention(qkv);
+ *   x2 = x + o Wo^T + bo; n2 = Norm2(x2); up = n2 Wup^T + bup; h = act(up);
+ *   x_out = x2 + h Wdown^T + bdown.
+ *   x_in  [B, T, C] dtype input;  x_out [B, T, C] dtype output (must not alias x_in)
+ *   saved block_saved_bytes(cfg) bytes, written (read later by block_backward)
+ *   workspace block_workspace_bytes(cfg) bytes, scratch */
+int block_forward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const void *x_in,
+                  void *x_out, void *saved, void *workspace, void *stream);
+
+/* block_backward: the backward of block_forward (nanoeuler run_train's
+ * backward sequence; llm.c gpt2_backward):
+ *   dh = dy Wdown (+dWdown, dbdown); dup = act'(dh); dn2 = dup Wup (+dWup, dbup);
+ *   dx2 = dy + Norm2^T(dn2) (+dg2, db2); do = dx2 Wo (+dWo, dbo);
+ *   dqkv = attention^T(do); inverse RoPE on dq, dk; dn1 = dqkv Wqkv (+dWqkv, dbqkv);
+ *   dx = dx2 + Norm1^T(dn1) (+dg1, db1).
+ *   x_in   the block input given to block_forward
+ *   saved  as written by block_forward for the same x_in and weights
+ *   dx_out [B, T, C] dtype: gradient of the loss w.r.t. x_out (input)
+ *   dx_in  [B, T, C] dtype: gradient w.r.t. x_in (output, OVERWRITTEN);
+ *          may alias dx_out (the residual gradient is updated in place)
+ *   g      parameter gradients, fp32, ACCUMULATED
+ *   workspace block_workspace_bytes(cfg) bytes, scratch */
+int block_backward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const void *x_in,
+                   const void *saved, const void *dx_out, void *dx_in,
+                   const dtb_block_grads *g, void *workspace, void *stream);
+
+/* ---- misc ---------------------------------------------------------------- */
+const char *dtb_strerror(int code);
+const char *dtb_version(void);
+
+/* Optional per-kernel timing for measurement: while enabled, every kernel the
+ * library enqueues is bracketed by HIP events on its stream, grouped by kernel
+ * class (0 gemm, 1 attn_fwd, 2 attn_bwd, 3 elementwise), together with the
+ * algorithmic flops / bytes of each launch.  dtb_timing_collect() waits for
+ * the recorded events, adds the elapsed times to the running totals and
+ * returns the number of classes filled (at most max_classes).  Not for use
+ * under graph capture. */
+typedef struct {
+    double ms;          /* summed kernel time */
+    double flops;       /* summed algorithmic flops */
+    double bytes;       /* summed algorithmic HBM bytes */
+    long long launches; /* number of launches */
+} dtb_timing;
+int dtb_timing_enable(int on);
+int dtb_timing_collect(dtb_timing *out, int max_classes);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/dtb.h declares, and rejects invalid arguments with the
+documented error codes before touching a stream."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from decoder_only_transformer_block_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from decoder_only_transformer_block_amd import build
+        build.build()
+    return binding
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dtb.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(B):
+    names = declared_functions()
+    assert {"block_forward", "block_backward", "attn_forward", "attn_backward"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    L = B.lib()
+    for n in names:
+        getattr(L, n)
+
+
+def _cfg(binding, **kw):
+    from decoder_only_transformer_block_amd import configs
+    return binding.make_cfg(configs.LLAMA_GQA.replace(**kw))
+
+
+def test_shape_validation(B):
+    L = B.lib()
+    for kw in [dict(NH=31), dict(NKV=3), dict(C=2048 + 8, NH=8), dict(H=5630), dict(B=-1),
+               dict(C=96, NH=1, NKV=1),          # hd 96 unsupported
+               dict(C=64, NH=16, NKV=16)]:       # bf16 hd 4 unsupported
+        c = _cfg(B, **kw)
+        assert L.block_saved_bytes(ctypes.byref(c)) == 0, kw
+        assert L.block_workspace_bytes(ctypes.byref(c)) == 0, kw
+        rc = L.block_forward(ctypes.byref(c), None, None, None, None, None, None)
+        assert rc == -1, (kw, rc)
+        assert "shape" in L.dtb_strerror(rc).decode()
+
+
+def test_enum_dtype_pointer_validation(B):
+    L = B.lib()
+    c = _cfg(B)
+    c.norm = 7
+    assert L.block_forward(ctypes.byref(c), None, None, None, None, None, None) == -4
+    c = _cfg(B)
+    c.dtype = 5
+    assert L.block_forward(ctypes.byref(c), None, None, None, None, None, None) == -3
+    c = _cfg(B)
+    w = B.BlockWeights()
+    assert L.block_forward(ctypes.byref(c), ctypes.byref(w), None, None, None, None, None) == -2
+    assert L.block_forward(None, None, None, None, None, None, None) == -2
+    # misaligned pointer
+    bad = ctypes.c_void_p(0x1008)
+    assert L.attn_forward(bad, bad, bad, 1, 16, 64, 4, 2, 0, None) == -2
+    assert L.attn_forward(None, None, None, 1, 16, 64, 4, 2, 9, None) == -3
+    assert L.attn_backward(None, None, None, None, None, 1, 16, 64, 3, 1, 0, None, None) == -1
+
+
+def test_empty_problem_is_ok_without_pointers(B):
+    L = B.lib()
+    assert L.attn_forward(None, None, None, 0, 16, 64, 4, 2, 0, None) == 0
+    assert L.attn_backward(None, None, None, None, None, 3, 0, 64, 4, 2, 1, None, None) == 0
+    c = _cfg(B, B=0)
+    assert L.block_forward(ctypes.byref(c), None, None, None, None, None, None) == 0
+
+
+def test_saved_layout_consistent(B):
+    from decoder_only_transformer_block_amd import configs
+    for cfg in configs.BLOCK_CONFIGS.values():
+        c = B.make_cfg(cfg)
+        lay = B.block_saved_layout(c)
+        assert lay.total == B.block_saved_bytes(c)
+        es = 2 if cfg.dtype == "bf16" else 4
+        BT = cfg.B * cfg.T
+        offs = sorted((getattr(lay, n), n) for n in ("n1", "r1", "mu1", "qkv", "o", "lse", "x2", "n2", "r2",
+                                                       "mu2", "up", "h") if getattr(lay, n) >= 0)
+        assert all(o % 256 == 0 for o, _ in offs)
+        assert lay.h + BT * cfg.H * es <= lay.total
+        assert (lay.mu1 >= 0) == (cfg.norm == "layer")
+        assert B.block_workspace_bytes(c) > 0
+    assert B.attn_workspace_bytes(1, 16384, 32) >= 16384 * 32 * 4
