@@ -1,0 +1,218 @@
+"""Benchmark: one training step of a stack of pre-norm decoder blocks
+(forward + backward of every layer, inputs resident in HBM) on one MI355X.
+
+Default workload: the Llama-style GQA stack -- 4 layers, B=8, T=2048, C=2048,
+NH=32, NKV=8, head 64, SwiGLU H=5632, RMSNorm gamma, NeoX RoPE base 1e4, bf16
+storage / fp32 accumulation, seeded N(0, 0.02) weights, x_in = embedding rows
+of seeded uniform token ids, seeded N(0, 1) upstream gradient.
+
+Prints ONE JSON line.  value = tokens/s per block = B*T*L / (time of one
+forward+backward of the L-block stack).  The roofline object reports the
+dominant kernel class (the MFMA GEMMs) from HIP events recorded around every
+launch on its stream during the timed region; cpu_baseline times the oracle
+(plain fp64 C) on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X datasheet)
+HBM_PEAK = 8000.0                        # GB/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama_gqa",
+                    choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
+    ap.add_argument("--cpu-tokens", type=int, default=256,
+                    help="tokens of the oracle's bounded sample (one sequence, one layer)")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, tokens):
+    import numpy as np
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    oracle.build(force=False)
+    sub = cfg.replace(L=1, B=1, T=tokens)
+    w = configs.block_weights(sub, 0)
+    x = configs.block_input(sub)
+    dy = configs.block_dout(sub)
+    t0 = time.perf_counter()
+    y, sv = oracle.block_forward(sub, w, x)
+    oracle.block_backward(sub, w, x, sv, dy)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one {cfg.name} block (C={cfg.C}, NH={cfg.NH}, NKV={cfg.NKV}, H={cfg.H}) forward+backward "
+                      f"on B=1, T={tokens} in fp64, {dt:.2f} s"}
+
+
+def cpu_baseline_attn(cfg, tokens):
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    oracle.build(force=False)
+    sub = cfg.replace(T=tokens)
+    qkv, dout = configs.attn_inputs(sub)
+    t0 = time.perf_counter()
+    oracle.attn_forward(qkv, sub.B, sub.T, sub.C, sub.NH, sub.NKV)
+    oracle.attn_backward(qkv, dout, sub.B, sub.T, sub.C, sub.NH, sub.NKV)
+    dt = time.perf_counter() - t0
+    return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"attention forward+backward B=1, T={tokens}, NH={cfg.NH}, NKV={cfg.NKV}, hd={cfg.hd} "
+                      f"in fp64, {dt:.2f} s"}
+
+
+def bench_block(args, cfg):
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    from decoder_only_transformer_block_amd.runtime import BlockStack, to_device
+
+    ws = [configs.block_weights(cfg, l) for l in range(cfg.L)]
+    x = to_device(configs.block_input(cfg), cfg.dtype)
+    dy = to_device(configs.block_dout(cfg), cfg.dtype)
+    st = BlockStack(cfg, ws)
+    del ws
+
+    def step():
+        st.forward(x)
+        st.backward(dy)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_timing:
+        binding.timing_enable(True)
+        binding.timing_collect()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tim = {}
+    if not args.no_timing:
+        tim = binding.timing_collect()
+        binding.timing_enable(False)
+    ms = dt * 1e3 / args.steps
+    tokens = cfg.B * cfg.T
+    value = tokens * cfg.L / (dt / args.steps)
+    return ms, value, tim
+
+
+def bench_attn(args, cfg):
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    from decoder_only_transformer_block_amd.runtime import to_device
+    qkv_np, dout_np = configs.attn_inputs(cfg)
+    q, d = to_device(qkv_np, cfg.dtype), to_device(dout_np, cfg.dtype)
+    del qkv_np, dout_np
+    B, T, C = cfg.B, cfg.T, cfg.C
+    out = torch.empty((B, T, C), dtype=q.dtype, device="cuda")
+    lse = torch.empty((B, cfg.NH, T), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    wsb = torch.empty(binding.attn_workspace_bytes(B, T, cfg.NH), dtype=torch.uint8, device="cuda")
+
+    def step():
+        binding.attn_forward(out, lse, q, B, T, C, cfg.NH, cfg.NKV, cfg.dtype)
+        binding.attn_backward(dq, q, out, d, lse, B, T, C, cfg.NH, cfg.NKV, cfg.dtype, wsb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if not args.no_timing:
+        binding.timing_enable(True)
+        binding.timing_collect()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tim = {}
+    if not args.no_timing:
+        tim = binding.timing_collect()
+        binding.timing_enable(False)
+    return dt * 1e3 / args.steps, B * T / (dt / args.steps), tim
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this build has no multi-GPU "
+              "path: the block shards over sequences with one gradient all-reduce per layer, described in the "
+              "design notes but not built.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from decoder_only_transformer_block_amd import configs
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    cfg = configs.ALL_CONFIGS[args.workload]
+
+    if args.workload == "attn_long":
+        ms, value, tim = bench_attn(args, cfg)
+        flops_step = cfg.fwd_flops() * 3.5
+        config = {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "NH": cfg.NH, "NKV": cfg.NKV, "hd": cfg.hd,
+                  "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "none (1 GPU)"}
+    else:
+        ms, value, tim = bench_block(args, cfg)
+        flops_step = (cfg.gemm_flops_per_layer() + cfg.attn_flops_per_layer()) * cfg.L
+        config = {"workload": cfg.name, "layers": cfg.L, "B": cfg.B, "T": cfg.T, "C": cfg.C, "NH": cfg.NH,
+                  "NKV": cfg.NKV, "head_dim": cfg.hd, "H": cfg.H, "norm": cfg.norm, "mlp": cfg.mlp,
+                  "rope": cfg.rope, "global_batch": cfg.B, "seq_len": cfg.T, "parallelism": "none (1 GPU)"}
+
+    peak = PEAK[cfg.dtype]
+    breakdown = {}
+    for k, v in tim.items():
+        if v["launches"] == 0:
+            continue
+        e = {"ms_per_step": round(v["ms"] / args.steps, 4), "launches_per_step": v["launches"] // args.steps}
+        if v["flops"] > 0:
+            tf = v["flops"] / (v["ms"] * 1e-3) / 1e12
+            e["tflops"] = round(tf, 2)
+            e["frac_mfma_peak"] = round(tf / peak, 4)
+        if v["bytes"] > 0 and v["flops"] == 0:
+            gb = v["bytes"] / (v["ms"] * 1e-3) / 1e9
+            e["gbps"] = round(gb, 1)
+            e["frac_hbm_peak"] = round(gb / HBM_PEAK, 4)
+        breakdown[k] = e
+    dom = "attn_bwd" if args.workload == "attn_long" else "gemm"
+    roof = None
+    if dom in tim and tim[dom]["launches"]:
+        d = tim[dom]
+        ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        roof = {"kernel": "attention backward (dq + dk/dv kernels)" if dom == "attn_bwd" else
+                "MFMA GEMM (all QKV/O/MLP forward, dinp and dW launches)",
+                "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None,
+                "avg_launch_ms": round(d["ms"] / d["launches"], 4),
+                "flops_per_launch": d["flops"] / d["launches"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline_attn(cfg, 1024) if args.workload == "attn_long" else cpu_baseline(cfg, args.cpu_tokens)
+
+    line = {
+        "metric": "train tokens/s per block fwd+bwd; attn+GEMM TFLOP/s as % MFMA peak",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic (seeded N(0,0.02) weights, uniform token ids, random init)",
+        "config": config,
+        "algorithmic_tflops_per_step": round(flops_step / 1e12, 4),
+        "achieved_tflops": round(flops_step / (ms * 1e-3) / 1e12, 2),
+        "roofline": roof, "breakdown": breakdown, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
