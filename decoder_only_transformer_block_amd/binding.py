@@ -76,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.block_saved_layout.argtypes = [cp, ctypes.POINTER(SavedLayout)]
         L.block_forward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, v]
         L.block_backward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, ctypes.POINTER(BlockGrads), v, v]
+        L.linear_forward.argtypes = [v, v, v, v, v, i, i, i, i, v]
+        L.linear_backward.argtypes = [v, v, v, v, v, v, i, i, i, i, v, v]
+        L.linear_workspace_bytes.argtypes = [i, i, i, i]
+        L.linear_workspace_bytes.restype = z
         L.dtb_strerror.argtypes = [i]
         L.dtb_strerror.restype = ctypes.c_char_p
         L.dtb_version.restype = ctypes.c_char_p
@@ -135,6 +139,20 @@ def attn_workspace_bytes(B, T, NH) -> int:
 def attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, workspace, stream=None):
     check(lib().attn_backward(_ptr(dqkv), _ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, T, C, NH, NKV,
                               DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_backward")
+
+
+def linear_forward(out, inp, w, bias, res, R, K, N, dtype, stream=None):
+    check(lib().linear_forward(_ptr(out), _ptr(inp), _ptr(w), _ptr(bias), _ptr(res), R, K, N, DTYPE[dtype],
+                               _stream(stream)), "linear_forward")
+
+
+def linear_workspace_bytes(R, K, N, dtype) -> int:
+    return lib().linear_workspace_bytes(R, K, N, DTYPE[dtype])
+
+
+def linear_backward(dinp, dw, db, dout, inp, w, R, K, N, dtype, workspace, stream=None):
+    check(lib().linear_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w), R, K, N,
+                                DTYPE[dtype], _ptr(workspace), _stream(stream)), "linear_backward")
 
 
 def block_saved_bytes(cfg: BlockCfg) -> int:

@@ -267,6 +267,71 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
                                 (hipStream_t)stream);
 }
 
+static int check_linear(int R, int K, int N, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (R < 0 || K <= 0 || N <= 0 || K % 8 || N % 8) return DTB_EINVAL_SHAPE;
+    if ((long long)R * (K > N ? K : N) >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+size_t linear_workspace_bytes(int R, int K, int N, int dtype) {
+    if (check_linear(R, K, N, dtype)) return 0;
+    size_t g = gemm_ws_bytes(N, K, R, dtype);
+    size_t b = (size_t)bias_grad_parts(R) * N * 4;
+    return al(g) + al(b) + 256;
+}
+
+int linear_forward(void *out, const void *inp, const void *w, const void *bias, const void *res, int R, int K,
+                   int N, int dtype, void *stream) {
+    int e = check_linear(R, K, N, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(out) || !ptr_ok(inp) || !ptr_ok(w)) return DTB_EINVAL_PTR;
+    if ((bias && !aligned(bias)) || (res && !aligned(res))) return DTB_EINVAL_PTR;
+    GemmArgs g{};
+    g.dtype = dtype;
+    g.a_kmajor = g.b_kmajor = true;
+    g.A = inp; g.lda = K; g.B = w; g.ldb = K; g.M = R; g.N = N; g.K = K;
+    g.out = out; g.ldo = N; g.bias = bias; g.res = res; g.ldr = N;
+    return gemm(g, nullptr, 0, (hipStream_t)stream);
+}
+
+int linear_backward(void *dinp, float *dw, float *db, const void *dout, const void *inp, const void *w, int R,
+                    int K, int N, int dtype, void *workspace, void *stream) {
+    int e = check_linear(R, K, N, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(dout) || (dinp && !ptr_ok(w)) || (dw && !ptr_ok(inp))) return DTB_EINVAL_PTR;
+    if ((dinp && !aligned(dinp)) || (dw && !aligned(dw)) || (db && !aligned(db))) return DTB_EINVAL_PTR;
+    if ((dw || db) && !ptr_ok(workspace)) return DTB_EINVAL_PTR;
+    hipStream_t s = (hipStream_t)stream;
+    if (dinp) {
+        GemmArgs g{};
+        g.dtype = dtype;
+        g.a_kmajor = true;
+        g.b_kmajor = false;
+        g.A = dout; g.lda = N; g.B = w; g.ldb = K; g.M = R; g.N = K; g.K = N; g.out = dinp; g.ldo = K;
+        int r = gemm(g, nullptr, 0, s);
+        if (r) return r;
+    }
+    size_t gbytes = gemm_ws_bytes(N, K, R, dtype);
+    if (dw) {
+        GemmArgs g{};
+        g.dtype = dtype;
+        g.a_kmajor = g.b_kmajor = false;
+        g.out_f32 = g.accumulate = true;
+        g.A = dout; g.lda = N; g.B = inp; g.ldb = K; g.M = N; g.N = K; g.K = R; g.out = dw; g.ldo = K;
+        int r = gemm(g, workspace, gbytes, s);
+        if (r) return r;
+    }
+    if (db) {
+        float *part = (float *)((char *)workspace + al(gbytes));
+        int r = bias_grad(dtype, dout, R, N, db, part, bias_grad_parts(R), s);
+        if (r) return r;
+    }
+    return DTB_OK;
+}
+
 static int check_weights(const dtb_block_cfg *c, const dtb_block_weights *w) {
     if (!w) return DTB_EINVAL_PTR;
     if (!ptr_ok(w->wqkv) || !ptr_ok(w->wo) || !ptr_ok(w->w_up) || !ptr_ok(w->w_down)) return DTB_EINVAL_PTR;

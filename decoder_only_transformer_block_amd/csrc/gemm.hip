@@ -281,6 +281,192 @@ __global__ __launch_bounds__(256) void gemm_kernel(KParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 256x256 kernel: 8 waves (4 x 2), wave tile 64 x 128 (2 x 4 MFMA blocks),
+// two waves per SIMD so that one wave's LDS / barrier waits are covered by the
+// other's MFMAs.  K slab 64; every operand layout stages 16 VGPRs per thread:
+// k-major as four 16-byte row chunks, m/n-major as one 4(k) x 8(m) block
+// transposed in registers.  LDS rows are 128 bytes; the 16-byte chunk index is
+// XOR-ed with (row ^ row/8) & 7, which keeps both the MFMA fragment reads (32
+// consecutive rows) and the transposed 8-byte writes (rows 8 apart) spread over
+// the banks.  Interior tiles take branch-free loads.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int swz2(int row, int chunk) {
+    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+template <bool KMAJOR> struct Stage256;
+
+template <> struct Stage256<true> {
+    // 256 rows x 8 chunks = 2048 chunks, 4 per thread: row = t/8 + 64 p, chunk = t%8
+    u32x4 reg[4];
+    template <bool FULL>
+    __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
+        const int t = threadIdx.x, c = t & 7;
+        const int kk = k0 + c * 8;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            int r = (t >> 3) + 64 * p, gr = row0 + r;
+            if (FULL || (gr < nrows && kk < kend)) reg[p] = ld16(base + (long long)gr * ld + kk);
+            else reg[p] = u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const {
+        const int t = threadIdx.x, c = t & 7;
+#pragma unroll
+        for (int p = 0; p < 4; p++) {
+            int r = (t >> 3) + 64 * p;
+            *reinterpret_cast<u32x4 *>(lds + swz2(r, c)) = reg[p];
+        }
+    }
+};
+
+template <> struct Stage256<false> {
+    // element (k, r) at base[k*ld + r]; thread t owns the 4(k) x 8(r) block
+    // rb = t % 32 (rows rb*8..+8), kb = t / 32 (k kb*4..+4)
+    u32x4 reg[4];
+    template <bool FULL>
+    __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
+        const int t = threadIdx.x;
+        const int rb = t & 31, kb = t >> 5;
+        const int gr = row0 + rb * 8;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int k = k0 + kb * 4 + i;
+            if (FULL || (gr < nrows && k < kend)) reg[i] = ld16(base + (long long)k * ld + gr);
+            else reg[i] = u32x4{0, 0, 0, 0};
+        }
+    }
+    __device__ __forceinline__ void store(char *lds) const {
+        const int t = threadIdx.x;
+        const int rb = t & 31, kb = t >> 5;
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            u32x2 o;
+#pragma unroll
+            for (int q = 0; q < 2; q++) {
+                uint32_t a = reg[2 * q][j >> 1], b = reg[2 * q + 1][j >> 1];
+                o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+            }
+            int r = rb * 8 + j;
+            *reinterpret_cast<u32x2 *>(lds + swz2(r, kb >> 1) + ((kb & 1) << 3)) = o;
+        }
+    }
+};
+
+template <bool AK, bool BKM, int MODE>
+__global__ __launch_bounds__(512) void gemm256_kernel(KParams p) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int STAGE = (BM + BN) * 128;
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(nm, nn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = blockIdx.z * p.kchunk;
+    const int kend = min(p.K, kbeg + p.kchunk);
+    const int nk = (kend - kbeg + BK - 1) / BK;
+    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
+
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
+
+    const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
+    const bf16 *B = reinterpret_cast<const bf16 *>(p.B);
+    Stage256<AK> la;
+    Stage256<BKM> lb;
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; i++)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
+
+    auto load = [&](int k0) {
+        if (interior && k0 + BK <= kend) {
+            la.template load<true>(A, p.lda, m0, p.M, k0, kend);
+            lb.template load<true>(B, p.ldb, n0, p.N, k0, kend);
+        } else {
+            la.template load<false>(A, p.lda, m0, p.M, k0, kend);
+            lb.template load<false>(B, p.ldb, n0, p.N, k0, kend);
+        }
+    };
+
+    if (nk > 0) {
+        load(kbeg);
+        la.store(smem);
+        lb.store(smem + BM * 128);
+    }
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; kt++) {
+        const bool more = kt + 1 < nk;
+        if (more) load(kbeg + (kt + 1) * BK);
+        const char *As = smem + (kt & 1) * STAGE;
+        const char *Bs = As + BM * 128;
+        u32x4 af[2][2], bfr[2][4];
+#pragma unroll
+        for (int i = 0; i < 2; i++) af[0][i] = *reinterpret_cast<const u32x4 *>(As + swz2(wm * 64 + i * 32 + l32, g));
+#pragma unroll
+        for (int j = 0; j < 4; j++) bfr[0][j] = *reinterpret_cast<const u32x4 *>(Bs + swz2(wn * 128 + j * 32 + l32, g));
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+            const int cur = c & 1, nxt = cur ^ 1;
+            if (c < 3) {
+#pragma unroll
+                for (int i = 0; i < 2; i++)
+                    af[nxt][i] = *reinterpret_cast<const u32x4 *>(As + swz2(wm * 64 + i * 32 + l32, 2 * (c + 1) + g));
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    bfr[nxt][j] = *reinterpret_cast<const u32x4 *>(Bs + swz2(wn * 128 + j * 32 + l32, 2 * (c + 1) + g));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++)
+                    acc[i][j] = mfma32(__builtin_bit_cast(bf16x8, af[cur][i]), __builtin_bit_cast(bf16x8, bfr[cur][j]),
+                                       acc[i][j]);
+        }
+        if (more) {
+            char *nx = smem + ((kt + 1) & 1) * STAGE;
+            la.store(nx);
+            lb.store(nx + BM * 128);
+        }
+        __syncthreads();
+    }
+
+    // ---- epilogue (MODE 0: bf16 store with optional bias / residual; 2: fp32 +=; 3: split partial)
+    const bf16 *bias = reinterpret_cast<const bf16 *>(p.bias);
+    const bf16 *res = reinterpret_cast<const bf16 *>(p.res);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int n = n0 + wn * 128 + j * 32 + l32;
+        if (n >= p.N) continue;
+        const float bv = (MODE == 0 && bias) ? (float)bias[n] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const int m = m0 + wm * 64 + i * 32 + acc_row(r, lane);
+                if (m >= p.M) continue;
+                float v = acc[i][j][r];
+                if constexpr (MODE == 0) {
+                    v += bv;
+                    if (res) v += (float)res[(long long)m * p.ldr + n];
+                    reinterpret_cast<bf16 *>(p.out)[(long long)m * p.ldo + n] = (bf16)v;
+                } else if constexpr (MODE == 2) {
+                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] += v;
+                } else {
+                    p.part[((long long)blockIdx.z * p.M + m) * p.N + n] = v;
+                }
+            }
+        }
+    }
+}
+
 // out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0)
 __global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *out, long long ldo, int M, int N,
                                                       int splits) {
@@ -320,12 +506,42 @@ static hipError_t launch_layout(const KParams &p, bool ak, bool bk, int splits, 
     return launch_t<T, BM, BN, false, true>(p, splits, s);
 }
 
+template <bool AK, bool BKM, int MODE>
+static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
+    constexpr int LDS = 2 * (256 + 256) * 128;
+    static bool attr_set = false;
+    if (!attr_set) {
+        hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<AK, BKM, MODE>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
+        if (e != hipSuccess) return e;
+        attr_set = true;
+    }
+    int nm = (p.M + 255) / 256, nn = (p.N + 255) / 256;
+    hipLaunchKernelGGL((gemm256_kernel<AK, BKM, MODE>), dim3(nm * nn, 1, splits), dim3(512), LDS, s, p);
+    return hipGetLastError();
+}
+
+template <int MODE>
+static hipError_t launch256_mode(const KParams &p, bool ak, bool bk, int splits, hipStream_t s) {
+    if (ak && bk) return launch256_t<true, true, MODE>(p, splits, s);
+    if (ak && !bk) return launch256_t<true, false, MODE>(p, splits, s);
+    if (!ak && !bk) return launch256_t<false, false, MODE>(p, splits, s);
+    return launch256_t<false, true, MODE>(p, splits, s);
+}
+
+static hipError_t launch256(const KParams &p, bool ak, bool bk, int splits, hipStream_t s) {
+    if (p.out_mode == 0) return launch256_mode<0>(p, ak, bk, splits, s);
+    if (p.out_mode == 2) return launch256_mode<2>(p, ak, bk, splits, s);
+    return launch256_mode<3>(p, ak, bk, splits, s);
+}
+
 struct TileChoice {
     int bm, bn;
 };
-static TileChoice choose_tile(int M, int N, int dtype) {
+static TileChoice choose_tile(int M, int N, int dtype, bool splittable) {
     auto tiles = [&](int bm, int bn) { return (long long)((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (dtype == DTB_BF16) {
+        if (M >= 256 && N >= 256 && (tiles(256, 256) >= 120 || splittable)) return {256, 256};
         if (tiles(256, 128) >= 512) return {256, 128};
         if (tiles(128, 128) >= 256) return {128, 128};
         return {64, 64};
@@ -346,14 +562,16 @@ static int choose_splits(const GemmArgs &g, TileChoice tc) {
 size_t gemm_ws_bytes(int M, int N, int K, int dtype) {
     GemmArgs g{};
     g.M = M; g.N = N; g.K = K; g.dtype = dtype; g.out_f32 = true; g.accumulate = true;
-    TileChoice tc = choose_tile(M, N, dtype);
+    TileChoice tc = choose_tile(M, N, dtype, true);
     int sp = choose_splits(g, tc);
     return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
 }
 
 int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     if (g.M <= 0 || g.N <= 0) return DTB_OK;
-    TileChoice tc = choose_tile(g.M, g.N, g.dtype);
+    const bool splittable = g.out_f32 && g.accumulate && !g.bias && !g.res;
+    TileChoice tc = choose_tile(g.M, g.N, g.dtype, splittable);
+    if (tc.bm == 256 && tc.bn == 256 && g.out_f32 && !g.accumulate) tc = {128, 128};
     int splits = choose_splits(g, tc);
     if (splits > 1 && (!ws || ws_bytes < (size_t)splits * g.M * g.N * sizeof(float))) splits = 1;
     const int BK = g.dtype == DTB_BF16 ? 64 : 32;
@@ -371,7 +589,8 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     if (g_timing_on) timing_begin(s);
     hipError_t e;
     if (g.dtype == DTB_BF16) {
-        if (tc.bm == 256) e = launch_layout<bf16, 256, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
+        if (tc.bm == 256 && tc.bn == 256) e = launch256(p, g.a_kmajor, g.b_kmajor, splits, s);
+        else if (tc.bm == 256) e = launch_layout<bf16, 256, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
         else if (tc.bm == 128) e = launch_layout<bf16, 128, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
         else e = launch_layout<bf16, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
     } else {

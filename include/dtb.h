@@ -177,6 +177,23 @@ int block_backward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const v
                    const void *saved, const void *dx_out, void *dx_in,
                    const dtb_block_grads *g, void *workspace, void *stream);
 
+/* ---- component: one linear layer ------------------------------------------
+ * The GEMMs block_forward / block_backward run, exposed on their own
+ * ("nanoeuler — CUDA kernels": matmul_forward_cuda, matmul_backward_dinp_cuda,
+ * matmul_backward_dw_cuda; llm.c matmul_forward / matmul_backward with bias).
+ * linear_forward:  out[R, N] = inp[R, K] W[N, K]^T (+ bias[N]) (+ res[R, N])
+ *   out, inp, w, bias, res: dtype; bias and res may be NULL; res may alias out.
+ * linear_backward: dinp[R, K] = dout W (OVERWRITTEN);  dw[N, K] += dout^T inp;
+ *   db[N] += sum_r dout[r, :]   (dw, db fp32, ACCUMULATED; dinp, dw or db may be
+ *   NULL to skip that product).  workspace: linear_workspace_bytes(R, K, N, dtype)
+ *   bytes (split-K partial sums of dw and column partials of db).
+ * K and N must be multiples of 8; R >= 0. */
+int linear_forward(void *out, const void *inp, const void *w, const void *bias, const void *res, int R,
+                   int K, int N, int dtype, void *stream);
+int linear_backward(void *dinp, float *dw, float *db, const void *dout, const void *inp, const void *w,
+                    int R, int K, int N, int dtype, void *workspace, void *stream);
+size_t linear_workspace_bytes(int R, int K, int N, int dtype);
+
 /* ---- misc ---------------------------------------------------------------- */
 const char *dtb_strerror(int code);
 const char *dtb_version(void);

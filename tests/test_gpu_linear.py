@@ -1,0 +1,68 @@
+"""linear_forward / linear_backward (the block's GEMMs, through the C ABI)
+against the oracle's linear layer, element by element.  Shapes are chosen so
+that every kernel path runs: the 256x256 bf16 kernel for the forward (k-major
+operands), the input gradient (n-major weight) and the weight gradient (both
+operands m/n-major) with split-K partials and without; the generic kernel;
+ragged M, N and K tails; and tiny shapes."""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, announce, check, require_gpu
+
+pytestmark = pytest.mark.gpu
+
+# (name, R, K, N): out[R, N] = inp[R, K] W[N, K]^T
+SHAPES = [
+    ("fwd256_ragged", 1100, 136, 6144),     # forward on 5 x 24 tiles of 256 (ragged rows, ragged K slab)
+    ("dinp256", 1100, 6144, 136),           # input gradient on 5 x 24 tiles
+    ("dw256_split", 600, 520, 776),         # weight gradient M=776, N=520 with split-K
+    ("dw256_nosplit", 64, 1024, 2048),      # weight gradient M=2048, N=1024, K=64: one split
+    ("generic_mid", 333, 264, 328),
+    ("tiny", 7, 8, 16),
+    ("one_row", 1, 64, 8),
+]
+
+
+def _run(dtype, R, K, N, seed=3):
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_device, to_numpy
+    tag = f"{R}.{K}.{N}"
+    x = inputs.tensor(seed, "lin.x" + tag, (R, K), dtype=dtype)
+    w = inputs.tensor(seed, "lin.w" + tag, (N, K), std=0.05, dtype=dtype)
+    b = inputs.tensor(seed, "lin.b" + tag, (N,), dtype=dtype)
+    res = inputs.tensor(seed, "lin.res" + tag, (R, N), dtype=dtype)
+    dy = inputs.tensor(seed, "lin.dy" + tag, (R, N), dtype=dtype)
+    announce(f"linear dtype={dtype} R={R} K={K} N={N}")
+    X, W, Bb, RS, DY = (to_device(a, dtype) for a in (x, w, b, res, dy))
+    out = torch.empty((R, N), dtype=X.dtype, device="cuda")
+    binding.linear_forward(out, X, W, Bb, RS, R, K, N, dtype)
+    dinp = torch.full((R, K), float("nan"), dtype=X.dtype, device="cuda")
+    dw = torch.full((N, K), 0.5, dtype=torch.float32, device="cuda")      # accumulates onto 0.5
+    db = torch.full((N,), -0.25, dtype=torch.float32, device="cuda")
+    ws = torch.empty(binding.linear_workspace_bytes(R, K, N, dtype), dtype=torch.uint8, device="cuda")
+    binding.linear_backward(dinp, dw, db, DY, X, W, R, K, N, dtype, ws)
+    torch.cuda.synchronize()
+    ref_out = oracle.linear_forward(x, w, b) + res.astype(np.float64)
+    r_dinp, r_dw, r_db = oracle.linear_backward(dy, x, w)
+    return (to_numpy(out), to_numpy(dinp), to_numpy(dw) - 0.5, to_numpy(db) + 0.25), (ref_out, r_dinp, r_dw, r_db)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("name,R,K,N", SHAPES)
+def test_linear_parity(dtype, name, R, K, N):
+    require_gpu()
+    got, ref = _run(dtype, R, K, N)
+    tol = TOL[dtype]
+    for nm, g, r in zip(("out", "dinp", "dw", "db"), got, ref):
+        check(nm, g, r, tol)
+
+
+def test_linear_rejects_bad_shapes():
+    require_gpu()
+    from decoder_only_transformer_block_amd import binding
+    L = binding.lib()
+    assert L.linear_forward(None, None, None, None, None, 4, 12, 16, 1, None) == -1   # K % 8
+    assert L.linear_forward(None, None, None, None, None, 0, 16, 16, 1, None) == 0    # empty
+    assert L.linear_workspace_bytes(4, 16, 16, 7) == 0
