@@ -68,14 +68,13 @@ template <typename T, int HD, int ROWS, int NT> struct Nat {
     __device__ static __forceinline__ void load(u32x4 *reg, const T *g, long long stride, int row0, int nrows,
                                                 int hd, int tl) {
         constexpr int NCH = AT<T, HD>::NCH, EPC = AT<T, HD>::EPC;
+        const Buf buf(g + (long long)row0 * stride);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int idx = tl + NT * p;
             int r = idx / NCH, c = idx % NCH;
-            if (idx < ITEMS && row0 + r < nrows && c * EPC < hd)
-                reg[p] = ld16(g + (long long)(row0 + r) * stride + c * EPC);
-            else
-                reg[p] = u32x4{0, 0, 0, 0};
+            bool ok = idx < ITEMS && row0 + r < nrows && c * EPC < hd;
+            reg[p] = buf.ld16((int)(((long long)r * stride + c * EPC) * (int)sizeof(T)), ok);
         }
     }
     __device__ static __forceinline__ void store(const u32x4 *reg, char *lds, int tl) {
@@ -93,8 +92,9 @@ template <int HD, int ROWS, int NT> struct Blk {
     static constexpr int NBD = HD / 8, NBR = ROWS / 8;
     static constexpr int ITEMS = NBD * NBR;
     static constexpr int P = (ITEMS + NT - 1) / NT;
-    __device__ static __forceinline__ void load(u32x4 (*reg)[8], const bf16 *g, long long stride, int row0,
+    __device__ static __forceinline__ void load(u32x4 *reg, const bf16 *g, long long stride, int row0,
                                                 int nrows, int hd, int tl) {
+        const Buf buf(g + (long long)row0 * stride);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int idx = tl + NT * p;
@@ -102,14 +102,13 @@ template <int HD, int ROWS, int NT> struct Blk {
             bool live = idx < ITEMS && db * 8 < hd;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                int row = row0 + rb * 8 + i;
-                if (live && row < nrows) reg[p][i] = ld16(g + (long long)row * stride + db * 8);
-                else reg[p][i] = u32x4{0, 0, 0, 0};
+                int row = rb * 8 + i;
+                reg[p * 8 + i] = buf.ld16((int)(((long long)row * stride + db * 8) * 2), live && row0 + row < nrows);
             }
         }
     }
     template <bool NAT, bool TR>
-    __device__ static __forceinline__ void store(const u32x4 (*reg)[8], char *nat, char *tr, int tl) {
+    __device__ static __forceinline__ void store(const u32x4 *reg, char *nat, char *tr, int tl) {
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int idx = tl + NT * p;
@@ -118,11 +117,11 @@ template <int HD, int ROWS, int NT> struct Blk {
             if constexpr (NAT) {
 #pragma unroll
                 for (int i = 0; i < 8; i++)
-                    *reinterpret_cast<u32x4 *>(nat + nat_off<bf16, HD>(rb * 8 + i, db)) = reg[p][i];
+                    *reinterpret_cast<u32x4 *>(nat + nat_off<bf16, HD>(rb * 8 + i, db)) = reg[p * 8 + i];
             }
             if constexpr (TR) {
                 u32x4 o[8];
-                transpose8x8(reg[p], o);
+                transpose8x8(reg + p * 8, o);
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     int d = db * 8 + j;
@@ -133,6 +132,15 @@ template <int HD, int ROWS, int NT> struct Blk {
         }
     }
 };
+
+// Both sides of a wave-uniform "which tensor do I stage" branch must write every
+// element of the shared register array in the same order; otherwise the
+// optimizer merges the two sides' last stores through a pointer and the array
+// is demoted to scratch memory.
+template <int FROM, int TO> __device__ __forceinline__ void zero_tail(u32x4 *reg) {
+#pragma unroll
+    for (int i = FROM; i < TO; i++) reg[i] = u32x4{0, 0, 0, 0};
+}
 
 // ---------------------------------------------------------------------------
 // fragment helpers
@@ -163,9 +171,10 @@ __device__ __forceinline__ void mma_trans(f32x16 *acc, const f32x16 &x, const ch
     if constexpr (std::is_same<T, bf16>::value) {
 #pragma unroll
         for (int hh = 0; hh < 2; hh++) {
-            bf16x8 xb;
+            u32x4 xw;
 #pragma unroll
-            for (int e = 0; e < 8; e++) xb[e] = (bf16)x[8 * hh + e];
+            for (int e = 0; e < 4; e++) xw[e] = pack2_bf16(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
+            const bf16x8 xb = __builtin_bit_cast(bf16x8, xw);
             const int koff = j * 32 + 16 * hh + 4 * g;
 #pragma unroll
             for (int db = 0; db < AT<T, HD>::ND; db++)
@@ -194,13 +203,17 @@ __device__ __forceinline__ void mma_rows(f32x16 &acc, const char *tile, int rowb
     }
 }
 
-// per-lane fragments of one row: chunks 2c+g
+// per-lane fragments of row `row` of a uniform base (row stride `stride`
+// elements): chunks 2c+g of the head slice
 template <typename T, int HD>
-__device__ __forceinline__ void load_row_frag(u32x4 *f, const T *row, bool valid, int hd, int g) {
+__device__ __forceinline__ void load_row_frag(u32x4 *f, const T *base, long long stride, int row, bool valid,
+                                              int hd, int g) {
+    const Buf buf(base);
 #pragma unroll
     for (int c = 0; c < AT<T, HD>::NC; c++) {
         int ch = 2 * c + g;
-        f[c] = (valid && ch * AT<T, HD>::EPC < hd) ? ld16(row + ch * AT<T, HD>::EPC) : u32x4{0, 0, 0, 0};
+        f[c] = buf.ld16((int)(((long long)row * stride + ch * AT<T, HD>::EPC) * (int)sizeof(T)),
+                        valid && ch * AT<T, HD>::EPC < hd);
     }
 }
 
@@ -259,23 +272,26 @@ template <typename T, int HD>
 __device__ __forceinline__ void fwd_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
                                                int T_, int hd) {
     const int t = threadIdx.x;
-    if (t >= 128) {
+    using FC = FwdCfg<T, HD>;
+    if (__builtin_amdgcn_readfirstlane(t >> 6) >= 2) {
         Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t - 128);
+        zero_tail<FC::PK, FC::PREG>(reg);
     } else {
         if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), vb, stride, kv0, T_, hd, t);
+            Blk<HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t);
         else
             Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t);
+        zero_tail<FC::PV, FC::PREG>(reg);
     }
 }
 template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = FwdCfg<T, HD>::KB;
-    if (t >= 128) {
+    if (__builtin_amdgcn_readfirstlane(t >> 6) >= 2) {
         Nat<T, HD, 64, 128>::store(reg, st, t - 128);
     } else {
         if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::template store<false, true>(reinterpret_cast<const u32x4(*)[8]>(reg), nullptr,
+            Blk<HD, 64, 128>::template store<false, true>(reg, nullptr,
                                                          st + KB, t);
         else
             Nat<T, HD, 64, 128>::store(reg, st + KB, t);
@@ -303,7 +319,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
     const T *vbase = kbase + p.NKV * p.hd;
 
     u32x4 qf[A::NC];
-    load_row_frag<T, HD>(qf, base + (long long)qi * stride + h * p.hd, qi < p.T, p.hd, g);
+    load_row_frag<T, HD>(qf, base + h * p.hd, stride, qi, qi < p.T, p.hd, g);
 
     f32x16 O[A::ND];
 #pragma unroll
@@ -335,30 +351,35 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
                 for (int r = 0; r < 16; r++) S[j][r] = 0.f;
                 mma_rows<T, HD>(S[j], Ks, j * 32, qf, lane);
             }
-            float mt = -INFINITY;
+            // keys above the diagonal only occur in the last tiles of a wave
+            if (kv0 + BKV - 1 > qw0) {
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++)
+                        if (kv0 + j * 32 + acc_row(r, lane) > qi) S[j][r] = -INFINITY;
+            }
+            float mt = S[0][0];
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    int key = kv0 + j * 32 + acc_row(r, lane);
-                    float x = key <= qi ? S[j][r] * p.sl2 : -INFINITY;
-                    S[j][r] = x;
-                    mt = fmaxf(mt, x);
-                }
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+                for (int r = 0; r < 16; r++) mt = fmaxf(mt, S[j][r]);
+            mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;   // running max in log2 units
             const float mn = fmaxf(m, mt);
-            const float alpha = exp2f(m - mn);
+            if (!__all(mn == m)) {
+                const float alpha = exp2f(m - mn);
+                lsum *= alpha;
+#pragma unroll
+                for (int d = 0; d < A::ND; d++)
+#pragma unroll
+                    for (int r = 0; r < 16; r++) O[d][r] *= alpha;
+            }
             m = mn;
-            lsum *= alpha;
-#pragma unroll
-            for (int d = 0; d < A::ND; d++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) O[d][r] *= alpha;
 #pragma unroll
             for (int j = 0; j < 2; j++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    float e = exp2f(S[j][r] - mn);
+                    float e = exp2f(fmaf(S[j][r], p.sl2, -mn));
                     S[j][r] = e;
                     lsum += e;
                 }
@@ -432,21 +453,24 @@ template <typename T, int HD>
 __device__ __forceinline__ void dq_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
                                               int T_, int hd) {
     const int t = threadIdx.x;
-    if (t < 128) {
+    using FC = DqCfg<T, HD>;
+    if (__builtin_amdgcn_readfirstlane(t >> 6) < 2) {
         if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), kb, stride, kv0, T_, hd, t);
+            Blk<HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t);
         else
             Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t);
+        zero_tail<FC::PK, FC::PREG>(reg);
     } else {
         Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t - 128);
+        zero_tail<FC::PV, FC::PREG>(reg);
     }
 }
 template <typename T, int HD> __device__ __forceinline__ void dq_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = DqCfg<T, HD>::KB;
-    if (t < 128) {
+    if (__builtin_amdgcn_readfirstlane(t >> 6) < 2) {
         if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::template store<true, true>(reinterpret_cast<const u32x4(*)[8]>(reg), st,
+            Blk<HD, 64, 128>::template store<true, true>(reg, st,
                                                         st + 2 * KB, t);
         else
             Nat<T, HD, 64, 128>::store(reg, st, t);
@@ -476,8 +500,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
     const T *vbase = kbase + p.NKV * p.hd;
 
     u32x4 qf[A::NC], df[A::NC];
-    load_row_frag<T, HD>(qf, base + (long long)qi * stride + h * p.hd, qi < p.T, p.hd, g);
-    load_row_frag<T, HD>(df, reinterpret_cast<const T *>(p.dout) + ((long long)b * p.T + qi) * p.C + h * p.hd,
+    load_row_frag<T, HD>(qf, base + h * p.hd, stride, qi, qi < p.T, p.hd, g);
+    load_row_frag<T, HD>(df, reinterpret_cast<const T *>(p.dout) + (long long)b * p.T * p.C + h * p.hd, p.C, qi,
                          qi < p.T, p.hd, g);
     const long long li = ((long long)b * p.NH + h) * p.T + qi;
     const float lse2 = qi < p.T ? p.lse_in[li] * LOG2E : INFINITY;
@@ -513,10 +537,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
                 for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
                 mma_rows<T, HD>(S, Ks, j * 32, qf, lane);
                 mma_rows<T, HD>(dP, Vs, j * 32, df, lane);
+                const bool diag = kv0 + j * 32 + 31 > qw0;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    int key = kv0 + j * 32 + acc_row(r, lane);
-                    float pr = key <= qi ? exp2f(S[r] * p.sl2 - lse2) : 0.f;
+                    float pr = exp2f(fmaf(S[r], p.sl2, -lse2));
+                    if (diag && kv0 + j * 32 + acc_row(r, lane) > qi) pr = 0.f;
                     S[r] = pr * (dP[r] - Dq);
                 }
                 mma_trans<T, HD, BKV>(dQ, S, Kt, j, lane);
@@ -551,18 +576,21 @@ __device__ __forceinline__ void dkv_stage_load(u32x4 *reg, float &aux, const T *
                                                int hd) {
     const int t = threadIdx.x;
     constexpr int BQ = DkvCfg<T, HD>::BQ;
-    const T *g = t < 128 ? qb : db;
-    const long long st = t < 128 ? qstride : dstride;
+    const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+    const T *g = lo ? qb : db;
+    const long long st = lo ? qstride : dstride;
     const int tl = t & 127;
     if constexpr (std::is_same<T, bf16>::value)
-        Blk<HD, BQ, 128>::load(reinterpret_cast<u32x4(*)[8]>(reg), g, st, q0, T_, hd, tl);
+        Blk<HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
     else
         Nat<T, HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
     // threads 0..BQ-1: lse*log2e of query q0+t; threads 128..128+BQ-1: D
-    if (tl < BQ) {
+    {
         int q = q0 + tl;
-        if (t < 128) aux = q < T_ ? lse[q] * LOG2E : INFINITY;
-        else aux = q < T_ ? D[q] : 0.f;
+        bool ok = tl < BQ && q < T_;
+        const float *src = lo ? lse : D;
+        float v = ok ? src[ok ? q : 0] : 0.f;
+        aux = lo ? (ok ? v * LOG2E : INFINITY) : v;
     }
 }
 template <typename T, int HD>
@@ -572,7 +600,7 @@ __device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, cha
     char *nat = st + (t < 128 ? 0 : FC::QB);
     if constexpr (std::is_same<T, bf16>::value) {
         char *tr = st + (t < 128 ? 2 : 3) * FC::QB;
-        Blk<HD, FC::BQ, 128>::template store<true, true>(reinterpret_cast<const u32x4(*)[8]>(reg), nat, tr, tl);
+        Blk<HD, FC::BQ, 128>::template store<true, true>(reg, nat, tr, tl);
     } else {
         Nat<T, HD, FC::BQ, 128>::store(reg, nat, tl);
     }
@@ -599,12 +627,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
 
     const long long stride = p.QKV;
     const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
-    const T *krow = base + (long long)ki * stride + p.C + kh * p.hd;
-    const T *vrow = krow + p.NKV * p.hd;
-
     u32x4 kf[A::NC], vf[A::NC];
-    load_row_frag<T, HD>(kf, krow, ki < p.T, p.hd, g);
-    load_row_frag<T, HD>(vf, vrow, ki < p.T, p.hd, g);
+    load_row_frag<T, HD>(kf, base + p.C + kh * p.hd, stride, ki, ki < p.T, p.hd, g);
+    load_row_frag<T, HD>(vf, base + p.C + (p.NKV + kh) * p.hd, stride, ki, ki < p.T, p.hd, g);
 
     f32x16 dK[A::ND], dV[A::ND];
 #pragma unroll
@@ -662,11 +687,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
                 for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
                 mma_rows<T, HD>(S, Qs, j * 32, kf, lane);
                 mma_rows<T, HD>(dP, dOs, j * 32, vf, lane);
+                const bool diag = q0 + j * 32 < kw0 + 31;
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
-                    int ql = j * 32 + acc_row(r, lane);
-                    int q = q0 + ql;
-                    float pr = q >= ki ? exp2f(S[r] * p.sl2 - lse2[ql]) : 0.f;
+                    const int ql = j * 32 + acc_row(r, lane);
+                    float pr = exp2f(fmaf(S[r], p.sl2, -lse2[ql]));
+                    if (diag && q0 + ql < ki) pr = 0.f;
                     S[r] = pr;
                     dP[r] = pr * (dP[r] - Dt[ql]);
                 }

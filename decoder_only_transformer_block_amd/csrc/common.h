@@ -43,6 +43,28 @@ template <typename T> __device__ __forceinline__ void st16(T *p, u32x4 v) {
     *reinterpret_cast<u32x4 *>(p) = v;
 }
 
+// Branch-free masked 16-byte loads: a raw buffer resource over a base pointer;
+// an invalid lane passes an offset past num_records and the hardware returns
+// zeros (no divergent branch, so no wait is forced before the next load).
+// Byte offsets must stay below 2^31 from the base.
+struct Buf {
+    __amdgpu_buffer_rsrc_t r;
+    __device__ __forceinline__ explicit Buf(const void *p)
+        : r(__builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, 0x7fffffff, 0x00020000)) {}
+    __device__ __forceinline__ u32x4 ld16(int byte_off, bool ok) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, ok ? byte_off : (int)0x80000000, 0, 0);
+    }
+    __device__ __forceinline__ u32x4 ld16(int byte_off) const {
+        return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+    }
+};
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
 // unpack / pack a 16-byte vector into floats
 template <typename T> __device__ __forceinline__ void unpack16(u32x4 v, float *f);
 template <> __device__ __forceinline__ void unpack16<float>(u32x4 v, float *f) {
@@ -56,10 +78,7 @@ template <> __device__ __forceinline__ void unpack16<bf16>(u32x4 v, float *f) {
         f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
     }
 }
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    bf16 a = (bf16)lo, b = (bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return pack2_bf16(lo, hi); }
 template <typename T> __device__ __forceinline__ u32x4 pack16(const float *f);
 template <> __device__ __forceinline__ u32x4 pack16<float>(const float *f) {
     u32x4 v;

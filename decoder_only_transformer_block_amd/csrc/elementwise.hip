@@ -27,22 +27,17 @@ template <typename T, int NPL, int MODE>
 __global__ __launch_bounds__(256) void norm_fwd_kernel(const T *x, const T *g, const T *bta, float eps, long R,
                                                         int C, T *out, float *rstd, float *mean) {
     constexpr int EPC = 16 / sizeof(T);
-    const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= R) return;
     const int nch = C / EPC;
-    const T *xr = x + row * C;
+    const Buf bx(x + row * C);
     float v[NPL][EPC];
     float s = 0.f;
 #pragma unroll
     for (int k = 0; k < NPL; k++) {
         int c = lane + 64 * k;
-        if (c < nch) {
-            unpack16<T>(ld16(xr + c * EPC), v[k]);
-        } else {
-#pragma unroll
-            for (int e = 0; e < EPC; e++) v[k][e] = 0.f;
-        }
+        unpack16<T>(bx.ld16(c * 16, c < nch), v[k]);
 #pragma unroll
         for (int e = 0; e < EPC; e++) s += (MODE == DTB_NORM_LAYER) ? v[k][e] : v[k][e] * v[k][e];
     }
@@ -97,7 +92,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
     constexpr int EPC = 16 / sizeof(T);
     constexpr bool HAS_G = MODE != DTB_NORM_RMS_NOGAMMA;
     constexpr bool LN = MODE == DTB_NORM_LAYER;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = C / EPC;
     const long nwaves = (long)gridDim.x * 4;
     float ag[NPL][EPC], ab[NPL][EPC];
@@ -118,16 +113,12 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         const float mu = LN ? mean[row] : 0.f;
         float xh[NPL][EPC], d[NPL][EPC];
         float s1 = 0.f, s2 = 0.f;
+        const Buf bx(x + row * C), bd(dy + row * C);
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
             int c = lane + 64 * k;
-            if (c < nch) {
-                unpack16<T>(ld16(x + row * C + c * EPC), xh[k]);
-                unpack16<T>(ld16(dy + row * C + c * EPC), d[k]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < EPC; e++) xh[k][e] = d[k][e] = 0.f;
-            }
+            unpack16<T>(bx.ld16(c * 16, c < nch), xh[k]);
+            unpack16<T>(bd.ld16(c * 16, c < nch), d[k]);
 #pragma unroll
             for (int e = 0; e < EPC; e++) {
                 xh[k][e] = (xh[k][e] - mu) * r;        // normalised input
@@ -138,12 +129,16 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         }
         s2 = wave_sum(s2) / C;
         if (LN) s1 = wave_sum(s1) / C;
+        const Buf br(dres + row * C);
+        u32x4 rsv[NPL];
+#pragma unroll
+        for (int k = 0; k < NPL; k++) rsv[k] = br.ld16((lane + 64 * k) * 16, lane + 64 * k < nch);
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
             int c = lane + 64 * k;
             if (c >= nch) continue;
             float rs[EPC], o[EPC];
-            unpack16<T>(ld16(dres + row * C + c * EPC), rs);
+            unpack16<T>(rsv[k], rs);
 #pragma unroll
             for (int e = 0; e < EPC; e++) {
                 float dn = d[k][e] * gv[k][e];

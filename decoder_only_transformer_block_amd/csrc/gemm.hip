@@ -31,6 +31,8 @@
 // * Workgroup ids are remapped so that each XCD (ids are dealt round-robin to
 //   the 8 XCDs) works on a contiguous, row-grouped range of tiles and shares
 //   operand panels in its own L2.
+#include <type_traits>
+
 #include "common.h"
 
 namespace dtb {
@@ -71,11 +73,11 @@ template <typename T, int R> struct Loader<T, R, true> {
     __device__ __forceinline__ void load(const T *base, long long ld, int row0, int nrows, int k0, int kend) {
         const int t = threadIdx.x, c = t & 7;
         const int kk = k0 + c * GT<T>::EPC;
+        const Buf buf(base + (long long)row0 * ld + k0);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int r = (t >> 3) + 32 * p, gr = row0 + r;
-            if (gr < nrows && kk < kend) reg[p] = ld16(base + (long long)gr * ld + kk);
-            else reg[p] = u32x4{0, 0, 0, 0};
+            reg[p] = buf.ld16((int)(((long long)r * ld + c * GT<T>::EPC) * (int)sizeof(T)), gr < nrows && kk < kend);
         }
     }
     __device__ __forceinline__ void store(char *lds) const {
@@ -95,6 +97,7 @@ template <int R> struct Loader<bf16, R, false> {
     u32x4 reg[P][8];
     __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
         const int t = threadIdx.x;
+        const Buf buf(base + (long long)k0 * ld + row0);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int blk = t + 256 * p;
@@ -103,9 +106,8 @@ template <int R> struct Loader<bf16, R, false> {
             bool live = blk < NB && gr < nrows;
 #pragma unroll
             for (int i = 0; i < 8; i++) {
-                int k = k0 + kb * 8 + i;
-                if (live && k < kend) reg[p][i] = ld16(base + (long long)k * ld + gr);
-                else reg[p][i] = u32x4{0, 0, 0, 0};
+                int k = kb * 8 + i;
+                reg[p][i] = buf.ld16((int)(((long long)k * ld + rb * 8) * 2), live && k0 + k < kend);
             }
         }
     }
@@ -133,6 +135,7 @@ template <int R> struct Loader<float, R, false> {
     u32x4 reg[P][4];
     __device__ __forceinline__ void load(const float *base, long long ld, int row0, int nrows, int k0, int kend) {
         const int t = threadIdx.x;
+        const Buf buf(base + (long long)k0 * ld + row0);
 #pragma unroll
         for (int p = 0; p < P; p++) {
             int blk = t + 256 * p;
@@ -141,9 +144,8 @@ template <int R> struct Loader<float, R, false> {
             bool live = blk < NB && gr < nrows;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                int k = k0 + kb * 4 + i;
-                if (live && k < kend) reg[p][i] = ld16(base + (long long)k * ld + gr);
-                else reg[p][i] = u32x4{0, 0, 0, 0};
+                int k = kb * 4 + i;
+                reg[p][i] = buf.ld16((int)(((long long)k * ld + rb * 4) * 4), live && k0 + k < kend);
             }
         }
     }
@@ -178,6 +180,97 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int &tm, int &tn) {
     int in_group = pid - group * per_group;
     tm = first_m + in_group % gsize;
     tn = in_group / gsize;
+}
+
+// ---- epilogue through LDS ----------------------------------------------------
+// One wave writes a 32-row block of its accumulators (NI blocks of 32 columns,
+// fp32) to its private LDS region, then reads it back as rows of float4 so
+// that the bias / residual reads and the output writes are contiguous vector
+// accesses (8 bytes of bf16 or 16 bytes of fp32 per lane) issued without
+// intervening waits.  Requires that no other wave still reads that LDS region.
+// mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial
+template <typename T, int NI>
+__device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int m_base, int n_base,
+                                               const KParams &p, int mode, int lane) {
+    constexpr int W = NI * 32;          // floats per row
+    constexpr int CPR = W / 4;          // float4 chunks per row
+    constexpr int RPP = 64 / CPR;       // rows per pass
+    constexpr int PASSES = 32 / RPP;
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int j = 0; j < NI; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+    const int cc = lane % CPR, rr = lane / CPR;
+    const int n = n_base + cc * 4;
+    const bool nok = n < p.N;
+    f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+    if ((mode == 0 || mode == 1) && p.bias) {
+        const Buf bb(p.bias);
+        if constexpr (std::is_same<T, bf16>::value) {
+            u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(bb.r, nok ? n * 2 : (int)0x80000000, 0, 0);
+            bv = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                       __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+        } else {
+            bv = __builtin_bit_cast(f32x4, bb.ld16(n * 4, nok));
+        }
+    }
+    // residual / accumulate inputs for all passes first (uniform branches outside
+    // the loops, so the loads issue back to back and are waited for at first use)
+    f32x4 in[PASSES];
+#pragma unroll
+    for (int q = 0; q < PASSES; q++) in[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (mode == 0 && p.res) {
+        const Buf br(p.res);
+        if constexpr (std::is_same<T, bf16>::value) {
+            u32x2 w[PASSES];
+#pragma unroll
+            for (int q = 0; q < PASSES; q++) {
+                const int m = m_base + q * RPP + rr;
+                w[q] = __builtin_amdgcn_raw_buffer_load_b64(
+                    br.r, (nok && m < p.M) ? (int)(((long long)m * p.ldr + n) * 2) : (int)0x80000000, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < PASSES; q++)
+                in[q] = f32x4{__uint_as_float(w[q][0] << 16), __uint_as_float(w[q][0] & 0xffff0000u),
+                              __uint_as_float(w[q][1] << 16), __uint_as_float(w[q][1] & 0xffff0000u)};
+        } else {
+#pragma unroll
+            for (int q = 0; q < PASSES; q++) {
+                const int m = m_base + q * RPP + rr;
+                in[q] = __builtin_bit_cast(f32x4, br.ld16((int)(((long long)m * p.ldr + n) * 4), nok && m < p.M));
+            }
+        }
+    } else if (mode == 2) {
+        const Buf bo(p.out);
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int m = m_base + q * RPP + rr;
+            in[q] = __builtin_bit_cast(f32x4, bo.ld16((int)(((long long)m * p.ldo + n) * 4), nok && m < p.M));
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < PASSES; q++) {
+        const int row = q * RPP + rr;
+        const int m = m_base + row;
+        f32x4 v = *reinterpret_cast<const f32x4 *>(lw + row * W + cc * 4);
+        if (!(nok && m < p.M)) continue;
+        if (mode == 0) {
+            v = v + bv + in[q];
+            if constexpr (std::is_same<T, bf16>::value) {
+                u32x2 w{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+                *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16 *>(p.out) + (long long)m * p.ldo + n) = w;
+            } else {
+                *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v;
+            }
+        } else if (mode == 1) {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + bv;
+        } else if (mode == 2) {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + in[q];
+        } else {
+            *reinterpret_cast<f32x4 *>(p.part + ((long long)blockIdx.z * p.M + m) * p.N + n) = v;
+        }
+    }
 }
 
 template <typename T, int BM, int BN, bool AK, bool BKM>
@@ -250,33 +343,13 @@ __global__ __launch_bounds__(256) void gemm_kernel(KParams p) {
         __syncthreads();
     }
 
-    // ---- epilogue ----
-    const T *bias = reinterpret_cast<const T *>(p.bias);
-    const T *res = reinterpret_cast<const T *>(p.res);
-#pragma unroll
-    for (int j = 0; j < NI; j++) {
-        const int n = n0 + wn * (BN / 2) + j * 32 + l32;
-        if (n >= p.N) continue;
-        const float bv = bias ? to_f32(bias[n]) : 0.f;
+    // ---- epilogue (LDS is free after the last barrier) ----
+    {
+        constexpr int W = NI * 32;
+        float *lw = reinterpret_cast<float *>(smem) + wave * 32 * W;
 #pragma unroll
         for (int i = 0; i < MI; i++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * (BM / 2) + i * 32 + acc_row(r, lane);
-                if (m >= p.M) continue;
-                float v = acc[i][j][r];
-                if (p.out_mode == 0) {
-                    v += bv;
-                    if (res) v += to_f32(res[(long long)m * p.ldr + n]);
-                    reinterpret_cast<T *>(p.out)[(long long)m * p.ldo + n] = from_f32<T>(v);
-                } else if (p.out_mode == 1) {
-                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] = v + bv;
-                } else if (p.out_mode == 2) {
-                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] += v;
-                } else {
-                    p.part[((long long)blockIdx.z * p.M + m) * p.N + n] = v;
-                }
-            }
+            epilogue_block<T, NI>(acc[i], lw, m0 + wm * (BM / 2) + i * 32, n0 + wn * (BN / 2), p, p.out_mode, lane);
         }
     }
 }
@@ -304,11 +377,19 @@ template <> struct Stage256<true> {
     __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
         const int t = threadIdx.x, c = t & 7;
         const int kk = k0 + c * 8;
+        if (FULL) {
 #pragma unroll
-        for (int p = 0; p < 4; p++) {
-            int r = (t >> 3) + 64 * p, gr = row0 + r;
-            if (FULL || (gr < nrows && kk < kend)) reg[p] = ld16(base + (long long)gr * ld + kk);
-            else reg[p] = u32x4{0, 0, 0, 0};
+            for (int p = 0; p < 4; p++) {
+                int r = (t >> 3) + 64 * p;
+                reg[p] = ld16(base + (long long)(row0 + r) * ld + kk);
+            }
+        } else {
+            const Buf buf(base + (long long)row0 * ld + k0);
+#pragma unroll
+            for (int p = 0; p < 4; p++) {
+                int r = (t >> 3) + 64 * p;
+                reg[p] = buf.ld16((int)(((long long)r * ld + c * 8) * 2), row0 + r < nrows && kk < kend);
+            }
         }
     }
     __device__ __forceinline__ void store(char *lds) const {
@@ -330,11 +411,16 @@ template <> struct Stage256<false> {
         const int t = threadIdx.x;
         const int rb = t & 31, kb = t >> 5;
         const int gr = row0 + rb * 8;
+        if (FULL) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int k = k0 + kb * 4 + i;
-            if (FULL || (gr < nrows && k < kend)) reg[i] = ld16(base + (long long)k * ld + gr);
-            else reg[i] = u32x4{0, 0, 0, 0};
+            for (int i = 0; i < 4; i++) reg[i] = ld16(base + (long long)(k0 + kb * 4 + i) * ld + gr);
+        } else {
+            const Buf buf(base + (long long)k0 * ld + row0);
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                int k = kb * 4 + i;
+                reg[i] = buf.ld16((int)(((long long)k * ld + rb * 8) * 2), gr < nrows && k0 + k < kend);
+            }
         }
     }
     __device__ __forceinline__ void store(char *lds) const {
@@ -438,32 +524,11 @@ __global__ __launch_bounds__(512) void gemm256_kernel(KParams p) {
         __syncthreads();
     }
 
-    // ---- epilogue (MODE 0: bf16 store with optional bias / residual; 2: fp32 +=; 3: split partial)
-    const bf16 *bias = reinterpret_cast<const bf16 *>(p.bias);
-    const bf16 *res = reinterpret_cast<const bf16 *>(p.res);
+    // ---- epilogue (LDS is free after the last barrier): MODE 0 bf16 (+bias, +res), 2 fp32 +=, 3 partial
+    {
+        float *lw = reinterpret_cast<float *>(smem) + wave * 32 * 128;
 #pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int n = n0 + wn * 128 + j * 32 + l32;
-        if (n >= p.N) continue;
-        const float bv = (MODE == 0 && bias) ? (float)bias[n] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-#pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const int m = m0 + wm * 64 + i * 32 + acc_row(r, lane);
-                if (m >= p.M) continue;
-                float v = acc[i][j][r];
-                if constexpr (MODE == 0) {
-                    v += bv;
-                    if (res) v += (float)res[(long long)m * p.ldr + n];
-                    reinterpret_cast<bf16 *>(p.out)[(long long)m * p.ldo + n] = (bf16)v;
-                } else if constexpr (MODE == 2) {
-                    reinterpret_cast<float *>(p.out)[(long long)m * p.ldo + n] += v;
-                } else {
-                    p.part[((long long)blockIdx.z * p.M + m) * p.N + n] = v;
-                }
-            }
-        }
+        for (int i = 0; i < 2; i++) epilogue_block<bf16, 4>(acc[i], lw, m0 + wm * 64 + i * 32, n0 + wn * 128, p, MODE, lane);
     }
 }
 
