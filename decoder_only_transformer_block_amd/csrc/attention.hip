@@ -133,15 +133,6 @@ template <int HD, int ROWS, int NT> struct Blk {
     }
 };
 
-// Both sides of a wave-uniform "which tensor do I stage" branch must write every
-// element of the shared register array in the same order; otherwise the
-// optimizer merges the two sides' last stores through a pointer and the array
-// is demoted to scratch memory.
-template <int FROM, int TO> __device__ __forceinline__ void zero_tail(u32x4 *reg) {
-#pragma unroll
-    for (int i = FROM; i < TO; i++) reg[i] = u32x4{0, 0, 0, 0};
-}
-
 // ---------------------------------------------------------------------------
 // fragment helpers
 // ---------------------------------------------------------------------------
@@ -262,39 +253,32 @@ template <typename T, int HD> struct FwdCfg {
     static constexpr int BQ = 128, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);  // K natural tile bytes (= V tile bytes)
     static constexpr int STAGE = 2 * KB;
-    // staging: K natural by threads [128, 256); V by [0, 128) (transposed bf16 / natural fp32)
-    static constexpr int PK = Nat<T, HD, BKV, 128>::P;
-    static constexpr int PV = std::is_same<T, bf16>::value ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
-    static constexpr int PREG = PK > PV ? PK : PV;
+    static constexpr bool BF = std::is_same<T, bf16>::value;
+    // staging: threads [0, 128) load V, [128, 256) load K with the same loader
+    // (bf16: 8x8 blocks, V stored transposed, K natural; fp32: natural rows)
+    static constexpr int PREG = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
 };
 
 template <typename T, int HD>
 __device__ __forceinline__ void fwd_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
                                                int T_, int hd) {
     const int t = threadIdx.x;
-    using FC = FwdCfg<T, HD>;
-    if (__builtin_amdgcn_readfirstlane(t >> 6) >= 2) {
-        Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t - 128);
-        zero_tail<FC::PK, FC::PREG>(reg);
-    } else {
-        if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t);
-        else
-            Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t);
-        zero_tail<FC::PV, FC::PREG>(reg);
-    }
+    const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+    const T *g = lo ? vb : kb;
+    if constexpr (std::is_same<T, bf16>::value)
+        Blk<HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    else
+        Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
 }
 template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = FwdCfg<T, HD>::KB;
-    if (__builtin_amdgcn_readfirstlane(t >> 6) >= 2) {
-        Nat<T, HD, 64, 128>::store(reg, st, t - 128);
+    const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (lo) Blk<HD, 64, 128>::template store<false, true>(reg, nullptr, st + KB, t & 127);
+        else Blk<HD, 64, 128>::template store<true, false>(reg, st, nullptr, t & 127);
     } else {
-        if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::template store<false, true>(reg, nullptr,
-                                                         st + KB, t);
-        else
-            Nat<T, HD, 64, 128>::store(reg, st + KB, t);
+        Nat<T, HD, 64, 128>::store(reg, lo ? st + KB : st, t & 127);
     }
 }
 
@@ -335,6 +319,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
     u32x4 reg[FC::PREG];
     fwd_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
     fwd_stage_store<T, HD>(reg, smem);
+    // the per-lane fragments loaded above are complete before the loop, so the
+    // loop body never waits on them (nor, by extension, on the prefetch it issues)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; kt++) {
@@ -442,40 +429,32 @@ template <typename T, int HD> struct DqCfg {
     static constexpr int BQ = 128, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);
     static constexpr bool BF = std::is_same<T, bf16>::value;
-    // LDS stage: K natural, V natural, (bf16) K transposed
+    // LDS stage: K natural, V natural, (bf16) K transposed.  Threads [0, 128)
+    // load K, [128, 256) load V with the same loader.
     static constexpr int STAGE = (BF ? 3 : 2) * KB;
-    static constexpr int PK = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
-    static constexpr int PV = Nat<T, HD, BKV, 128>::P;
-    static constexpr int PREG = PK > PV ? PK : PV;
+    static constexpr int PREG = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
 };
 
 template <typename T, int HD>
 __device__ __forceinline__ void dq_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
                                               int T_, int hd) {
     const int t = threadIdx.x;
-    using FC = DqCfg<T, HD>;
-    if (__builtin_amdgcn_readfirstlane(t >> 6) < 2) {
-        if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t);
-        else
-            Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t);
-        zero_tail<FC::PK, FC::PREG>(reg);
-    } else {
-        Nat<T, HD, 64, 128>::load(reg, vb, stride, kv0, T_, hd, t - 128);
-        zero_tail<FC::PV, FC::PREG>(reg);
-    }
+    const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+    const T *g = lo ? kb : vb;
+    if constexpr (std::is_same<T, bf16>::value)
+        Blk<HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    else
+        Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
 }
 template <typename T, int HD> __device__ __forceinline__ void dq_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = DqCfg<T, HD>::KB;
-    if (__builtin_amdgcn_readfirstlane(t >> 6) < 2) {
-        if constexpr (std::is_same<T, bf16>::value)
-            Blk<HD, 64, 128>::template store<true, true>(reg, st,
-                                                        st + 2 * KB, t);
-        else
-            Nat<T, HD, 64, 128>::store(reg, st, t);
+    const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
+    if constexpr (std::is_same<T, bf16>::value) {
+        if (lo) Blk<HD, 64, 128>::template store<true, true>(reg, st, st + 2 * KB, t & 127);
+        else Blk<HD, 64, 128>::template store<true, false>(reg, st + KB, nullptr, t & 127);
     } else {
-        Nat<T, HD, 64, 128>::store(reg, st + KB, t - 128);
+        Nat<T, HD, 64, 128>::store(reg, lo ? st : st + KB, t & 127);
     }
 }
 
@@ -520,6 +499,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
     u32x4 reg[FC::PREG];
     dq_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
     dq_stage_store<T, HD>(reg, smem);
+    // the per-lane fragments loaded above are complete before the loop, so the
+    // loop body never waits on them (nor, by extension, on the prefetch it issues)
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int kt = 0; kt < ntiles; kt++) {
@@ -584,17 +566,17 @@ __device__ __forceinline__ void dkv_stage_load(u32x4 *reg, float &aux, const T *
         Blk<HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
     else
         Nat<T, HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
-    // threads 0..BQ-1: lse*log2e of query q0+t; threads 128..128+BQ-1: D
+    // threads 0..BQ-1: lse of query q0+t; threads 128..128+BQ-1: D (raw; the
+    // transform to log2 units happens at the LDS store, away from the load)
     {
-        int q = q0 + tl;
-        bool ok = tl < BQ && q < T_;
-        const float *src = lo ? lse : D;
-        float v = ok ? src[ok ? q : 0] : 0.f;
-        aux = lo ? (ok ? v * LOG2E : INFINITY) : v;
+        const int q = q0 + tl;
+        const bool ok = tl < BQ && q < T_;
+        const Buf bl(lo ? lse : D);
+        aux = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(bl.r, ok ? q * 4 : (int)0x80000000, 0, 0));
     }
 }
 template <typename T, int HD>
-__device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, char *st) {
+__device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, char *st, int q0, int T_) {
     using FC = DkvCfg<T, HD>;
     const int t = threadIdx.x, tl = t & 127;
     char *nat = st + (t < 128 ? 0 : FC::QB);
@@ -605,7 +587,11 @@ __device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, cha
         Nat<T, HD, FC::BQ, 128>::store(reg, nat, tl);
     }
     float *f = reinterpret_cast<float *>(st + (FC::BF ? 4 : 2) * FC::QB);
-    if (tl < FC::BQ) f[(t < 128 ? 0 : FC::BQ) + tl] = aux;
+    if (tl < FC::BQ) {
+        const bool lo = t < 128;
+        const bool ok = q0 + tl < T_;
+        f[(lo ? 0 : FC::BQ) + tl] = lo ? (ok ? aux * LOG2E : INFINITY) : aux;
+    }
 }
 
 template <typename T, int HD>
@@ -659,8 +645,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
         int q0;
         srcs(0, qb, db, lse, D, q0);
         dkv_stage_load<T, HD>(reg, aux, qb, db, stride, p.C, lse, D, q0, p.T, p.hd);
-        dkv_stage_store<T, HD>(reg, aux, smem);
+        dkv_stage_store<T, HD>(reg, aux, smem, q0, p.T);
     }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
     for (int it = 0; it < niter; it++) {
@@ -688,19 +675,27 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
                 mma_rows<T, HD>(S, Qs, j * 32, kf, lane);
                 mma_rows<T, HD>(dP, dOs, j * 32, vf, lane);
                 const bool diag = q0 + j * 32 < kw0 + 31;
+                // the 16 query rows of this lane: 4 groups of 4 consecutive rows
+                f32x4 lq[4], dq4[4];
+#pragma unroll
+                for (int r4 = 0; r4 < 4; r4++) {
+                    const int ql = j * 32 + 8 * r4 + 4 * g;
+                    lq[r4] = *reinterpret_cast<const f32x4 *>(lse2 + ql);
+                    dq4[r4] = *reinterpret_cast<const f32x4 *>(Dt + ql);
+                }
 #pragma unroll
                 for (int r = 0; r < 16; r++) {
                     const int ql = j * 32 + acc_row(r, lane);
-                    float pr = exp2f(fmaf(S[r], p.sl2, -lse2[ql]));
+                    float pr = exp2f(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
                     if (diag && q0 + ql < ki) pr = 0.f;
                     S[r] = pr;
-                    dP[r] = pr * (dP[r] - Dt[ql]);
+                    dP[r] = pr * (dP[r] - dq4[r >> 2][r & 3]);
                 }
                 mma_trans<T, HD, BQ>(dV, S, dOt, j, lane);
                 mma_trans<T, HD, BQ>(dK, dP, Qt, j, lane);
             }
         }
-        if (more) dkv_stage_store<T, HD>(reg, aux, smem + ((it + 1) & 1) * FC::STAGE);
+        if (more) dkv_stage_store<T, HD>(reg, aux, smem + ((it + 1) & 1) * FC::STAGE, (qt0 + (it + 1) % nqt) * BQ, p.T);
         __syncthreads();
     }
     if (ki < p.T) {
