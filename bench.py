@@ -36,6 +36,9 @@ def parse():
                     choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB three times (the known-size "
+                         "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the oracle's bounded sample (one sequence, one layer)")
     return ap.parse_args()
@@ -156,6 +159,15 @@ def main():
     import torch
     from decoder_only_transformer_block_amd import configs
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "repeats": 3}))
+        return
     cfg = configs.ALL_CONFIGS[args.workload]
 
     if args.workload == "attn_long":
