@@ -52,10 +52,26 @@ static constexpr bool is_bf16(int) { return false; }
 template <typename T, int HD> __device__ __forceinline__ int nat_off(int row, int chunk) {
     return row * AT<T, HD>::RB + ((chunk ^ (row & AT<T, HD>::XM)) << 4);
 }
-// transposed bf16 tile: HD rows (head dim) x ROWS columns (keys or queries),
-// 8-byte slots of 4 columns, slot index XOR (row & (ROWS/4 - 1))
-template <int ROWS> __device__ __forceinline__ int tr_off(int d, int slot) {
-    return d * (ROWS * 2) + ((slot ^ (d & (ROWS / 4 - 1))) << 3);
+// transposed bf16 tile: HD rows (head dim) x 64 columns (keys or queries) =
+// 16 slots of 8 bytes (4 columns) per 128-byte row.  The slot index is XOR-ed
+// with h(d) = (d & 15) ^ g(d >> 4): for the fragment reads (16 consecutive d,
+// one slot) h is a bijection of d & 15; for the staging stores (16 lanes =
+// NBD = HD/8 head-dim blocks x 16/NBD column blocks, d = 8*db + j) g deposits
+// the bits of db >> 1 into the slot bits not already varied by the column
+// block and by db & 1, so the 16 stores land in 16 different slots.
+template <int HD> __device__ __forceinline__ int tr_hash(int d) {
+    constexpr int NBD = HD / 8;
+    const int x = d >> 4;
+    int gx;
+    if constexpr (NBD >= 16) gx = x & 7;
+    else if constexpr (NBD == 8) gx = (x & 1) | ((x & 2) << 1);
+    else if constexpr (NBD == 4) gx = x & 1;
+    else gx = 0;
+    return (d & 15) ^ gx;
+}
+template <int ROWS, int HD> __device__ __forceinline__ int tr_off(int d, int slot) {
+    static_assert(ROWS == 64, "transposed tiles are 64 columns wide");
+    return d * (ROWS * 2) + ((slot ^ tr_hash<HD>(d)) << 3);
 }
 
 // ---------------------------------------------------------------------------
@@ -125,8 +141,8 @@ template <int HD, int ROWS, int NT> struct Blk {
 #pragma unroll
                 for (int j = 0; j < 8; j++) {
                     int d = db * 8 + j;
-                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS>(d, 2 * rb)) = u32x2{o[j][0], o[j][1]};
-                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS>(d, 2 * rb + 1)) = u32x2{o[j][2], o[j][3]};
+                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS, HD>(d, 2 * rb)) = u32x2{o[j][0], o[j][1]};
+                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS, HD>(d, 2 * rb + 1)) = u32x2{o[j][2], o[j][3]};
                 }
             }
         }
@@ -143,8 +159,8 @@ template <int HD, int ROWS, int NT> struct Blk {
 template <int HD, int ROWS>
 __device__ __forceinline__ bf16x8 tr_frag(const char *tr, int d, int koff) {
     if (HD < 32 && d >= HD) return bf16x8{};
-    u32x2 a = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS>(d, koff >> 2));
-    u32x2 b = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS>(d, (koff >> 2) + 2));
+    u32x2 a = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS, HD>(d, koff >> 2));
+    u32x2 b = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS, HD>(d, (koff >> 2) + 2));
     return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
 }
 // fp32: element (row, d) of a natural tile

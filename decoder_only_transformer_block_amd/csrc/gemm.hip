@@ -61,7 +61,12 @@ struct KParams {
     float *part;   // split partials [splits][M][N]
 };
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+// 128-byte LDS rows, 16-byte chunk XOR-ed with (row ^ row/8) & 7: conflict-free for
+// the 16-byte fragment reads of consecutive rows, the 16-byte k-major row
+// stores, and the transposed m/n-major stores whose lanes write rows 8 apart.
+__device__ __forceinline__ int swz(int row, int chunk) {
+    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
 
 // ---- slab loaders ---------------------------------------------------------
 // rows R of an operand tile starting at row0 (< nrows valid), k in [k0, kend)
@@ -364,9 +369,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(KParams p) {
 // consecutive rows) and the transposed 8-byte writes (rows 8 apart) spread over
 // the banks.  Interior tiles take branch-free loads.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz2(int row, int chunk) {
-    return row * 128 + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
-}
+__device__ __forceinline__ int swz2(int row, int chunk) { return swz(row, chunk); }
 
 template <bool KMAJOR> struct Stage256;
 
@@ -404,12 +407,13 @@ template <> struct Stage256<true> {
 
 template <> struct Stage256<false> {
     // element (k, r) at base[k*ld + r]; thread t owns the 4(k) x 8(r) block
-    // rb = t % 32 (rows rb*8..+8), kb = t / 32 (k kb*4..+4)
+    // rb = (t % 64) / 2 (rows rb*8..+8), kb = t % 2 + 2 * (t / 64) (k kb*4..+4):
+    // the 16 lanes of one 8-byte LDS store pass then cover 8 chunks x 2 halves.
     u32x4 reg[4];
     template <bool FULL>
     __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
         const int t = threadIdx.x;
-        const int rb = t & 31, kb = t >> 5;
+        const int rb = (t & 63) >> 1, kb = (t & 1) | ((t >> 6) << 1);
         const int gr = row0 + rb * 8;
         if (FULL) {
 #pragma unroll
@@ -425,7 +429,7 @@ template <> struct Stage256<false> {
     }
     __device__ __forceinline__ void store(char *lds) const {
         const int t = threadIdx.x;
-        const int rb = t & 31, kb = t >> 5;
+        const int rb = (t & 63) >> 1, kb = (t & 1) | ((t >> 6) << 1);
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             u32x2 o;
