@@ -173,6 +173,19 @@ def attn_backward_materialized(qkv, att, dout, B, T, C, NH, NKV):
     return dqkv
 
 
+def attn_tail(q_tail, k, v, dout_tail, T, R, NH, NKV, hd):
+    """Attention of the last R query positions of one sequence (all keys):
+    returns o_tail [R, NH*hd], lse_tail [NH, R], dq_tail [R, NH*hd] and the
+    exact dk / dv of the last R key positions [R, NKV*hd]."""
+    q_tail, k, v, dout_tail = _d(q_tail), _d(k), _d(v), _d(dout_tail)
+    C, KV = NH * hd, NKV * hd
+    o = np.empty((R, C)); lse = np.empty((NH, R)); dq = np.empty((R, C))
+    dk = np.empty((R, KV)); dv = np.empty((R, KV))
+    lib().orc_attn_tail(_p(q_tail), _p(k), _p(v), _p(dout_tail), T, R, NH, NKV, hd, _p(o), _p(lse), _p(dq),
+                        _p(dk), _p(dv))
+    return o, lse, dq, dk, dv
+
+
 def act_forward(mlp: str, up, H):
     up = _d(up)
     W = up.shape[-1]

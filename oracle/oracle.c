@@ -446,6 +446,82 @@ void orc_attn_backward_materialized(const double *qkv, const double *att, const 
     free(dpre);
 }
 
+/* Attention restricted to the last R query rows of ONE sequence (same
+ * definition as orc_attn_forward / orc_attn_backward, evaluated on a subset):
+ *   q_tail [R][NH*hd]  queries of positions T-R .. T-1
+ *   k, v   [T][NKV*hd] keys / values of all positions
+ *   dout_tail [R][NH*hd]
+ * Outputs o_tail [R][NH*hd], lse_tail [NH][R], dq_tail [R][NH*hd], and
+ * dk_tail / dv_tail [R][NKV*hd] for key positions T-R .. T-1.  Causality makes
+ * the tail's dk / dv exact: only queries t >= j see key j, and all of them are
+ * in the tail. */
+void orc_attn_tail(const double *q_tail, const double *k, const double *v, const double *dout_tail,
+                   int T, int R, int NH, int NKV, int hd, double *o_tail, double *lse_tail,
+                   double *dq_tail, double *dk_tail, double *dv_tail)
+{
+    int grp = NH / NKV, C = NH * hd, KV = NKV * hd, t0 = T - R;
+    double scale = 1.0 / sqrt((double)hd);
+    memset(dk_tail, 0, sizeof(double) * (size_t)R * KV);
+    memset(dv_tail, 0, sizeof(double) * (size_t)R * KV);
+    #pragma omp parallel
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)T);
+        double *p = (double *)malloc(sizeof(double) * (size_t)T);
+        double *dp = (double *)malloc(sizeof(double) * (size_t)T);
+        #pragma omp for schedule(dynamic, 1)
+        for (int kh = 0; kh < NKV; kh++)
+            for (int h = kh * grp; h < (kh + 1) * grp; h++)
+                for (int r = 0; r < R; r++) {
+                    int t = t0 + r;
+                    const double *q = q_tail + (long)r * C + (long)h * hd;
+                    const double *dO = dout_tail + (long)r * C + (long)h * hd;
+                    for (int j = 0; j <= t; j++) {
+                        const double *kj = k + (long)j * KV + (long)kh * hd;
+                        double acc = 0.0;
+                        for (int d = 0; d < hd; d++) acc += q[d] * kj[d];
+                        s[j] = acc * scale;
+                    }
+                    double m = s[0];
+                    for (int j = 1; j <= t; j++) if (s[j] > m) m = s[j];
+                    double l = 0.0;
+                    for (int j = 0; j <= t; j++) l += exp(s[j] - m);
+                    double *o = o_tail + (long)r * C + (long)h * hd;
+                    for (int d = 0; d < hd; d++) o[d] = 0.0;
+                    double D = 0.0;
+                    for (int j = 0; j <= t; j++) {
+                        p[j] = exp(s[j] - m) / l;
+                        const double *vj = v + (long)j * KV + (long)kh * hd;
+                        double acc = 0.0;
+                        for (int d = 0; d < hd; d++) {
+                            o[d] += p[j] * vj[d];
+                            acc += dO[d] * vj[d];
+                        }
+                        dp[j] = acc;
+                        D += p[j] * dp[j];
+                    }
+                    lse_tail[(long)h * R + r] = m + log(l);
+                    double *dq = dq_tail + (long)r * C + (long)h * hd;
+                    for (int d = 0; d < hd; d++) dq[d] = 0.0;
+                    for (int j = 0; j <= t; j++) {
+                        double ds = p[j] * (dp[j] - D);
+                        const double *kj = k + (long)j * KV + (long)kh * hd;
+                        for (int d = 0; d < hd; d++) dq[d] += scale * ds * kj[d];
+                        if (j >= t0) {
+                            double *dk = dk_tail + (long)(j - t0) * KV + (long)kh * hd;
+                            double *dv = dv_tail + (long)(j - t0) * KV + (long)kh * hd;
+                            for (int d = 0; d < hd; d++) {
+                                dk[d] += scale * ds * q[d];
+                                dv[d] += p[j] * dO[d];
+                            }
+                        }
+                    }
+                }
+        free(s);
+        free(p);
+        free(dp);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* MLP activations                                                            */
 /* ------------------------------------------------------------------------ */

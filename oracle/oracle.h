@@ -59,6 +59,9 @@ void orc_attn_forward_materialized(const double *qkv, int B, int T, int C, int N
                                    double *out, double *att);
 void orc_attn_backward_materialized(const double *qkv, const double *att, const double *dout,
                                     int B, int T, int C, int NH, int NKV, double *dqkv);
+void orc_attn_tail(const double *q_tail, const double *k, const double *v, const double *dout_tail,
+                   int T, int R, int NH, int NKV, int hd, double *o_tail, double *lse_tail,
+                   double *dq_tail, double *dk_tail, double *dv_tail);
 void orc_act_forward(int mlp, const double *up, long R, int H, double *h);
 void orc_act_backward(int mlp, const double *dh, const double *up, long R, int H, double *dup);
 void orc_block_forward(const orc_cfg *c, const orc_weights *w, const double *x, double *y,

@@ -1,0 +1,120 @@
+"""Parity at the full sizes the benchmark times, on outputs the oracle can
+compute one by one, plus properties that hold at any size.
+
+* long-context attention (B=1, T=16384, NH=32, NKV=8, hd=128, bf16):
+  - strided query rows: row t of the attention equals the attention of the
+    prefix 0..t evaluated at its last row (causality), so the oracle computes
+    o, lse and dq of each sampled row from that prefix alone;
+  - the last 48 key rows: their dk / dv only receive contributions from the
+    last 48 query rows, so the oracle's tail evaluator gives them exactly;
+  - sum over keys of dk is 0 and sum over keys of dv is the sum of dO over the
+    group's query rows (every row of dS sums to zero), checked on the whole
+    GPU result.
+* Llama-GQA block (B=8, T=2048, C=2048, bf16) and GPT-2-small block
+  (B=4, T=1024, C=768, fp32), one layer each: the forward output and the
+  input gradient of the last rows of two sequences, composed from the
+  oracle's per-op functions (the last rows' dk/dv are exact as above), and a
+  random-projection check that dW_down = dy^T h on the full gradient.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import TOL, announce, check, require_gpu
+from oracle_compose import block_tail_reference
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows_of_prefix(orc, q, k, v, dout, t, NH, NKV, hd):
+    """o, lse, dq of query row t from the prefix 0..t."""
+    o, lse, dq, _, _ = orc.attn_tail(q[t:t + 1], k[:t + 1], v[:t + 1], dout[t:t + 1], t + 1, 1, NH, NKV, hd)
+    return o[0], lse[:, 0], dq[0]
+
+
+def test_attn_long_full_size_sampled():
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, configs
+    from decoder_only_transformer_block_amd.runtime import to_device, to_numpy
+    cfg = configs.ATTN_LONG
+    B, T, NH, NKV, hd, C = cfg.B, cfg.T, cfg.NH, cfg.NKV, cfg.hd, cfg.C
+    KV = NKV * hd
+    qkv, dout = configs.attn_inputs(cfg)
+    announce(f"attention full size B={B} T={T} NH={NH} NKV={NKV} hd={hd} bf16")
+    q = to_device(qkv, "bf16")
+    d = to_device(dout, "bf16")
+    out = torch.empty((B, T, C), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, NH, T), dtype=torch.float32, device="cuda")
+    dq = torch.empty_like(q)
+    ws = torch.empty(binding.attn_workspace_bytes(B, T, NH), dtype=torch.uint8, device="cuda")
+    binding.attn_forward(out, lse, q, B, T, C, NH, NKV, "bf16")
+    binding.attn_backward(dq, q, out, d, lse, B, T, C, NH, NKV, "bf16", ws)
+    torch.cuda.synchronize()
+    O, L, DQ = to_numpy(out)[0], to_numpy(lse)[0], to_numpy(dq)[0]
+    del out, dq
+    Q, K, V, DO = qkv[0, :, :C], qkv[0, :, C:C + KV], qkv[0, :, C + KV:], dout[0]
+
+    rows = [0, 1, 63, 64, 127, 128, 1000, 4097, 8191, 12289, T - 129, T - 1]
+    ref = [_rows_of_prefix(oracle, Q, K, V, DO, t, NH, NKV, hd) for t in rows]
+    tol = TOL["bf16"]
+    check("o[rows]", O[rows], np.stack([r[0] for r in ref]), tol)
+    check("lse[rows]", L[:, rows].T, np.stack([r[1] for r in ref]), tol)
+    check("dq[rows]", DQ[rows, :C], np.stack([r[2] for r in ref]), tol)
+
+    R = 48
+    o_t, l_t, dq_t, dk_t, dv_t = oracle.attn_tail(Q[T - R:], K, V, DO[T - R:], T, R, NH, NKV, hd)
+    check("o[tail]", O[T - R:], o_t, tol)
+    check("dq[tail]", DQ[T - R:, :C], dq_t, tol)
+    check("dk[tail]", DQ[T - R:, C:C + KV], dk_t, tol)
+    check("dv[tail]", DQ[T - R:, C + KV:], dv_t, tol)
+
+    # properties of the whole result
+    dk = DQ[:, C:C + KV].astype(np.float64)
+    dv = DQ[:, C + KV:].astype(np.float64)
+    s_dk = np.abs(dk.sum(0)) / np.sqrt((dk ** 2).sum(0))
+    print(f"    sum_keys dk / ||dk|| max {s_dk.max():.2e}", flush=True)
+    assert s_dk.max() < 0.05
+    dO_group = DO.astype(np.float64).reshape(T, NKV, NH // NKV, hd).sum(2).reshape(T, KV)
+    check("sum dv", dv.sum(0), dO_group.sum(0), tol)
+
+
+def _block_full_size(cfg_name, batches, R):
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    from decoder_only_transformer_block_amd.runtime import BlockStack, to_device, to_numpy
+    cfg = configs.BLOCK_CONFIGS[cfg_name].replace(L=1)
+    w = configs.block_weights(cfg, 0, perturb=True)
+    x = configs.block_input(cfg)
+    dy = configs.block_dout(cfg)
+    announce(f"block full size {cfg.name} B={cfg.B} T={cfg.T} C={cfg.C} H={cfg.H} {cfg.dtype}")
+    st = BlockStack(cfg, [w])
+    y = to_numpy(st.forward(to_device(x, cfg.dtype)))
+    dx = to_numpy(st.backward(to_device(dy, cfg.dtype)))
+    lse = to_numpy(st.saved_tensor(0, "lse", (cfg.B, cfg.NH, cfg.T)))
+    tol = TOL[cfg.dtype]
+    for b in batches:
+        ry, rdx, rl = block_tail_reference(oracle, cfg, w, x[b], dy[b], R)
+        check(f"y[b{b},tail]", y[b, cfg.T - R:], ry, tol)
+        check(f"lse[b{b},tail]", lse[b][:, cfg.T - R:], rl, tol)
+        check(f"dx[b{b},tail]", dx[b, cfg.T - R:], rdx, tol)
+    # dW_down = dy^T h on the whole gradient (random projection, fp32 on the GPU)
+    h = st.saved_tensor(0, "h", (cfg.B * cfg.T, cfg.H)).float()
+    dyt = to_device(dy, cfg.dtype).float().reshape(-1, cfg.C)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    vv = torch.randn(cfg.H, 1, device="cuda", generator=gen)
+    lhs = (st.grads[0]["w_down"] @ vv).double().cpu().numpy()
+    rhs = (dyt.t() @ (h @ vv)).double().cpu().numpy()
+    check("dWdown.v", lhs, rhs, tol)
+    torch.cuda.synchronize()
+
+
+def test_llama_gqa_block_full_size_sampled():
+    require_gpu()
+    _block_full_size("llama_gqa", batches=(0, 7), R=16)
+
+
+def test_gpt2_small_block_full_size_sampled():
+    require_gpu()
+    _block_full_size("gpt2_small", batches=(0, 3), R=16)

@@ -181,3 +181,22 @@ def test_planted_mistakes_are_caught(orc):
     assert rel(orc.block_forward(c, bad, x)[0], yt) > 1e-3
     bad = dict(w, b2=-w["b2"])
     assert rel(orc.block_forward(c, bad, x)[0], yt) > 1e-3
+
+
+@pytest.mark.parametrize("norm,mlp,rope,bias", [("rms", "swiglu", "neox", False), ("layer", "gelu_tanh", "none", True),
+                                                ("rms_nogamma", "relu", "none", False)])
+def test_block_tail_composition_matches_full_block(orc, norm, mlp, rope, bias):
+    """The per-op composition used for the full-size sampled checks (last R rows
+    of one sequence) equals the whole-block oracle on those rows."""
+    from oracle_compose import block_tail_reference
+    c = make_cfg(norm, mlp, rope, bias, B=1, T=19, C=16, NH=4, NKV=2, H=24)
+    w = make_weights(c)
+    x = rng.standard_normal((1, c.T, c.C))
+    dy = rng.standard_normal((1, c.T, c.C))
+    y, sv = orc.block_forward(c, w, x)
+    dx, _ = orc.block_backward(c, w, x, sv, dy)
+    R = 6
+    ry, rdx, rl = block_tail_reference(orc, c, w, x[0], dy[0], R)
+    assert rel(ry, y[0, c.T - R:]) < 1e-12
+    assert rel(rdx, dx[0, c.T - R:]) < 1e-12
+    assert rel(rl, sv.lse[0][:, c.T - R:]) < 1e-12

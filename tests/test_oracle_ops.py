@@ -344,3 +344,19 @@ def test_activation_special_values(orc):
     # gelu tanh closed form at x = 1: 0.5 (1 + tanh(sqrt(2/pi) 1.044715))
     v = orc.act_forward("gelu_tanh", np.array([[1.0]]), 1)[0, 0]
     assert abs(v - 0.5 * (1 + np.tanh(np.sqrt(2 / np.pi) * 1.044715))) < 1e-16
+
+
+def test_attention_tail_equals_full(orc):
+    """The tail evaluator is the same definition on a subset: it must agree
+    with the full row-wise forward/backward on every tail row."""
+    B, T, NH, NKV, hd, R = 1, 23, 4, 2, 8, 7
+    qkv, C = _qkv(B, T, NH, NKV, hd)
+    dout = rng.standard_normal((B, T, C))
+    o, lse = orc.attn_forward(qkv, B, T, C, NH, NKV)
+    d = orc.attn_backward(qkv, dout, B, T, C, NH, NKV)
+    KV = NKV * hd
+    ot, lt, dqt, dkt, dvt = orc.attn_tail(qkv[0, T - R:, :C], qkv[0, :, C:C + KV], qkv[0, :, C + KV:],
+                                         dout[0, T - R:], T, R, NH, NKV, hd)
+    assert rel(ot, o[0, T - R:]) < 1e-13 and rel(lt, lse[0, :, T - R:]) < 1e-13
+    assert rel(dqt, d[0, T - R:, :C]) < 1e-12
+    assert rel(dkt, d[0, T - R:, C:C + KV]) < 1e-12 and rel(dvt, d[0, T - R:, C + KV:]) < 1e-12
