@@ -360,179 +360,194 @@ __global__ __launch_bounds__(256) void gemm_kernel(KParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 256x256 kernel: 8 waves (4 x 2), wave tile 64 x 128 (2 x 4 MFMA blocks),
-// two waves per SIMD so that one wave's LDS / barrier waits are covered by the
-// other's MFMAs.  K slab 64; every operand layout stages 16 VGPRs per thread:
-// k-major as four 16-byte row chunks, m/n-major as one 4(k) x 8(m) block
-// transposed in registers.  LDS rows are 128 bytes; the 16-byte chunk index is
-// XOR-ed with (row ^ row/8) & 7, which keeps both the MFMA fragment reads (32
-// consecutive rows) and the transposed 8-byte writes (rows 8 apart) spread over
-// the banks.  Interior tiles take branch-free loads.
+// bf16 256x256 kernel, direct-to-LDS pipeline.  8 waves (4 x 2), wave tile
+// 64 x 128 (2 x 4 MFMA blocks), two waves per SIMD.  Every operand slab (32 k)
+// is moved from global memory into LDS by buffer loads with the LDS bit (no
+// VGPR staging), into a ring of four stages; slab k+3 is issued while slab k is
+// multiplied, so each load has three iterations to land.
+// The 16-byte chunk swizzles below were chosen by measurement (the LDS
+// bank-conflict counter over the whole kernel reads zero with them; the
+// unswizzled k-major layout, or a swizzle on row bits 0-1, conflicts).
+// Permuting 16-byte chunks inside a row does not split the global requests.
+// * k-major tiles: 256 rows x 64 B; chunk c of row r at c ^ ((r>>3)&3);
+//   MFMA fragments are ds_read_b128 (16 B = 8 k of one row).
+// * m/n-major tiles stay in their global orientation: 32 k-rows x 512 B;
+//   chunk c of k-row r at c ^ (2(r&3) | 8(r&1)).  Fragments use the gfx950 transposing
+//   read ds_read_b64_tr_b16: within each 16-lane group, lane l receives
+//   elements l, l+16, l+32, l+48 of the 4x16 block the group reads, so with
+//   lane i pointing at (k0 + i/4, m0 + 4(i%4)) each lane gets 4 consecutive k
+//   of its own m; two such reads give the 8 k an MFMA lane needs.
+// * The swizzles are applied by permuting which global chunk each lane DMAs.
+// * Stages are four distinct __shared__ objects and the loop is unrolled by 4
+//   so that the compiler's alias analysis keeps its LDS-DMA waits per stage;
+//   the barrier is issued as a bare s_barrier after an explicit wait for this
+//   wave's DMAs of the stage about to be read (a compiler barrier would also
+//   wait for the slabs still in flight).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int swz2(int row, int chunk) { return swz(row, chunk); }
+__shared__ __attribute__((aligned(16))) char g_dma_st0[32768];
+__shared__ __attribute__((aligned(16))) char g_dma_st1[32768];
+__shared__ __attribute__((aligned(16))) char g_dma_st2[32768];
+__shared__ __attribute__((aligned(16))) char g_dma_st3[32768];
 
-template <bool KMAJOR> struct Stage256;
+template <int S> __device__ __forceinline__ char *dma_stage() {
+    if constexpr (S == 0) return g_dma_st0;
+    else if constexpr (S == 1) return g_dma_st1;
+    else if constexpr (S == 2) return g_dma_st2;
+    else return g_dma_st3;
+}
 
-template <> struct Stage256<true> {
-    // 256 rows x 8 chunks = 2048 chunks, 4 per thread: row = t/8 + 64 p, chunk = t%8
-    u32x4 reg[4];
-    template <bool FULL>
-    __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
-        const int t = threadIdx.x, c = t & 7;
-        const int kk = k0 + c * 8;
-        if (FULL) {
+typedef __attribute__((address_space(3))) void *lds_vptr;
+typedef short __attribute__((ext_vector_type(4))) s16x4;
+
+__device__ __forceinline__ int kmaj_swz(int r) { return (r >> 3) & 3; }
+__device__ __forceinline__ int mmaj_swz(int kr) { return ((kr & 3) << 1) | ((kr & 1) << 3); }
+__device__ __forceinline__ int kmaj_off(int r, int c) { return r * 64 + ((c ^ kmaj_swz(r)) << 4); }
+__device__ __forceinline__ int mmaj_off(int kr, int c) { return kr * 512 + ((c ^ mmaj_swz(kr)) << 4); }
+
+// issue this wave's BPW 1 KB DMA instructions for one operand slab; the
+// buffer resource is rebased on the slab so offsets stay small
+template <bool KMAJOR, int BPW>
+__device__ __forceinline__ void dma_slab(char *region, const bf16 *base, long long ld, int row0, int nrows, int k0,
+                                         int kend, int wave, int lane) {
+    const Buf buf(KMAJOR ? base + (long long)row0 * ld + k0 : base + (long long)k0 * ld + row0);
 #pragma unroll
-            for (int p = 0; p < 4; p++) {
-                int r = (t >> 3) + 64 * p;
-                reg[p] = ld16(base + (long long)(row0 + r) * ld + kk);
-            }
+    for (int q = 0; q < BPW; q++) {
+        const int blk = wave * BPW + q;  // 16 blocks of 1 KB, BPW per wave
+        int off;
+        bool ok;
+        if constexpr (KMAJOR) {
+            const int r = blk * 16 + (lane >> 2), pc = lane & 3;
+            const int c = pc ^ kmaj_swz(r);
+            ok = row0 + r < nrows && k0 + c * 8 < kend;
+            off = (r * (int)ld + c * 8) * 2;
         } else {
-            const Buf buf(base + (long long)row0 * ld + k0);
-#pragma unroll
-            for (int p = 0; p < 4; p++) {
-                int r = (t >> 3) + 64 * p;
-                reg[p] = buf.ld16((int)(((long long)r * ld + c * 8) * 2), row0 + r < nrows && kk < kend);
-            }
+            const int kr = blk * 2 + (lane >> 5), pc = lane & 31;
+            const int c = pc ^ mmaj_swz(kr);
+            ok = k0 + kr < kend && row0 + c * 8 < nrows;
+            off = (kr * (int)ld + c * 8) * 2;
         }
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(buf.r, (lds_vptr)(region + blk * 1024), 16,
+                                                 ok ? off : (int)0x80000000, 0, 0, 0);
     }
-    __device__ __forceinline__ void store(char *lds) const {
-        const int t = threadIdx.x, c = t & 7;
-#pragma unroll
-        for (int p = 0; p < 4; p++) {
-            int r = (t >> 3) + 64 * p;
-            *reinterpret_cast<u32x4 *>(lds + swz2(r, c)) = reg[p];
-        }
-    }
-};
+}
 
-template <> struct Stage256<false> {
-    // element (k, r) at base[k*ld + r]; thread t owns the 4(k) x 8(r) block
-    // rb = (t % 64) / 2 (rows rb*8..+8), kb = t % 2 + 2 * (t / 64) (k kb*4..+4):
-    // the 16 lanes of one 8-byte LDS store pass then cover 8 chunks x 2 halves.
-    u32x4 reg[4];
-    template <bool FULL>
-    __device__ __forceinline__ void load(const bf16 *base, long long ld, int row0, int nrows, int k0, int kend) {
-        const int t = threadIdx.x;
-        const int rb = (t & 63) >> 1, kb = (t & 1) | ((t >> 6) << 1);
-        const int gr = row0 + rb * 8;
-        if (FULL) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) reg[i] = ld16(base + (long long)(k0 + kb * 4 + i) * ld + gr);
-        } else {
-            const Buf buf(base + (long long)k0 * ld + row0);
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                int k = kb * 4 + i;
-                reg[i] = buf.ld16((int)(((long long)k * ld + rb * 8) * 2), gr < nrows && k0 + k < kend);
-            }
-        }
+// MFMA fragment (8 bf16 along k) of row `r` of a tile, k16 step s (0..1), lane half g
+template <bool KMAJOR>
+__device__ __forceinline__ bf16x8 dma_frag(const char *region, int r, int s, int lane) {
+    if constexpr (KMAJOR) {
+        const int g = lane >> 5;
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(region + kmaj_off(r, 2 * s + g)));
+    } else {
+        // lane i16 of each 16-lane group reads (k = kb + i16/4, m = mb + 4 (i16%4))
+        const int g = lane >> 5, i16 = lane & 15;
+        const int mb = (r & ~15);                 // first row of this lane's 16-row group
+        const int m = mb + 4 * (i16 & 3);
+        const int kb = 16 * s + 8 * g + (i16 >> 2);
+        const char *p0 = region + mmaj_off(kb, m >> 3) + (m & 7) * 2;
+        const char *p1 = region + mmaj_off(kb + 4, m >> 3) + (m & 7) * 2;
+        s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p0);
+        s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p1);
+        typedef short __attribute__((ext_vector_type(8))) s16x8;
+        s16x8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+        return __builtin_bit_cast(bf16x8, v);
     }
-    __device__ __forceinline__ void store(char *lds) const {
-        const int t = threadIdx.x;
-        const int rb = (t & 63) >> 1, kb = (t & 1) | ((t >> 6) << 1);
-#pragma unroll
-        for (int j = 0; j < 8; j++) {
-            u32x2 o;
-#pragma unroll
-            for (int q = 0; q < 2; q++) {
-                uint32_t a = reg[2 * q][j >> 1], b = reg[2 * q + 1][j >> 1];
-                o[q] = (j & 1) ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-            }
-            int r = rb * 8 + j;
-            *reinterpret_cast<u32x2 *>(lds + swz2(r, kb >> 1) + ((kb & 1) << 3)) = o;
-        }
-    }
-};
+}
 
-template <bool AK, bool BKM, int MODE>
-__global__ __launch_bounds__(512) void gemm256_kernel(KParams p) {
-    constexpr int BM = 256, BN = 256, BK = 64;
-    constexpr int STAGE = (BM + BN) * 128;
-    extern __shared__ __attribute__((aligned(16))) char smem[];
+// s_waitcnt immediate for vmcnt(n) lgkmcnt(0) (vmcnt bits [3:0] and [15:14],
+// expcnt [6:4] left at its maximum, lgkmcnt [11:8])
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
+// NW waves: 8 -> 4 x 2 waves of 64 x 128, 4 -> 2 x 2 waves of 128 x 128.
+template <bool AK, bool BKM, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
+    constexpr int BM = 256, BN = 256, BK = 32;
+    constexpr int WGN = 2, WGM = NW / WGN, TM = BM / WGM, FI = TM / 32, FJ = 4;
+    constexpr int BPW = 16 / NW;          // DMA blocks per operand per wave
+    constexpr int WAIT = wait_vm_lgkm0(2 * 2 * BPW);  // two younger slabs in flight
     const int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(nm, nn, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int kbeg = blockIdx.z * p.kchunk;
     const int kend = min(p.K, kbeg + p.kchunk);
-    const int nk = (kend - kbeg + BK - 1) / BK;
-    const bool interior = m0 + BM <= p.M && n0 + BN <= p.N;
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
 
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-    const int wm = wave >> 1, wn = wave & 1, g = lane >> 5, l32 = lane & 31;
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WGN, wn = wave % WGN, l32 = lane & 31;
+    const bf16 *gA = static_cast<const bf16 *>(p.A), *gB = static_cast<const bf16 *>(p.B);
 
-    const bf16 *A = reinterpret_cast<const bf16 *>(p.A);
-    const bf16 *B = reinterpret_cast<const bf16 *>(p.B);
-    Stage256<AK> la;
-    Stage256<BKM> lb;
-
-    f32x16 acc[2][4];
+    f32x16 acc[FI][FJ];
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int i = 0; i < FI; i++)
 #pragma unroll
-        for (int j = 0; j < 4; j++)
+        for (int j = 0; j < FJ; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
-    auto load = [&](int k0) {
-        if (interior && k0 + BK <= kend) {
-            la.template load<true>(A, p.lda, m0, p.M, k0, kend);
-            lb.template load<true>(B, p.ldb, n0, p.N, k0, kend);
-        } else {
-            la.template load<false>(A, p.lda, m0, p.M, k0, kend);
-            lb.template load<false>(B, p.ldb, n0, p.N, k0, kend);
+    auto issue = [&](char *st, int k0) {
+        dma_slab<AK, BPW>(st, gA, p.lda, m0, p.M, k0, kend, wave, lane);
+        dma_slab<BKM, BPW>(st + 16384, gB, p.ldb, n0, p.N, k0, kend, wave, lane);
+    };
+    auto compute = [&](const char *st) {
+        const char *As = st, *Bs = st + 16384;
+#pragma unroll
+        for (int sidx = 0; sidx < 2; sidx++) {
+            bf16x8 af[FI], bfr[FJ];
+#pragma unroll
+            for (int i = 0; i < FI; i++) af[i] = dma_frag<AK>(As, wm * TM + i * 32 + l32, sidx, lane);
+#pragma unroll
+            for (int j = 0; j < FJ; j++) bfr[j] = dma_frag<BKM>(Bs, wn * 128 + j * 32 + l32, sidx, lane);
+#pragma unroll
+            for (int i = 0; i < FI; i++)
+#pragma unroll
+                for (int j = 0; j < FJ; j++) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
         }
     };
-
-    if (nk > 0) {
-        load(kbeg);
-        la.store(smem);
-        lb.store(smem + BM * 128);
+    // Main loop: whole groups of four slabs.  Every step issues the slab three
+    // ahead (past the end of K the loads are out of range and write zeros into
+    // a stage that is no longer read), so exactly two younger slabs (4 BPW DMA
+    // instructions of this wave) are in flight when a stage is waited for.
+    // The wait also drains this wave's LDS reads of the previous stage, which
+    // the next step overwrites once every wave has passed the barrier.
+#define DMA_STEP(S)                                                             \
+    {                                                                           \
+        __builtin_amdgcn_s_waitcnt(WAIT);                                       \
+        asm volatile("s_barrier" ::: "memory");                                 \
+        issue(dma_stage<(S + 3) & 3>(), kbeg + (kt + S + 3) * BK);              \
+        compute(dma_stage<S>());                                                \
     }
+    issue(dma_stage<0>(), kbeg);
+    issue(dma_stage<1>(), kbeg + BK);
+    issue(dma_stage<2>(), kbeg + 2 * BK);
+    int kt = 0;
+    for (; kt + 4 <= nk; kt += 4) {
+        DMA_STEP(0)
+        DMA_STEP(1)
+        DMA_STEP(2)
+        DMA_STEP(3)
+    }
+#undef DMA_STEP
+    // tail of 0..3 slabs, all already issued
+    if (kt < nk) {
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(0));
+        asm volatile("s_barrier" ::: "memory");
+        compute(dma_stage<0>());
+        if (kt + 1 < nk) compute(dma_stage<1>());
+        if (kt + 2 < nk) compute(dma_stage<2>());
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kt = 0; kt < nk; kt++) {
-        const bool more = kt + 1 < nk;
-        if (more) load(kbeg + (kt + 1) * BK);
-        const char *As = smem + (kt & 1) * STAGE;
-        const char *Bs = As + BM * 128;
-        u32x4 af[2][2], bfr[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; i++) af[0][i] = *reinterpret_cast<const u32x4 *>(As + swz2(wm * 64 + i * 32 + l32, g));
-#pragma unroll
-        for (int j = 0; j < 4; j++) bfr[0][j] = *reinterpret_cast<const u32x4 *>(Bs + swz2(wn * 128 + j * 32 + l32, g));
-#pragma unroll
-        for (int c = 0; c < 4; c++) {
-            const int cur = c & 1, nxt = cur ^ 1;
-            if (c < 3) {
-#pragma unroll
-                for (int i = 0; i < 2; i++)
-                    af[nxt][i] = *reinterpret_cast<const u32x4 *>(As + swz2(wm * 64 + i * 32 + l32, 2 * (c + 1) + g));
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    bfr[nxt][j] = *reinterpret_cast<const u32x4 *>(Bs + swz2(wn * 128 + j * 32 + l32, 2 * (c + 1) + g));
-            }
-#pragma unroll
-            for (int i = 0; i < 2; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-                    acc[i][j] = mfma32(__builtin_bit_cast(bf16x8, af[cur][i]), __builtin_bit_cast(bf16x8, bfr[cur][j]),
-                                       acc[i][j]);
-        }
-        if (more) {
-            char *nx = smem + ((kt + 1) & 1) * STAGE;
-            la.store(nx);
-            lb.store(nx + BM * 128);
-        }
-        __syncthreads();
-    }
-
-    // ---- epilogue (LDS is free after the last barrier): MODE 0 bf16 (+bias, +res), 2 fp32 +=, 3 partial
+    // ---- epilogue through LDS (16 KB per wave; all DMA has landed and all reads are done)
     {
-        float *lw = reinterpret_cast<float *>(smem) + wave * 32 * 128;
+        constexpr int PER_STAGE = NW / 4;  // waves sharing one 32 KB stage
+        const int sidx = wave / PER_STAGE;
+        char *reg = sidx == 0 ? dma_stage<0>() : sidx == 1 ? dma_stage<1>() : sidx == 2 ? dma_stage<2>() : dma_stage<3>();
+        float *lw = reinterpret_cast<float *>(reg + (wave % PER_STAGE) * 16384);
 #pragma unroll
-        for (int i = 0; i < 2; i++) epilogue_block<bf16, 4>(acc[i], lw, m0 + wm * 64 + i * 32, n0 + wn * 128, p, MODE, lane);
+        for (int i = 0; i < FI; i++)
+            epilogue_block<bf16, 4>(acc[i], lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane);
     }
 }
 
@@ -577,16 +592,9 @@ static hipError_t launch_layout(const KParams &p, bool ak, bool bk, int splits, 
 
 template <bool AK, bool BKM, int MODE>
 static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
-    constexpr int LDS = 2 * (256 + 256) * 128;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm256_kernel<AK, BKM, MODE>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    constexpr int NW = 8;  // measured faster than 4 waves of 128 x 128 on every block shape
     int nm = (p.M + 255) / 256, nn = (p.N + 255) / 256;
-    hipLaunchKernelGGL((gemm256_kernel<AK, BKM, MODE>), dim3(nm * nn, 1, splits), dim3(512), LDS, s, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, MODE, NW>), dim3(nm * nn, 1, splits), dim3(NW * 64), 0, s, p);
     return hipGetLastError();
 }
 
