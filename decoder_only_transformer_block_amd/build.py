@@ -23,6 +23,9 @@ FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     # packed fp32 VALU ops stay off (v_pk_* fp32 forms are avoided)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax / epilogue arithmetic on
+    # them then needs no AGPR copies
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"),
     "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
 ]

@@ -34,7 +34,7 @@
 //   summed over the group in registers -- no atomics, deterministic.
 #include <type_traits>
 
-#include "common.h"
+#include "attention.h"
 
 namespace dtb {
 
@@ -245,22 +245,6 @@ __device__ __forceinline__ void store_rows(T *row, const f32x16 *acc, float s, i
             }
         }
 }
-
-struct AttnP {
-    const void *qkv;
-    const void *out;
-    const void *dout;
-    void *o;        // forward output / dqkv for the backward
-    float *lse;     // forward output
-    const float *lse_in;
-    const float *D;
-    int B, T, C, NH, NKV, hd, QKV;
-    float sl2;      // log2(e) / sqrt(hd)
-    float scale;    // 1 / sqrt(hd)
-};
-
-constexpr float LOG2E = 1.4426950408889634f;
-constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
 // forward
@@ -800,11 +784,7 @@ int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, in
     p.lse = lse;
     int hdp = pad_hd(p.hd, dtype);
     if (g_timing_on) timing_begin(s);
-    hipError_t e = dtype == DTB_BF16 ? (hdp == 16   ? fwd_t<bf16, 16>(p, s)
-                                        : hdp == 32 ? fwd_t<bf16, 32>(p, s)
-                                        : hdp == 64 ? fwd_t<bf16, 64>(p, s)
-                                                    : fwd_t<bf16, 128>(p, s))
-                                     : DTB_HD_DISPATCH(fwd_t, float, hdp, p, s);
+    hipError_t e = dtype == DTB_BF16 ? attn_fwd_bf16(p, hdp, s) : DTB_HD_DISPATCH(fwd_t, float, hdp, p, s);
     if (e != hipSuccess) return set_launch_error(e, "attn_forward");
     if (g_timing_on) {
         double es = dtype == DTB_BF16 ? 2 : 4;

@@ -1,0 +1,277 @@
+// Causal grouped-query flash attention in bf16 for gfx950.
+//
+// What is computed ("nanoeuler — CUDA kernels": the flash attention forward /
+// backward declarations and the CPU attention definitions): s_tj = q_t.k_j /
+// sqrt(hd) for j <= t, o_t = softmax(s_t) V, lse_t = logsumexp_j s_tj; query
+// head h reads kv head h / (NH / NKV).
+//
+// Design:
+// * Tiles of 64 positions x HD (the head width padded to 16/32/64/128) are
+//   staged in LDS in their natural row-major form only, by buffer loads that
+//   write LDS directly (no VGPR staging), into a ring of NS stages: the tile
+//   NS-1 steps ahead is issued while the current one is multiplied.  The
+//   16-byte chunk index of a row is XOR-ed with a function of the row; the
+//   permutation is applied by choosing which global chunk each lane loads, so
+//   every row is still fetched as whole contiguous segments.
+// * Scores are computed transposed, S^T = K Q^T, so a lane owns one query
+//   (column l%32) and 16 keys of each 32x32 block; K is read as rows
+//   (ds_read_b128).  The product O^T += V^T P^T takes P^T from the score
+//   registers as its B operand (the k order of an MFMA is free as long as both
+//   operands follow it: lane half g holds keys 4g..4g+3 and 8+4g..8+4g+3 of
+//   each 16-key step), and V^T fragments come from the natural V tile through
+//   the transposing read ds_read_b64_tr_b16: within a 16-lane group, lane i
+//   addresses (key kb + i/4, head dims d0 + 4(i%4) .. +3) and lane l receives
+//   keys kb..kb+3 of head dim d0 + l.
+// * Every lane's LDS addresses are a per-lane base plus compile-time offsets.
+// * The online softmax runs in base 2 with the hardware exp2.
+#include "attention.h"
+
+namespace dtb {
+namespace {
+
+typedef short __attribute__((ext_vector_type(4))) short4_t;
+typedef __attribute__((address_space(3))) void *lds_vptr;
+typedef __attribute__((address_space(3))) short4_t *lds_s4ptr;
+
+template <int HD> struct TL {
+    static constexpr int RB = HD * 2;          // row bytes
+    static constexpr int NCH = HD / 8;         // 16-byte chunks per row
+    static constexpr int TILE = 64 * RB;       // 64-row tile bytes
+    static constexpr int NDMA = TILE / 1024;   // 1 KB DMA instructions per tile
+    static constexpr int NC = HD / 16;         // 16-wide MFMA k steps over the head
+    static constexpr int ND = HD >= 32 ? HD / 32 : 1;  // 32-row output blocks over the head
+};
+
+// chunk swizzle of tiles read as rows (32 consecutive rows, one chunk)
+template <int HD> __device__ __forceinline__ int swz_rows(int r) {
+    constexpr int M = TL<HD>::NCH - 1;
+    r &= 31;
+    if constexpr (HD <= 32) return (r >> 3) & M;
+    else return (r ^ (r >> 3)) & M;
+}
+// chunk swizzle of tiles read transposed (groups of 4 rows; depends on the
+// row modulo 8 only, so row offsets that are multiples of 8 stay immediates)
+template <int HD> __device__ __forceinline__ int swz_cols(int r) { return r & 7 & (TL<HD>::NCH - 1); }
+
+constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// DMA instruction q (1 KB) of a 64-row tile at row0 of a row-major tensor
+template <int HD, bool COLS>
+__device__ __forceinline__ void dma_tile(char *lds, const bf16 *g, long long stride, int row0, int nrows, int hd,
+                                         int q, int lane) {
+    constexpr int RB = TL<HD>::RB;
+    const int off = q * 1024 + lane * 16;
+    const int r = off / RB, pc = (off % RB) >> 4;
+    const int c = pc ^ (COLS ? swz_cols<HD>(r) : swz_rows<HD>(r));
+    const Buf buf(g + (long long)row0 * stride);
+    const bool ok = row0 + r < nrows && c * 8 < hd;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buf.r, (lds_vptr)(lds + q * 1024), 16,
+                                             ok ? (int)((r * stride + c * 8) * 2) : (int)0x80000000, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 lds_row16(const char *p) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(p));
+}
+// two transposing reads 8 rows apart: 8 consecutive k of the lane's column
+template <int RB> __device__ __forceinline__ bf16x8 lds_tr8(const char *p) {
+    short4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)p);
+    short4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4ptr)(p + 8 * RB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// write ND accumulator blocks (lane = position, registers = head dim) scaled by s
+template <int HD>
+__device__ __forceinline__ void store_rows_bf16(bf16 *row, const f32x16 *acc, float s, int hd, int lane) {
+#pragma unroll
+    for (int db = 0; db < TL<HD>::ND; db++)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+            const int d = db * 32 + 8 * r4 + 4 * (lane >> 5);
+            if (d < hd) {
+                u32x2 v{pack2_bf16(acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s),
+                        pack2_bf16(acc[db][4 * r4 + 2] * s, acc[db][4 * r4 + 3] * s)};
+                *reinterpret_cast<u32x2 *>(row + d) = v;
+            }
+        }
+}
+
+// ---------------------------------------------------------------------------
+// forward: one workgroup = 4 waves x 32 queries of one (b, h); key tiles of 64;
+// last query blocks launched first (causal load balance)
+// ---------------------------------------------------------------------------
+template <int HD, int NS>
+__global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
+    using L = TL<HD>;
+    constexpr int BQ = 128, BKV = 64, RB = L::RB;
+    constexpr int DPW = L::NDMA / 2;  // DMA instructions per wave per tile (waves 0-1: K, 2-3: V)
+    constexpr int STB = 2 * L::TILE;
+    __shared__ __attribute__((aligned(1024))) char s0[STB];
+    __shared__ __attribute__((aligned(1024))) char s1[STB];
+    __shared__ __attribute__((aligned(1024))) char s2[NS > 2 ? STB : 16];
+#define STG(S) ((S) == 0 ? s0 : (S) == 1 ? s1 : s2)
+
+    const int nqb = (p.T + BQ - 1) / BQ, BH = p.B * p.NH;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+    const long long stride = p.QKV;
+    const bf16 *base = reinterpret_cast<const bf16 *>(p.qkv) + (long long)b * p.T * stride;
+    const bf16 *kbase = base + p.C + kh * p.hd;
+    const bf16 *vbase = kbase + p.NKV * p.hd;
+    const int kv_end = min(p.T, q0 + BQ);
+    const int ntiles = (kv_end + BKV - 1) / BKV;
+    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
+
+    const bool isK = wave < 2;
+    const bf16 *src = isK ? kbase : vbase;
+    const int qsub = (wave & 1) * DPW;
+    auto issue = [&](char *st, int kt) {
+#pragma unroll
+        for (int i = 0; i < DPW; i++) {
+            if (isK) dma_tile<HD, false>(st, src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
+            else dma_tile<HD, true>(st + L::TILE, src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
+        }
+    };
+
+    // query fragments (chunks 2c+g of row qi), then the first NS-1 tiles
+    u32x4 qf[L::NC];
+    {
+        const Buf bq(base + h * p.hd);
+#pragma unroll
+        for (int c = 0; c < L::NC; c++) {
+            const int ch = 2 * c + g;
+            qf[c] = bq.ld16((int)(((long long)qi * stride + ch * 8) * 2), qi < p.T && ch * 8 < p.hd);
+        }
+    }
+    issue(s0, 0);
+    if (NS > 2) issue(s1, 1);
+
+    int kofs[L::NC];
+#pragma unroll
+    for (int c = 0; c < L::NC; c++) kofs[c] = l32 * RB + (((2 * c + g) ^ swz_rows<HD>(l32)) << 4);
+    int vofs[L::ND];
+    {
+        const int i16 = lane & 15, vr = 4 * g + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < L::ND; db++) {
+            const int d = 32 * db + (l32 & 16) + 4 * (i16 & 3);
+            const int ch = (d >> 3) & (L::NCH - 1);
+            vofs[db] = vr * RB + ((ch ^ swz_cols<HD>(vr)) << 4) + 8 * (i16 & 1);
+        }
+    }
+
+    f32x16 O[L::ND];
+#pragma unroll
+    for (int d = 0; d < L::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) O[d][r] = 0.f;
+    float m = -1e30f, lsum = 0.f;
+
+    auto compute = [&](const char *st, int kt) {
+        const char *Ks = st, *Vs = st + L::TILE;
+        const int kv0 = kt * BKV;
+        f32x16 S[2];
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[j][r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < L::NC; c++)
+                S[j] = mfma32(lds_row16(Ks + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, qf[c]), S[j]);
+        }
+        if (kv0 + BKV - 1 > qw0) {  // diagonal tile
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (kv0 + j * 32 + acc_row(r, lane) > qi) S[j][r] = -INFINITY;
+        }
+        float mt = S[0][0];
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) mt = fmaxf(mt, S[j][r]);
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;  // running max in log2 units
+        const float mn = fmaxf(m, mt);
+        if (!__all(mn == m)) {
+            const float alpha = fast_exp2(m - mn);
+            lsum *= alpha;
+#pragma unroll
+            for (int d = 0; d < L::ND; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) O[d][r] *= alpha;
+        }
+        m = mn;
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                const float e = fast_exp2(fmaf(S[j][r], p.sl2, -mn));
+                S[j][r] = e;
+                lsum += e;
+            }
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                u32x4 xw;
+#pragma unroll
+                for (int e = 0; e < 4; e++) xw[e] = pack2_bf16(S[j][8 * hh + 2 * e], S[j][8 * hh + 2 * e + 1]);
+                const bf16x8 xb = __builtin_bit_cast(bf16x8, xw);
+#pragma unroll
+                for (int db = 0; db < L::ND; db++)
+                    O[db] = mfma32(lds_tr8<RB>(Vs + vofs[db] + (32 * j + 16 * hh) * RB), xb, O[db]);
+            }
+    };
+
+    // all fragment and prologue loads complete before the loop
+    __builtin_amdgcn_s_waitcnt(0);
+#define FWD_STEP(S)                                                              \
+    {                                                                            \
+        const int kt = kt0 + (S);                                                \
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 2) * DPW));               \
+        asm volatile("s_barrier" ::: "memory");                                  \
+        issue(STG(((S) + NS - 1) % NS), kt + NS - 1);                            \
+        if (kt < wtiles) compute(STG(S), kt);                                    \
+    }
+    for (int kt0 = 0; kt0 < ntiles; kt0 += NS) {
+        FWD_STEP(0)
+        FWD_STEP(1)
+        if constexpr (NS > 2) FWD_STEP(2)
+    }
+#undef FWD_STEP
+#undef STG
+    __builtin_amdgcn_s_waitcnt(0);
+
+    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    if (qi < p.T) {
+        bf16 *orow = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + qi) * p.C + h * p.hd;
+        store_rows_bf16<HD>(orow, O, 1.f / ltot, p.hd, lane);
+        if (g == 0) p.lse[((long long)b * p.NH + h) * p.T + qi] = (m + log2f(ltot)) * LN2;
+    }
+}
+
+template <int HD> hipError_t fwd_launch(const AttnP &p, hipStream_t s) {
+    constexpr int NS = HD >= 128 ? 2 : 3;
+    const int nqb = (p.T + 127) / 128;
+    hipLaunchKernelGGL((fwd_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s) {
+    switch (HD) {
+    case 16: return fwd_launch<16>(p, s);
+    case 32: return fwd_launch<32>(p, s);
+    case 64: return fwd_launch<64>(p, s);
+    case 128: return fwd_launch<128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace dtb
