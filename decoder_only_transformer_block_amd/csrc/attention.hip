@@ -7,19 +7,15 @@
 //   backward with P_tj = exp(s_tj - lse_t), D_t = dO_t.o_t, dS = P (dO V^T - D).
 // Query head h reads kv head h / (NH/NKV).
 //
-// Design (CDNA4, wave64, 32x32 MFMA blocks):
+// This file holds the fp32 path (bf16 has its own kernels): fp32 operands
+// use the 32x32x2 fp32 MFMA.
 // * Scores are computed transposed, S^T = K Q^T, so a lane owns one query
 //   (column l%32) and 16 keys (rows) of each 32x32 block: the running max and
 //   sum of the online softmax are in-register reductions plus one exchange
 //   with the partner lane l^32.  The same layout makes P^T (and dS^T) usable
-//   directly as the B operand of the next product: the k order of an MFMA is
-//   ours to choose as long as both operands use it, so lane half g feeds the
-//   keys its accumulators hold (8*(r/4) + 4g + r%4).
-// * The A operand of those products needs several keys of one head dimension
-//   per lane (V^T, K^T, Q^T, dO^T).  For bf16 the tile is staged a second time
-//   transposed in LDS (8x8 register transposes during staging, 8-byte slots
-//   XOR-swizzled with the row); for fp32 one element per lane is read from the
-//   natural tile.
+//   directly as the B operand of the next product.
+// * The A operand of those products needs one element of a natural tile per
+//   lane and k step (V^T, K^T, Q^T, dO^T), read straight from LDS.
 // * Natural tiles are rows of hd elements in 16-byte chunks, XOR-swizzled
 //   with (row & 7).  Two LDS stages; the next tile's global loads are issued
 //   before the current tile's MFMAs (one barrier per tile).  Half of the
@@ -47,33 +43,10 @@ template <typename T, int HD> struct AT {
     static constexpr int XM = (NCH < 8 ? NCH : 8) - 1;  // swizzle mask
     static constexpr int ND = HD >= 32 ? HD / 32 : 1;   // 32-row blocks over hd
 };
-static constexpr bool is_bf16(int) { return false; }
 
 template <typename T, int HD> __device__ __forceinline__ int nat_off(int row, int chunk) {
     return row * AT<T, HD>::RB + ((chunk ^ (row & AT<T, HD>::XM)) << 4);
 }
-// transposed bf16 tile: HD rows (head dim) x 64 columns (keys or queries) =
-// 16 slots of 8 bytes (4 columns) per 128-byte row.  The slot index is XOR-ed
-// with h(d) = (d & 15) ^ g(d >> 4): for the fragment reads (16 consecutive d,
-// one slot) h is a bijection of d & 15; for the staging stores (16 lanes =
-// NBD = HD/8 head-dim blocks x 16/NBD column blocks, d = 8*db + j) g deposits
-// the bits of db >> 1 into the slot bits not already varied by the column
-// block and by db & 1, so the 16 stores land in 16 different slots.
-template <int HD> __device__ __forceinline__ int tr_hash(int d) {
-    constexpr int NBD = HD / 8;
-    const int x = d >> 4;
-    int gx;
-    if constexpr (NBD >= 16) gx = x & 7;
-    else if constexpr (NBD == 8) gx = (x & 1) | ((x & 2) << 1);
-    else if constexpr (NBD == 4) gx = x & 1;
-    else gx = 0;
-    return (d & 15) ^ gx;
-}
-template <int ROWS, int HD> __device__ __forceinline__ int tr_off(int d, int slot) {
-    static_assert(ROWS == 64, "transposed tiles are 64 columns wide");
-    return d * (ROWS * 2) + ((slot ^ tr_hash<HD>(d)) << 3);
-}
-
 // ---------------------------------------------------------------------------
 // staging helpers (a subset of NT threads, local id tl)
 // ---------------------------------------------------------------------------
@@ -103,66 +76,9 @@ template <typename T, int HD, int ROWS, int NT> struct Nat {
     }
 };
 
-// bf16 8x8 blocks of a [ROWS][HD] tile, stored natural and/or transposed
-template <int HD, int ROWS, int NT> struct Blk {
-    static constexpr int NBD = HD / 8, NBR = ROWS / 8;
-    static constexpr int ITEMS = NBD * NBR;
-    static constexpr int P = (ITEMS + NT - 1) / NT;
-    __device__ static __forceinline__ void load(u32x4 *reg, const bf16 *g, long long stride, int row0,
-                                                int nrows, int hd, int tl) {
-        const Buf buf(g + (long long)row0 * stride);
-#pragma unroll
-        for (int p = 0; p < P; p++) {
-            int idx = tl + NT * p;
-            int db = idx % NBD, rb = idx / NBD;
-            bool live = idx < ITEMS && db * 8 < hd;
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                int row = rb * 8 + i;
-                reg[p * 8 + i] = buf.ld16((int)(((long long)row * stride + db * 8) * 2), live && row0 + row < nrows);
-            }
-        }
-    }
-    template <bool NAT, bool TR>
-    __device__ static __forceinline__ void store(const u32x4 *reg, char *nat, char *tr, int tl) {
-#pragma unroll
-        for (int p = 0; p < P; p++) {
-            int idx = tl + NT * p;
-            if (idx >= ITEMS) continue;
-            int db = idx % NBD, rb = idx / NBD;
-            if constexpr (NAT) {
-#pragma unroll
-                for (int i = 0; i < 8; i++)
-                    *reinterpret_cast<u32x4 *>(nat + nat_off<bf16, HD>(rb * 8 + i, db)) = reg[p * 8 + i];
-            }
-            if constexpr (TR) {
-                u32x4 o[8];
-                transpose8x8(reg + p * 8, o);
-#pragma unroll
-                for (int j = 0; j < 8; j++) {
-                    int d = db * 8 + j;
-                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS, HD>(d, 2 * rb)) = u32x2{o[j][0], o[j][1]};
-                    *reinterpret_cast<u32x2 *>(tr + tr_off<ROWS, HD>(d, 2 * rb + 1)) = u32x2{o[j][2], o[j][3]};
-                }
-            }
-        }
-    }
-};
-
 // ---------------------------------------------------------------------------
 // fragment helpers
 // ---------------------------------------------------------------------------
-// A operand "transposed": lane (d = l%32 + 32*db, half g) supplies the keys that
-// accumulator registers r0..r0+7 (bf16) / r (fp32) of an S^T-layout block hold.
-// bf16: keys koff + {0..3} and koff + 8 + {0..3}, koff = j*32 + 16*hh + 4g, read
-// from the transposed tile; zero for d >= HD.
-template <int HD, int ROWS>
-__device__ __forceinline__ bf16x8 tr_frag(const char *tr, int d, int koff) {
-    if (HD < 32 && d >= HD) return bf16x8{};
-    u32x2 a = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS, HD>(d, koff >> 2));
-    u32x2 b = *reinterpret_cast<const u32x2 *>(tr + tr_off<ROWS, HD>(d, (koff >> 2) + 2));
-    return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
-}
 // fp32: element (row, d) of a natural tile
 template <int HD> __device__ __forceinline__ float nat_elem(const char *nat, int row, int d) {
     if (HD < 32 && d >= HD) return 0.f;
@@ -174,27 +90,13 @@ template <int HD> __device__ __forceinline__ float nat_elem(const char *nat, int
 // S^T-layout registers x (one 32x32 block) and A^T read from LDS.
 template <typename T, int HD, int ROWS>
 __device__ __forceinline__ void mma_trans(f32x16 *acc, const f32x16 &x, const char *tile, int j, int lane) {
-    const int g = lane >> 5, l32 = lane & 31;
-    if constexpr (std::is_same<T, bf16>::value) {
+    const int l32 = lane & 31;
 #pragma unroll
-        for (int hh = 0; hh < 2; hh++) {
-            u32x4 xw;
+    for (int r = 0; r < 16; r++) {
+        const int row = j * 32 + acc_row(r, lane);
 #pragma unroll
-            for (int e = 0; e < 4; e++) xw[e] = pack2_bf16(x[8 * hh + 2 * e], x[8 * hh + 2 * e + 1]);
-            const bf16x8 xb = __builtin_bit_cast(bf16x8, xw);
-            const int koff = j * 32 + 16 * hh + 4 * g;
-#pragma unroll
-            for (int db = 0; db < AT<T, HD>::ND; db++)
-                acc[db] = mfma32(tr_frag<HD, ROWS>(tile, db * 32 + l32, koff), xb, acc[db]);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < 16; r++) {
-            const int row = j * 32 + acc_row(r, lane);
-#pragma unroll
-            for (int db = 0; db < AT<T, HD>::ND; db++)
-                acc[db] = mfma32(nat_elem<HD>(tile, row, db * 32 + l32), x[r], acc[db]);
-        }
+        for (int db = 0; db < AT<T, HD>::ND; db++)
+            acc[db] = mfma32(nat_elem<HD>(tile, row, db * 32 + l32), x[r], acc[db]);
     }
 }
 
@@ -233,15 +135,9 @@ __device__ __forceinline__ void store_rows(T *row, const f32x16 *acc, float s, i
         for (int r4 = 0; r4 < 4; r4++) {
             int d = db * 32 + 8 * r4 + 4 * (lane >> 5);
             if (d < hd) {
-                if constexpr (std::is_same<T, bf16>::value) {
-                    u32x2 v{pack_bf16x2(acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s),
-                            pack_bf16x2(acc[db][4 * r4 + 2] * s, acc[db][4 * r4 + 3] * s)};
-                    *reinterpret_cast<u32x2 *>(row + d) = v;
-                } else {
-                    f32x4 v{acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s, acc[db][4 * r4 + 2] * s,
+                f32x4 v{acc[db][4 * r4] * s, acc[db][4 * r4 + 1] * s, acc[db][4 * r4 + 2] * s,
                             acc[db][4 * r4 + 3] * s};
                     *reinterpret_cast<f32x4 *>(row + d) = v;
-                }
             }
         }
 }
@@ -253,10 +149,8 @@ template <typename T, int HD> struct FwdCfg {
     static constexpr int BQ = 128, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);  // K natural tile bytes (= V tile bytes)
     static constexpr int STAGE = 2 * KB;
-    static constexpr bool BF = std::is_same<T, bf16>::value;
     // staging: threads [0, 128) load V, [128, 256) load K with the same loader
-    // (bf16: 8x8 blocks, V stored transposed, K natural; fp32: natural rows)
-    static constexpr int PREG = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
+    static constexpr int PREG = Nat<T, HD, BKV, 128>::P;
 };
 
 template <typename T, int HD>
@@ -265,21 +159,13 @@ __device__ __forceinline__ void fwd_stage_load(u32x4 *reg, const T *kb, const T 
     const int t = threadIdx.x;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
     const T *g = lo ? vb : kb;
-    if constexpr (std::is_same<T, bf16>::value)
-        Blk<HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
-    else
-        Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
 }
 template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = FwdCfg<T, HD>::KB;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
-    if constexpr (std::is_same<T, bf16>::value) {
-        if (lo) Blk<HD, 64, 128>::template store<false, true>(reg, nullptr, st + KB, t & 127);
-        else Blk<HD, 64, 128>::template store<true, false>(reg, st, nullptr, t & 127);
-    } else {
-        Nat<T, HD, 64, 128>::store(reg, lo ? st + KB : st, t & 127);
-    }
+    Nat<T, HD, 64, 128>::store(reg, lo ? st + KB : st, t & 127);
 }
 
 template <typename T, int HD>
@@ -386,10 +272,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: D = rowsum(dO * O)   [B][NH][T] fp32, one wave per (b, t) row
+// backward: D = rowsum(dO * O)   [B][NH][T] fp32, one wave per (b, t) row;
+// optionally L2 = lse * log2(e) in the same layout
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *L2) {
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= (long long)p.B * p.T) return;
@@ -417,7 +304,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
         }
         if (c < nch && (c % hch) == 0) {
             int h = c / hch;
-            D[((long long)b * p.NH + h) * p.T + tq] = s;
+            const long long i = ((long long)b * p.NH + h) * p.T + tq;
+            D[i] = s;
+            if (L2) L2[i] = p.lse_in[i] * LOG2E;
         }
     }
 }
@@ -428,11 +317,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
 template <typename T, int HD> struct DqCfg {
     static constexpr int BQ = 128, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);
-    static constexpr bool BF = std::is_same<T, bf16>::value;
-    // LDS stage: K natural, V natural, (bf16) K transposed.  Threads [0, 128)
-    // load K, [128, 256) load V with the same loader.
-    static constexpr int STAGE = (BF ? 3 : 2) * KB;
-    static constexpr int PREG = BF ? 8 * Blk<HD, BKV, 128>::P : Nat<T, HD, BKV, 128>::P;
+    // LDS stage: K natural, V natural.  Threads [0, 128) load K, [128, 256)
+    // load V with the same loader.
+    static constexpr int STAGE = 2 * KB;
+    static constexpr int PREG = Nat<T, HD, BKV, 128>::P;
 };
 
 template <typename T, int HD>
@@ -441,21 +329,13 @@ __device__ __forceinline__ void dq_stage_load(u32x4 *reg, const T *kb, const T *
     const int t = threadIdx.x;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
     const T *g = lo ? kb : vb;
-    if constexpr (std::is_same<T, bf16>::value)
-        Blk<HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
-    else
-        Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
 }
 template <typename T, int HD> __device__ __forceinline__ void dq_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = DqCfg<T, HD>::KB;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
-    if constexpr (std::is_same<T, bf16>::value) {
-        if (lo) Blk<HD, 64, 128>::template store<true, true>(reg, st, st + 2 * KB, t & 127);
-        else Blk<HD, 64, 128>::template store<true, false>(reg, st + KB, nullptr, t & 127);
-    } else {
-        Nat<T, HD, 64, 128>::store(reg, lo ? st : st + KB, t & 127);
-    }
+    Nat<T, HD, 64, 128>::store(reg, lo ? st : st + KB, t & 127);
 }
 
 template <typename T, int HD>
@@ -509,7 +389,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
         if (more) dq_stage_load<T, HD>(reg, kbase, vbase, stride, (kt + 1) * BKV, p.T, p.hd);
         const char *Ks = smem + (kt & 1) * FC::STAGE;
         const char *Vs = Ks + FC::KB;
-        const char *Kt = FC::BF ? Ks + 2 * FC::KB : Ks;
+        const char *Kt = Ks;
         if (kt < wtiles) {
             const int kv0 = kt * BKV;
 #pragma unroll
@@ -544,11 +424,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
 template <typename T, int HD> struct DkvCfg {
     static constexpr int BK = 128;   // keys per workgroup (4 waves x 32)
     static constexpr int BQ = 64;    // queries per tile
-    static constexpr bool BF = std::is_same<T, bf16>::value;
     static constexpr int QB = BQ * HD * (int)sizeof(T);
-    // LDS stage: Q natural, dO natural, (bf16) Q transposed, dO transposed, then lse2[BQ], D[BQ]
-    static constexpr int STAGE = (BF ? 4 : 2) * QB + 2 * BQ * 4;
-    static constexpr int PQ = BF ? 8 * Blk<HD, BQ, 128>::P : Nat<T, HD, BQ, 128>::P;
+    // LDS stage: Q natural, dO natural, then lse2[BQ], D[BQ]
+    static constexpr int STAGE = 2 * QB + 2 * BQ * 4;
+    static constexpr int PQ = Nat<T, HD, BQ, 128>::P;
     static constexpr int PREG = PQ;
 };
 
@@ -562,10 +441,7 @@ __device__ __forceinline__ void dkv_stage_load(u32x4 *reg, float &aux, const T *
     const T *g = lo ? qb : db;
     const long long st = lo ? qstride : dstride;
     const int tl = t & 127;
-    if constexpr (std::is_same<T, bf16>::value)
-        Blk<HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
-    else
-        Nat<T, HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
+    Nat<T, HD, BQ, 128>::load(reg, g, st, q0, T_, hd, tl);
     // threads 0..BQ-1: lse of query q0+t; threads 128..128+BQ-1: D (raw; the
     // transform to log2 units happens at the LDS store, away from the load)
     {
@@ -580,13 +456,8 @@ __device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, cha
     using FC = DkvCfg<T, HD>;
     const int t = threadIdx.x, tl = t & 127;
     char *nat = st + (t < 128 ? 0 : FC::QB);
-    if constexpr (std::is_same<T, bf16>::value) {
-        char *tr = st + (t < 128 ? 2 : 3) * FC::QB;
-        Blk<HD, FC::BQ, 128>::template store<true, true>(reg, nat, tr, tl);
-    } else {
-        Nat<T, HD, FC::BQ, 128>::store(reg, nat, tl);
-    }
-    float *f = reinterpret_cast<float *>(st + (FC::BF ? 4 : 2) * FC::QB);
+    Nat<T, HD, FC::BQ, 128>::store(reg, nat, tl);
+    float *f = reinterpret_cast<float *>(st + 2 * FC::QB);
     if (tl < FC::BQ) {
         const bool lo = t < 128;
         const bool ok = q0 + tl < T_;
@@ -661,9 +532,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
         }
         const char *st = smem + (it & 1) * FC::STAGE;
         const char *Qs = st, *dOs = st + FC::QB;
-        const char *Qt = FC::BF ? st + 2 * FC::QB : Qs;
-        const char *dOt = FC::BF ? st + 3 * FC::QB : dOs;
-        const float *lse2 = reinterpret_cast<const float *>(st + (FC::BF ? 4 : 2) * FC::QB);
+        const char *Qt = Qs;
+        const char *dOt = dOs;
+        const float *lse2 = reinterpret_cast<const float *>(st + 2 * FC::QB);
         const float *Dt = lse2 + BQ;
         const int q0 = (qt0 + it % nqt) * BQ;
         if (q0 + BQ - 1 >= kw0 && kw0 < p.T) {
@@ -744,7 +615,8 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
         init = true;
     }
     long long rows = (long long)p.B * p.T;
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D,
+                       (float *)nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
@@ -756,6 +628,19 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     int nkb = (p.T + KC::BK - 1) / KC::BK;
     hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
     return hipGetLastError();
+}
+
+// bf16: D and lse * log2(e) by the row kernel, then the dQ and dK/dV kernels
+static hipError_t bwd_bf16(const AttnP &p, int hdp, float *D, hipStream_t s) {
+    float *L2 = D + (long long)p.B * p.NH * p.T;
+    long long rows = (long long)p.B * p.T;
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, L2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    AttnP q = p;
+    q.D = D;
+    q.L2 = L2;
+    return attn_bwd_bf16(q, hdp, s);
 }
 
 static AttnP make_params(const void *qkv, int B, int T, int C, int NH, int NKV) {
@@ -805,11 +690,7 @@ int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const voi
     p.lse_in = lse;
     int hdp = pad_hd(p.hd, dtype);
     if (g_timing_on) timing_begin(s);
-    hipError_t e = dtype == DTB_BF16 ? (hdp == 16   ? bwd_t<bf16, 16>(p, D, s)
-                                        : hdp == 32 ? bwd_t<bf16, 32>(p, D, s)
-                                        : hdp == 64 ? bwd_t<bf16, 64>(p, D, s)
-                                                    : bwd_t<bf16, 128>(p, D, s))
-                                     : DTB_HD_DISPATCH(bwd_t, float, hdp, p, D, s);
+    hipError_t e = dtype == DTB_BF16 ? bwd_bf16(p, hdp, D, s) : DTB_HD_DISPATCH(bwd_t, float, hdp, p, D, s);
     if (e != hipSuccess) return set_launch_error(e, "attn_backward");
     if (g_timing_on) {
         double es = dtype == DTB_BF16 ? 2 : 4;

@@ -53,6 +53,10 @@ template <int HD> __device__ __forceinline__ int swz_rows(int r) {
 // row modulo 8 only, so row offsets that are multiples of 8 stay immediates)
 template <int HD> __device__ __forceinline__ int swz_cols(int r) { return r & 7 & (TL<HD>::NCH - 1); }
 
+// tiles read both ways (backward): the transposed reads need the row-mod-8
+// form, which the row reads then share
+template <int HD> __device__ __forceinline__ int swz_dual(int r) { return swz_cols<HD>(r); }
+
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 // DMA instruction q (1 KB) of a 64-row tile at row0 of a row-major tensor
@@ -67,6 +71,13 @@ __device__ __forceinline__ void dma_tile(char *lds, const bf16 *g, long long str
     const bool ok = row0 + r < nrows && c * 8 < hd;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(buf.r, (lds_vptr)(lds + q * 1024), 16,
                                              ok ? (int)((r * stride + c * 8) * 2) : (int)0x80000000, 0, 0, 0);
+}
+
+// 64 fp32 values (4 bytes per lane) of a row of a [rows][T] array into LDS
+__device__ __forceinline__ void dma_vec64(char *lds, const float *g, int q0, int n, bool live, int lane) {
+    const Buf buf(g);
+    const bool ok = live && q0 + lane < n;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(buf.r, (lds_vptr)lds, 4, ok ? (q0 + lane) * 4 : (int)0x80000000, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 lds_row16(const char *p) {
@@ -262,6 +273,312 @@ template <int HD> hipError_t fwd_launch(const AttnP &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+
+// ---------------------------------------------------------------------------
+// backward dQ: one workgroup = 4 waves x 32 queries of one (b, h), key tiles of
+// 64 (K and V, natural).  S^T = K Q^T and dP^T = V dO^T from the tile rows,
+// dS^T = P^T (dP^T - D), dQ^T += K^T dS^T with K^T through transposing reads.
+// ---------------------------------------------------------------------------
+template <int HD, int NS>
+__global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
+    using L = TL<HD>;
+    constexpr int BQ = 128, BKV = 64, RB = L::RB;
+    constexpr int DPW = L::NDMA / 2;
+    constexpr int STB = 2 * L::TILE;
+    __shared__ __attribute__((aligned(1024))) char s0[STB];
+    __shared__ __attribute__((aligned(1024))) char s1[STB];
+    __shared__ __attribute__((aligned(1024))) char s2[NS > 2 ? STB : 16];
+#define STG(S) ((S) == 0 ? s0 : (S) == 1 ? s1 : s2)
+
+    const int nqb = (p.T + BQ - 1) / BQ, BH = p.B * p.NH;
+    const int qb = nqb - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+    const long long stride = p.QKV;
+    const bf16 *base = reinterpret_cast<const bf16 *>(p.qkv) + (long long)b * p.T * stride;
+    const bf16 *kbase = base + p.C + kh * p.hd;
+    const bf16 *vbase = kbase + p.NKV * p.hd;
+    const int kv_end = min(p.T, q0 + BQ);
+    const int ntiles = (kv_end + BKV - 1) / BKV;
+    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
+
+    const bool isK = wave < 2;
+    const bf16 *src = isK ? kbase : vbase;
+    const int qsub = (wave & 1) * DPW;
+    auto issue = [&](char *st, int kt) {
+#pragma unroll
+        for (int i = 0; i < DPW; i++)
+            dma_tile<HD, true>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
+    };
+
+    u32x4 qf[L::NC], df[L::NC];
+    const long long li = ((long long)b * p.NH + h) * p.T + qi;
+    float l2 = 0.f, Dq = 0.f;
+    {
+        const Buf bq(base + h * p.hd);
+        const Buf bd(reinterpret_cast<const bf16 *>(p.dout) + (long long)b * p.T * p.C + h * p.hd);
+#pragma unroll
+        for (int c = 0; c < L::NC; c++) {
+            const int ch = 2 * c + g;
+            const bool ok = qi < p.T && ch * 8 < p.hd;
+            qf[c] = bq.ld16((int)(((long long)qi * stride + ch * 8) * 2), ok);
+            df[c] = bd.ld16((int)(((long long)qi * p.C + ch * 8) * 2), ok);
+        }
+        if (qi < p.T) {
+            l2 = p.L2[li];
+            Dq = p.D[li];
+        }
+    }
+    issue(s0, 0);
+    if (NS > 2) issue(s1, 1);
+
+    int kofs[L::NC];
+#pragma unroll
+    for (int c = 0; c < L::NC; c++) kofs[c] = l32 * RB + (((2 * c + g) ^ swz_dual<HD>(l32)) << 4);
+    int tofs[L::ND];
+    {
+        const int i16 = lane & 15, xr = 4 * g + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < L::ND; db++) {
+            const int d = 32 * db + (l32 & 16) + 4 * (i16 & 3);
+            const int ch = (d >> 3) & (L::NCH - 1);
+            tofs[db] = xr * RB + ((ch ^ swz_dual<HD>(xr)) << 4) + 8 * (i16 & 1);
+        }
+    }
+
+    f32x16 dQ[L::ND];
+#pragma unroll
+    for (int d = 0; d < L::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) dQ[d][r] = 0.f;
+
+    auto compute = [&](const char *st, int kt) {
+        const char *Ks = st, *Vs = st + L::TILE;
+        const int kv0 = kt * BKV;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            f32x16 S, dP;
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < L::NC; c++) {
+                S = mfma32(lds_row16(Ks + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, qf[c]), S);
+                dP = mfma32(lds_row16(Vs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, df[c]), dP);
+            }
+            const bool diag = kv0 + j * 32 + 31 > qw0;
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float pr = fast_exp2(fmaf(S[r], p.sl2, -l2));
+                if (diag && kv0 + j * 32 + acc_row(r, lane) > qi) pr = 0.f;
+                S[r] = pr * (dP[r] - Dq);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                u32x4 xw;
+#pragma unroll
+                for (int e = 0; e < 4; e++) xw[e] = pack2_bf16(S[8 * hh + 2 * e], S[8 * hh + 2 * e + 1]);
+                const bf16x8 xb = __builtin_bit_cast(bf16x8, xw);
+#pragma unroll
+                for (int db = 0; db < L::ND; db++)
+                    dQ[db] = mfma32(lds_tr8<RB>(Ks + tofs[db] + (32 * j + 16 * hh) * RB), xb, dQ[db]);
+            }
+        }
+    };
+
+    __builtin_amdgcn_s_waitcnt(0);
+#define BWD_STEP(S)                                                              \
+    {                                                                            \
+        const int kt = kt0 + (S);                                                \
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 2) * DPW));               \
+        asm volatile("s_barrier" ::: "memory");                                  \
+        issue(STG(((S) + NS - 1) % NS), kt + NS - 1);                            \
+        if (kt < wtiles) compute(STG(S), kt);                                    \
+    }
+    for (int kt0 = 0; kt0 < ntiles; kt0 += NS) {
+        BWD_STEP(0)
+        BWD_STEP(1)
+        if constexpr (NS > 2) BWD_STEP(2)
+    }
+#undef BWD_STEP
+#undef STG
+    __builtin_amdgcn_s_waitcnt(0);
+    if (qi < p.T) {
+        bf16 *row = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + qi) * p.QKV + h * p.hd;
+        store_rows_bf16<HD>(row, dQ, p.scale, p.hd, lane);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// backward dK, dV: one workgroup = 4 waves x 32 keys of one (b, kv head),
+// looping over the group's query heads and the query tiles (64) at or after
+// its keys, so dK / dV are summed over the group in registers (no atomics).
+// S = Q K^T and dP = dO V^T from the tile rows, dV^T += dO^T P and
+// dK^T += Q^T dS with dO^T and Q^T through transposing reads.  A stage holds
+// the Q tile, the dO tile and the 64 lse*log2(e) and D values of its queries.
+// ---------------------------------------------------------------------------
+template <int HD, int NS>
+__global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
+    using L = TL<HD>;
+    constexpr int BK = 128, BQ = 64, RB = L::RB;
+    constexpr int DPW = L::NDMA / 2 + 1;   // tile share plus one 256-byte vector
+    constexpr int AUX = 2 * L::TILE;       // [lse2 64][D 64][unused 128 floats]
+    constexpr int STB = 2 * L::TILE + 1024;
+    __shared__ __attribute__((aligned(1024))) char s0[STB];
+    __shared__ __attribute__((aligned(1024))) char s1[STB];
+    __shared__ __attribute__((aligned(1024))) char s2[NS > 2 ? STB : 16];
+#define STG(S) ((S) == 0 ? s0 : (S) == 1 ? s1 : s2)
+
+    const int BKVH = p.B * p.NKV;
+    const int kb = (int)(blockIdx.x / BKVH);  // low key blocks (most work) first
+    const int bk = blockIdx.x % BKVH;
+    const int b = bk / p.NKV, kh = bk % p.NKV;
+    const int grp = p.NH / p.NKV;
+    const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int k0 = kb * BK, kw0 = k0 + wave * 32, ki = kw0 + l32;
+    const long long stride = p.QKV;
+    const bf16 *base = reinterpret_cast<const bf16 *>(p.qkv) + (long long)b * p.T * stride;
+    const bf16 *dbase = reinterpret_cast<const bf16 *>(p.dout) + (long long)b * p.T * p.C;
+
+    const int qt0 = k0 / BQ;                    // first query tile touching these keys
+    const int nqt = (p.T + BQ - 1) / BQ - qt0;  // query tiles per head
+    const int niter = nqt * grp;
+
+    const bool isQ = wave < 2;
+    const int qsub = (wave & 1) * (DPW - 1);
+    auto issue = [&](char *st, int it) {
+        const bool live = it < niter;
+        const int hh = live ? it / nqt : 0, q0 = (qt0 + (live ? it % nqt : 0)) * BQ;
+        const int h = kh * grp + hh;
+        const bf16 *src = isQ ? base + h * p.hd : dbase + h * p.hd;
+        const long long st_ = isQ ? stride : (long long)p.C;
+#pragma unroll
+        for (int i = 0; i < DPW - 1; i++)
+            dma_tile<HD, true>(st + (isQ ? 0 : L::TILE), src, st_, q0, live ? p.T : 0, p.hd, qsub + i, lane);
+        const float *vec = (wave == 0 ? p.L2 : p.D) + ((long long)b * p.NH + h) * p.T;
+        dma_vec64(st + AUX + wave * 256, vec, q0, p.T, live && wave < 2, lane);
+    };
+
+    u32x4 kf[L::NC], vf[L::NC];
+    {
+        const Buf bkk(base + p.C + kh * p.hd);
+        const Buf bvv(base + p.C + (p.NKV + kh) * p.hd);
+#pragma unroll
+        for (int c = 0; c < L::NC; c++) {
+            const int ch = 2 * c + g;
+            const bool ok = ki < p.T && ch * 8 < p.hd;
+            kf[c] = bkk.ld16((int)(((long long)ki * stride + ch * 8) * 2), ok);
+            vf[c] = bvv.ld16((int)(((long long)ki * stride + ch * 8) * 2), ok);
+        }
+    }
+    issue(s0, 0);
+    if (NS > 2) issue(s1, 1);
+
+    int kofs[L::NC];
+#pragma unroll
+    for (int c = 0; c < L::NC; c++) kofs[c] = l32 * RB + (((2 * c + g) ^ swz_dual<HD>(l32)) << 4);
+    int tofs[L::ND];
+    {
+        const int i16 = lane & 15, xr = 4 * g + (i16 >> 2);
+#pragma unroll
+        for (int db = 0; db < L::ND; db++) {
+            const int d = 32 * db + (l32 & 16) + 4 * (i16 & 3);
+            const int ch = (d >> 3) & (L::NCH - 1);
+            tofs[db] = xr * RB + ((ch ^ swz_dual<HD>(xr)) << 4) + 8 * (i16 & 1);
+        }
+    }
+
+    f32x16 dK[L::ND], dV[L::ND];
+#pragma unroll
+    for (int d = 0; d < L::ND; d++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) dK[d][r] = dV[d][r] = 0.f;
+
+    auto compute = [&](const char *st, int it) {
+        const char *Qs = st, *dOs = st + L::TILE;
+        const float *l2s = reinterpret_cast<const float *>(st + AUX), *Ds = l2s + BQ;
+        const int q0 = (qt0 + it % nqt) * BQ;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            f32x16 S, dP;
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < L::NC; c++) {
+                S = mfma32(lds_row16(Qs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, kf[c]), S);
+                dP = mfma32(lds_row16(dOs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, vf[c]), dP);
+            }
+            const bool diag = q0 + j * 32 < kw0 + 31;
+            // the 16 query rows of this lane: 4 groups of 4 consecutive rows
+            f32x4 lq[4], dq4[4];
+#pragma unroll
+            for (int r4 = 0; r4 < 4; r4++) {
+                const int ql = j * 32 + 8 * r4 + 4 * g;
+                lq[r4] = *reinterpret_cast<const f32x4 *>(l2s + ql);
+                dq4[r4] = *reinterpret_cast<const f32x4 *>(Ds + ql);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                float pr = fast_exp2(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
+                if (diag && q0 + j * 32 + acc_row(r, lane) < ki) pr = 0.f;
+                S[r] = pr;
+                dP[r] = pr * (dP[r] - dq4[r >> 2][r & 3]);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; hh++) {
+                u32x4 xs, xd;
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    xs[e] = pack2_bf16(S[8 * hh + 2 * e], S[8 * hh + 2 * e + 1]);
+                    xd[e] = pack2_bf16(dP[8 * hh + 2 * e], dP[8 * hh + 2 * e + 1]);
+                }
+#pragma unroll
+                for (int db = 0; db < L::ND; db++) {
+                    const int o = tofs[db] + (32 * j + 16 * hh) * RB;
+                    dV[db] = mfma32(lds_tr8<RB>(dOs + o), __builtin_bit_cast(bf16x8, xs), dV[db]);
+                    dK[db] = mfma32(lds_tr8<RB>(Qs + o), __builtin_bit_cast(bf16x8, xd), dK[db]);
+                }
+            }
+        }
+    };
+
+    __builtin_amdgcn_s_waitcnt(0);
+#define BWD_STEP(S)                                                              \
+    {                                                                            \
+        const int it = it0 + (S);                                                \
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0((NS - 2) * DPW));               \
+        asm volatile("s_barrier" ::: "memory");                                  \
+        issue(STG(((S) + NS - 1) % NS), it + NS - 1);                            \
+        if (it < niter && (qt0 + it % nqt) * BQ + BQ - 1 >= kw0 && kw0 < p.T) compute(STG(S), it); \
+    }
+    for (int it0 = 0; it0 < niter; it0 += NS) {
+        BWD_STEP(0)
+        BWD_STEP(1)
+        if constexpr (NS > 2) BWD_STEP(2)
+    }
+#undef BWD_STEP
+#undef STG
+    __builtin_amdgcn_s_waitcnt(0);
+    if (ki < p.T) {
+        bf16 *row = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + ki) * p.QKV + p.C + kh * p.hd;
+        store_rows_bf16<HD>(row, dK, p.scale, p.hd, lane);
+        store_rows_bf16<HD>(row + p.NKV * p.hd, dV, 1.f, p.hd, lane);
+    }
+}
+
+template <int HD> hipError_t bwd_launch(const AttnP &p, hipStream_t s) {
+    constexpr int NS = HD >= 128 ? 2 : 3;
+    const int nqb = (p.T + 127) / 128;
+    hipLaunchKernelGGL((dq_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int nkb = (p.T + 127) / 128;
+    hipLaunchKernelGGL((dkv_bf16_kernel<HD, NS>), dim3(nkb * p.B * p.NKV), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s) {
@@ -270,6 +587,16 @@ hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s) {
     case 32: return fwd_launch<32>(p, s);
     case 64: return fwd_launch<64>(p, s);
     case 128: return fwd_launch<128>(p, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t attn_bwd_bf16(const AttnP &p, int HD, hipStream_t s) {
+    switch (HD) {
+    case 16: return bwd_launch<16>(p, s);
+    case 32: return bwd_launch<32>(p, s);
+    case 64: return bwd_launch<64>(p, s);
+    case 128: return bwd_launch<128>(p, s);
     default: return hipErrorInvalidValue;
     }
 }
