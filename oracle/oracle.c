@@ -36,6 +36,12 @@
 #include <string.h>
 #ifdef _OPENMP
 #include <omp.h>
+
+/* Thread teams only for loops with enough work: small calls (the unit
+ * tests' finite differences) would otherwise be dominated by team start-up.
+ * Every output is still computed by one thread in a fixed order, so the
+ * results do not depend on this choice. */
+#define ORC_PARALLEL(work) ((work) >= 65536.0)
 #endif
 
 #include "oracle.h"
@@ -53,7 +59,7 @@
 void orc_norm_forward(int mode, const double *x, const double *g, const double *b,
                       double eps, long R, int C, double *out, double *rstd, double *mean)
 {
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * C))
     for (long r = 0; r < R; r++) {
         const double *xr = x + r * C;
         double mu = 0.0;
@@ -87,7 +93,7 @@ void orc_norm_backward(int mode, const double *dy, const double *x, const double
                        const double *rstd, const double *mean, long R, int C,
                        double *dx, double *dg, double *db)
 {
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * C))
     for (long r = 0; r < R; r++) {
         const double *xr = x + r * C, *dyr = dy + r * C;
         double *dxr = dx + r * C;
@@ -123,7 +129,7 @@ void orc_norm_backward(int mode, const double *dy, const double *x, const double
     }
     if (mode == ORC_NORM_RMS_NOGAMMA) return;
     /* parameter gradients: one thread per column, rows summed in order */
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * C))
     for (int i = 0; i < C; i++) {
         double sg = 0.0, sb = 0.0;
         for (long r = 0; r < R; r++) {
@@ -145,7 +151,7 @@ void orc_norm_backward(int mode, const double *dy, const double *x, const double
 void orc_linear_forward(const double *inp, const double *w, const double *bias,
                         long R, int K, int N, double *out)
 {
-    #pragma omp parallel
+    #pragma omp parallel if(ORC_PARALLEL((double)R * K * N))
     {
         double *acc = (double *)malloc(sizeof(double) * (size_t)N);
         #pragma omp for schedule(static)
@@ -168,7 +174,7 @@ void orc_linear_backward(const double *dout, const double *inp, const double *w,
                          long R, int K, int N, double *dinp, double *dw, double *dbias)
 {
     if (dinp) {
-        #pragma omp parallel
+        #pragma omp parallel if(ORC_PARALLEL((double)R * K * N))
         {
             double *acc = (double *)malloc(sizeof(double) * (size_t)K);
             #pragma omp for schedule(static)
@@ -185,7 +191,7 @@ void orc_linear_backward(const double *dout, const double *inp, const double *w,
         }
     }
     if (dw || dbias) {
-        #pragma omp parallel
+        #pragma omp parallel if(ORC_PARALLEL((double)R * K * N))
         {
             double *acc = (double *)malloc(sizeof(double) * (size_t)K);
             #pragma omp for schedule(static)
@@ -222,7 +228,7 @@ void orc_rope(double *buf, int B, int T, int stride, int off, int nheads, int hd
               double base, int inverse)
 {
     int half = hd / 2;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)B * T * nheads * hd))
     for (long bt = 0; bt < (long)B * T; bt++) {
         int t = (int)(bt % T);
         for (int h = 0; h < nheads; h++) {
@@ -273,7 +279,7 @@ void orc_attn_forward(const double *qkv, int B, int T, int C, int NH, int NKV,
                       double *out, double *lse)
 {
     int hd = C / NH, QKV = C + 2 * NKV * hd, kh_div = NH / NKV;
-    #pragma omp parallel
+    #pragma omp parallel if(ORC_PARALLEL((double)B * NH * T * T * hd))
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
         #pragma omp for schedule(dynamic, 1) collapse(2)
@@ -312,7 +318,7 @@ void orc_attn_backward(const double *qkv, const double *dout, int B, int T, int 
     int hd = C / NH, QKV = C + 2 * NKV * hd, grp = NH / NKV;
     double scale = 1.0 / sqrt((double)hd);
     memset(dqkv, 0, sizeof(double) * (size_t)B * T * QKV);
-    #pragma omp parallel
+    #pragma omp parallel if(ORC_PARALLEL((double)B * NH * T * T * hd))
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
         double *p = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
@@ -463,7 +469,7 @@ void orc_attn_tail(const double *q_tail, const double *k, const double *v, const
     double scale = 1.0 / sqrt((double)hd);
     memset(dk_tail, 0, sizeof(double) * (size_t)R * KV);
     memset(dv_tail, 0, sizeof(double) * (size_t)R * KV);
-    #pragma omp parallel
+    #pragma omp parallel if(ORC_PARALLEL((double)R * T * NH * hd))
     {
         double *s = (double *)malloc(sizeof(double) * (size_t)T);
         double *p = (double *)malloc(sizeof(double) * (size_t)T);
@@ -538,7 +544,7 @@ static const double GELU_C = 0.044715;
 void orc_act_forward(int mlp, const double *up, long R, int H, double *h)
 {
     int W = (mlp == ORC_MLP_SWIGLU) ? 2 * H : H;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * H))
     for (long r = 0; r < R; r++)
         for (int j = 0; j < H; j++) {
             double f = up[r * W + j], y;
@@ -557,7 +563,7 @@ void orc_act_forward(int mlp, const double *up, long R, int H, double *h)
 void orc_act_backward(int mlp, const double *dh, const double *up, long R, int H, double *dup)
 {
     int W = (mlp == ORC_MLP_SWIGLU) ? 2 * H : H;
-    #pragma omp parallel for schedule(static)
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * H))
     for (long r = 0; r < R; r++)
         for (int j = 0; j < H; j++) {
             double d = dh[r * H + j], f = up[r * W + j];
