@@ -25,6 +25,82 @@ sys.path.insert(0, ROOT)
 
 PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X datasheet)
 HBM_PEAK = 8000.0                        # GB/s
+GEMM_FWD_KERNEL = "gemm_dma_kernel<true, true, 0, 8>"   # the bf16 forward-projection GEMM
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_llama_gqa_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "decoder_only_transformer_block_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
+
+
+def gemm_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch of the forward-projection GEMM from the committed
+    counter summary, or None when it is missing or was taken on other kernel
+    sources or another workload."""
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"```json\n(.*?)\n```", text, re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_hash") != gemm_source_hash() or d.get("workload") != workload:
+        return None
+    return d
+
+
+def traffic_summary(root: str, cmds: dict) -> str:
+    """Markdown summary of four rocprofv3 --pmc runs under root/{fetch,write,copy_fetch,copy_write}:
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the forward-projection GEMM
+    dispatches, each scaled by the ratio of known bytes to what the same counter
+    reads for a plain copy of known size."""
+    import glob
+    import sqlite3
+
+    def per_dispatch(sub, counter, match):
+        vals = {}
+        for db in glob.glob(os.path.join(root, sub, "**", "*.db"), recursive=True):
+            c = sqlite3.connect(db)
+            for name, disp, v in c.execute("select kernel_name, dispatch_id, value from counters_collection "
+                                           "where counter_name = ?", (counter,)):
+                if match(name):
+                    vals[disp] = vals.get(disp, 0.0) + v
+        return vals
+
+    is_gemm = lambda n: "gemm_dma_kernel<true, true, 0, 8>" in n or "gemm_dma_kernelILb1ELb1ELi0ELi8E" in n
+    is_copy = lambda n: "copy" in n.lower()
+    f = per_dispatch("fetch", "FETCH_SIZE", is_gemm)
+    w = per_dispatch("write", "WRITE_SIZE", is_gemm)
+    cf = per_dispatch("copy_fetch", "FETCH_SIZE", is_copy)
+    cw = per_dispatch("copy_write", "WRITE_SIZE", is_copy)
+    known = cmds["copy_bytes"]
+    fs = known / (1024.0 * max(cf.values()))
+    ws = known / (1024.0 * max(cw.values()))
+    fk = sum(f.values()) / len(f)
+    wk = sum(w.values()) / len(w)
+    traffic = (fk * fs + wk * ws) * 1024.0
+    d = {"workload": cmds["workload"], "kernel": GEMM_FWD_KERNEL, "source_hash": gemm_source_hash(),
+         "dispatches": len(f), "fetch_kib_per_dispatch": round(fk, 1), "write_kib_per_dispatch": round(wk, 1),
+         "copy_fetch_kib": round(max(cf.values()), 1), "copy_write_kib": round(max(cw.values()), 1),
+         "copy_bytes": known, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+         "traffic_bytes_per_launch": round(traffic)}
+    lines = ["# HBM traffic of the forward-projection GEMM (%s, Llama-GQA 4-layer stack)" % GEMM_FWD_KERNEL, "",
+             "Counter runs (repository root on the GPU box, one counter per run):", "", "```"]
+    lines += cmds["commands"] + ["```", "",
+              "FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch and averaged over the kernel's dispatches "
+              "(QKV, O, MLP up and MLP down projections of every layer).  Each is scaled by known bytes / "
+              "counter reading of the plain copy kernel in the copy-probe run.  `source_hash` is the SHA-256 "
+              "prefix of gemm.hip + common.h when the counters were taken; bench.py reports the traffic only "
+              "while the sources still match.", "", "```json", json.dumps(d), "```", ""]
+    return "\n".join(lines)
 
 
 def parse():
@@ -39,6 +115,9 @@ def parse():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (the known-size "
                          "reference kernel that scales the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--traffic-summary", default="",
+                    help="only write the forward-GEMM traffic summary from the rocprofv3 runs under this "
+                         "directory (subdirectories fetch, write, copy_fetch, copy_write) and exit")
     ap.add_argument("--cpu-tokens", type=int, default=256,
                     help="tokens of the oracle's bounded sample (one sequence, one layer)")
     return ap.parse_args()
@@ -156,6 +235,18 @@ def main():
               "path: the block shards over sequences with one gradient all-reduce per layer, described in the "
               "design notes but not built.", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_summary:
+        n = 256 * (1 << 20)
+        root = args.traffic_summary
+        bench = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-timing"
+        cmds = ["export TMPDIR=/tmp"]
+        for sub, ctr, prog in (("fetch", "FETCH_SIZE", bench), ("write", "WRITE_SIZE", bench),
+                               ("copy_fetch", "FETCH_SIZE", "python3 bench.py --copy-probe-mib 256"),
+                               ("copy_write", "WRITE_SIZE", "python3 bench.py --copy-probe-mib 256")):
+            cmds.append(f"timeout -s KILL 120 rocprofv3 --pmc {ctr} -d {root}/{sub} -o p -- {prog}")
+        cmds.append(f"python3 bench.py --traffic-summary {root} > profiles/gemm_fwd_llama_gqa_traffic.md")
+        print(traffic_summary(root, {"workload": "llama_gqa", "copy_bytes": n, "commands": cmds}))
+        return
     import torch
     from decoder_only_transformer_block_amd import configs
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -197,17 +288,30 @@ def main():
             e["gbps"] = round(gb, 1)
             e["frac_hbm_peak"] = round(gb / HBM_PEAK, 4)
         breakdown[k] = e
-    dom = "attn_bwd" if args.workload == "attn_long" else "gemm"
+    gem = [tim[k] for k in ("gemm_fwd", "gemm_dinp", "gemm_dw") if k in tim and tim[k]["launches"]]
+    if gem:
+        ms_g = sum(v["ms"] for v in gem)
+        fl_g = sum(v["flops"] for v in gem)
+        tf = fl_g / (ms_g * 1e-3) / 1e12
+        breakdown["gemm"] = {"ms_per_step": round(ms_g / args.steps, 4),
+                             "launches_per_step": sum(v["launches"] for v in gem) // args.steps,
+                             "tflops": round(tf, 2), "frac_mfma_peak": round(tf / peak, 4)}
+    dom = "attn_bwd" if args.workload == "attn_long" else "gemm_fwd"
     roof = None
     if dom in tim and tim[dom]["launches"]:
         d = tim[dom]
         ach = d["flops"] / (d["ms"] * 1e-3) / 1e12
+        traffic = None
+        if dom == "gemm_fwd":
+            st = stored_traffic(args.workload) if cfg.dtype == "bf16" else None
+            traffic = st["traffic_bytes_per_launch"] if st else None
         roof = {"kernel": "attention backward (dq + dk/dv kernels)" if dom == "attn_bwd" else
-                "MFMA GEMM (all QKV/O/MLP forward, dinp and dW launches)",
+                f"forward-projection GEMM {GEMM_FWD_KERNEL} (QKV, O, MLP up, MLP down)",
                 "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": None,
+                "frac": round(ach / peak, 4), "traffic": traffic,
                 "avg_launch_ms": round(d["ms"] / d["launches"], 4),
-                "flops_per_launch": d["flops"] / d["launches"]}
+                "flops_per_launch": d["flops"] / d["launches"],
+                "algorithmic_bytes_per_launch": round(d["bytes"] / d["launches"])}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -187,8 +187,8 @@ def timing_enable(on: bool) -> None:
 
 
 def timing_collect():
-    arr = (Timing * 4)()
-    n = lib().dtb_timing_collect(arr, 4)
-    names = ["gemm", "attn_fwd", "attn_bwd", "elementwise"]
+    names = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw"]
+    arr = (Timing * len(names))()
+    n = lib().dtb_timing_collect(arr, len(names))
     return {names[i]: {"ms": arr[i].ms, "flops": arr[i].flops, "bytes": arr[i].bytes,
                        "launches": arr[i].launches} for i in range(n)}

@@ -152,7 +152,10 @@ struct Launch {
 };
 
 // per-kernel-class timing (measurement only)
-enum KClass { K_GEMM = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_NCLASS = 4 };
+// timing classes: GEMMs by role (forward projections: both operands k-major,
+// output in the storage dtype; input gradients: B m/n-major; weight gradients:
+// fp32 accumulation), attention, everything else
+enum KClass { K_GEMM_FWD = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_GEMM_DINP = 4, K_GEMM_DW = 5, K_NCLASS = 6 };
 void timing_begin(hipStream_t s);
 void timing_end(hipStream_t s, int cls, double flops, double bytes);
 extern bool g_timing_on;

@@ -174,13 +174,22 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
     }
 }
 
-// dst[i] += sum_p part[p][i] for i < n (part row stride ld)
+// dst[i] += sum_p part[p][i] for i < n (part row stride ld).  A workgroup
+// covers 32 columns; its 8 groups of 32 threads sum the parts p = pg, pg+8, ...
+// (independent loads, issued back to back), then combine in a fixed order.
 __global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst) {
-    int i = blockIdx.x * 256 + threadIdx.x;
-    if (i >= n) return;
+    __shared__ float red[8][32];
+    const int c = threadIdx.x & 31, pg = threadIdx.x >> 5;
+    const int i = blockIdx.x * 32 + c;
     float s = 0.f;
-    for (int p = 0; p < np; p++) s += part[(long)p * ld + i];
-    dst[i] += s;
+    if (i < n) {
+#pragma unroll 8
+        for (int p = pg; p < np; p += 8) s += part[(long)p * ld + i];
+    }
+    red[pg][c] = s;
+    __syncthreads();
+    if (pg == 0 && i < n)
+        dst[i] += ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) + ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
 }
 
 static int npl_for(int C, int dtype) {
@@ -266,9 +275,9 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
                        : NPL_DISPATCH(norm_bwd_t, float, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s);
     if (e != hipSuccess) return set_launch_error(e, "norm_backward");
     if (mode != DTB_NORM_RMS_NOGAMMA) {
-        hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part, npart, 2L * C, C, dg);
+        hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C, dg);
         if (mode == DTB_NORM_LAYER)
-            hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 255) / 256), dim3(256), 0, s, part + C, npart, 2L * C,
+            hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part + C, npart, 2L * C,
                                C, db);
         e = hipGetLastError();
         if (e != hipSuccess) return set_launch_error(e, "norm_backward reduce");
@@ -494,7 +503,7 @@ int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, 
         hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
     else
         hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
-    hipLaunchKernelGGL(reduce_parts_kernel, dim3((N + 255) / 256), dim3(256), 0, s, part, npart, (long)N, N, db);
+    hipLaunchKernelGGL(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, npart, (long)N, N, db);
     DTB_LAUNCH_CHECK("bias_grad");
     if (g_timing_on) timing_end(s, K_ELEM, 0, (double)R * N * (dtype == DTB_BF16 ? 2 : 4));
     return DTB_OK;

@@ -687,7 +687,8 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         const double es = g.dtype == DTB_BF16 ? 2.0 : 4.0;
         double bytes = es * ((double)g.M * g.K + (double)g.N * g.K) +
                        (g.out_f32 ? 4.0 * (g.accumulate ? 2.0 : 1.0) : es) * g.M * g.N;
-        timing_end(s, K_GEMM, flops, bytes);
+        const int cls = g.out_f32 ? K_GEMM_DW : (g.b_kmajor ? K_GEMM_FWD : K_GEMM_DINP);
+        timing_end(s, cls, flops, bytes);
     }
     return DTB_OK;
 }

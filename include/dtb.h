@@ -201,7 +201,8 @@ const char *dtb_version(void);
 
 /* Optional per-kernel timing for measurement: while enabled, every kernel the
  * library enqueues is bracketed by HIP events on its stream, grouped by kernel
- * class (0 gemm, 1 attn_fwd, 2 attn_bwd, 3 elementwise), together with the
+ * class (0 forward-projection GEMMs, 1 attn_fwd, 2 attn_bwd, 3 elementwise,
+ * 4 input-gradient GEMMs, 5 weight-gradient GEMMs), together with the
  * algorithmic flops / bytes of each launch.  dtb_timing_collect() waits for
  * the recorded events, adds the elapsed times to the running totals and
  * returns the number of classes filled (at most max_classes).  Not for use
