@@ -49,9 +49,15 @@ template <int HD> __device__ __forceinline__ int swz_rows(int r) {
     if constexpr (HD <= 32) return (r >> 3) & M;
     else return (r ^ (r >> 3)) & M;
 }
-// chunk swizzle of tiles read transposed (groups of 4 rows; depends on the
-// row modulo 8 only, so row offsets that are multiples of 8 stay immediates)
-template <int HD> __device__ __forceinline__ int swz_cols(int r) { return r & 7 & (TL<HD>::NCH - 1); }
+// chunk swizzle of tiles read transposed (groups of 4 rows).  It depends on the
+// row modulo 8 only, so row offsets that are multiples of 8 stay immediates;
+// this permutation was chosen with the LDS bank-conflict counter (none left in
+// the forward; half of the identity's in the backward, whose tiles are also
+// read as rows).
+template <int HD> __device__ __forceinline__ int swz_cols(int r) {
+    r &= 7;
+    return (((r & 3) << 1) | ((r >> 2) & 1)) & (TL<HD>::NCH - 1);
+}
 
 // tiles read both ways (backward): the transposed reads need the row-mod-8
 // form, which the row reads then share
