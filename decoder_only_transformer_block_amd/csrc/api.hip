@@ -263,7 +263,7 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
     if ((long long)B * T == 0) return DTB_OK;
     if (!ptr_ok(dqkv) || !ptr_ok(qkv) || !ptr_ok(out) || !ptr_ok(dout) || !ptr_ok(lse) || !ptr_ok(workspace))
         return DTB_EINVAL_PTR;
-    return launch_attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, (float *)workspace,
+    return launch_attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, (float *)workspace, nullptr,
                                 (hipStream_t)stream);
 }
 
@@ -476,13 +476,13 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     dw.A = dx2; dw.lda = C; dw.B = o; dw.ldb = C; dw.M = C; dw.N = C; dw.K = BT; dw.out = gr->wo; dw.ldo = C;
     TRY(gemm(dw, gws, W.gemm_bytes, s));
     if (c->o_bias) TRY(bias_grad(dt, dx2, BT, C, gr->bo, bpart, W.bparts, s));
-    // attention
-    TRY(launch_attn_backward(dqkv, qkv, o, dO, lse, c->B, c->T, C, c->NH, c->NKV, dt, Dbuf, s));
+    // attention (dq and dk leave the kernels already rotated back by the transposed RoPE)
+    float *cs = nullptr;
     if (c->rope == DTB_ROPE_NEOX) {
-        float *cs = (float *)(ws + W.cs);
+        cs = (float *)(ws + W.cs);
         TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
-        TRY(rope_apply(dt, dqkv, cs, c->B, c->T, d.QKV, c->NH, c->NKV, d.hd, 1, s));
     }
+    TRY(launch_attn_backward(dqkv, qkv, o, dO, lse, c->B, c->T, C, c->NH, c->NKV, dt, Dbuf, cs, s));
     // qkv projection: dn1 = dqkv Wqkv; dWqkv += dqkv^T n1
     dinp.A = dqkv; dinp.lda = d.QKV; dinp.B = w->wqkv; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.QKV;
     dinp.out = dn1; dinp.ldo = C;

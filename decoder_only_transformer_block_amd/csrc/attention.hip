@@ -412,6 +412,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
         if (more) dq_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
         __syncthreads();
     }
+    if (p.rope_cs) rope_rotate_acc<A::ND>(dQ, p.rope_cs + (long long)min(qi, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (qi < p.T) {
         T *row = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + qi) * p.QKV + h * p.hd;
         store_rows<T, HD>(row, dQ, p.scale, p.hd, lane);
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
         if (more) dkv_stage_store<T, HD>(reg, aux, smem + ((it + 1) & 1) * FC::STAGE, (qt0 + (it + 1) % nqt) * BQ, p.T);
         __syncthreads();
     }
+    if (p.rope_cs) rope_rotate_acc<A::ND>(dK, p.rope_cs + (long long)min(ki, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (ki < p.T) {
         T *row = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + ki) * p.QKV + p.C + kh * p.hd;
         store_rows<T, HD>(row, dK, p.scale, p.hd, lane);
@@ -681,9 +683,10 @@ int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, in
 }
 
 int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout, const float *lse, int B,
-                         int T, int C, int NH, int NKV, int dtype, float *D, hipStream_t s) {
+                         int T, int C, int NH, int NKV, int dtype, float *D, const float *rope_cs, hipStream_t s) {
     if (B == 0 || T == 0) return DTB_OK;
     AttnP p = make_params(qkv, B, T, C, NH, NKV);
+    p.rope_cs = reinterpret_cast<const float2 *>(rope_cs);
     p.o = dqkv;
     p.out = out;
     p.dout = dout;

@@ -410,6 +410,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
 #undef BWD_STEP
 #undef STG
     __builtin_amdgcn_s_waitcnt(0);
+    if (p.rope_cs) rope_rotate_acc<L::ND>(dQ, p.rope_cs + (long long)min(qi, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (qi < p.T) {
         bf16 *row = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + qi) * p.QKV + h * p.hd;
         store_rows_bf16<HD>(row, dQ, p.scale, p.hd, lane);
@@ -567,6 +568,7 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
 #undef BWD_STEP
 #undef STG
     __builtin_amdgcn_s_waitcnt(0);
+    if (p.rope_cs) rope_rotate_acc<L::ND>(dK, p.rope_cs + (long long)min(ki, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (ki < p.T) {
         bf16 *row = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + ki) * p.QKV + p.C + kh * p.hd;
         store_rows_bf16<HD>(row, dK, p.scale, p.hd, lane);

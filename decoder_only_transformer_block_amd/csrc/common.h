@@ -195,9 +195,11 @@ size_t gemm_ws_bytes(int M, int N, int K, int dtype);
 int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV,
                         int dtype, hipStream_t s);
 // D: fp32 scratch [B][NH][T]
+// rope_cs: NeoX (cos, sin) table [T][hd/2] -> dq and dk are rotated back
+// (transposed rotation) before they are stored; null for plain attention
 int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout,
                          const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
-                         float *D, hipStream_t s);
+                         float *D, const float *rope_cs, hipStream_t s);
 
 // elementwise / reductions
 int norm_forward(int mode, int dtype, const void *x, const void *g, const void *b, float eps, long R, int C,

@@ -20,6 +20,13 @@ def _reduced():
         "llama_gqa_reduced": K.LLAMA_GQA.replace(L=2, B=2, T=200, C=512, NH=8, NKV=2, H=1408),
         "llama_gqa_f32_mqa": K.LLAMA_GQA.replace(L=1, B=1, T=130, C=256, NH=4, NKV=1, H=512, dtype="f32"),
         "gpt2_bf16_t1": K.GPT2_SMALL.replace(L=1, B=4, T=1, C=256, NH=4, NKV=4, H=1024, dtype="bf16"),
+        # NeoX RoPE at every head width (the rotation pairs d, d + hd/2 sit in
+        # different places of the attention accumulators for each)
+        "rope_hd4_f32": K.MINI_QWEN2.replace(L=1, B=2, T=45, C=16, NH=4, NKV=2, H=32),
+        "rope_hd8_f32": K.LLAMA_GQA.replace(L=1, B=2, T=70, C=64, NH=8, NKV=4, H=128, dtype="f32"),
+        "rope_hd8_bf16": K.LLAMA_GQA.replace(L=1, B=2, T=70, C=64, NH=8, NKV=4, H=128),
+        "rope_hd32_bf16": K.LLAMA_GQA.replace(L=1, B=1, T=150, C=256, NH=8, NKV=2, H=512),
+        "rope_hd128_bf16": K.LLAMA_GQA.replace(L=1, B=1, T=140, C=512, NH=4, NKV=2, H=1024),
     }
 
 
