@@ -384,15 +384,16 @@ int block_forward(const dtb_block_cfg *c, const dtb_block_weights *w, const void
     GemmArgs g{};
     g.dtype = dt;
     g.a_kmajor = g.b_kmajor = true;
-    // qkv = n1 Wqkv^T + bqkv
+    // qkv = RoPE(n1 Wqkv^T + bqkv) on the q and k heads (rotation in the GEMM epilogue)
     g.A = n1; g.lda = C; g.B = w->wqkv; g.ldb = C; g.M = BT; g.N = d.QKV; g.K = C;
     g.out = qkv; g.ldo = d.QKV; g.bias = c->qkv_bias ? w->bqkv : nullptr; g.res = nullptr;
-    TRY(gemm(g, nullptr, 0, s));
     if (c->rope == DTB_ROPE_NEOX) {
         float *cs = (float *)(ws + W.cs);
         TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
-        TRY(rope_apply(dt, qkv, cs, c->B, c->T, d.QKV, c->NH, c->NKV, d.hd, 0, s));
+        g.rope_cs = cs; g.rope_T = c->T; g.rope_hd = d.hd; g.rope_cols = C + c->NKV * d.hd;
     }
+    TRY(gemm(g, nullptr, 0, s));
+    g.rope_cs = nullptr;
     TRY(launch_attn_forward(o, lse, qkv, c->B, c->T, C, c->NH, c->NKV, dt, s));
     // x2 = x + o Wo^T + bo
     g.A = o; g.lda = C; g.B = w->wo; g.ldb = C; g.M = BT; g.N = C; g.K = C;

@@ -187,6 +187,11 @@ struct GemmArgs {
     const void *bias;     // [N] dtype, may be NULL
     const void *res;      // [M, ldr] dtype, may be NULL (may alias out)
     long long ldr;
+    // NeoX RoPE of the output (after the bias): columns [0, rope_cols) are
+    // heads of rope_hd, row m is position m % rope_T; table [rope_T][rope_hd/2]
+    // of (cos, sin).  Null rope_cs: none.  Only with the plain dtype output.
+    const float *rope_cs;
+    int rope_T, rope_hd, rope_cols;
 };
 // ws: fp32 scratch for split-K partials (may be NULL -> no split)
 int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s);

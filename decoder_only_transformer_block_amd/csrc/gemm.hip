@@ -59,6 +59,8 @@ struct KParams {
     const void *res;
     long long ldr;
     float *part;   // split partials [splits][M][N]
+    const float2 *rope_cs;  // NeoX RoPE of the output columns [0, rope_cols) (mode 0), or null
+    int rope_T, rope_hd, rope_cols;
 };
 
 // 128-byte LDS rows, 16-byte chunk XOR-ed with (row ^ row/8) & 7: conflict-free for
@@ -209,17 +211,27 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
     const int cc = lane % CPR, rr = lane / CPR;
     const int n = n_base + cc * 4;
     const bool nok = n < p.N;
-    f32x4 bv = {0.f, 0.f, 0.f, 0.f};
-    if ((mode == 0 || mode == 1) && p.bias) {
+    auto load_bias = [&](int col, bool ok) -> f32x4 {
         const Buf bb(p.bias);
         if constexpr (std::is_same<T, bf16>::value) {
-            u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(bb.r, nok ? n * 2 : (int)0x80000000, 0, 0);
-            bv = f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
-                       __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+            u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(bb.r, ok ? col * 2 : (int)0x80000000, 0, 0);
+            return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
         } else {
-            bv = __builtin_bit_cast(f32x4, bb.ld16(n * 4, nok));
+            return __builtin_bit_cast(f32x4, bb.ld16(col * 4, ok));
         }
-    }
+    };
+    f32x4 bv = {0.f, 0.f, 0.f, 0.f};
+    if ((mode == 0 || mode == 1) && p.bias) bv = load_bias(n, nok);
+    // RoPE: the rotation partner of column n is n +- hd/2, in this wave's LDS
+    // rows (the host only asks for it when a wave's columns hold whole heads)
+    const bool rope = mode == 0 && p.rope_cs && n < p.rope_cols;
+    const int rhalf = p.rope_hd / 2;
+    const int ri = n % (p.rope_hd > 0 ? p.rope_hd : 1);
+    const bool rlow = ri < rhalf;
+    const int rk = rlow ? ri : ri - rhalf, roff = rlow ? rhalf : -rhalf;
+    f32x4 bvp = {0.f, 0.f, 0.f, 0.f};
+    if (rope && rhalf >= 4 && p.bias) bvp = load_bias(n + roff, nok);
     // residual / accumulate inputs for all passes first (uniform branches outside
     // the loops, so the loads issue back to back and are waited for at first use)
     f32x4 in[PASSES];
@@ -262,6 +274,25 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
         if (!(nok && m < p.M)) continue;
         if (mode == 0) {
             v = v + bv + in[q];
+            if (rope) {
+                const float2 *cs = p.rope_cs + (long long)(m % p.rope_T) * rhalf;
+                if (rhalf >= 4) {
+                    const f32x4 w = *reinterpret_cast<const f32x4 *>(lw + row * W + cc * 4 + roff) + bvp;
+                    const float sg = rlow ? -1.f : 1.f;
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float2 c = cs[rk + e];
+                        v[e] = v[e] * c.x + sg * w[e] * c.y;
+                    }
+                } else {  // head width 4: pairs (0, 2), (1, 3) of the vector
+                    const float2 c0 = cs[0], c1 = cs[1];
+                    const f32x4 x = v;
+                    v[0] = x[0] * c0.x - x[2] * c0.y;
+                    v[2] = x[2] * c0.x + x[0] * c0.y;
+                    v[1] = x[1] * c1.x - x[3] * c1.y;
+                    v[3] = x[3] * c1.x + x[1] * c1.y;
+                }
+            }
             if constexpr (std::is_same<T, bf16>::value) {
                 u32x2 w{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
                 *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16 *>(p.out) + (long long)m * p.ldo + n) = w;
@@ -662,6 +693,11 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     p.out_mode = splits > 1 ? 3 : (g.out_f32 ? (g.accumulate ? 2 : 1) : 0);
     p.bias = g.bias; p.res = g.res; p.ldr = g.ldr;
     p.part = splits > 1 ? reinterpret_cast<float *>(ws) : nullptr;
+    // RoPE in the epilogue needs whole heads inside one wave's columns
+    const int wave_cols = (g.dtype == DTB_BF16 && tc.bm == 256 && tc.bn == 256) ? 128 : tc.bn / 2;
+    const bool rope_fused = g.rope_cs && splits == 1 && !g.out_f32 && g.rope_hd <= wave_cols;
+    p.rope_cs = rope_fused ? reinterpret_cast<const float2 *>(g.rope_cs) : nullptr;
+    p.rope_T = g.rope_T; p.rope_hd = g.rope_hd; p.rope_cols = g.rope_cols;
     double flops = 2.0 * g.M * g.N * (double)g.K;
     if (g_timing_on) timing_begin(s);
     hipError_t e;
@@ -682,6 +718,11 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
                            g.N, splits);
         e = hipGetLastError();
         if (e != hipSuccess) return set_launch_error(e, "splitk_reduce");
+    }
+    if (g.rope_cs && !rope_fused) {  // heads wider than a wave's columns: separate pass
+        const int r = rope_apply(g.dtype, g.out, g.rope_cs, g.M / g.rope_T, g.rope_T, (int)g.ldo,
+                                 g.rope_cols / g.rope_hd, 0, g.rope_hd, 0, s);
+        if (r) return r;
     }
     if (g_timing_on) {
         const double es = g.dtype == DTB_BF16 ? 2.0 : 4.0;

@@ -27,6 +27,8 @@ def _reduced():
         "rope_hd8_bf16": K.LLAMA_GQA.replace(L=1, B=2, T=70, C=64, NH=8, NKV=4, H=128),
         "rope_hd32_bf16": K.LLAMA_GQA.replace(L=1, B=1, T=150, C=256, NH=8, NKV=2, H=512),
         "rope_hd128_bf16": K.LLAMA_GQA.replace(L=1, B=1, T=140, C=512, NH=4, NKV=2, H=1024),
+        # heads wider than a wave's GEMM columns: RoPE as a separate pass
+        "rope_hd128_f32": K.LLAMA_GQA.replace(L=1, B=1, T=70, C=256, NH=2, NKV=1, H=256, dtype="f32"),
     }
 
 
