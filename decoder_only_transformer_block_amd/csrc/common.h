@@ -117,6 +117,27 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, f32x16 c) {
 }
 __device__ __forceinline__ int acc_row(int r, int lane) { return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3); }
 
+// ---- activation backward, per element --------------------------------------
+// d: gradient of the activation output; a: its input (SwiGLU: the gate g);
+// u: the SwiGLU up value.  Returns the gradient of a; *du receives the SwiGLU
+// gradient of u.  ("nanoeuler — CUDA kernels": swiglu_backward_kernel;
+// "microgpt.cu": relu_backward_kernel; llm.c gelu_backward, tanh form.)
+constexpr float GELU_K = 0.7978845608028654f;  // sqrt(2/pi)
+constexpr float GELU_C = 0.044715f;
+__device__ __forceinline__ float act_grad(int mlp, float d, float a, float u, float *du) {
+    if (mlp == DTB_MLP_SWIGLU) {
+        const float sg = 1.f / (1.f + __expf(-a));
+        *du = d * a * sg;
+        return d * u * sg * (1.f + a * (1.f - sg));
+    } else if (mlp == DTB_MLP_RELU) {
+        return a > 0.f ? d : 0.f;
+    } else {
+        const float t = GELU_K * (a + GELU_C * a * a * a);
+        const float th = tanhf(t);
+        return d * (0.5f * (1.f + th) + 0.5f * a * (1.f - th * th) * GELU_K * (1.f + 3.f * GELU_C * a * a));
+    }
+}
+
 // ---- MFMA on one 16-byte chunk of A and B ---------------------------------
 __device__ __forceinline__ void mma_chunk(f32x16 &acc, u32x4 a, u32x4 b, bf16) {
     acc = mfma32(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), acc);
@@ -192,6 +213,17 @@ struct GemmArgs {
     // of (cos, sin).  Null rope_cs: none.  Only with the plain dtype output.
     const float *rope_cs;
     int rope_T, rope_hd, rope_cols;
+    // activation backward in the epilogue: the output is not written as is;
+    // with d = the GEMM result at (m, n), act_up = the saved activation input
+    // [M][W] (W = ldo = 2 act_H for SwiGLU, gate columns then up columns), the
+    // epilogue writes the gradient of that input into out[M][W].  Null: none.
+    const void *act_up;
+    // activation forward: out = [M][ldo] activation input (ldo = N = 2 act_H for
+    // SwiGLU, gate columns then up columns) and act_h [M][act_H] = activation
+    // output (fused into the GEMM where the tiling allows, else a second pass).
+    // Null: none.
+    void *act_h;
+    int act_mode, act_H;
 };
 // ws: fp32 scratch for split-K partials (may be NULL -> no split)
 int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s);

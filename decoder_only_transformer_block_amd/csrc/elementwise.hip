@@ -353,9 +353,6 @@ int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int
 
 // ------------------------------------------------------------ activations ---
 __device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
-constexpr float GELU_K = 0.7978845608028654f;  // sqrt(2/pi)
-constexpr float GELU_C = 0.044715f;
-
 template <typename T, int MLP>
 __global__ __launch_bounds__(256) void act_fwd_kernel(const T *up, long R, int H, T *h) {
     constexpr int EPC = 16 / sizeof(T);
@@ -394,31 +391,13 @@ __global__ __launch_bounds__(256) void act_bwd_kernel(const T *dh, const T *up, 
     if (i >= R * hc) return;
     long r = i / hc;
     int c = (int)(i % hc);
-    float d[EPC], a[EPC], o[EPC];
+    float d[EPC], a[EPC], u[EPC], o[EPC], du[EPC];
     unpack16<T>(ld16(dh + r * H + c * EPC), d);
     unpack16<T>(ld16(up + r * W + c * EPC), a);
-    if (MLP == DTB_MLP_SWIGLU) {
-        float u[EPC], du[EPC];
-        unpack16<T>(ld16(up + r * W + H + c * EPC), u);
+    if (MLP == DTB_MLP_SWIGLU) unpack16<T>(ld16(up + r * W + H + c * EPC), u);
 #pragma unroll
-        for (int e = 0; e < EPC; e++) {
-            float sg = sigm(a[e]);
-            o[e] = d[e] * u[e] * sg * (1.f + a[e] * (1.f - sg));
-            du[e] = d[e] * a[e] * sg;
-        }
-        st16(dup + r * W + H + c * EPC, pack16<T>(du));
-    } else if (MLP == DTB_MLP_RELU) {
-#pragma unroll
-        for (int e = 0; e < EPC; e++) o[e] = a[e] > 0.f ? d[e] : 0.f;
-    } else {
-#pragma unroll
-        for (int e = 0; e < EPC; e++) {
-            float f = a[e];
-            float u = GELU_K * (f + GELU_C * f * f * f);
-            float th = tanhf(u);
-            o[e] = d[e] * (0.5f * (1.f + th) + 0.5f * f * (1.f - th * th) * GELU_K * (1.f + 3.f * GELU_C * f * f));
-        }
-    }
+    for (int e = 0; e < EPC; e++) o[e] = act_grad(MLP, d[e], a[e], MLP == DTB_MLP_SWIGLU ? u[e] : 0.f, &du[e]);
+    if (MLP == DTB_MLP_SWIGLU) st16(dup + r * W + H + c * EPC, pack16<T>(du));
     st16(dup + r * W + c * EPC, pack16<T>(o));
 }
 

@@ -54,13 +54,24 @@ struct KParams {
     int kchunk;  // k range per split (multiple of BK)
     void *out;
     long long ldo;
-    int out_mode;  // 0 store dtype, 1 store fp32, 2 accumulate fp32, 3 split partial fp32
+    int out_mode;  // 0 store dtype, 1 store fp32, 2 accumulate fp32, 3 split partial fp32,
+                   // 4 activation backward, 5 SwiGLU forward
     const void *bias;
     const void *res;
     long long ldr;
     float *part;   // split partials [splits][M][N]
     const float2 *rope_cs;  // NeoX RoPE of the output columns [0, rope_cols) (mode 0), or null
     int rope_T, rope_hd, rope_cols;
+    // mode 4: activation backward -- the GEMM result is the gradient of the
+    // activation output; act_up [M][ldo] holds the saved activation input
+    // (SwiGLU: gate columns [0, act_H), up columns [act_H, 2 act_H)); out
+    // receives its gradient in the same layout.
+    // mode 5: SwiGLU forward (256 x 256 kernel) -- tile column block tn holds
+    // gate columns tn*128 .. +127 and the matching up columns act_H + tn*128 ..;
+    // out receives [g | u] and act_h [M][act_H] receives silu(g) u.
+    const void *act_up;
+    void *act_h;
+    int act_mode, act_H;
 };
 
 // 128-byte LDS rows, 16-byte chunk XOR-ed with (row ^ row/8) & 7: conflict-free for
@@ -189,13 +200,35 @@ __device__ __forceinline__ void tile_coords(int nm, int nn, int &tm, int &tn) {
     tn = in_group / gsize;
 }
 
+// four consecutive elements of a row-major T array as floats (zeros if !ok),
+// and the store of four floats as T
+template <typename T> __device__ __forceinline__ f32x4 load_row4(const void *base, long long idx, bool ok) {
+    const Buf b(base);
+    if constexpr (std::is_same<T, bf16>::value) {
+        u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(b.r, ok ? (int)(idx * 2) : (int)0x80000000, 0, 0);
+        return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u), __uint_as_float(w[1] << 16),
+                     __uint_as_float(w[1] & 0xffff0000u)};
+    } else {
+        return __builtin_bit_cast(f32x4, b.ld16(ok ? (int)(idx * 4) : (int)0x80000000, true));
+    }
+}
+template <typename T> __device__ __forceinline__ void store_row4(void *base, long long idx, f32x4 v) {
+    if constexpr (std::is_same<T, bf16>::value) {
+        u32x2 w{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<bf16 *>(base) + idx) = w;
+    } else {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(base) + idx) = v;
+    }
+}
+
 // ---- epilogue through LDS ----------------------------------------------------
 // One wave writes a 32-row block of its accumulators (NI blocks of 32 columns,
 // fp32) to its private LDS region, then reads it back as rows of float4 so
 // that the bias / residual reads and the output writes are contiguous vector
 // accesses (8 bytes of bf16 or 16 bytes of fp32 per lane) issued without
 // intervening waits.  Requires that no other wave still reads that LDS region.
-// mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial
+// mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial,
+// 4 activation backward (dtype)
 template <typename T, int NI>
 __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int m_base, int n_base,
                                                const KParams &p, int mode, int lane) {
@@ -232,38 +265,38 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
     const int rk = rlow ? ri : ri - rhalf, roff = rlow ? rhalf : -rhalf;
     f32x4 bvp = {0.f, 0.f, 0.f, 0.f};
     if (rope && rhalf >= 4 && p.bias) bvp = load_bias(n + roff, nok);
-    // residual / accumulate inputs for all passes first (uniform branches outside
-    // the loops, so the loads issue back to back and are waited for at first use)
-    f32x4 in[PASSES];
+    // residual / accumulate / activation inputs for all passes first (uniform
+    // branches outside the loops, so the loads issue back to back and are
+    // waited for at first use).  Buffer offsets are taken from the first row of
+    // this 32-row block, so they stay far below 2^31 bytes.
+    f32x4 in[PASSES], inu[PASSES];
 #pragma unroll
-    for (int q = 0; q < PASSES; q++) in[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < PASSES; q++) in[q] = inu[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const long long es = std::is_same<T, bf16>::value ? 2 : 4;
     if (mode == 0 && p.res) {
-        const Buf br(p.res);
-        if constexpr (std::is_same<T, bf16>::value) {
-            u32x2 w[PASSES];
-#pragma unroll
-            for (int q = 0; q < PASSES; q++) {
-                const int m = m_base + q * RPP + rr;
-                w[q] = __builtin_amdgcn_raw_buffer_load_b64(
-                    br.r, (nok && m < p.M) ? (int)(((long long)m * p.ldr + n) * 2) : (int)0x80000000, 0, 0);
-            }
-#pragma unroll
-            for (int q = 0; q < PASSES; q++)
-                in[q] = f32x4{__uint_as_float(w[q][0] << 16), __uint_as_float(w[q][0] & 0xffff0000u),
-                              __uint_as_float(w[q][1] << 16), __uint_as_float(w[q][1] & 0xffff0000u)};
-        } else {
-#pragma unroll
-            for (int q = 0; q < PASSES; q++) {
-                const int m = m_base + q * RPP + rr;
-                in[q] = __builtin_bit_cast(f32x4, br.ld16((int)(((long long)m * p.ldr + n) * 4), nok && m < p.M));
-            }
-        }
-    } else if (mode == 2) {
-        const Buf bo(p.out);
+        const char *rb = static_cast<const char *>(p.res) + (long long)m_base * p.ldr * es;
 #pragma unroll
         for (int q = 0; q < PASSES; q++) {
-            const int m = m_base + q * RPP + rr;
-            in[q] = __builtin_bit_cast(f32x4, bo.ld16((int)(((long long)m * p.ldo + n) * 4), nok && m < p.M));
+            const int row = q * RPP + rr;
+            in[q] = load_row4<T>(rb, (long long)row * p.ldr + n, nok && m_base + row < p.M);
+        }
+    } else if (mode == 2) {
+        const char *ob = static_cast<const char *>(p.out) + (long long)m_base * p.ldo * 4;
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int row = q * RPP + rr;
+            in[q] = load_row4<float>(ob, (long long)row * p.ldo + n, nok && m_base + row < p.M);
+        }
+    } else if (mode == 4) {
+        // the saved activation input at (m, n) and the SwiGLU up value at (m, act_H + n)
+        const bool sw = p.act_mode == DTB_MLP_SWIGLU;
+        const char *ub = static_cast<const char *>(p.act_up) + (long long)m_base * p.ldo * es;
+#pragma unroll
+        for (int q = 0; q < PASSES; q++) {
+            const int row = q * RPP + rr;
+            const bool ok = nok && m_base + row < p.M;
+            in[q] = load_row4<T>(ub, (long long)row * p.ldo + n, ok);
+            inu[q] = load_row4<T>(ub, (long long)row * p.ldo + p.act_H + n, ok && sw);
         }
     }
 #pragma unroll
@@ -303,10 +336,64 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + bv;
         } else if (mode == 2) {
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + in[q];
+        } else if (mode == 4) {
+            f32x4 ga, gu;
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                float du = 0.f;
+                ga[e] = act_grad(p.act_mode, v[e], in[q][e], inu[q][e], &du);
+                gu[e] = du;
+            }
+            store_row4<T>(p.out, (long long)m * p.ldo + n, ga);
+            if (p.act_mode == DTB_MLP_SWIGLU) store_row4<T>(p.out, (long long)m * p.ldo + p.act_H + n, gu);
         } else {
             *reinterpret_cast<f32x4 *>(p.part + ((long long)blockIdx.z * p.M + m) * p.N + n) = v;
         }
     }
+}
+
+// SwiGLU forward epilogue of the 256 x 256 kernel (mode 5).  The two waves of
+// a pair (same rows, wn = 0 and 1) hold the gate and the up columns of the same
+// 128 hidden units; after a workgroup barrier each reads its partner's block
+// from LDS.  Each wave stores its own values into out ([g | u] layout) and
+// computes h = silu(g) u for half of the rows.  Every wave of the workgroup
+// must call this the same number of times (two barriers per call).
+__device__ __forceinline__ void epilogue_swiglu(const f32x16 *acc, float *lw, const float *lw_partner, int m_base,
+                                                int col_base, bool gate_wave, const KParams &p, int lane) {
+    constexpr int W = 128, CPR = 32, RPP = 2, PASSES = 16;
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+    __syncthreads();
+    const int cc = lane % CPR, rr = lane / CPR;
+    const int n = col_base + cc * 4;  // hidden unit (gate column n, up column act_H + n)
+    f32x4 bg = {0.f, 0.f, 0.f, 0.f}, bu = bg;
+    if (p.bias) {
+        bg = load_row4<bf16>(p.bias, n, true);
+        bu = load_row4<bf16>(p.bias, (long long)p.act_H + n, true);
+    }
+    const f32x4 b_own = gate_wave ? bg : bu, b_par = gate_wave ? bu : bg;
+    const int own_col = gate_wave ? n : p.act_H + n;
+    const int q0 = gate_wave ? 0 : PASSES / 2;
+#pragma unroll
+    for (int q = 0; q < PASSES; q++) {
+        const int row = q * RPP + rr;
+        const int m = m_base + row;
+        if (m >= p.M) continue;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(lw + row * W + cc * 4) + b_own;
+        store_row4<bf16>(p.out, (long long)m * p.ldo + own_col, v);
+        if (q >= q0 && q < q0 + PASSES / 2) {
+            const f32x4 w = *reinterpret_cast<const f32x4 *>(lw_partner + row * W + cc * 4) + b_par;
+            const f32x4 gv = gate_wave ? v : w, uv = gate_wave ? w : v;
+            f32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; e++) h[e] = gv[e] / (1.f + __expf(-gv[e])) * uv[e];
+            store_row4<bf16>(p.act_h, (long long)m * p.act_H + n, h);
+        }
+    }
+    __syncthreads();
 }
 
 template <typename T, int BM, int BN, bool AK, bool BKM>
@@ -516,9 +603,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
 #pragma unroll
             for (int r = 0; r < 16; r++) acc[i][j][r] = 0.f;
 
+    // mode 5: B rows 0..127 of the tile are gate rows tn*128.., rows 128..255
+    // the up rows act_H + tn*128.. (each wave's DMA blocks lie in one half)
+    const int nb0 = MODE == 5 ? (wave < NW / 2 ? tn * 128 : p.act_H + tn * 128 - 128) : n0;
     auto issue = [&](char *st, int k0) {
         dma_slab<AK, BPW>(st, gA, p.lda, m0, p.M, k0, kend, wave, lane);
-        dma_slab<BKM, BPW>(st + 16384, gB, p.ldb, n0, p.N, k0, kend, wave, lane);
+        dma_slab<BKM, BPW>(st + 16384, gB, p.ldb, nb0, p.N, k0, kend, wave, lane);
     };
     auto compute = [&](const char *st) {
         const char *As = st, *Bs = st + 16384;
@@ -573,12 +663,22 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
     // ---- epilogue through LDS (16 KB per wave; all DMA has landed and all reads are done)
     {
         constexpr int PER_STAGE = NW / 4;  // waves sharing one 32 KB stage
-        const int sidx = wave / PER_STAGE;
-        char *reg = sidx == 0 ? dma_stage<0>() : sidx == 1 ? dma_stage<1>() : sidx == 2 ? dma_stage<2>() : dma_stage<3>();
-        float *lw = reinterpret_cast<float *>(reg + (wave % PER_STAGE) * 16384);
+        auto region = [&](int w) {
+            const int sidx = w / PER_STAGE;
+            char *reg = sidx == 0 ? dma_stage<0>() : sidx == 1 ? dma_stage<1>() : sidx == 2 ? dma_stage<2>() : dma_stage<3>();
+            return reinterpret_cast<float *>(reg + (w % PER_STAGE) * 16384);
+        };
+        float *lw = region(wave);
+        if constexpr (MODE == 5) {
+            const float *lp = region(wave ^ 1);
 #pragma unroll
-        for (int i = 0; i < FI; i++)
-            epilogue_block<bf16, 4>(acc[i], lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane);
+            for (int i = 0; i < FI; i++)
+                epilogue_swiglu(acc[i], lw, lp, m0 + wm * TM + i * 32, tn * 128, wn == 0, p, lane);
+        } else {
+#pragma unroll
+            for (int i = 0; i < FI; i++)
+                epilogue_block<bf16, 4>(acc[i], lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane);
+        }
     }
 }
 
@@ -640,6 +740,8 @@ static hipError_t launch256_mode(const KParams &p, bool ak, bool bk, int splits,
 static hipError_t launch256(const KParams &p, bool ak, bool bk, int splits, hipStream_t s) {
     if (p.out_mode == 0) return launch256_mode<0>(p, ak, bk, splits, s);
     if (p.out_mode == 2) return launch256_mode<2>(p, ak, bk, splits, s);
+    if (p.out_mode == 4) return launch256_mode<4>(p, ak, bk, splits, s);
+    if (p.out_mode == 5) return launch256_t<true, true, 5>(p, splits, s);  // the host checks the layout
     return launch256_mode<3>(p, ak, bk, splits, s);
 }
 
@@ -698,6 +800,12 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     const bool rope_fused = g.rope_cs && splits == 1 && !g.out_f32 && g.rope_hd <= wave_cols;
     p.rope_cs = rope_fused ? reinterpret_cast<const float2 *>(g.rope_cs) : nullptr;
     p.rope_T = g.rope_T; p.rope_hd = g.rope_hd; p.rope_cols = g.rope_cols;
+    p.act_up = g.act_up; p.act_h = g.act_h; p.act_mode = g.act_mode; p.act_H = g.act_H;
+    if (g.act_up) p.out_mode = 4;
+    const bool swiglu_fused = g.act_h && g.act_mode == DTB_MLP_SWIGLU && g.dtype == DTB_BF16 && tc.bm == 256 &&
+                              tc.bn == 256 && g.act_H % 128 == 0 && g.N == 2 * g.act_H && g.ldo == g.N &&
+                              g.a_kmajor && g.b_kmajor && splits == 1 && !g.out_f32 && !g.res && !g.rope_cs;
+    if (swiglu_fused) p.out_mode = 5;
     double flops = 2.0 * g.M * g.N * (double)g.K;
     if (g_timing_on) timing_begin(s);
     hipError_t e;
@@ -719,17 +827,24 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         e = hipGetLastError();
         if (e != hipSuccess) return set_launch_error(e, "splitk_reduce");
     }
-    if (g.rope_cs && !rope_fused) {  // heads wider than a wave's columns: separate pass
-        const int r = rope_apply(g.dtype, g.out, g.rope_cs, g.M / g.rope_T, g.rope_T, (int)g.ldo,
-                                 g.rope_cols / g.rope_hd, 0, g.rope_hd, 0, s);
-        if (r) return r;
-    }
     if (g_timing_on) {
         const double es = g.dtype == DTB_BF16 ? 2.0 : 4.0;
         double bytes = es * ((double)g.M * g.K + (double)g.N * g.K) +
                        (g.out_f32 ? 4.0 * (g.accumulate ? 2.0 : 1.0) : es) * g.M * g.N;
+        if (g.act_up) bytes += es * (double)g.M * (2.0 * g.ldo - g.N);  // read act input, write its gradient
+        if (swiglu_fused) bytes += es * (double)g.M * g.act_H;          // write the activation output
         const int cls = g.out_f32 ? K_GEMM_DW : (g.b_kmajor ? K_GEMM_FWD : K_GEMM_DINP);
         timing_end(s, cls, flops, bytes);
+    }
+    // passes the epilogue could not take (timed as their own launches)
+    if (g.act_h && !swiglu_fused) {
+        const int r = act_forward(g.act_mode, g.dtype, g.out, g.M, g.act_H, g.act_h, s);
+        if (r) return r;
+    }
+    if (g.rope_cs && !rope_fused) {  // heads wider than a wave's columns: separate pass
+        const int r = rope_apply(g.dtype, g.out, g.rope_cs, g.M / g.rope_T, g.rope_T, (int)g.ldo,
+                                 g.rope_cols / g.rope_hd, 0, g.rope_hd, 0, s);
+        if (r) return r;
     }
     return DTB_OK;
 }
