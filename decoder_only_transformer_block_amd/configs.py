@@ -43,6 +43,13 @@ class BlockConfig:
     vocab: int
     std: float
     seed: int
+    # model harness around the block stack: learned position table, an RMSNorm
+    # (no gamma) of the embedding, a final norm of the blocks' kind, and an LM
+    # head tied to the token embedding
+    wpe: bool = False
+    embed_norm: bool = False
+    final_norm: bool = True
+    tied_head: bool = False
 
     @property
     def hd(self) -> int:
@@ -103,7 +110,8 @@ class AttnConfig:
 MICROGPT = BlockConfig("microgpt", L=1, B=1, T=16, C=16, NH=4, NKV=4, H=64,
                        norm="rms_nogamma", mlp="relu", rope="none", rope_base=0.0,
                        eps=1e-5, qkv_bias=False, o_bias=False, mlp_bias=False,
-                       dtype="f32", vocab=27, std=0.08, seed=0xD7B0 + 1)
+                       dtype="f32", vocab=27, std=0.08, seed=0xD7B0 + 1,
+                       wpe=True, embed_norm=True, final_norm=False)
 MINI_QWEN2 = BlockConfig("mini_qwen2", L=2, B=1, T=64, C=16, NH=1, NKV=1, H=32,
                          norm="rms", mlp="swiglu", rope="neox", rope_base=1e6,
                          eps=1e-5, qkv_bias=True, o_bias=False, mlp_bias=False,
@@ -111,7 +119,8 @@ MINI_QWEN2 = BlockConfig("mini_qwen2", L=2, B=1, T=64, C=16, NH=1, NKV=1, H=32,
 GPT2_SMALL = BlockConfig("gpt2_small", L=12, B=4, T=1024, C=768, NH=12, NKV=12, H=3072,
                          norm="layer", mlp="gelu_tanh", rope="none", rope_base=0.0,
                          eps=1e-5, qkv_bias=True, o_bias=True, mlp_bias=True,
-                         dtype="f32", vocab=50257, std=0.02, seed=0xD7B0 + 3)
+                         dtype="f32", vocab=50257, std=0.02, seed=0xD7B0 + 3,
+                         wpe=True, tied_head=True)
 LLAMA_GQA = BlockConfig("llama_gqa", L=4, B=8, T=2048, C=2048, NH=32, NKV=8, H=5632,
                         norm="rms", mlp="swiglu", rope="neox", rope_base=1e4,
                         eps=1e-5, qkv_bias=False, o_bias=False, mlp_bias=False,
@@ -190,6 +199,26 @@ def block_input(cfg: BlockConfig) -> np.ndarray:
 def block_dout(cfg: BlockConfig, std: float = 1.0) -> np.ndarray:
     """Upstream gradient of the top block's output, N(0, std^2), [B, T, C]."""
     return inputs.tensor(cfg.seed, "dy", (cfg.B, cfg.T, cfg.C), std=std, dtype=cfg.dtype)
+
+
+def harness_weights(cfg: BlockConfig, perturb: bool = False) -> dict:
+    """Seeded harness parameters: token embedding 'wte' [vocab, C] (the same
+    seeded matrix whose rows block_input picks), position table 'wpe' [T, C],
+    final-norm 'gf' / 'bf' and LM head 'head' [vocab, C] as the configuration
+    has them.  Matrices ~ N(0, std^2); gamma 1 and beta 0 unless perturb."""
+    V, C = cfg.vocab, cfg.C
+    out = {"wte": inputs.tensor(cfg.seed, "E", (V, C), std=cfg.std, dtype=cfg.dtype)}
+    if cfg.wpe:
+        out["wpe"] = inputs.tensor(cfg.seed, "wpe", (cfg.T, C), std=cfg.std, dtype=cfg.dtype)
+    if cfg.final_norm and cfg.norm != "rms_nogamma":
+        out["gf"] = (inputs.tensor(cfg.seed, "gf", (C,), std=0.1, mean=1.0, dtype=cfg.dtype)
+                     if perturb else inputs.const((C,), 1.0))
+    if cfg.final_norm and cfg.norm == "layer":
+        out["bf"] = (inputs.tensor(cfg.seed, "bf", (C,), std=0.02, dtype=cfg.dtype)
+                     if perturb else inputs.const((C,), 0.0))
+    if not cfg.tied_head:
+        out["head"] = inputs.tensor(cfg.seed, "head", (V, C), std=cfg.std, dtype=cfg.dtype)
+    return out
 
 
 def attn_inputs(cfg: AttnConfig):

@@ -272,3 +272,113 @@ def block_stack(cfg, layer_weights, x, dy):
     for i in reversed(range(len(layer_weights))):
         g, grads[i] = block_backward(cfg, layer_weights[i], xs[i], saved[i], g)
     return y, g, grads, saved
+
+
+# ---------------------------------------------------------------------------
+# model harness: embedding, final norm, LM head, softmax cross-entropy
+# ---------------------------------------------------------------------------
+_IP = ctypes.POINTER(ctypes.c_int)
+
+
+def _ip(a):
+    assert a.dtype == np.int32 and a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(_IP)
+
+
+def embed_forward(ids, wte, wpe=None):
+    """x[b,t] = wte[ids[b,t]] (+ wpe[t]).  ids [B, T] int."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    B, T = ids.shape
+    wte = _d(wte)
+    C = wte.shape[1]
+    x = np.empty((B, T, C))
+    lib().orc_embed_forward(_ip(ids), _p(wte), _p(None if wpe is None else _d(wpe)), B, T, C, _p(x))
+    return x
+
+
+def embed_backward(ids, dx, V, with_wpe=False):
+    """(dwte [V, C], dwpe [T, C] or None), both from zero."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    B, T = ids.shape
+    dx = _d(dx)
+    C = dx.shape[-1]
+    dwte = np.zeros((V, C))
+    dwpe = np.zeros((T, C)) if with_wpe else None
+    lib().orc_embed_backward(_ip(ids), _p(dx), B, T, C, _p(dwte), _p(dwpe))
+    return dwte, dwpe
+
+
+def softmax_ce(logits, targets, scale):
+    """Returns (scale * sum of row losses, dlogits, row losses); rows with a
+    negative target are masked (zero loss, zero gradient)."""
+    logits = _d(logits)
+    V = logits.shape[-1]
+    R = logits.size // V
+    targets = np.ascontiguousarray(targets, dtype=np.int32).reshape(-1)
+    assert targets.size == R
+    dl = np.empty((R, V))
+    rl = np.empty(R)
+    f = lib().orc_softmax_ce
+    f.restype = ctypes.c_double
+    loss = f(_p(logits), _ip(targets), ctypes.c_long(R), V, ctypes.c_double(scale), _p(dl), _p(rl))
+    return loss, dl, rl
+
+
+def model_step(cfg, layer_weights, hw: dict, ids):
+    """Loss and every gradient of the whole model for one batch.
+
+    Harness layout (the configuration's attributes): token embedding hw['wte']
+    [V, C], position table hw['wpe'] [T, C] if cfg.wpe, an RMSNorm without gamma
+    of the embedding if cfg.embed_norm, then the block stack, a final norm of
+    the blocks' kind (gamma hw['gf'], beta hw['bf']) if cfg.final_norm, the LM
+    head hw['head'] [V, C] (hw['wte'] itself if cfg.tied_head) and the mean
+    softmax cross-entropy over the B*T positions with targets ids[:, t+1].
+    Returns (loss, grads: dict of harness gradients, per-layer block gradients,
+    extras: logits, dlogits, row losses and the final hidden state)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    B, T = cfg.B, cfg.T
+    inp, tgt = ids[:, :T], ids[:, 1:T + 1]
+    V = hw["wte"].shape[0]
+    x = embed_forward(inp, hw["wte"], hw.get("wpe") if cfg.wpe else None)
+    if cfg.embed_norm:
+        x0, r0, m0 = norm_forward("rms_nogamma", x, eps=cfg.eps)
+    else:
+        x0 = x
+    saved, xs = [], []
+    h = x0
+    for w in layer_weights:
+        xs.append(h)
+        h, sv = block_forward(cfg, w, h)
+        saved.append(sv)
+    if cfg.final_norm:
+        nf, rf, mf = norm_forward(cfg.norm, h, hw.get("gf"), hw.get("bf"), eps=cfg.eps)
+    else:
+        nf = h
+    head = hw["wte"] if cfg.tied_head else hw["head"]
+    logits = linear_forward(nf, head)
+    loss, dlogits, rows = softmax_ce(logits.reshape(B * T, V), tgt, 1.0 / (B * T))
+    dnf, dhead, _ = linear_backward(dlogits.reshape(B, T, V), nf, head)
+    grads = {}
+    if cfg.final_norm:
+        g, dgf, dbf = norm_backward(cfg.norm, dnf, h, hw.get("gf"), rf, mf)
+        if cfg.norm != "rms_nogamma":
+            grads["gf"] = dgf
+        if cfg.norm == "layer":
+            grads["bf"] = dbf
+    else:
+        g = dnf
+    bgrads = [None] * len(layer_weights)
+    for i in reversed(range(len(layer_weights))):
+        g, bgrads[i] = block_backward(cfg, layer_weights[i], xs[i], saved[i], g)
+    if cfg.embed_norm:
+        g = norm_backward("rms_nogamma", g, x, None, r0, m0)[0]
+    dwte, dwpe = embed_backward(inp, g, V, with_wpe=bool(cfg.wpe))
+    if cfg.tied_head:
+        dwte = dwte + dhead
+    else:
+        grads["head"] = dhead
+    grads["wte"] = dwte
+    if cfg.wpe:
+        grads["wpe"] = dwpe
+    extras = SimpleNamespace(logits=logits.reshape(B * T, V), dlogits=dlogits, rows=rows, nf=nf.reshape(B * T, -1))
+    return loss, grads, bgrads, extras

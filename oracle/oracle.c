@@ -655,6 +655,81 @@ void orc_block_backward(const orc_cfg *c, const orc_weights *w, const double *x,
     free(dh); free(dup); free(dn2); free(dx2); free(dO); free(dqkv); free(dn1);
 }
 
+/* ------------------------------------------------------------------------ */
+/* model harness: embedding, softmax cross-entropy                            */
+/* ------------------------------------------------------------------------ */
+
+/* Token (+ position) embedding (llm.c encoder_forward; microgpt
+ * forward_position adds wte and wpe rows; nanoeuler encoder_forward_kernel
+ * has no position table):  x[b,t,i] = wte[ids[b,t], i] (+ wpe[t, i]).
+ * wpe may be NULL. */
+void orc_embed_forward(const int *ids, const double *wte, const double *wpe, int B, int T, int C,
+                       double *x)
+{
+    for (long bt = 0; bt < (long)B * T; bt++) {
+        int t = (int)(bt % T);
+        const double *e = wte + (size_t)ids[bt] * C;
+        for (int i = 0; i < C; i++)
+            x[bt * C + i] = e[i] + (wpe ? wpe[(size_t)t * C + i] : 0.0);
+    }
+}
+
+/* Embedding backward (llm.c encoder_backward; nanoeuler encoder_backward_cpu):
+ *   dwte[ids[b,t], i] += dx[b,t,i];  dwpe[t, i] += dx[b,t,i].
+ * Positions are added in order b, t for every element (threads split the
+ * columns i), so repeated ids sum in a fixed order.  dwpe may be NULL. */
+void orc_embed_backward(const int *ids, const double *dx, int B, int T, int C, double *dwte,
+                        double *dwpe)
+{
+    long BT = (long)B * T;
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)BT * C))
+    for (int i = 0; i < C; i++) {
+        for (long bt = 0; bt < BT; bt++) {
+            double d = dx[bt * C + i];
+            dwte[(size_t)ids[bt] * C + i] += d;
+            if (dwpe) dwpe[(size_t)(bt % T) * C + i] += d;
+        }
+    }
+}
+
+/* Softmax cross-entropy of R rows of V logits (nanoeuler softmax_ce_cpu with
+ * one head; llm.c crossentropy_forward / crossentropy_softmax_backward):
+ *   lse_r = m_r + log sum_v exp(l_rv - m_r),  m_r = max_v l_rv
+ *   loss_r = lse_r - l_r,target_r
+ *   dlogits_rv = scale * (exp(l_rv - lse_r) - [v == target_r])
+ * A row whose target is negative (a masked position) has loss_r = 0 and a
+ * zero gradient row.  Returns scale * sum_r loss_r.  row_loss may be NULL. */
+double orc_softmax_ce(const double *logits, const int *targets, long R, int V, double scale,
+                      double *dlogits, double *row_loss)
+{
+    double total = 0.0;
+    double *rl = (double *)malloc(sizeof(double) * (size_t)(R > 0 ? R : 1));
+    #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * V))
+    for (long r = 0; r < R; r++) {
+        const double *l = logits + (size_t)r * V;
+        double *dl = dlogits ? dlogits + (size_t)r * V : NULL;
+        int tg = targets[r];
+        if (tg < 0) {
+            rl[r] = 0.0;
+            if (dl) for (int v = 0; v < V; v++) dl[v] = 0.0;
+            continue;
+        }
+        double m = l[0];
+        for (int v = 1; v < V; v++) if (l[v] > m) m = l[v];
+        double s = 0.0;
+        for (int v = 0; v < V; v++) s += exp(l[v] - m);
+        double lse = m + log(s);
+        rl[r] = lse - l[tg];
+        if (dl) for (int v = 0; v < V; v++) dl[v] = scale * (exp(l[v] - lse) - (v == tg ? 1.0 : 0.0));
+    }
+    for (long r = 0; r < R; r++) {
+        total += rl[r];
+        if (row_loss) row_loss[r] = rl[r];
+    }
+    free(rl);
+    return scale * total;
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -68,6 +68,12 @@ void orc_block_forward(const orc_cfg *c, const orc_weights *w, const double *x, 
                        orc_saved *sv);
 void orc_block_backward(const orc_cfg *c, const orc_weights *w, const double *x,
                         const orc_saved *sv, const double *dy, double *dx, orc_grads *gr);
+void orc_embed_forward(const int *ids, const double *wte, const double *wpe, int B, int T, int C,
+                       double *x);
+void orc_embed_backward(const int *ids, const double *dx, int B, int T, int C, double *dwte,
+                        double *dwpe);
+double orc_softmax_ce(const double *logits, const int *targets, long R, int V, double scale,
+                      double *dlogits, double *row_loss);
 int orc_num_threads(void);
 void orc_set_num_threads(int n);
 
