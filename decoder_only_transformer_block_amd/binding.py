@@ -80,6 +80,17 @@ def lib() -> ctypes.CDLL:
         L.linear_backward.argtypes = [v, v, v, v, v, v, i, i, i, i, v, v]
         L.linear_workspace_bytes.argtypes = [i, i, i, i]
         L.linear_workspace_bytes.restype = z
+        L.encoder_forward.argtypes = [v, v, v, v, i, i, i, i, i, v]
+        L.encoder_backward.argtypes = [v, v, v, v, i, i, i, i, i, v]
+        L.norm_forward.argtypes = [v, v, v, v, v, v, i, i, i, f, i, v]
+        L.norm_backward.argtypes = [v, v, v, v, v, v, v, v, v, i, i, i, i, v, v]
+        L.norm_workspace_bytes.argtypes = [i, i]
+        L.norm_workspace_bytes.restype = z
+        L.lm_head_forward.argtypes = [v, i, v, v, i, i, i, i, v]
+        L.lm_head_backward.argtypes = [v, v, v, i, v, v, i, i, i, i, v, v]
+        L.lm_head_workspace_bytes.argtypes = [i, i, i, i]
+        L.lm_head_workspace_bytes.restype = z
+        L.softmax_ce.argtypes = [v, v, v, v, i, v, i, i, f, i, v]
         L.dtb_strerror.argtypes = [i]
         L.dtb_strerror.restype = ctypes.c_char_p
         L.dtb_version.restype = ctypes.c_char_p
@@ -153,6 +164,50 @@ def linear_workspace_bytes(R, K, N, dtype) -> int:
 def linear_backward(dinp, dw, db, dout, inp, w, R, K, N, dtype, workspace, stream=None):
     check(lib().linear_backward(_ptr(dinp), _ptr(dw), _ptr(db), _ptr(dout), _ptr(inp), _ptr(w), R, K, N,
                                 DTYPE[dtype], _ptr(workspace), _stream(stream)), "linear_backward")
+
+
+def encoder_forward(x, ids, wte, wpe, B, T, C, V, dtype, stream=None):
+    check(lib().encoder_forward(_ptr(x), _ptr(ids), _ptr(wte), _ptr(wpe), B, T, C, V, DTYPE[dtype], _stream(stream)),
+          "encoder_forward")
+
+
+def encoder_backward(dwte, dwpe, ids, dx, B, T, C, V, dtype, stream=None):
+    check(lib().encoder_backward(_ptr(dwte), _ptr(dwpe), _ptr(ids), _ptr(dx), B, T, C, V, DTYPE[dtype],
+                                 _stream(stream)), "encoder_backward")
+
+
+def norm_forward(out, rstd, mean, x, g, b, R, C, norm, eps, dtype, stream=None):
+    check(lib().norm_forward(_ptr(out), _ptr(rstd), _ptr(mean), _ptr(x), _ptr(g), _ptr(b), R, C, NORM[norm],
+                             float(eps), DTYPE[dtype], _stream(stream)), "norm_forward")
+
+
+def norm_workspace_bytes(R, C) -> int:
+    return lib().norm_workspace_bytes(R, C)
+
+
+def norm_backward(dx, dg, db, dy, x, g, rstd, mean, dres, R, C, norm, dtype, workspace, stream=None):
+    check(lib().norm_backward(_ptr(dx), _ptr(dg), _ptr(db), _ptr(dy), _ptr(x), _ptr(g), _ptr(rstd), _ptr(mean),
+                              _ptr(dres), R, C, NORM[norm], DTYPE[dtype], _ptr(workspace), _stream(stream)),
+          "norm_backward")
+
+
+def lm_head_forward(logits, ldl, inp, w, R, C, V, dtype, stream=None):
+    check(lib().lm_head_forward(_ptr(logits), ldl, _ptr(inp), _ptr(w), R, C, V, DTYPE[dtype], _stream(stream)),
+          "lm_head_forward")
+
+
+def lm_head_workspace_bytes(R, C, V, dtype) -> int:
+    return lib().lm_head_workspace_bytes(R, C, V, DTYPE[dtype])
+
+
+def lm_head_backward(dinp, dw, dlogits, ldl, inp, w, R, C, V, dtype, workspace, stream=None):
+    check(lib().lm_head_backward(_ptr(dinp), _ptr(dw), _ptr(dlogits), ldl, _ptr(inp), _ptr(w), R, C, V,
+                                 DTYPE[dtype], _ptr(workspace), _stream(stream)), "lm_head_backward")
+
+
+def softmax_ce(loss, row_loss, dlogits, logits, ldl, targets, R, V, scale, dtype, stream=None):
+    check(lib().softmax_ce(_ptr(loss), _ptr(row_loss), _ptr(dlogits), _ptr(logits), ldl, _ptr(targets), R, V,
+                           float(scale), DTYPE[dtype], _stream(stream)), "softmax_ce")
 
 
 def block_saved_bytes(cfg: BlockCfg) -> int:

@@ -331,6 +331,131 @@ int linear_backward(void *dinp, float *dw, float *db, const void *dout, const vo
     return DTB_OK;
 }
 
+// ---- model harness -----------------------------------------------------------
+static bool aligned4(const void *p) { return p && ((uintptr_t)p & 3) == 0; }
+
+int encoder_forward(void *x, const int *ids, const void *wte, const void *wpe, int B, int T, int C, int V,
+                    int dtype, void *stream) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (B < 0 || T < 0 || C <= 0 || C % 8 || V <= 0 || (long long)B * T >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    if ((long long)B * T == 0) return DTB_OK;
+    if (!ptr_ok(x) || !aligned4(ids) || !ptr_ok(wte) || (wpe && !aligned(wpe))) return DTB_EINVAL_PTR;
+    return embed_fwd(dtype, ids, wte, wpe, (long)B * T, T, C, V, x, (hipStream_t)stream);
+}
+
+int encoder_backward(float *dwte, float *dwpe, const int *ids, const void *dx, int B, int T, int C, int V,
+                     int dtype, void *stream) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (B < 0 || T < 0 || C <= 0 || C % 8 || V <= 0 || (long long)B * T >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    if ((long long)B * T == 0) return DTB_OK;
+    if (!ptr_ok(dx) || (dwte && (!aligned(dwte) || !aligned4(ids))) || (dwpe && !aligned(dwpe)))
+        return DTB_EINVAL_PTR;
+    return embed_bwd(dtype, ids, dx, B, T, C, V, dwte, dwpe, (hipStream_t)stream);
+}
+
+static int check_norm(int R, int C, int norm, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (norm < 0 || norm > 2) return DTB_EINVAL_ENUM;
+    if (R < 0 || C <= 0 || C % 8 || C > (dtype == DTB_BF16 ? 8192 : 4096)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+int norm_forward(void *out, float *rstd, float *mean, const void *x, const void *g, const void *b, int R, int C,
+                 int norm, float eps, int dtype, void *stream) {
+    int e = check_norm(R, C, norm, dtype);
+    if (e) return e;
+    if (!(eps > 0.f)) return DTB_EINVAL_SHAPE;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(out) || !ptr_ok(rstd) || !ptr_ok(x)) return DTB_EINVAL_PTR;
+    if (norm != DTB_NORM_RMS_NOGAMMA && !ptr_ok(g)) return DTB_EINVAL_PTR;
+    if (norm == DTB_NORM_LAYER && (!ptr_ok(b) || !ptr_ok(mean))) return DTB_EINVAL_PTR;
+    return dtb::norm_forward(norm, dtype, x, g, b, eps, R, C, out, rstd, mean, (hipStream_t)stream);
+}
+
+size_t norm_workspace_bytes(int R, int C) {
+    if (R < 0 || C <= 0) return 0;
+    return al((size_t)norm_backward_parts(R) * 2 * C * 4);
+}
+
+int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x, const void *g, const float *rstd,
+                  const float *mean, const void *dres, int R, int C, int norm, int dtype, void *workspace,
+                  void *stream) {
+    int e = check_norm(R, C, norm, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(dx) || !ptr_ok(dy) || !ptr_ok(x) || !ptr_ok(rstd) || !ptr_ok(workspace)) return DTB_EINVAL_PTR;
+    if (dres && !aligned(dres)) return DTB_EINVAL_PTR;
+    if (norm != DTB_NORM_RMS_NOGAMMA && (!ptr_ok(g) || !ptr_ok(dg))) return DTB_EINVAL_PTR;
+    if (norm == DTB_NORM_LAYER && (!ptr_ok(db) || !ptr_ok(mean))) return DTB_EINVAL_PTR;
+    return dtb::norm_backward(norm, dtype, dy, x, g, rstd, mean, dres, R, C, dx, dg, db, (float *)workspace,
+                              norm_backward_parts(R), (hipStream_t)stream);
+}
+
+static int check_head(int R, int C, int V, int ldl, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (R < 0 || C <= 0 || C % 8 || V <= 0 || ldl < V || ldl % 8) return DTB_EINVAL_SHAPE;
+    if ((long long)R * ldl >= (1LL << 40) || (long long)V * C >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+int lm_head_forward(void *logits, int ldl, const void *inp, const void *w, int R, int C, int V, int dtype,
+                    void *stream) {
+    int e = check_head(R, C, V, ldl, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(logits) || !ptr_ok(inp) || !ptr_ok(w)) return DTB_EINVAL_PTR;
+    GemmArgs g{};
+    g.dtype = dtype;
+    g.a_kmajor = g.b_kmajor = true;
+    g.A = inp; g.lda = C; g.B = w; g.ldb = C; g.M = R; g.N = V; g.K = C;
+    g.out = logits; g.ldo = ldl;
+    return gemm(g, nullptr, 0, (hipStream_t)stream);
+}
+
+size_t lm_head_workspace_bytes(int R, int C, int V, int dtype) {
+    if (R < 0 || C <= 0 || V <= 0 || (dtype != DTB_F32 && dtype != DTB_BF16)) return 0;
+    return al(gemm_ws_bytes(V, C, R, dtype)) + 256;
+}
+
+int lm_head_backward(void *dinp, float *dw, const void *dlogits, int ldl, const void *inp, const void *w, int R,
+                     int C, int V, int dtype, void *workspace, void *stream) {
+    int e = check_head(R, C, V, ldl, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(dlogits) || (dinp && (!ptr_ok(w) || !aligned(dinp))) || (dw && (!ptr_ok(inp) || !aligned(dw))))
+        return DTB_EINVAL_PTR;
+    if (dw && !ptr_ok(workspace)) return DTB_EINVAL_PTR;
+    hipStream_t s = (hipStream_t)stream;
+    if (dinp) {  // dinp[R, C] = dlogits[R, :V] W[V, C]
+        GemmArgs g{};
+        g.dtype = dtype;
+        g.a_kmajor = true;
+        g.b_kmajor = false;
+        g.A = dlogits; g.lda = ldl; g.B = w; g.ldb = C; g.M = R; g.N = C; g.K = V; g.out = dinp; g.ldo = C;
+        int r = gemm(g, nullptr, 0, s);
+        if (r) return r;
+    }
+    if (dw) {  // dw[V, C] += dlogits[:, :V]^T inp
+        GemmArgs g{};
+        g.dtype = dtype;
+        g.a_kmajor = g.b_kmajor = false;
+        g.out_f32 = g.accumulate = true;
+        g.A = dlogits; g.lda = ldl; g.B = inp; g.ldb = C; g.M = V; g.N = C; g.K = R; g.out = dw; g.ldo = C;
+        int r = gemm(g, workspace, gemm_ws_bytes(V, C, R, dtype), s);
+        if (r) return r;
+    }
+    return DTB_OK;
+}
+
+int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, int ldl, const int *targets, int R,
+               int V, float scale, int dtype, void *stream) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (R < 0 || V <= 0 || ldl < V || ldl % 8 || (long long)R * ldl >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    if (!ptr_ok(loss) || (R > 0 && (!ptr_ok(row_loss) || !ptr_ok(dlogits) || !ptr_ok(logits) || !aligned4(targets))))
+        return DTB_EINVAL_PTR;
+    return softmax_xent_rows(dtype, logits, ldl, targets, R, V, scale, row_loss, dlogits, loss, (hipStream_t)stream);
+}
+
 static int check_weights(const dtb_block_cfg *c, const dtb_block_weights *w) {
     if (!w) return DTB_EINVAL_PTR;
     if (!ptr_ok(w->wqkv) || !ptr_ok(w->wo) || !ptr_ok(w->w_up) || !ptr_ok(w->w_down)) return DTB_EINVAL_PTR;

@@ -256,4 +256,12 @@ int act_backward(int mlp, int dtype, const void *dh, const void *up, long R, int
 int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, int npart, hipStream_t s);
 int bias_grad_parts(long R);
 
+// model harness
+int embed_fwd(int dtype, const int *ids, const void *wte, const void *wpe, long BT, int T, int C, int V, void *x,
+              hipStream_t s);
+int embed_bwd(int dtype, const int *ids, const void *dx, int B, int T, int C, int V, float *dwte, float *dwpe,
+              hipStream_t s);
+int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *targets, long R, int V, float scale,
+                      float *row_loss, void *dlogits, float *loss, hipStream_t s);
+
 }  // namespace dtb

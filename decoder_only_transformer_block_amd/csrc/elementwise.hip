@@ -129,10 +129,11 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         }
         s2 = wave_sum(s2) / C;
         if (LN) s1 = wave_sum(s1) / C;
-        const Buf br(dres + row * C);
+        // residual gradient added to the result (none when dres is null)
+        const Buf br(dres ? dres + row * C : dy + row * C);
         u32x4 rsv[NPL];
 #pragma unroll
-        for (int k = 0; k < NPL; k++) rsv[k] = br.ld16((lane + 64 * k) * 16, lane + 64 * k < nch);
+        for (int k = 0; k < NPL; k++) rsv[k] = br.ld16((lane + 64 * k) * 16, dres != nullptr && lane + 64 * k < nch);
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
             int c = lane + 64 * k;

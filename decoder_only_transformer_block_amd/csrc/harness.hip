@@ -1,0 +1,255 @@
+// Model harness around the block stack: token / position embedding and its
+// backward, and the softmax cross-entropy of the LM head (forward and
+// backward in one pass pair), with a deterministic mean-loss reduction.
+//
+// Sources (page title, section):
+//   "nanoeuler — CUDA kernels": encoder_forward_kernel (a row of the token
+//     table per position), encoder_backward_kernel (atomic scatter-add into
+//     the table, ids repeat), softmax_ce_kernel (max, sum of exp, normalised
+//     probabilities, dlogits = (p - onehot) * scale, a negative target masks
+//     the row).
+//   "microgpt.cu": forward_position (token row + position row).
+//   llm.c train_gpt2.c: encoder_forward / encoder_backward (wte and wpe),
+//     crossentropy_forward / crossentropy_softmax_backward (vocabulary rows
+//     padded to a wider stride, padded columns not part of the softmax).
+//
+// Design: one wave64 per embedding row with 16-byte vectors; one 256-thread
+// workgroup per logits row for the cross-entropy (an online max / sum pass,
+// then the gradient pass; probabilities are never stored, and the gradient may
+// overwrite the logits in place).  The position-table gradient sums the B
+// sequences in order; the token-table gradient uses fp32 atomics (repeated ids
+// add in an unspecified order).
+#include <math.h>
+
+#include "common.h"
+
+namespace dtb {
+
+// x[bt, :] = wte[ids[bt], :] (+ wpe[bt % T, :]); an id outside [0, V) gives wpe only
+template <typename T>
+__global__ __launch_bounds__(256) void embed_fwd_kernel(const int *ids, const T *wte, const T *wpe, long BT, int Tn,
+                                                        int C, int V, T *x) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= BT) return;
+    const int lane = threadIdx.x & 63;
+    const int id = ids[row];
+    const bool ok = id >= 0 && id < V;
+    const long t = row % Tn;
+    const int nch = C / EPC;
+    for (int c = lane; c < nch; c += 64) {
+        float a[EPC], b[EPC];
+        if (ok) {
+            unpack16<T>(ld16(wte + (long)id * C + c * EPC), a);
+        } else {
+#pragma unroll
+            for (int e = 0; e < EPC; e++) a[e] = 0.f;
+        }
+        if (wpe) {
+            unpack16<T>(ld16(wpe + t * C + c * EPC), b);
+#pragma unroll
+            for (int e = 0; e < EPC; e++) a[e] += b[e];
+        }
+        st16(x + row * C + c * EPC, pack16<T>(a));
+    }
+}
+
+// dwte[ids[bt], :] += dx[bt, :]   (fp32 atomics; ids outside [0, V) skipped)
+template <typename T>
+__global__ __launch_bounds__(256) void embed_bwd_kernel(const int *ids, const T *dx, long BT, int C, int V,
+                                                        float *dwte) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= BT) return;
+    const int lane = threadIdx.x & 63;
+    const int id = ids[row];
+    if (id < 0 || id >= V) return;
+    const int nch = C / EPC;
+    float *dst = dwte + (long)id * C;
+    for (int c = lane; c < nch; c += 64) {
+        float d[EPC];
+        unpack16<T>(ld16(dx + row * C + c * EPC), d);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) unsafeAtomicAdd(dst + c * EPC + e, d[e]);
+    }
+}
+
+// dwpe[t, c] += sum_b dx[b, t, c]   (b in order)
+template <typename T>
+__global__ __launch_bounds__(256) void embed_pos_bwd_kernel(const T *dx, int B, int Tn, int C, float *dwpe) {
+    const long i = (long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (long)Tn * C) return;
+    float s = 0.f;
+    for (int b = 0; b < B; b++) s += to_f32(dx[(long)b * Tn * C + i]);
+    dwpe[i] += s;
+}
+
+// ---- softmax cross-entropy --------------------------------------------------
+// combine two (max, sum-of-exp relative to that max) pairs
+__device__ __forceinline__ void lse_merge(float &m, float &s, float m2, float s2) {
+    const float M = fmaxf(m, m2);
+    if (M == -INFINITY) {
+        s = 0.f;
+    } else {
+        s = s * __expf(m - M) + s2 * __expf(m2 - M);
+    }
+    m = M;
+}
+
+// One workgroup per row r of logits [R, ldl] (V valid columns):
+//   lse = max + ln sum exp(l - max);  row_loss[r] = lse - l[target]
+//   dlogits[r, v] = scale * (exp(l_v - lse) - [v == target]) for v < V, 0 for
+//   the padded columns V <= v < ldl.  target < 0: row_loss 0, zero gradient.
+// dlogits may alias logits (each vector is read before the same thread writes it).
+template <typename T>
+__global__ __launch_bounds__(256) void softmax_xent_kernel(const T *logits, long ldl, const int *targets, int V,
+                                                           float scale, float *row_loss, T *dlogits) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long r = blockIdx.x;
+    const T *l = logits + r * ldl;
+    T *dl = dlogits + r * ldl;
+    const int tg = targets[r];
+    const int nv = (V + EPC - 1) / EPC;  // vectors holding valid columns
+    const int nvl = (int)(ldl / EPC);    // vectors of the padded row
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float sm[4], ss[4];
+    if (tg < 0 || tg >= V) {  // masked row
+        float z[EPC];
+#pragma unroll
+        for (int e = 0; e < EPC; e++) z[e] = 0.f;
+        for (int c = tid; c < nvl; c += 256) st16(dl + c * EPC, pack16<T>(z));
+        if (tid == 0) row_loss[r] = 0.f;
+        return;
+    }
+    // pass 1: running max and sum of exp
+    float m = -INFINITY, s = 0.f;
+    for (int c = tid; c < nv; c += 256) {
+        float v[EPC];
+        unpack16<T>(ld16(l + c * EPC), v);
+        float mv = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPC; e++)
+            if (c * EPC + e < V) mv = fmaxf(mv, v[e]);
+        if (mv > m) {
+            s = (m == -INFINITY) ? 0.f : s * __expf(m - mv);
+            m = mv;
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; e++)
+            if (c * EPC + e < V) s += __expf(v[e] - m);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        lse_merge(m, s, m2, s2);
+    }
+    if (lane == 0) {
+        sm[wave] = m;
+        ss[wave] = s;
+    }
+    __syncthreads();
+    m = sm[0];
+    s = ss[0];
+#pragma unroll
+    for (int w = 1; w < 4; w++) lse_merge(m, s, sm[w], ss[w]);
+    const float lse = m + logf(s);
+    if (tid == 0) row_loss[r] = lse - to_f32(l[tg]);
+    // pass 2: the gradient (and zeros in the padded columns)
+    for (int c = tid; c < nvl; c += 256) {
+        float v[EPC], o[EPC];
+        if (c < nv) unpack16<T>(ld16(l + c * EPC), v);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            const int idx = c * EPC + e;
+            o[e] = (c < nv && idx < V) ? scale * (__expf(v[e] - lse) - (idx == tg ? 1.f : 0.f)) : 0.f;
+        }
+        st16(dl + c * EPC, pack16<T>(o));
+    }
+}
+
+// loss = scale * sum_r row_loss[r], one workgroup, fixed order (double sums)
+__global__ __launch_bounds__(256) void loss_sum_kernel(const float *rows, long R, float scale, float *loss) {
+    __shared__ double part[256];
+    double acc = 0.0;
+    for (long i = threadIdx.x; i < R; i += 256) acc += rows[i];
+    part[threadIdx.x] = acc;
+    __syncthreads();
+    for (int w = 128; w >= 1; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) loss[0] = (float)(scale * part[0]);
+}
+
+// ---- host side ----------------------------------------------------------------
+int embed_fwd(int dtype, const int *ids, const void *wte, const void *wpe, long BT, int Tn, int C, int V, void *x,
+              hipStream_t s) {
+    if (BT <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    dim3 grid((unsigned)((BT + 3) / 4));
+    if (dtype == DTB_BF16)
+        hipLaunchKernelGGL(embed_fwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)wte, (const bf16 *)wpe,
+                           BT, Tn, C, V, (bf16 *)x);
+    else
+        hipLaunchKernelGGL(embed_fwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)wte,
+                           (const float *)wpe, BT, Tn, C, V, (float *)x);
+    DTB_LAUNCH_CHECK("encoder_forward");
+    if (g_timing_on) {
+        const double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, (double)BT * (4 + es * C * (wpe ? 3 : 2)));
+    }
+    return DTB_OK;
+}
+
+int embed_bwd(int dtype, const int *ids, const void *dx, int B, int Tn, int C, int V, float *dwte, float *dwpe,
+              hipStream_t s) {
+    const long BT = (long)B * Tn;
+    if (BT <= 0) return DTB_OK;
+    if (g_timing_on) timing_begin(s);
+    if (dwte) {
+        dim3 grid((unsigned)((BT + 3) / 4));
+        if (dtype == DTB_BF16)
+            hipLaunchKernelGGL(embed_bwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)dx, BT, C, V, dwte);
+        else
+            hipLaunchKernelGGL(embed_bwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)dx, BT, C, V,
+                               dwte);
+        DTB_LAUNCH_CHECK("encoder_backward");
+    }
+    if (dwpe) {
+        dim3 grid((unsigned)(((long)Tn * C + 255) / 256));
+        if (dtype == DTB_BF16)
+            hipLaunchKernelGGL(embed_pos_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dx, B, Tn, C, dwpe);
+        else
+            hipLaunchKernelGGL(embed_pos_bwd_kernel<float>, grid, dim3(256), 0, s, (const float *)dx, B, Tn, C,
+                               dwpe);
+        DTB_LAUNCH_CHECK("encoder_backward (positions)");
+    }
+    if (g_timing_on) {
+        const double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, (double)BT * C * (es + (dwte ? 8 : 0)) + (dwpe ? 8.0 * Tn * C : 0));
+    }
+    return DTB_OK;
+}
+
+int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *targets, long R, int V, float scale,
+                      float *row_loss, void *dlogits, float *loss, hipStream_t s) {
+    if (g_timing_on) timing_begin(s);
+    if (R > 0) {
+        if (dtype == DTB_BF16)
+            hipLaunchKernelGGL(softmax_xent_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)logits,
+                               ldl, targets, V, scale, row_loss, (bf16 *)dlogits);
+        else
+            hipLaunchKernelGGL(softmax_xent_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
+                               (const float *)logits, ldl, targets, V, scale, row_loss, (float *)dlogits);
+        DTB_LAUNCH_CHECK("softmax_ce");
+    }
+    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, R, scale, loss);
+    DTB_LAUNCH_CHECK("softmax_ce loss");
+    if (g_timing_on) {
+        const double es = dtype == DTB_BF16 ? 2 : 4;
+        timing_end(s, K_ELEM, 0, (double)R * (3.0 * es * ldl + 12));
+    }
+    return DTB_OK;
+}
+
+}  // namespace dtb

@@ -86,3 +86,89 @@ class BlockStack:
         n = int(np.prod(shape))
         es = torch.tensor([], dtype=dt).element_size()
         return self.saved[layer][off:off + n * es].view(dt).view(*shape)
+
+
+class Model:
+    """The whole model of one configuration around a BlockStack: token (and
+    position) embedding, the embedding RMSNorm (cfg.embed_norm), the block
+    stack, the final norm (cfg.final_norm), the LM head (tied to the token
+    table if cfg.tied_head) and the mean softmax cross-entropy over the B*T
+    positions with targets ids[:, t+1].  Every step runs in libdtb through the
+    C ABI; torch only holds the buffers."""
+
+    def __init__(self, cfg, layer_weights, harness_weights: dict, device="cuda"):
+        import torch
+        self.cfg = cfg
+        self.stack = BlockStack(cfg, layer_weights, device)
+        td = torch_dtype(cfg.dtype)
+        self.hw = {k: to_device(v, cfg.dtype, device) for k, v in harness_weights.items()}
+        self.hgrads = {k: torch.zeros(v.shape, dtype=torch.float32, device=device) for k, v in self.hw.items()}
+        B, T, C = cfg.B, cfg.T, cfg.C
+        self.V = self.hw["wte"].shape[0]
+        self.ldl = (self.V + 7) // 8 * 8
+        R = B * T
+        self.x = torch.empty((B, T, C), dtype=td, device=device)        # embedding output
+        self.x0 = torch.empty((B, T, C), dtype=td, device=device)       # after the embedding norm
+        self.r0 = torch.empty(R, dtype=torch.float32, device=device)
+        self.nf = torch.empty((B, T, C), dtype=td, device=device)       # final norm output
+        self.rf = torch.empty(R, dtype=torch.float32, device=device)
+        self.mf = torch.empty(R, dtype=torch.float32, device=device)
+        self.logits = torch.empty((R, self.ldl), dtype=td, device=device)  # dlogits in place after the loss
+        self.rows = torch.empty(R, dtype=torch.float32, device=device)
+        self.loss = torch.empty(1, dtype=torch.float32, device=device)
+        self.dnf = torch.empty((B, T, C), dtype=td, device=device)
+        self.dtop = torch.empty((B, T, C), dtype=td, device=device)
+        self.dx = torch.empty((B, T, C), dtype=td, device=device)
+        nws = max(binding.norm_workspace_bytes(R, C), binding.lm_head_workspace_bytes(R, C, self.V, cfg.dtype))
+        self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
+
+    def _head_w(self):
+        return self.hw["wte"] if self.cfg.tied_head else self.hw["head"]
+
+    def step(self, ids, stream=None):
+        """ids: int32 device tensor [B, T+1].  Forward and backward of the
+        whole model; returns the loss tensor [1] (gradients accumulate)."""
+        cfg, s = self.cfg, self.stack
+        B, T, C, V, dt = cfg.B, cfg.T, cfg.C, self.V, cfg.dtype
+        R = B * T
+        inp = ids[:, :T].contiguous()
+        tgt = ids[:, 1:T + 1].contiguous()
+        self._inp = inp
+        binding.encoder_forward(self.x, inp, self.hw["wte"], self.hw.get("wpe") if cfg.wpe else None,
+                                B, T, C, V, dt, stream)
+        x0 = self.x
+        if cfg.embed_norm:
+            binding.norm_forward(self.x0, self.r0, None, self.x, None, None, R, C, "rms_nogamma", cfg.eps, dt,
+                                 stream)
+            x0 = self.x0
+        h = s.forward(x0, stream)
+        nf = h
+        if cfg.final_norm:
+            binding.norm_forward(self.nf, self.rf, self.mf, h, self.hw.get("gf"), self.hw.get("bf"), R, C,
+                                 cfg.norm, cfg.eps, dt, stream)
+            nf = self.nf
+        binding.lm_head_forward(self.logits, self.ldl, nf, self._head_w(), R, C, V, dt, stream)
+        binding.softmax_ce(self.loss, self.rows, self.logits, self.logits, self.ldl, tgt, R, V, 1.0 / R, dt,
+                           stream)
+        # backward (self.logits now holds dlogits)
+        dhead = self.hgrads["wte"] if cfg.tied_head else self.hgrads["head"]
+        binding.lm_head_backward(self.dnf, dhead, self.logits, self.ldl, nf, self._head_w(), R, C, V, dt, self.ws,
+                                 stream)
+        dtop = self.dnf
+        if cfg.final_norm:
+            binding.norm_backward(self.dtop, self.hgrads.get("gf"), self.hgrads.get("bf"), self.dnf, h,
+                                  self.hw.get("gf"), self.rf, self.mf, None, R, C, cfg.norm, dt, self.ws, stream)
+            dtop = self.dtop
+        g = s.backward(dtop, stream)
+        if cfg.embed_norm:
+            binding.norm_backward(self.dx, None, None, g, self.x, None, self.r0, None, None, R, C, "rms_nogamma",
+                                  dt, self.ws, stream)
+            g = self.dx
+        binding.encoder_backward(self.hgrads["wte"], self.hgrads.get("wpe") if cfg.wpe else None, inp, g,
+                                 B, T, C, V, dt, stream)
+        return self.loss
+
+    def zero_grads(self):
+        self.stack.zero_grads()
+        for t in self.hgrads.values():
+            t.zero_()

@@ -195,6 +195,70 @@ int linear_backward(void *dinp, float *dw, float *db, const void *dout, const vo
                     int R, int K, int N, int dtype, void *workspace, void *stream);
 size_t linear_workspace_bytes(int R, int K, int N, int dtype);
 
+/* ---- model harness ----------------------------------------------------------
+ * The steps around the block stack that turn token ids into a loss and back:
+ * embedding, a norm on its own (the final norm; the embedding RMSNorm of the
+ * "microgpt.cu" forward_position), the LM head and the softmax cross-entropy.
+ * ids / targets are int32 device arrays (4-byte aligned).
+ *
+ * encoder_forward: x[b, t, :] = wte[ids[b, t], :] (+ wpe[t, :])   ("nanoeuler —
+ *   CUDA kernels" encoder_forward_kernel; llm.c encoder_forward with wpe).
+ *   x [B, T, C], wte [V, C], wpe [T, C] or NULL: dtype.  An id outside [0, V)
+ *   reads as a zero row.  C must be a multiple of 8.
+ * encoder_backward: dwte[ids[b, t], :] += dx[b, t, :];  dwpe[t, :] += sum_b dx[b, t, :]
+ *   (nanoeuler encoder_backward_kernel; llm.c encoder_backward).  dwte [V, C]
+ *   and dwpe [T, C] fp32, ACCUMULATED; either may be NULL.  Repeated ids add
+ *   into dwte by fp32 atomics, so the summation order (not the set of terms)
+ *   varies from run to run; dwpe sums the B sequences in order. */
+int encoder_forward(void *x, const int *ids, const void *wte, const void *wpe, int B, int T, int C, int V,
+                    int dtype, void *stream);
+int encoder_backward(float *dwte, float *dwpe, const int *ids, const void *dx, int B, int T, int C, int V,
+                     int dtype, void *stream);
+
+/* norm_forward / norm_backward: the block's norms on their own (DTB_NORM_*;
+ * nanoeuler rmsnorm_forward_kernel / rmsnorm_backward_kernel, llm.c
+ * layernorm_forward / layernorm_backward).
+ *   out = Norm(x) [R, C] dtype; rstd [R] fp32; mean [R] fp32 (LayerNorm only,
+ *   else may be NULL).  g, b [C] dtype (g unused for RMS_NOGAMMA, b LayerNorm only).
+ *   norm_backward: dx = dres + Norm^T(dy) (OVERWRITTEN; dres may be NULL, may
+ *   alias dx);  dg, db [C] fp32 ACCUMULATED.  workspace norm_workspace_bytes(R, C)
+ *   bytes (per-workgroup partial sums; deterministic).  C a multiple of 8, at
+ *   most 8192 (bf16) / 4096 (fp32). */
+int norm_forward(void *out, float *rstd, float *mean, const void *x, const void *g, const void *b, int R, int C,
+                 int norm, float eps, int dtype, void *stream);
+int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x, const void *g, const float *rstd,
+                  const float *mean, const void *dres, int R, int C, int norm, int dtype, void *workspace,
+                  void *stream);
+size_t norm_workspace_bytes(int R, int C);
+
+/* lm_head_forward: logits[R, :V] = inp[R, C] W[V, C]^T ("nanoeuler — CUDA
+ *   kernels" forward_gpu's head matmul; llm.c gpt2_forward, where W is wte when
+ *   the head is tied).  logits rows have stride ldl >= V, ldl a multiple of 8
+ *   (llm.c pads the vocabulary the same way); columns V..ldl-1 are not part
+ *   of the result (unspecified on return; softmax_ce never reads them).
+ * lm_head_backward: dinp[R, C] = dlogits[:, :V] W (OVERWRITTEN);
+ *   dw[V, C] += dlogits[:, :V]^T inp (fp32, ACCUMULATED).  dlogits' padded
+ *   columns must hold zeros (softmax_ce writes them so).  dinp or dw may be
+ *   NULL.  workspace lm_head_workspace_bytes(R, C, V, dtype) bytes. */
+int lm_head_forward(void *logits, int ldl, const void *inp, const void *w, int R, int C, int V, int dtype,
+                    void *stream);
+int lm_head_backward(void *dinp, float *dw, const void *dlogits, int ldl, const void *inp, const void *w, int R,
+                     int C, int V, int dtype, void *workspace, void *stream);
+size_t lm_head_workspace_bytes(int R, int C, int V, int dtype);
+
+/* softmax_ce: softmax cross-entropy of R rows of logits [R, ldl] (V valid
+ * columns) against targets [R] ("nanoeuler — CUDA kernels" softmax_ce_kernel
+ * with one head; llm.c crossentropy_forward / crossentropy_softmax_backward):
+ *   lse_r = max + ln sum_v exp(l_rv - max);  row_loss[r] = lse_r - l_r,target
+ *   dlogits[r, v] = scale * (exp(l_rv - lse_r) - [v == target_r]),  v < V
+ *   loss[0] = scale * sum_r row_loss[r]   (fixed-order reduction)
+ * A target outside [0, V) (e.g. -1, a masked position) gives row_loss 0 and a
+ * zero gradient row.  dlogits [R, ldl] dtype is OVERWRITTEN, its padded columns
+ * with zeros, and may alias logits.  row_loss [R] and loss [1] fp32,
+ * OVERWRITTEN.  Probabilities are not stored. */
+int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, int ldl, const int *targets, int R,
+               int V, float scale, int dtype, void *stream);
+
 /* ---- misc ---------------------------------------------------------------- */
 const char *dtb_strerror(int code);
 const char *dtb_version(void);
