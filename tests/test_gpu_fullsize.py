@@ -118,3 +118,68 @@ def test_llama_gqa_block_full_size_sampled():
 def test_gpt2_small_block_full_size_sampled():
     require_gpu()
     _block_full_size("gpt2_small", batches=(0, 3), R=16)
+
+
+def _model_full_size(cfg_name, rows):
+    """The whole model at the workload's full size (all layers, the full
+    vocabulary): sampled rows of the loss, of dlogits and of the final hidden
+    state's gradient against the oracle (from the GPU's own final hidden state,
+    one row at a time), the mean-loss identity, the initial loss against ln V,
+    and the head (and tied token-table) gradient by a random projection."""
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    from decoder_only_transformer_block_amd.runtime import Model, to_numpy
+    cfg = configs.BLOCK_CONFIGS[cfg_name]
+    V, C, R = cfg.vocab, cfg.C, cfg.B * cfg.T
+    announce(f"model full size {cfg.name} L={cfg.L} B={cfg.B} T={cfg.T} C={C} V={V} {cfg.dtype}")
+    lw = [configs.block_weights(cfg, l) for l in range(cfg.L)]
+    hw = configs.harness_weights(cfg)
+    ids = configs.token_ids(cfg)
+    m = Model(cfg, lw, hw)
+    del lw
+    announce("  weights on the device; running the step")
+    ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    loss = float(to_numpy(m.step(ids_d))[0])
+    torch.cuda.synchronize()
+    tol = TOL[cfg.dtype]
+    row_loss = to_numpy(m.rows)
+    print(f"    loss {loss:.5f}  ln V {np.log(V):.5f}", flush=True)
+    assert abs(loss - np.log(V)) < 0.05 * np.log(V)
+    check("mean rows", np.array([loss]), np.array([row_loss.astype(np.float64).mean()]), tol)
+    nf = (m.nf if cfg.final_norm else m.stack.acts[cfg.L]).reshape(R, C)
+    head = hw["wte"] if cfg.tied_head else hw["head"]
+    tgt = ids[:, 1:].reshape(-1)
+    nf_s = to_numpy(nf[rows])
+    dl_s = to_numpy(m.logits[rows])[:, :V]
+    lg_ref = oracle.linear_forward(nf_s, head)
+    _, dl_ref, rows_ref = oracle.softmax_ce(lg_ref, tgt[rows], 1.0 / R)
+    check("row loss", row_loss[rows], rows_ref, tol)
+    check("dlogits[rows]", dl_s, dl_ref, tol)
+    dnf_ref, _, _ = oracle.linear_backward(dl_s, nf_s, head)
+    check("dnf[rows]", to_numpy(m.dnf.reshape(R, C)[rows]), dnf_ref, tol)
+    # head gradient: u^T dW v = sum_r (u . dlogits_r)(nf_r . v) (+ the token
+    # table's scatter-add when the head is tied), from the GPU's own tensors
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    u = torch.randn(V, 1, device="cuda", generator=gen, dtype=torch.float64)
+    v = torch.randn(C, 1, device="cuda", generator=gen, dtype=torch.float64)
+    dl_full = m.logits[:, :V].double()
+    rhs = ((dl_full @ u) * (nf.double() @ v)).sum()
+    if cfg.tied_head:
+        dx = m.stack.dx.reshape(R, C).double()
+        rhs = rhs + (u[ids_d[:, :cfg.T].reshape(-1).long()] * (dx @ v)).sum()
+        dw = m.hgrads["wte"]
+    else:
+        dw = m.hgrads["head"]
+    lhs = (u.t() @ (dw.double() @ v)).item()
+    check("u.dW.v", np.array([lhs]), np.array([rhs.item()]), tol)
+
+
+def test_llama_gqa_model_full_size_sampled():
+    require_gpu()
+    _model_full_size("llama_gqa", rows=[0, 1, 2047, 2048, 9000, 16383])
+
+
+def test_gpt2_small_model_full_size_sampled():
+    require_gpu()
+    _model_full_size("gpt2_small", rows=[0, 1, 1023, 1024, 3000, 4095])
