@@ -176,7 +176,7 @@ static void saved_layout(const dtb_block_cfg *c, const Dims &d, dtb_saved_layout
 }
 
 struct WsLayout {
-    size_t cs, dup, dn2, dx2, dO, dqkv, dn1, D, npart, bpart, gemm, total;
+    size_t cs, dh, dup, dn2, dx2, dO, dqkv, dn1, D, npart, bpart, gemm, total;
     int nparts, bparts;
     size_t gemm_bytes;
 };
@@ -189,6 +189,7 @@ static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
         return r;
     };
     W->cs = take((size_t)c->T * (d.hd / 2) * 8);
+    W->dh = take((size_t)d.BT * c->H * d.es);
     W->dup = take((size_t)d.BT * d.W * d.es);
     W->dn2 = take((size_t)d.BT * c->C * d.es);
     W->dx2 = take((size_t)d.BT * c->C * d.es);
@@ -560,7 +561,7 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     const float *mu1 = L.mu1 >= 0 ? (const float *)(sv + L.mu1) : nullptr;
     const float *mu2 = L.mu2 >= 0 ? (const float *)(sv + L.mu2) : nullptr;
     const float *lse = (const float *)(sv + L.lse);
-    void *dup = ws + W.dup, *dn2 = ws + W.dn2, *dx2 = ws + W.dx2, *dO = ws + W.dO,
+    void *dh = ws + W.dh, *dup = ws + W.dup, *dn2 = ws + W.dn2, *dx2 = ws + W.dx2, *dO = ws + W.dO,
          *dqkv = ws + W.dqkv, *dn1 = ws + W.dn1;
     float *Dbuf = (float *)(ws + W.D), *npart = (float *)(ws + W.npart), *bpart = (float *)(ws + W.bpart);
     void *gws = ws + W.gemm;
@@ -577,15 +578,17 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     dw.out_f32 = true;
     dw.accumulate = true;
 
-    // down projection: dh = dy Wdown, and in the same epilogue the activation
-    // backward dup = act'(up) dh; dWdown += dy^T h; db_down
+    // down projection: dh = dy Wdown; dWdown += dy^T h; db_down
+    // (the activation backward stays a kernel of its own: in the GEMM epilogue
+    // its 8 bytes per element of extra HBM traffic, which no MFMA work hides,
+    // measured slower than the separate streaming pass)
     dinp.A = dy; dinp.lda = C; dinp.B = w->w_down; dinp.ldb = H; dinp.M = BT; dinp.N = H; dinp.K = C;
-    dinp.out = dup; dinp.ldo = d.W; dinp.act_up = up; dinp.act_mode = c->mlp; dinp.act_H = H;
+    dinp.out = dh; dinp.ldo = H;
     TRY(gemm(dinp, nullptr, 0, s));
-    dinp.act_up = nullptr;
     dw.A = dy; dw.lda = C; dw.B = h; dw.ldb = H; dw.M = C; dw.N = H; dw.K = BT; dw.out = gr->w_down; dw.ldo = H;
     TRY(gemm(dw, gws, W.gemm_bytes, s));
     if (c->mlp_bias) TRY(bias_grad(dt, dy, BT, C, gr->b_down, bpart, W.bparts, s));
+    TRY(act_backward(c->mlp, dt, dh, up, BT, H, dup, s));
     // up projection: dn2 = dup Wup; dWup += dup^T n2
     dinp.A = dup; dinp.lda = d.W; dinp.B = w->w_up; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.W;
     dinp.out = dn2; dinp.ldo = C;

@@ -213,11 +213,6 @@ struct GemmArgs {
     // of (cos, sin).  Null rope_cs: none.  Only with the plain dtype output.
     const float *rope_cs;
     int rope_T, rope_hd, rope_cols;
-    // activation backward in the epilogue: the output is not written as is;
-    // with d = the GEMM result at (m, n), act_up = the saved activation input
-    // [M][W] (W = ldo = 2 act_H for SwiGLU, gate columns then up columns), the
-    // epilogue writes the gradient of that input into out[M][W].  Null: none.
-    const void *act_up;
     // activation forward: out = [M][ldo] activation input (ldo = N = 2 act_H for
     // SwiGLU, gate columns then up columns) and act_h [M][act_H] = activation
     // output (fused into the GEMM where the tiling allows, else a second pass).

@@ -55,21 +55,16 @@ struct KParams {
     void *out;
     long long ldo;
     int out_mode;  // 0 store dtype, 1 store fp32, 2 accumulate fp32, 3 split partial fp32,
-                   // 4 activation backward, 5 SwiGLU forward
+                   // 5 SwiGLU forward
     const void *bias;
     const void *res;
     long long ldr;
     float *part;   // split partials [splits][M][N]
     const float2 *rope_cs;  // NeoX RoPE of the output columns [0, rope_cols) (mode 0), or null
     int rope_T, rope_hd, rope_cols;
-    // mode 4: activation backward -- the GEMM result is the gradient of the
-    // activation output; act_up [M][ldo] holds the saved activation input
-    // (SwiGLU: gate columns [0, act_H), up columns [act_H, 2 act_H)); out
-    // receives its gradient in the same layout.
     // mode 5: SwiGLU forward (256 x 256 kernel) -- tile column block tn holds
     // gate columns tn*128 .. +127 and the matching up columns act_H + tn*128 ..;
     // out receives [g | u] and act_h [M][act_H] receives silu(g) u.
-    const void *act_up;
     void *act_h;
     int act_mode, act_H;
 };
@@ -227,8 +222,7 @@ template <typename T> __device__ __forceinline__ void store_row4(void *base, lon
 // that the bias / residual reads and the output writes are contiguous vector
 // accesses (8 bytes of bf16 or 16 bytes of fp32 per lane) issued without
 // intervening waits.  Requires that no other wave still reads that LDS region.
-// mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial,
-// 4 activation backward (dtype)
+// mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial
 template <typename T, int NI>
 __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int m_base, int n_base,
                                                const KParams &p, int mode, int lane) {
@@ -265,13 +259,13 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
     const int rk = rlow ? ri : ri - rhalf, roff = rlow ? rhalf : -rhalf;
     f32x4 bvp = {0.f, 0.f, 0.f, 0.f};
     if (rope && rhalf >= 4 && p.bias) bvp = load_bias(n + roff, nok);
-    // residual / accumulate / activation inputs for all passes first (uniform
+    // residual / accumulate inputs for all passes first (uniform
     // branches outside the loops, so the loads issue back to back and are
     // waited for at first use).  Buffer offsets are taken from the first row of
     // this 32-row block, so they stay far below 2^31 bytes.
-    f32x4 in[PASSES], inu[PASSES];
+    f32x4 in[PASSES];
 #pragma unroll
-    for (int q = 0; q < PASSES; q++) in[q] = inu[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < PASSES; q++) in[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     const long long es = std::is_same<T, bf16>::value ? 2 : 4;
     if (mode == 0 && p.res) {
         const char *rb = static_cast<const char *>(p.res) + (long long)m_base * p.ldr * es;
@@ -286,17 +280,6 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
         for (int q = 0; q < PASSES; q++) {
             const int row = q * RPP + rr;
             in[q] = load_row4<float>(ob, (long long)row * p.ldo + n, nok && m_base + row < p.M);
-        }
-    } else if (mode == 4) {
-        // the saved activation input at (m, n) and the SwiGLU up value at (m, act_H + n)
-        const bool sw = p.act_mode == DTB_MLP_SWIGLU;
-        const char *ub = static_cast<const char *>(p.act_up) + (long long)m_base * p.ldo * es;
-#pragma unroll
-        for (int q = 0; q < PASSES; q++) {
-            const int row = q * RPP + rr;
-            const bool ok = nok && m_base + row < p.M;
-            in[q] = load_row4<T>(ub, (long long)row * p.ldo + n, ok);
-            inu[q] = load_row4<T>(ub, (long long)row * p.ldo + p.act_H + n, ok && sw);
         }
     }
 #pragma unroll
@@ -336,16 +319,6 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + bv;
         } else if (mode == 2) {
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + in[q];
-        } else if (mode == 4) {
-            f32x4 ga, gu;
-#pragma unroll
-            for (int e = 0; e < 4; e++) {
-                float du = 0.f;
-                ga[e] = act_grad(p.act_mode, v[e], in[q][e], inu[q][e], &du);
-                gu[e] = du;
-            }
-            store_row4<T>(p.out, (long long)m * p.ldo + n, ga);
-            if (p.act_mode == DTB_MLP_SWIGLU) store_row4<T>(p.out, (long long)m * p.ldo + p.act_H + n, gu);
         } else {
             *reinterpret_cast<f32x4 *>(p.part + ((long long)blockIdx.z * p.M + m) * p.N + n) = v;
         }
@@ -783,7 +756,6 @@ static hipError_t launch256_mode(const KParams &p, bool ak, bool bk, int splits,
 static hipError_t launch256(const KParams &p, bool ak, bool bk, int splits, hipStream_t s) {
     if (p.out_mode == 0) return launch256_mode<0>(p, ak, bk, splits, s);
     if (p.out_mode == 2) return launch256_mode<2>(p, ak, bk, splits, s);
-    if (p.out_mode == 4) return launch256_mode<4>(p, ak, bk, splits, s);
     if (p.out_mode == 5) return launch256_t<true, true, 5>(p, splits, s);  // the host checks the layout
     return launch256_mode<3>(p, ak, bk, splits, s);
 }
@@ -843,8 +815,7 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     const bool rope_fused = g.rope_cs && splits == 1 && !g.out_f32 && g.rope_hd <= wave_cols;
     p.rope_cs = rope_fused ? reinterpret_cast<const float2 *>(g.rope_cs) : nullptr;
     p.rope_T = g.rope_T; p.rope_hd = g.rope_hd; p.rope_cols = g.rope_cols;
-    p.act_up = g.act_up; p.act_h = g.act_h; p.act_mode = g.act_mode; p.act_H = g.act_H;
-    if (g.act_up) p.out_mode = 4;
+    p.act_h = g.act_h; p.act_mode = g.act_mode; p.act_H = g.act_H;
     const bool swiglu_fused = g.act_h && g.act_mode == DTB_MLP_SWIGLU && g.dtype == DTB_BF16 && tc.bm == 256 &&
                               tc.bn == 256 && g.act_H % 128 == 0 && g.N == 2 * g.act_H && g.ldo == g.N &&
                               g.a_kmajor && g.b_kmajor && splits == 1 && !g.out_f32 && !g.res && !g.rope_cs;
@@ -874,7 +845,6 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         const double es = g.dtype == DTB_BF16 ? 2.0 : 4.0;
         double bytes = es * ((double)g.M * g.K + (double)g.N * g.K) +
                        (g.out_f32 ? 4.0 * (g.accumulate ? 2.0 : 1.0) : es) * g.M * g.N;
-        if (g.act_up) bytes += es * (double)g.M * (2.0 * g.ldo - g.N);  // read act input, write its gradient
         if (swiglu_fused) bytes += es * (double)g.M * g.act_H;          // write the activation output
         const int cls = g.out_f32 ? K_GEMM_DW : (g.b_kmajor ? K_GEMM_FWD : K_GEMM_DINP);
         timing_end(s, cls, flops, bytes);

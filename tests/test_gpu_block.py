@@ -18,10 +18,9 @@ def _reduced():
         "mini_qwen2": K.MINI_QWEN2,
         "gpt2_small_reduced": K.GPT2_SMALL.replace(L=2, B=2, T=200, C=384, NH=6, NKV=6, H=1536),
         "llama_gqa_reduced": K.LLAMA_GQA.replace(L=2, B=2, T=200, C=512, NH=8, NKV=2, H=1408),
-        # the 256 x 256 GEMM paths with the activation in the epilogue: SwiGLU
-        # forward (gate and up column halves of one tile, with an MLP bias) and
-        # the activation backward in the input-gradient GEMM, ragged rows and
-        # (H = 1920) ragged columns
+        # the 256 x 256 GEMM paths at ragged rows and (H = 1920) ragged columns,
+        # with the SwiGLU forward in the up projection's epilogue (gate and up
+        # column halves of one tile, with an MLP bias)
         "llama_gqa_wide_mlp_bias": K.LLAMA_GQA.replace(L=1, B=2, T=2000, C=256, NH=4, NKV=2, H=1920, mlp_bias=True),
         "llama_gqa_f32_mqa": K.LLAMA_GQA.replace(L=1, B=1, T=130, C=256, NH=4, NKV=1, H=512, dtype="f32"),
         "gpt2_bf16_t1": K.GPT2_SMALL.replace(L=1, B=4, T=1, C=256, NH=4, NKV=4, H=1024, dtype="bf16"),
