@@ -373,13 +373,16 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                 S = mfma32(lds_row16(Ks + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, qf[c]), S);
                 dP = mfma32(lds_row16(Vs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, df[c]), dP);
             }
-            const bool diag = kv0 + j * 32 + 31 > qw0;
+            // causal mask on diagonal blocks only: a real (uniform) branch, kept
+            // from being flattened into per-element selects on every block
+            if (kv0 + j * 32 + 31 > qw0) {
+                asm volatile("");
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                float pr = fast_exp2(fmaf(S[r], p.sl2, -l2));
-                if (diag && kv0 + j * 32 + acc_row(r, lane) > qi) pr = 0.f;
-                S[r] = pr * (dP[r] - Dq);
+                for (int r = 0; r < 16; r++)
+                    if (kv0 + j * 32 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * (dP[r] - Dq);
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 u32x4 xw;
@@ -526,10 +529,16 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
                 lq[r4] = *reinterpret_cast<const f32x4 *>(l2s + ql);
                 dq4[r4] = *reinterpret_cast<const f32x4 *>(Ds + ql);
             }
+            // causal mask on diagonal blocks only (a real uniform branch, as in dQ)
+            if (diag) {
+                asm volatile("");
+#pragma unroll
+                for (int r = 0; r < 16; r++)
+                    if (q0 + j * 32 + acc_row(r, lane) < ki) S[r] = -INFINITY;
+            }
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                float pr = fast_exp2(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
-                if (diag && q0 + j * 32 + acc_row(r, lane) < ki) pr = 0.f;
+                const float pr = fast_exp2(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
                 S[r] = pr;
                 dP[r] = pr * (dP[r] - dq4[r >> 2][r & 3]);
             }
