@@ -73,7 +73,7 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // bf16 kernels (head width padded to HD in {16, 32, 64, 128})
 hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s);
-// dQ and dK/dV; p.D and p.L2 must already hold rowsum(dO o) and lse * log2(e)
+// dQ and dK/dV; p.D and p.L2 must already hold -rowsum(dO o) (negated) and lse * log2(e)
 hipError_t attn_bwd_bf16(const AttnP &p, int HD, hipStream_t s);
 
 }  // namespace dtb

@@ -276,7 +276,9 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
 // optionally L2 = lse * log2(e) in the same layout
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *L2) {
+// D = rowsum(dO o) per (b, h, t), written times dsign (the bf16 kernels take
+// -D); with L2, also lse * log2(e)
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *L2, float dsign) {
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= (long long)p.B * p.T) return;
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, fl
         if (c < nch && (c % hch) == 0) {
             int h = c / hch;
             const long long i = ((long long)b * p.NH + h) * p.T + tq;
-            D[i] = s;
+            D[i] = dsign * s;
             if (L2) L2[i] = p.lse_in[i] * LOG2E;
         }
     }
@@ -618,7 +620,7 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     }
     long long rows = (long long)p.B * p.T;
     hipLaunchKernelGGL((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D,
-                       (float *)nullptr);
+                       (float *)nullptr, 1.f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
@@ -636,7 +638,9 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
 static hipError_t bwd_bf16(const AttnP &p, int hdp, float *D, hipStream_t s) {
     float *L2 = D + (long long)p.B * p.NH * p.T;
     long long rows = (long long)p.B * p.T;
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, L2);
+    // the bf16 kernels take -D: the dK/dV kernel starts its dP accumulation from it
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, L2,
+                       -1.f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;

@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
 
     u32x4 qf[L::NC], df[L::NC];
     const long long li = ((long long)b * p.NH + h) * p.T + qi;
-    float l2 = 0.f, Dq = 0.f;
+    float l2 = 0.f, nDq = 0.f;  // lse * log2(e) and -D of this lane's query
     {
         const Buf bq(base + h * p.hd);
         const Buf bd(reinterpret_cast<const bf16 *>(p.dout) + (long long)b * p.T * p.C + h * p.hd);
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
         }
         if (qi < p.T) {
             l2 = p.L2[li];
-            Dq = p.D[li];
+            nDq = p.D[li];
         }
     }
     issue(s0, 0);
@@ -382,7 +382,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                     if (kv0 + j * 32 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
 #pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * (dP[r] - Dq);
+            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * (dP[r] + nDq);
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 u32x4 xw;
@@ -512,23 +512,27 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
         const int q0 = (qt0 + it % nqt) * BQ;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
+            // the 16 query rows of this lane: 4 groups of 4 consecutive rows;
+            // Ds holds -D, in the accumulator's row order, so the dP = dO V^T
+            // accumulation starts from it and ends as dP - D
+            f32x4 lq[4];
             f32x16 S, dP;
 #pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+            for (int r4 = 0; r4 < 4; r4++) {
+                const int ql = j * 32 + 8 * r4 + 4 * g;
+                lq[r4] = *reinterpret_cast<const f32x4 *>(l2s + ql);
+                const f32x4 nd = *reinterpret_cast<const f32x4 *>(Ds + ql);
+#pragma unroll
+                for (int e = 0; e < 4; e++) dP[4 * r4 + e] = nd[e];
+            }
+#pragma unroll
+            for (int r = 0; r < 16; r++) S[r] = 0.f;
 #pragma unroll
             for (int c = 0; c < L::NC; c++) {
                 S = mfma32(lds_row16(Qs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, kf[c]), S);
                 dP = mfma32(lds_row16(dOs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, vf[c]), dP);
             }
             const bool diag = q0 + j * 32 < kw0 + 31;
-            // the 16 query rows of this lane: 4 groups of 4 consecutive rows
-            f32x4 lq[4], dq4[4];
-#pragma unroll
-            for (int r4 = 0; r4 < 4; r4++) {
-                const int ql = j * 32 + 8 * r4 + 4 * g;
-                lq[r4] = *reinterpret_cast<const f32x4 *>(l2s + ql);
-                dq4[r4] = *reinterpret_cast<const f32x4 *>(Ds + ql);
-            }
             // causal mask on diagonal blocks only (a real uniform branch, as in dQ)
             if (diag) {
                 asm volatile("");
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
             for (int r = 0; r < 16; r++) {
                 const float pr = fast_exp2(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
                 S[r] = pr;
-                dP[r] = pr * (dP[r] - dq4[r >> 2][r & 3]);
+                dP[r] = pr * dP[r];
             }
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
