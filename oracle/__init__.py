@@ -382,3 +382,14 @@ def model_step(cfg, layer_weights, hw: dict, ids):
         grads["wpe"] = dwpe
     extras = SimpleNamespace(logits=logits.reshape(B * T, V), dlogits=dlogits, rows=rows, nf=nf.reshape(B * T, -1))
     return loss, grads, bgrads, extras
+
+
+# ---------------------------------------------------------------------------
+# optimizer
+# ---------------------------------------------------------------------------
+def adamw(p, g, m, v, lr, b1, b2, eps, wd, t):
+    """One AdamW step (step number t >= 1); returns updated copies (p, m, v)."""
+    p, g, m, v = _d(p).copy(), _d(g), _d(m).copy(), _d(v).copy()
+    lib().orc_adamw(_p(p), _p(g), _p(m), _p(v), ctypes.c_long(p.size), ctypes.c_double(lr), ctypes.c_double(b1),
+                    ctypes.c_double(b2), ctypes.c_double(eps), ctypes.c_double(wd), int(t))
+    return p, m, v

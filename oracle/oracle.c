@@ -730,6 +730,28 @@ double orc_softmax_ce(const double *logits, const int *targets, long R, int V, d
     return scale * total;
 }
 
+/* ------------------------------------------------------------------------ */
+/* optimizer                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/* One AdamW step at step number t >= 1 ("nanoeuler — CUDA kernels"
+ * adamw_cpu; llm.c gpt2_update; microgpt adam_update_param without decay):
+ *   m = b1 m + (1 - b1) g;   v = b2 v + (1 - b2) g^2
+ *   mh = m / (1 - b1^t);     vh = v / (1 - b2^t)
+ *   p = p - lr (mh / (sqrt(vh) + eps) + wd p)     (wd on the old p)
+ * In place on p, m, v. */
+void orc_adamw(double *p, const double *g, double *m, double *v, long n, double lr, double b1,
+               double b2, double eps, double wd, int t)
+{
+    double c1 = 1.0 - pow(b1, t), c2 = 1.0 - pow(b2, t);
+    for (long i = 0; i < n; i++) {
+        m[i] = b1 * m[i] + (1.0 - b1) * g[i];
+        v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
+        double mh = m[i] / c1, vh = v[i] / c2;
+        p[i] -= lr * (mh / (sqrt(vh) + eps) + wd * p[i]);
+    }
+}
+
 int orc_num_threads(void)
 {
 #ifdef _OPENMP

@@ -74,6 +74,8 @@ void orc_embed_backward(const int *ids, const double *dx, int B, int T, int C, d
                         double *dwpe);
 double orc_softmax_ce(const double *logits, const int *targets, long R, int V, double scale,
                       double *dlogits, double *row_loss);
+void orc_adamw(double *p, const double *g, double *m, double *v, long n, double lr, double b1,
+               double b2, double eps, double wd, int t);
 int orc_num_threads(void);
 void orc_set_num_threads(int n);
 

@@ -216,3 +216,38 @@ def test_model_initial_loss_near_ln_vocab(orc):
     hw["head"] *= 0.001
     loss = orc.model_step(c, lw, hw, ids)[0]
     assert abs(loss - np.log(50)) < 1e-3
+
+
+# ---------------------------------------------------------------------------
+# optimizer
+# ---------------------------------------------------------------------------
+def test_adamw_vs_torch(orc):
+    """Five AdamW steps against torch.optim.AdamW in float64 (decoupled decay,
+    which equals the pages' lr * (mhat / (sqrt(vhat) + eps) + wd * p))."""
+    n = 1000
+    p0 = rng.standard_normal(n)
+    grads = [rng.standard_normal(n) * (0.1 + i) for i in range(5)]
+    lr, b1, b2, eps, wd = 3e-3, 0.9, 0.95, 1e-8, 0.1
+    pt = torch.tensor(p0.copy(), requires_grad=True)
+    opt = torch.optim.AdamW([pt], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    p, m, v = p0.copy(), np.zeros(n), np.zeros(n)
+    for t, g in enumerate(grads, start=1):
+        pt.grad = torch.tensor(g)
+        opt.step()
+        p, m, v = orc.adamw(p, g, m, v, lr, b1, b2, eps, wd, t)
+        assert rel(p, pt.detach().numpy()) < 1e-13, t
+    st = opt.state[pt]
+    assert rel(m, st["exp_avg"].numpy()) < 1e-13
+    assert rel(v, st["exp_avg_sq"].numpy()) < 1e-13
+
+
+def test_adamw_first_step_closed_form(orc):
+    """Step 1 from zero moments: mhat = g, vhat = g^2, so the update is
+    lr * (g / (|g| + eps) + wd * p) -- a signed step of lr plus the decay."""
+    g = np.array([2.0, -0.5, 1e-3, -7.0])
+    p = np.array([1.0, -1.0, 0.5, 0.0])
+    lr, wd, eps = 0.01, 0.1, 1e-8
+    p1, m1, v1 = orc.adamw(p, g, np.zeros(4), np.zeros(4), lr, 0.9, 0.999, eps, wd, 1)
+    np.testing.assert_allclose(p1, p - lr * (g / (np.abs(g) + eps) + wd * p), rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(m1, 0.1 * g, rtol=1e-15)
+    np.testing.assert_allclose(v1, 0.001 * g * g, rtol=1e-12)
