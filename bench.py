@@ -112,7 +112,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_gqa",
-                    choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long"])
+                    choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -231,6 +231,40 @@ def bench_attn(args, cfg):
     return dt * 1e3 / args.steps, B * T / (dt / args.steps), tim
 
 
+def bench_adamw(args):
+    """One AdamW step over every parameter of the Llama-GQA model (4 blocks,
+    token table and untied head: fp32 master values, moments and gradients,
+    the bf16 storage copy refreshed and the gradient cleared) as one launch."""
+    import numpy as np
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    cfg = configs.LLAMA_GQA
+    per_layer = sum(int(np.prod(s)) for s in configs.weight_shapes(cfg).values())
+    n = cfg.L * per_layer + 2 * cfg.vocab * cfg.C
+    g = torch.Generator(device="cuda").manual_seed(3)
+    p = torch.randn(n, device="cuda", generator=g) * 0.02
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    grads = torch.randn(n, device="cuda", generator=g) * 1e-3
+    lowp = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    step = [0]
+
+    def one():
+        step[0] += 1
+        binding.adamw_update(p, grads, m, v, lowp, n, 3e-4, 0.9, 0.95, 1e-8, 0.1, step[0], "bf16", False)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    nbytes = n * 30.0  # read p, g, m, v; write p, m, v; write the bf16 copy
+    return dt * 1e3, n, nbytes
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -261,6 +295,20 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "repeats": 3}))
+        return
+    if args.workload == "adamw":
+        ms, n, nbytes = bench_adamw(args)
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        print(json.dumps({
+            "metric": "AdamW parameter updates/s (fused, flat fp32 master buffer + bf16 copy)",
+            "value": round(n / (ms * 1e-3), 1), "unit": "params/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "adamw over the Llama-GQA model (4 blocks + token table + head)", "params": n},
+            "roofline": {"kernel": "adamw_kernel", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK,
+                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes},
+            "cpu_baseline": None}), flush=True)
         return
     cfg = configs.ALL_CONFIGS[args.workload]
 

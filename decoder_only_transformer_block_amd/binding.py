@@ -91,6 +91,7 @@ def lib() -> ctypes.CDLL:
         L.lm_head_workspace_bytes.argtypes = [i, i, i, i]
         L.lm_head_workspace_bytes.restype = z
         L.softmax_ce.argtypes = [v, v, v, v, i, v, i, i, f, i, v]
+        L.adamw_update.argtypes = [v, v, v, v, v, ctypes.c_longlong, f, f, f, f, f, i, i, i, v]
         L.dtb_strerror.argtypes = [i]
         L.dtb_strerror.restype = ctypes.c_char_p
         L.dtb_version.restype = ctypes.c_char_p
@@ -208,6 +209,13 @@ def lm_head_backward(dinp, dw, dlogits, ldl, inp, w, R, C, V, dtype, workspace, 
 def softmax_ce(loss, row_loss, dlogits, logits, ldl, targets, R, V, scale, dtype, stream=None):
     check(lib().softmax_ce(_ptr(loss), _ptr(row_loss), _ptr(dlogits), _ptr(logits), ldl, _ptr(targets), R, V,
                            float(scale), DTYPE[dtype], _stream(stream)), "softmax_ce")
+
+
+def adamw_update(params, grads, m, v, params_lowp, n, lr, beta1, beta2, eps, weight_decay, step, lowp_dtype="bf16",
+                 zero_grads=True, stream=None):
+    check(lib().adamw_update(_ptr(params), _ptr(grads), _ptr(m), _ptr(v), _ptr(params_lowp), int(n), float(lr),
+                             float(beta1), float(beta2), float(eps), float(weight_decay), int(step),
+                             DTYPE[lowp_dtype], int(bool(zero_grads)), _stream(stream)), "adamw_update")
 
 
 def block_saved_bytes(cfg: BlockCfg) -> int:

@@ -457,6 +457,19 @@ int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, 
     return softmax_xent_rows(dtype, logits, ldl, targets, R, V, scale, row_loss, dlogits, loss, (hipStream_t)stream);
 }
 
+int adamw_update(float *params, float *grads, float *m, float *v, void *params_lowp, long long n, float lr,
+                 float beta1, float beta2, float eps, float weight_decay, int step, int lowp_dtype, int zero_grads,
+                 void *stream) {
+    if (n < 0 || step < 1) return DTB_EINVAL_SHAPE;
+    if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f)) return DTB_EINVAL_SHAPE;
+    if (params_lowp && lowp_dtype != DTB_BF16) return DTB_EDTYPE;
+    if (n == 0) return DTB_OK;
+    if (!ptr_ok(params) || !ptr_ok(grads) || !ptr_ok(m) || !ptr_ok(v) || (params_lowp && !aligned(params_lowp)))
+        return DTB_EINVAL_PTR;
+    return adamw(params, grads, m, v, params_lowp, n, lr, beta1, beta2, eps, weight_decay, step, zero_grads,
+                 (hipStream_t)stream);
+}
+
 static int check_weights(const dtb_block_cfg *c, const dtb_block_weights *w) {
     if (!w) return DTB_EINVAL_PTR;
     if (!ptr_ok(w->wqkv) || !ptr_ok(w->wo) || !ptr_ok(w->w_up) || !ptr_ok(w->w_down)) return DTB_EINVAL_PTR;

@@ -181,6 +181,61 @@ __global__ __launch_bounds__(256) void loss_sum_kernel(const float *rows, long R
     if (threadIdx.x == 0) loss[0] = (float)(scale * part[0]);
 }
 
+// ---- AdamW over a flat parameter buffer --------------------------------------
+// ("nanoeuler — CUDA kernels" adamw_kernel; llm.c gpt2_update.)  fp32 master
+// p, gradient g, moments m and v; optionally the bf16 storage copy of p and the
+// gradient cleared for the next accumulation.  ic1 = 1 / (1 - b1^t),
+// ic2 = 1 / (1 - b2^t).  16-byte vectors for the first 4*n4 elements, one
+// element per thread for the tail.  Nothing is reused, so every access is
+// non-temporal, and the grid covers the buffer (a capped grid-stride loop and
+// cached accesses measured 4.5 instead of 5.9 TB/s).
+struct AdamArgs {
+    float *p, *g, *m, *v;
+    bf16 *lowp;
+    long long n;
+    float lr, b1, b2, eps, wd, ic1, ic2;
+    int zero_g;
+};
+__device__ __forceinline__ void adam_one(float &p, float g, float &m, float &v, const AdamArgs &a) {
+    m = a.b1 * m + (1.f - a.b1) * g;
+    v = a.b2 * v + (1.f - a.b2) * g * g;
+    const float mh = m * a.ic1, vh = v * a.ic2;
+    p -= a.lr * (mh / (sqrtf(vh) + a.eps) + a.wd * p);
+}
+__global__ __launch_bounds__(256) void adamw_kernel(AdamArgs a) {
+    const long long n4 = a.n / 4, stride = (long long)gridDim.x * 256;
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    for (long long i = tid; i < n4; i += stride) {
+        f32x4 p = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.p) + i);
+        f32x4 g = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.g) + i);
+        f32x4 m = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.m) + i);
+        f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(a.v) + i);
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float pe = p[e], me = m[e], ve = v[e];
+            adam_one(pe, g[e], me, ve, a);
+            p[e] = pe;
+            m[e] = me;
+            v[e] = ve;
+        }
+        __builtin_nontemporal_store(p, reinterpret_cast<f32x4 *>(a.p) + i);
+        __builtin_nontemporal_store(m, reinterpret_cast<f32x4 *>(a.m) + i);
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(a.v) + i);
+        if (a.lowp) __builtin_nontemporal_store(u32x2{pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3])}, reinterpret_cast<u32x2 *>(a.lowp) + i);
+        if (a.zero_g) __builtin_nontemporal_store(f32x4{0.f, 0.f, 0.f, 0.f}, reinterpret_cast<f32x4 *>(a.g) + i);
+    }
+    const long long j = 4 * n4 + tid;  // tail
+    if (j < a.n) {
+        float p = a.p[j], m = a.m[j], v = a.v[j];
+        adam_one(p, a.g[j], m, v, a);
+        a.p[j] = p;
+        a.m[j] = m;
+        a.v[j] = v;
+        if (a.lowp) a.lowp[j] = (bf16)p;
+        if (a.zero_g) a.g[j] = 0.f;
+    }
+}
+
 // ---- host side ----------------------------------------------------------------
 int embed_fwd(int dtype, const int *ids, const void *wte, const void *wpe, long BT, int Tn, int C, int V, void *x,
               hipStream_t s) {
@@ -249,6 +304,28 @@ int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *target
         const double es = dtype == DTB_BF16 ? 2 : 4;
         timing_end(s, K_ELEM, 0, (double)R * (3.0 * es * ldl + 12));
     }
+    return DTB_OK;
+}
+
+int adamw(float *p, float *g, float *m, float *v, void *lowp, long long n, float lr, float b1, float b2, float eps,
+          float wd, int t, int zero_g, hipStream_t s) {
+    if (n <= 0) return DTB_OK;
+    AdamArgs a{};
+    a.p = p; a.g = g; a.m = m; a.v = v;
+    a.lowp = reinterpret_cast<bf16 *>(lowp);
+    a.n = n;
+    a.lr = lr; a.b1 = b1; a.b2 = b2; a.eps = eps; a.wd = wd;
+    a.ic1 = (float)(1.0 / (1.0 - pow((double)b1, t)));
+    a.ic2 = (float)(1.0 / (1.0 - pow((double)b2, t)));
+    a.zero_g = zero_g;
+    const long long n4 = n / 4;
+    long long blocks = (n4 + 255) / 256;
+    if (blocks > (1LL << 20)) blocks = 1LL << 20;
+    if (blocks < 1) blocks = 1;
+    if (g_timing_on) timing_begin(s);
+    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    DTB_LAUNCH_CHECK("adamw_update");
+    if (g_timing_on) timing_end(s, K_ELEM, 0, (double)n * (28 + (lowp ? 2 : 0) + (zero_g ? 4 : 0)));
     return DTB_OK;
 }
 

@@ -25,18 +25,52 @@ def to_numpy(t) -> np.ndarray:
     return t.detach().float().cpu().numpy()
 
 
+class FlatBuffer:
+    """One device allocation holding named tensors as views, each starting on a
+    256-byte boundary (so every view passes the library's 16-byte alignment
+    check and a kernel can sweep the whole buffer at once)."""
+
+    ALIGN = 64  # elements
+
+    def __init__(self, shapes: dict, torch_dt, device="cuda", zero=True):
+        import torch
+        self.offsets, off = {}, 0
+        for k, shp in shapes.items():
+            self.offsets[k] = off
+            n = int(np.prod(shp)) if len(shp) else 1
+            off += (n + self.ALIGN - 1) // self.ALIGN * self.ALIGN
+        self.numel = off
+        self.flat = (torch.zeros if zero else torch.empty)(max(off, 1), dtype=torch_dt, device=device)
+        self.views = {}
+        for k, shp in shapes.items():
+            n = int(np.prod(shp)) if len(shp) else 1
+            self.views[k] = self.flat[self.offsets[k]:self.offsets[k] + n].view(*shp)
+
+
 class BlockStack:
     """L blocks of one configuration: weights, fp32 gradients, per-layer saved
-    activations and one shared workspace."""
+    activations and one shared workspace.  weight_views / grad_views (lists of
+    dicts of device tensors) place the weights and gradients in buffers the
+    caller owns (e.g. views of one flat buffer); otherwise they are allocated
+    here."""
 
-    def __init__(self, cfg, layer_weights, device="cuda"):
+    def __init__(self, cfg, layer_weights, device="cuda", weight_views=None, grad_views=None):
         import torch
         self.cfg = cfg
         self.c = binding.make_cfg(cfg)
         self.device = device
-        self.weights = [{k: to_device(v, cfg.dtype, device) for k, v in w.items()} for w in layer_weights]
-        self.grads = [{k: torch.zeros(v.shape, dtype=torch.float32, device=device) for k, v in w.items()}
-                      for w in layer_weights]
+        if weight_views is None:
+            self.weights = [{k: to_device(v, cfg.dtype, device) for k, v in w.items()} for w in layer_weights]
+        else:
+            self.weights = weight_views
+            for w, wv in zip(layer_weights, weight_views):
+                for k, v in w.items():
+                    wv[k].copy_(to_device(v, cfg.dtype, device))
+        if grad_views is None:
+            self.grads = [{k: torch.zeros(v.shape, dtype=torch.float32, device=device) for k, v in w.items()}
+                          for w in layer_weights]
+        else:
+            self.grads = grad_views
         nsv = binding.block_saved_bytes(self.c)
         nws = binding.block_workspace_bytes(self.c)
         if nsv == 0 or nws == 0:
@@ -99,10 +133,27 @@ class Model:
     def __init__(self, cfg, layer_weights, harness_weights: dict, device="cuda"):
         import torch
         self.cfg = cfg
-        self.stack = BlockStack(cfg, layer_weights, device)
         td = torch_dtype(cfg.dtype)
-        self.hw = {k: to_device(v, cfg.dtype, device) for k, v in harness_weights.items()}
-        self.hgrads = {k: torch.zeros(v.shape, dtype=torch.float32, device=device) for k, v in self.hw.items()}
+        # every parameter (block layers, then the harness) is a view of one
+        # flat storage buffer, and every gradient a view of one flat fp32
+        # buffer: the optimizer updates them all in one launch
+        shapes = {}
+        for l, w in enumerate(layer_weights):
+            for k, v in w.items():
+                shapes[f"L{l}.{k}"] = tuple(v.shape)
+        for k, v in harness_weights.items():
+            shapes[k] = tuple(v.shape)
+        self.wbuf = FlatBuffer(shapes, td, device)
+        self.gbuf = FlatBuffer(shapes, torch.float32, device)
+        wv = [{k: self.wbuf.views[f"L{l}.{k}"] for k in w} for l, w in enumerate(layer_weights)]
+        gv = [{k: self.gbuf.views[f"L{l}.{k}"] for k in w} for l, w in enumerate(layer_weights)]
+        self.stack = BlockStack(cfg, layer_weights, device, weight_views=wv, grad_views=gv)
+        self.hw = {k: self.wbuf.views[k] for k in harness_weights}
+        for k, v in harness_weights.items():
+            self.hw[k].copy_(to_device(v, cfg.dtype, device))
+        self.hgrads = {k: self.gbuf.views[k] for k in harness_weights}
+        self._master_init = (layer_weights, harness_weights)
+        self.opt = None
         B, T, C = cfg.B, cfg.T, cfg.C
         self.V = self.hw["wte"].shape[0]
         self.ldl = (self.V + 7) // 8 * 8
@@ -169,6 +220,31 @@ class Model:
         return self.loss
 
     def zero_grads(self):
-        self.stack.zero_grads()
-        for t in self.hgrads.values():
-            t.zero_()
+        self.gbuf.flat.zero_()
+
+    def optimizer_step(self, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, stream=None):
+        """One AdamW step over every parameter (a single launch over the flat
+        buffers); the gradients are cleared for the next step.  fp32 models
+        update their storage directly; bf16 models keep fp32 master values
+        (from the seeded fp32 initial values) and refresh the bf16 storage."""
+        import torch
+        if self.opt is None:
+            n = self.wbuf.numel
+            if self.cfg.dtype == "bf16":
+                master = FlatBuffer({k: v.shape for k, v in self.wbuf.views.items()}, torch.float32, self.wbuf.flat.device)
+                lw, hw = self._master_init
+                for l, w in enumerate(lw):
+                    for k, v in w.items():
+                        master.views[f"L{l}.{k}"].copy_(torch.from_numpy(np.ascontiguousarray(v, np.float32)))
+                for k, v in hw.items():
+                    master.views[k].copy_(torch.from_numpy(np.ascontiguousarray(v, np.float32)))
+                params, lowp = master.flat, self.wbuf.flat
+            else:
+                params, lowp = self.wbuf.flat, None
+            self.opt = {"params": params, "lowp": lowp, "n": n, "t": 0,
+                        "m": torch.zeros(n, dtype=torch.float32, device=params.device),
+                        "v": torch.zeros(n, dtype=torch.float32, device=params.device)}
+        o = self.opt
+        o["t"] += 1
+        binding.adamw_update(o["params"], self.gbuf.flat, o["m"], o["v"], o["lowp"], o["n"], lr, beta1, beta2, eps,
+                             weight_decay, o["t"], "bf16", True, stream)

@@ -259,6 +259,20 @@ size_t lm_head_workspace_bytes(int R, int C, int V, int dtype);
 int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, int ldl, const int *targets, int R,
                int V, float scale, int dtype, void *stream);
 
+/* ---- optimizer ----------------------------------------------------------------
+ * adamw_update: one AdamW step over a flat buffer of n parameters ("nanoeuler —
+ * CUDA kernels" adamw_kernel; llm.c gpt2_update; microgpt adam_update_param):
+ *   m = beta1 m + (1 - beta1) g;  v = beta2 v + (1 - beta2) g^2
+ *   p -= lr (m / (1 - beta1^step) / (sqrt(v / (1 - beta2^step)) + eps) + weight_decay p)
+ * params (the fp32 master values), grads, m, v: fp32 [n], updated in place
+ * (grads only read, then set to zero when zero_grads != 0, ready for the next
+ * accumulation).  params_lowp: NULL, or [n] of lowp_dtype (DTB_BF16 only)
+ * receiving the rounded parameters (the storage copy the kernels read).
+ * step >= 1 is the 1-based step number; 0 <= beta < 1.  Any n >= 0. */
+int adamw_update(float *params, float *grads, float *m, float *v, void *params_lowp, long long n, float lr,
+                 float beta1, float beta2, float eps, float weight_decay, int step, int lowp_dtype, int zero_grads,
+                 void *stream);
+
 /* ---- misc ---------------------------------------------------------------- */
 const char *dtb_strerror(int code);
 const char *dtb_version(void);

@@ -169,3 +169,85 @@ def test_model_parity(case):
     for l in range(cfg.L):
         for k in rbg[l]:
             check(f"L{l}.d{k}", to_numpy(m.stack.grads[l][k]), rbg[l][k], tol)
+
+
+def test_adamw_update_flat():
+    """adamw_update through the C ABI against the oracle over three steps, on a
+    ragged length (vector body + scalar tail), with the bf16 storage copy and
+    the gradient cleared after each step."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_numpy
+    n = 100003
+    announce(f"adamw_update n={n}")
+    p0 = inputs.tensor(21, "p", (n,), std=0.05)
+    lr, b1, b2, eps, wd = 1e-3, 0.9, 0.95, 1e-8, 0.1
+    p = torch.from_numpy(p0.copy()).cuda()
+    m = torch.zeros(n, device="cuda")
+    v = torch.zeros(n, device="cuda")
+    lowp = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    rp, rm, rv = p0.astype(np.float64), np.zeros(n), np.zeros(n)
+    for t in range(1, 4):
+        g0 = inputs.tensor(21, f"g{t}", (n,), std=0.01 * t)
+        g = torch.from_numpy(g0).cuda()
+        binding.adamw_update(p, g, m, v, lowp, n, lr, b1, b2, eps, wd, t, "bf16", True)
+        torch.cuda.synchronize()
+        rp, rm, rv = oracle.adamw(rp, g0, rm, rv, lr, b1, b2, eps, wd, t)
+        check(f"p[t={t}]", to_numpy(p), rp, 1e-4)
+        check(f"m[t={t}]", to_numpy(m), rm, 1e-4)
+        check(f"v[t={t}]", to_numpy(v), rv, 1e-4)
+        assert not to_numpy(g).any(), "gradient must be cleared"
+        assert torch.equal(lowp, p.to(torch.bfloat16)), "bf16 copy must be the rounded master"
+
+
+@pytest.mark.parametrize("case", ["mini_qwen2", "llama_gqa_reduced"])
+def test_model_two_training_steps(case):
+    """One full training step (forward, backward, AdamW over the flat buffers)
+    followed by a second forward + backward, against the oracle doing the same
+    from the GPU's own step-1 gradients.  (The step-1 gradients are checked
+    against the oracle in test_model_parity, the optimizer in
+    test_adamw_update_flat; feeding the oracle's gradients instead would let
+    AdamW's first step, a signed step of lr, turn tolerated bf16 errors on
+    near-zero gradients into sign flips.)  bf16 models: the oracle's updated
+    parameters are rounded to bf16 for the second forward, as the GPU's storage
+    copy is."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import configs, inputs
+    from decoder_only_transformer_block_amd.runtime import Model, to_numpy
+    cfg = _models()[case]
+    announce(f"model two steps {case} {cfg.dtype}")
+    lw = [configs.block_weights(cfg, l, perturb=True) for l in range(cfg.L)]
+    hw = configs.harness_weights(cfg, perturb=True)
+    ids = configs.token_ids(cfg)
+    hp = dict(lr=2e-3, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    m = Model(cfg, lw, hw)
+    l1 = float(to_numpy(m.step(_ids_dev(ids)))[0])
+    g1 = [{k: to_numpy(v) for k, v in g.items()} for g in m.stack.grads]
+    h1 = {k: to_numpy(v) for k, v in m.hgrads.items()}
+    m.optimizer_step(**hp)
+    l2 = float(to_numpy(m.step(_ids_dev(ids)))[0])
+    torch.cuda.synchronize()
+    rl1 = oracle.model_step(cfg, lw, hw, ids)[0]
+    rnd = (lambda a: inputs.round_bf16(a.astype(np.float32))) if cfg.dtype == "bf16" else (lambda a: a)
+
+    def upd(w, g):
+        p, _, _ = oracle.adamw(w, g, np.zeros(w.size), np.zeros(w.size), hp["lr"], hp["beta1"], hp["beta2"],
+                               hp["eps"], hp["weight_decay"], 1)
+        return rnd(p.reshape(w.shape))
+    lw2 = [{k: upd(w[k], g1[l][k]) for k in w} for l, w in enumerate(lw)]
+    hw2 = {k: upd(hw[k], h1[k]) for k in hw}
+    rl2, rg2, rbg2, _ = oracle.model_step(cfg, lw2, hw2, ids)
+    tol = TOL[cfg.dtype]
+    print(f"    loss step 1 gpu {l1:.6f} oracle {rl1:.6f}; step 2 gpu {l2:.6f} oracle {rl2:.6f}")
+    check("loss1", np.array([l1]), np.array([rl1]), tol)
+    check("loss2", np.array([l2]), np.array([rl2]), tol)
+    assert abs(rl2 - rl1) > 1e-3 * abs(rl1), "the update must change the loss measurably"
+    for k in rg2:
+        check(f"d{k}@2", to_numpy(m.hgrads[k]), rg2[k], tol)
+    for l in range(cfg.L):
+        for k in rbg2[l]:
+            check(f"L{l}.d{k}@2", to_numpy(m.stack.grads[l][k]), rbg2[l][k], tol)
