@@ -91,6 +91,9 @@ def lib() -> ctypes.CDLL:
         L.lm_head_workspace_bytes.argtypes = [i, i, i, i]
         L.lm_head_workspace_bytes.restype = z
         L.softmax_ce.argtypes = [v, v, v, v, i, v, i, i, f, i, v]
+        L.lm_head_ce.argtypes = [v, v, v, v, v, v, v, i, i, i, i, f, i, v, v]
+        L.lm_head_ce_workspace_bytes.argtypes = [i, i, i, i, i]
+        L.lm_head_ce_workspace_bytes.restype = z
         L.adamw_update.argtypes = [v, v, v, v, v, ctypes.c_longlong, f, f, f, f, f, i, i, i, v]
         L.dtb_strerror.argtypes = [i]
         L.dtb_strerror.restype = ctypes.c_char_p
@@ -209,6 +212,15 @@ def lm_head_backward(dinp, dw, dlogits, ldl, inp, w, R, C, V, dtype, workspace, 
 def softmax_ce(loss, row_loss, dlogits, logits, ldl, targets, R, V, scale, dtype, stream=None):
     check(lib().softmax_ce(_ptr(loss), _ptr(row_loss), _ptr(dlogits), _ptr(logits), ldl, _ptr(targets), R, V,
                            float(scale), DTYPE[dtype], _stream(stream)), "softmax_ce")
+
+
+def lm_head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, vchunk, scale, dtype, workspace, stream=None):
+    check(lib().lm_head_ce(_ptr(loss), _ptr(row_loss), _ptr(dinp), _ptr(dw), _ptr(inp), _ptr(w), _ptr(targets), R, C,
+                           V, vchunk, float(scale), DTYPE[dtype], _ptr(workspace), _stream(stream)), "lm_head_ce")
+
+
+def lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype) -> int:
+    return lib().lm_head_ce_workspace_bytes(R, C, V, vchunk, DTYPE[dtype])
 
 
 def adamw_update(params, grads, m, v, params_lowp, n, lr, beta1, beta2, eps, weight_decay, step, lowp_dtype="bf16",

@@ -457,6 +457,31 @@ int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, 
     return softmax_xent_rows(dtype, logits, ldl, targets, R, V, scale, row_loss, dlogits, loss, (hipStream_t)stream);
 }
 
+static int check_head_ce(int R, int C, int V, int vchunk, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (R < 0 || C <= 0 || C % 8 || V <= 0 || vchunk < 0 || vchunk % 256) return DTB_EINVAL_SHAPE;
+    if ((long long)R * C >= (1LL << 40) || (long long)V * C >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+static int head_chunk(int V, int vchunk) { return vchunk > 0 ? (vchunk < V ? vchunk : (V + 255) / 256 * 256) : (V < 4096 ? (V + 255) / 256 * 256 : 4096); }
+
+size_t lm_head_ce_workspace_bytes(int R, int C, int V, int vchunk, int dtype) {
+    if (check_head_ce(R, C, V, vchunk, dtype)) return 0;
+    return head_ce_ws_bytes(R, C, V, head_chunk(V, vchunk), dtype);
+}
+
+int lm_head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w, const int *targets,
+               int R, int C, int V, int vchunk, float scale, int dtype, void *workspace, void *stream) {
+    int e = check_head_ce(R, C, V, vchunk, dtype);
+    if (e) return e;
+    if (!ptr_ok(loss)) return DTB_EINVAL_PTR;
+    if (R > 0 && (!ptr_ok(row_loss) || !ptr_ok(inp) || !ptr_ok(w) || !aligned4(targets) || !ptr_ok(workspace)))
+        return DTB_EINVAL_PTR;
+    if ((dinp && !aligned(dinp)) || (dw && !aligned(dw))) return DTB_EINVAL_PTR;
+    return head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, head_chunk(V, vchunk), scale, dtype, workspace,
+                   (hipStream_t)stream);
+}
+
 int adamw_update(float *params, float *grads, float *m, float *v, void *params_lowp, long long n, float lr,
                  float beta1, float beta2, float eps, float weight_decay, int step, int lowp_dtype, int zero_grads,
                  void *stream) {

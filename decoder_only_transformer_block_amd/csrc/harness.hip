@@ -181,6 +181,110 @@ __global__ __launch_bounds__(256) void loss_sum_kernel(const float *rows, long R
     if (threadIdx.x == 0) loss[0] = (float)(scale * part[0]);
 }
 
+// ---- vocabulary-chunked cross-entropy ------------------------------------------
+// The head's logits are produced chunk by chunk ([R, ldc] for vocabulary
+// columns v0 .. v0+vc-1) and never exist for the whole vocabulary at once.
+// Pass 1 folds each chunk into running per-row (max, sum of exp) and catches
+// the target logit; pass 2 recomputes each chunk and turns it into the scaled
+// gradient in place.
+
+// pass 1: one workgroup per row
+template <typename T>
+__global__ __launch_bounds__(256) void ce_chunk_stats_kernel(const T *lg, long ldc, int vc, int v0, const int *targets,
+                                                             float *rm, float *rs, float *tl, int first) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long r = blockIdx.x;
+    const T *l = lg + r * ldc;
+    const int nv = (vc + EPC - 1) / EPC;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float sm[4], ss[4];
+    float m = -INFINITY, s = 0.f;
+    for (int c = tid; c < nv; c += 256) {
+        float v[EPC];
+        unpack16<T>(ld16(l + c * EPC), v);
+        float mv = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < EPC; e++)
+            if (c * EPC + e < vc) mv = fmaxf(mv, v[e]);
+        if (mv > m) {
+            s = (m == -INFINITY) ? 0.f : s * __expf(m - mv);
+            m = mv;
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; e++)
+            if (c * EPC + e < vc) s += __expf(v[e] - m);
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+        lse_merge(m, s, m2, s2);
+    }
+    if (lane == 0) {
+        sm[wave] = m;
+        ss[wave] = s;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        m = sm[0];
+        s = ss[0];
+#pragma unroll
+        for (int w = 1; w < 4; w++) lse_merge(m, s, sm[w], ss[w]);
+        if (!first) lse_merge(m, s, rm[r], rs[r]);
+        rm[r] = m;
+        rs[r] = s;
+        const int tg = targets[r];
+        if (tg >= v0 && tg < v0 + vc) tl[r] = to_f32(l[tg - v0]);
+    }
+}
+
+// after pass 1: lse (+inf for a masked row, so its gradient comes out zero)
+// and the row losses
+__global__ __launch_bounds__(256) void ce_finish_kernel(const float *rm, const float *rs, const float *tl,
+                                                        const int *targets, long R, int V, float *lse, float *row_loss) {
+    const long r = (long)blockIdx.x * 256 + threadIdx.x;
+    if (r >= R) return;
+    const int tg = targets[r];
+    const bool masked = tg < 0 || tg >= V;
+    const float l = rm[r] + logf(rs[r]);
+    lse[r] = masked ? INFINITY : l;
+    row_loss[r] = masked ? 0.f : l - tl[r];
+}
+
+// pass 2: the chunk's logits become scale * (exp(l - lse) - onehot) in place,
+// zeros in the padded columns; one workgroup per row
+template <typename T>
+__global__ __launch_bounds__(256) void ce_chunk_grad_kernel(T *lg, long ldc, int vc, int v0, const int *targets,
+                                                            const float *lse, float scale) {
+    constexpr int EPC = 16 / sizeof(T);
+    const long r = blockIdx.x;
+    T *l = lg + r * ldc;
+    const float ls = lse[r];
+    const int tg = targets[r] - v0;
+    const int nvl = (int)(ldc / EPC);
+    for (int c = threadIdx.x; c < nvl; c += 256) {
+        float v[EPC], o[EPC];
+        unpack16<T>(ld16(l + c * EPC), v);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            const int idx = c * EPC + e;
+            o[e] = idx < vc ? scale * (__expf(v[e] - ls) - (idx == tg ? 1.f : 0.f)) : 0.f;
+        }
+        st16(l + c * EPC, pack16<T>(o));
+    }
+}
+
+// x = 0 (fp32) / out = in (fp32 -> dtype), 4 elements per thread (n % 4 == 0)
+__global__ __launch_bounds__(256) void zero4_kernel(float *x, long long n4) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i < n4) reinterpret_cast<f32x4 *>(x)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+__global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float *in, bf16 *out, long long n4) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= n4) return;
+    const f32x4 v = reinterpret_cast<const f32x4 *>(in)[i];
+    reinterpret_cast<u32x2 *>(out)[i] = u32x2{pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3])};
+}
+
 // ---- AdamW over a flat parameter buffer --------------------------------------
 // ("nanoeuler — CUDA kernels" adamw_kernel; llm.c gpt2_update.)  fp32 master
 // p, gradient g, moments m and v; optionally the bf16 storage copy of p and the
@@ -303,6 +407,118 @@ int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *target
     if (g_timing_on) {
         const double es = dtype == DTB_BF16 ? 2 : 4;
         timing_end(s, K_ELEM, 0, (double)R * (3.0 * es * ldl + 12));
+    }
+    return DTB_OK;
+}
+
+// ---- chunked head + cross-entropy: orchestration -------------------------------
+static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t head_ce_ws_bytes(int R, int C, int V, int vc, int dtype) {
+    const size_t es = dtype == DTB_BF16 ? 2 : 4;
+    const size_t ldc = ((size_t)vc + 7) / 8 * 8;
+    size_t g1 = gemm_ws_bytes(vc, C, R, dtype), g2 = gemm_ws_bytes(R, C, vc, dtype);
+    return al256((size_t)R * ldc * es) + 5 * al256((size_t)R * 4) + (dtype == DTB_BF16 ? al256((size_t)R * C * 4) : 0) +
+           al256(g1 > g2 ? g1 : g2) + 256;
+}
+
+int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w, const int *targets,
+            int R, int C, int V, int vc, float scale, int dtype, void *workspace, hipStream_t s) {
+    const size_t es = dtype == DTB_BF16 ? 2 : 4;
+    const long ldc = ((long)vc + 7) / 8 * 8;
+    char *ws = static_cast<char *>(workspace);
+    void *chunk = ws;
+    ws += al256((size_t)R * ldc * es);
+    float *rm = reinterpret_cast<float *>(ws); ws += al256((size_t)R * 4);
+    float *rs = reinterpret_cast<float *>(ws); ws += al256((size_t)R * 4);
+    float *tl = reinterpret_cast<float *>(ws); ws += al256((size_t)R * 4);
+    float *lse = reinterpret_cast<float *>(ws); ws += al256((size_t)R * 4);
+    ws += al256((size_t)R * 4);
+    float *dacc = nullptr;
+    if (dinp) dacc = dtype == DTB_BF16 ? reinterpret_cast<float *>(ws) : reinterpret_cast<float *>(dinp);
+    if (dtype == DTB_BF16) ws += al256((size_t)R * C * 4);
+    void *gws = ws;
+    size_t g1 = gemm_ws_bytes(vc, C, R, dtype), g2 = gemm_ws_bytes(R, C, vc, dtype);
+    const size_t gws_bytes = g1 > g2 ? g1 : g2;
+    if (R <= 0) {  // no rows: the loss is zero
+        hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, 0L, scale, loss);
+        DTB_LAUNCH_CHECK("lm_head_ce loss");
+        return DTB_OK;
+    }
+    const bf16 *wb = static_cast<const bf16 *>(w);
+    const float *wf = static_cast<const float *>(w);
+    auto wchunk = [&](int v0) -> const void * {
+        return dtype == DTB_BF16 ? static_cast<const void *>(wb + (long)v0 * C) : static_cast<const void *>(wf + (long)v0 * C);
+    };
+    auto logits = [&](int v0, int n) {
+        GemmArgs g{};
+        g.dtype = dtype;
+        g.a_kmajor = g.b_kmajor = true;
+        g.A = inp; g.lda = C; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = n; g.K = C;
+        g.out = chunk; g.ldo = ldc;
+        return gemm(g, nullptr, 0, s);
+    };
+    // pass 1
+    for (int v0 = 0, i = 0; v0 < V; v0 += vc, i++) {
+        const int n = V - v0 < vc ? V - v0 : vc;
+        int r = logits(v0, n);
+        if (r) return r;
+        if (dtype == DTB_BF16)
+            hipLaunchKernelGGL(ce_chunk_stats_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)chunk, ldc,
+                               n, v0, targets, rm, rs, tl, i == 0);
+        else
+            hipLaunchKernelGGL(ce_chunk_stats_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (const float *)chunk,
+                               ldc, n, v0, targets, rm, rs, tl, i == 0);
+        DTB_LAUNCH_CHECK("lm_head_ce stats");
+    }
+    hipLaunchKernelGGL(ce_finish_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, rm, rs, tl, targets,
+                       (long)R, V, lse, row_loss);
+    DTB_LAUNCH_CHECK("lm_head_ce finish");
+    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, (long)R, scale, loss);
+    DTB_LAUNCH_CHECK("lm_head_ce loss");
+    if (!dinp && !dw) return DTB_OK;
+    if (dacc) {
+        const long long n4 = (long long)R * C / 4;
+        hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc, n4);
+        DTB_LAUNCH_CHECK("lm_head_ce zero");
+    }
+    // pass 2
+    for (int v0 = 0; v0 < V; v0 += vc) {
+        const int n = V - v0 < vc ? V - v0 : vc;
+        int r = logits(v0, n);
+        if (r) return r;
+        if (dtype == DTB_BF16)
+            hipLaunchKernelGGL(ce_chunk_grad_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (bf16 *)chunk, ldc, n,
+                               v0, targets, lse, scale);
+        else
+            hipLaunchKernelGGL(ce_chunk_grad_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (float *)chunk, ldc, n,
+                               v0, targets, lse, scale);
+        DTB_LAUNCH_CHECK("lm_head_ce gradient");
+        if (dacc) {  // dinp += dlogits_chunk W_chunk
+            GemmArgs g{};
+            g.dtype = dtype;
+            g.a_kmajor = true;
+            g.b_kmajor = false;
+            g.A = chunk; g.lda = ldc; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = C; g.K = n;
+            g.out = dacc; g.ldo = C; g.out_f32 = g.accumulate = true;
+            r = gemm(g, gws, gws_bytes, s);
+            if (r) return r;
+        }
+        if (dw) {  // dw[v0 .. v0+n) += dlogits_chunk^T inp
+            GemmArgs g{};
+            g.dtype = dtype;
+            g.a_kmajor = g.b_kmajor = false;
+            g.A = chunk; g.lda = ldc; g.B = inp; g.ldb = C; g.M = n; g.N = C; g.K = R;
+            g.out = dw + (long)v0 * C; g.ldo = C; g.out_f32 = g.accumulate = true;
+            r = gemm(g, gws, gws_bytes, s);
+            if (r) return r;
+        }
+    }
+    if (dinp && dtype == DTB_BF16) {
+        const long long n4 = (long long)R * C / 4;
+        hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc,
+                           (bf16 *)dinp, n4);
+        DTB_LAUNCH_CHECK("lm_head_ce convert");
     }
     return DTB_OK;
 }

@@ -130,9 +130,14 @@ class Model:
     positions with targets ids[:, t+1].  Every step runs in libdtb through the
     C ABI; torch only holds the buffers."""
 
-    def __init__(self, cfg, layer_weights, harness_weights: dict, device="cuda"):
+    def __init__(self, cfg, layer_weights, harness_weights: dict, device="cuda", vchunk=None):
+        """vchunk None: the head's logits for the whole vocabulary are
+        materialised once ([B*T, V]) and overwritten with their gradient;
+        an int: the fused, vocabulary-chunked head + cross-entropy
+        (lm_head_ce) with chunks of vchunk rows (0: the library's default)."""
         import torch
         self.cfg = cfg
+        self.vchunk = vchunk
         td = torch_dtype(cfg.dtype)
         # every parameter (block layers, then the harness) is a view of one
         # flat storage buffer, and every gradient a view of one flat fp32
@@ -164,13 +169,16 @@ class Model:
         self.nf = torch.empty((B, T, C), dtype=td, device=device)       # final norm output
         self.rf = torch.empty(R, dtype=torch.float32, device=device)
         self.mf = torch.empty(R, dtype=torch.float32, device=device)
-        self.logits = torch.empty((R, self.ldl), dtype=td, device=device)  # dlogits in place after the loss
+        self.logits = (torch.empty((R, self.ldl), dtype=td, device=device) if vchunk is None  # dlogits in place
+                       else None)
         self.rows = torch.empty(R, dtype=torch.float32, device=device)
         self.loss = torch.empty(1, dtype=torch.float32, device=device)
         self.dnf = torch.empty((B, T, C), dtype=td, device=device)
         self.dtop = torch.empty((B, T, C), dtype=td, device=device)
         self.dx = torch.empty((B, T, C), dtype=td, device=device)
         nws = max(binding.norm_workspace_bytes(R, C), binding.lm_head_workspace_bytes(R, C, self.V, cfg.dtype))
+        if vchunk is not None:
+            nws = max(nws, binding.lm_head_ce_workspace_bytes(R, C, self.V, vchunk, cfg.dtype))
         self.ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=device)
 
     def _head_w(self):
@@ -198,13 +206,17 @@ class Model:
             binding.norm_forward(self.nf, self.rf, self.mf, h, self.hw.get("gf"), self.hw.get("bf"), R, C,
                                  cfg.norm, cfg.eps, dt, stream)
             nf = self.nf
-        binding.lm_head_forward(self.logits, self.ldl, nf, self._head_w(), R, C, V, dt, stream)
-        binding.softmax_ce(self.loss, self.rows, self.logits, self.logits, self.ldl, tgt, R, V, 1.0 / R, dt,
-                           stream)
-        # backward (self.logits now holds dlogits)
         dhead = self.hgrads["wte"] if cfg.tied_head else self.hgrads["head"]
-        binding.lm_head_backward(self.dnf, dhead, self.logits, self.ldl, nf, self._head_w(), R, C, V, dt, self.ws,
-                                 stream)
+        if self.vchunk is None:
+            binding.lm_head_forward(self.logits, self.ldl, nf, self._head_w(), R, C, V, dt, stream)
+            binding.softmax_ce(self.loss, self.rows, self.logits, self.logits, self.ldl, tgt, R, V, 1.0 / R, dt,
+                               stream)
+            # backward (self.logits now holds dlogits)
+            binding.lm_head_backward(self.dnf, dhead, self.logits, self.ldl, nf, self._head_w(), R, C, V, dt,
+                                     self.ws, stream)
+        else:
+            binding.lm_head_ce(self.loss, self.rows, self.dnf, dhead, nf, self._head_w(), tgt, R, C, V, self.vchunk,
+                               1.0 / R, dt, self.ws, stream)
         dtop = self.dnf
         if cfg.final_norm:
             binding.norm_backward(self.dtop, self.hgrads.get("gf"), self.hgrads.get("bf"), self.dnf, h,

@@ -259,6 +259,24 @@ size_t lm_head_workspace_bytes(int R, int C, int V, int dtype);
 int softmax_ce(float *loss, float *row_loss, void *dlogits, const void *logits, int ldl, const int *targets, int R,
                int V, float scale, int dtype, void *stream);
 
+/* lm_head_ce: the LM head and the softmax cross-entropy fused and chunked over
+ * the vocabulary, forward and backward in one call: the logits of the whole
+ * vocabulary never exist at once, nor do probabilities.  Chunks of vchunk
+ * vocabulary rows (a multiple of 256; 0 = 4096): pass 1 computes each chunk's
+ * logits = inp W_chunk^T and folds them into running per-row max / sum of exp
+ * (catching the target logit); pass 2 recomputes each chunk, forms
+ * dlogits = scale (exp(l - lse) - onehot) in place and applies it:
+ *   dinp[R, C] = sum over chunks of dlogits W_chunk   (dtype, OVERWRITTEN)
+ *   dw[V, C]  += dlogits^T inp                         (fp32, ACCUMULATED)
+ * loss, row_loss as softmax_ce (targets outside [0, V) masked).  dinp or dw
+ * may be NULL (both NULL: loss only, one pass).  inp [R, C], w [V, C]: dtype.
+ * Cost against lm_head_forward + softmax_ce + lm_head_backward: one more
+ * GEMM of the head's forward size, for a workspace of R * vchunk logits
+ * instead of R * V.  workspace: lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype). */
+int lm_head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w, const int *targets,
+               int R, int C, int V, int vchunk, float scale, int dtype, void *workspace, void *stream);
+size_t lm_head_ce_workspace_bytes(int R, int C, int V, int vchunk, int dtype);
+
 /* ---- optimizer ----------------------------------------------------------------
  * adamw_update: one AdamW step over a flat buffer of n parameters ("nanoeuler —
  * CUDA kernels" adamw_kernel; llm.c gpt2_update; microgpt adam_update_param):

@@ -120,7 +120,7 @@ def test_gpt2_small_block_full_size_sampled():
     _block_full_size("gpt2_small", batches=(0, 3), R=16)
 
 
-def _model_full_size(cfg_name, rows):
+def _model_full_size(cfg_name, rows, vchunk=None):
     """The whole model at the workload's full size (all layers, the full
     vocabulary): sampled rows of the loss, of dlogits and of the final hidden
     state's gradient against the oracle (from the GPU's own final hidden state,
@@ -136,9 +136,9 @@ def _model_full_size(cfg_name, rows):
     lw = [configs.block_weights(cfg, l) for l in range(cfg.L)]
     hw = configs.harness_weights(cfg)
     ids = configs.token_ids(cfg)
-    m = Model(cfg, lw, hw)
+    m = Model(cfg, lw, hw, vchunk=vchunk)
     del lw
-    announce("  weights on the device; running the step")
+    announce(f"  weights on the device; running the step (vocabulary chunk {vchunk})")
     ids_d = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
     loss = float(to_numpy(m.step(ids_d))[0])
     torch.cuda.synchronize()
@@ -151,10 +151,15 @@ def _model_full_size(cfg_name, rows):
     head = hw["wte"] if cfg.tied_head else hw["head"]
     tgt = ids[:, 1:].reshape(-1)
     nf_s = to_numpy(nf[rows])
-    dl_s = to_numpy(m.logits[rows])[:, :V]
     lg_ref = oracle.linear_forward(nf_s, head)
     _, dl_ref, rows_ref = oracle.softmax_ce(lg_ref, tgt[rows], 1.0 / R)
     check("row loss", row_loss[rows], rows_ref, tol)
+    if vchunk is not None:
+        # the fused head keeps no logits: dnf rows from the oracle's own dlogits
+        dnf_ref, _, _ = oracle.linear_backward(dl_ref, nf_s, head)
+        check("dnf[rows]", to_numpy(m.dnf.reshape(R, C)[rows]), dnf_ref, tol)
+        return
+    dl_s = to_numpy(m.logits[rows])[:, :V]
     check("dlogits[rows]", dl_s, dl_ref, tol)
     dnf_ref, _, _ = oracle.linear_backward(dl_s, nf_s, head)
     check("dnf[rows]", to_numpy(m.dnf.reshape(R, C)[rows]), dnf_ref, tol)
@@ -183,3 +188,10 @@ def test_llama_gqa_model_full_size_sampled():
 def test_gpt2_small_model_full_size_sampled():
     require_gpu()
     _model_full_size("gpt2_small", rows=[0, 1, 1023, 1024, 3000, 4095])
+
+
+def test_llama_gqa_model_full_size_chunked_head():
+    """The same model with the fused, vocabulary-chunked head (4096-row chunks,
+    a ragged last chunk of 3328)."""
+    require_gpu()
+    _model_full_size("llama_gqa", rows=[0, 1, 2047, 2048, 9000, 16383], vchunk=4096)

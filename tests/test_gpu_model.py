@@ -134,6 +134,41 @@ def test_lm_head_and_softmax_ce(dtype, V):
     check("dw", to_numpy(dw), rdw, tol)
 
 
+@pytest.mark.parametrize("dtype,V,vchunk", [("f32", 1003, 256), ("bf16", 997, 256), ("bf16", 2048, 512),
+                                           ("bf16", 700, 0)])
+def test_lm_head_ce_chunked(dtype, V, vchunk):
+    """The fused, vocabulary-chunked head + cross-entropy against the oracle's
+    unfused definition (linear head, softmax cross-entropy, linear backward):
+    several chunks with a ragged last one, one chunk, masked targets."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_numpy
+    R, C = 300, 256
+    announce(f"lm_head_ce R={R} C={C} V={V} vchunk={vchunk} {dtype}")
+    inp = inputs.tensor(4, "inp", (R, C), dtype=dtype)
+    w = inputs.tensor(4, "w", (V, C), std=0.1, dtype=dtype)
+    tgt = inputs.ids(4, "tgt", R, V)
+    tgt[[0, 17, R - 1]] = -1
+    inpd, wd = _dev(inp, dtype), _dev(w, dtype)
+    loss = torch.empty(1, device="cuda")
+    rows = torch.empty(R, device="cuda")
+    dinp = torch.empty((R, C), dtype=inpd.dtype, device="cuda")
+    dw = torch.zeros((V, C), device="cuda")
+    ws = torch.empty(binding.lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype), dtype=torch.uint8, device="cuda")
+    binding.lm_head_ce(loss, rows, dinp, dw, inpd, wd, _ids_dev(tgt), R, C, V, vchunk, 1.0 / R, dtype, ws)
+    torch.cuda.synchronize()
+    rl = oracle.linear_forward(inp, w)
+    rloss, rdl, rrows = oracle.softmax_ce(rl, tgt, 1.0 / R)
+    rdinp, rdw, _ = oracle.linear_backward(rdl, inp, w)
+    tol = TOL[dtype]
+    check("row loss", to_numpy(rows), rrows, tol)
+    check("loss", to_numpy(loss), np.array([rloss]), tol)
+    check("dinp", to_numpy(dinp), rdinp, tol)
+    check("dw", to_numpy(dw), rdw, tol)
+
+
 def _models():
     from decoder_only_transformer_block_amd import configs as K
     return {
@@ -144,19 +179,21 @@ def _models():
     }
 
 
-@pytest.mark.parametrize("case", list(_models()))
-def test_model_parity(case):
+@pytest.mark.parametrize("case,vchunk", [(c, None) for c in ("microgpt", "mini_qwen2", "gpt2_reduced",
+                                                               "llama_gqa_reduced")] +
+                         [("gpt2_reduced", 256), ("llama_gqa_reduced", 256)])
+def test_model_parity(case, vchunk):
     require_gpu()
     import torch
     import oracle
     from decoder_only_transformer_block_amd import configs
     from decoder_only_transformer_block_amd.runtime import Model, to_numpy
     cfg = _models()[case]
-    announce(f"model {case} L={cfg.L} B={cfg.B} T={cfg.T} C={cfg.C} V={cfg.vocab} {cfg.dtype}")
+    announce(f"model {case} L={cfg.L} B={cfg.B} T={cfg.T} C={cfg.C} V={cfg.vocab} {cfg.dtype} vchunk={vchunk}")
     lw = [configs.block_weights(cfg, l, perturb=True) for l in range(cfg.L)]
     hw = configs.harness_weights(cfg, perturb=True)
     ids = configs.token_ids(cfg)
-    m = Model(cfg, lw, hw)
+    m = Model(cfg, lw, hw, vchunk=vchunk)
     loss = m.step(_ids_dev(ids))
     torch.cuda.synchronize()
     rloss, rg, rbg, _ = oracle.model_step(cfg, lw, hw, ids)
