@@ -112,7 +112,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_gqa",
-                    choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw"])
+                    choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw",
+                             "head_ce"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -265,6 +266,48 @@ def bench_adamw(args):
     return dt * 1e3, n, nbytes
 
 
+def bench_head_ce(args):
+    """The Llama-GQA LM head + cross-entropy forward and backward (R = 16384
+    positions, C = 2048, V = 32000, bf16): the fused vocabulary-chunked path
+    (lm_head_ce, 4096-row chunks) and, for context, the unfused one."""
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    cfg = configs.LLAMA_GQA
+    R, C, V = cfg.B * cfg.T, cfg.C, cfg.vocab
+    g = torch.Generator(device="cuda").manual_seed(4)
+    inp = torch.randn(R, C, device="cuda", generator=g).bfloat16()
+    w = (torch.randn(V, C, device="cuda", generator=g) * 0.02).bfloat16()
+    tgt = torch.randint(0, V, (R,), device="cuda", generator=g, dtype=torch.int32)
+    loss = torch.empty(1, device="cuda")
+    rows = torch.empty(R, device="cuda")
+    dinp = torch.empty(R, C, device="cuda", dtype=torch.bfloat16)
+    dw = torch.zeros(V, C, device="cuda")
+    ws = torch.empty(binding.lm_head_ce_workspace_bytes(R, C, V, 4096, "bf16"), dtype=torch.uint8, device="cuda")
+    ldl = (V + 7) // 8 * 8
+    logits = torch.empty(R, ldl, device="cuda", dtype=torch.bfloat16)
+    ws2 = torch.empty(binding.lm_head_workspace_bytes(R, C, V, "bf16"), dtype=torch.uint8, device="cuda")
+
+    def fused():
+        binding.lm_head_ce(loss, rows, dinp, dw, inp, w, tgt, R, C, V, 4096, 1.0 / R, "bf16", ws)
+
+    def unfused():
+        binding.lm_head_forward(logits, ldl, inp, w, R, C, V, "bf16")
+        binding.softmax_ce(loss, rows, logits, logits, ldl, tgt, R, V, 1.0 / R, "bf16")
+        binding.lm_head_backward(dinp, dw, logits, ldl, inp, w, R, C, V, "bf16", ws2)
+
+    out = {}
+    for name, fn in (("fused", fused), ("unfused", unfused)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        out[name] = (time.perf_counter() - t0) / args.steps * 1e3
+    return out, R, C, V, ws.numel(), logits.numel() * 2
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -308,6 +351,24 @@ def main():
             "roofline": {"kernel": "adamw_kernel", "bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK,
                          "unit": "GB/s", "frac": round(gbps / HBM_PEAK, 4), "traffic": None,
                          "algorithmic_bytes_per_launch": nbytes},
+            "cpu_baseline": None}), flush=True)
+        return
+    if args.workload == "head_ce":
+        t, R, C, V, ws_bytes, logit_bytes = bench_head_ce(args)
+        fl = 2.0 * R * C * V
+        tf = 4 * fl / (t["fused"] * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "LM head + cross-entropy forward and backward tokens/s (fused, vocabulary-chunked)",
+            "value": round(R / (t["fused"] * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(t["fused"], 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "Llama-GQA head: R=16384 positions, C=2048, V=32000, chunk 4096"},
+            "roofline": {"kernel": "lm_head_ce (four GEMMs of the head's size)", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4),
+                         "traffic": None},
+            "unfused_ms": round(t["unfused"], 4),
+            "unfused_tflops_3gemm": round(3 * fl / (t["unfused"] * 1e-3) / 1e12, 2),
+            "workspace_bytes_fused": ws_bytes, "logits_bytes_unfused": logit_bytes,
             "cpu_baseline": None}), flush=True)
         return
     cfg = configs.ALL_CONFIGS[args.workload]
