@@ -9,6 +9,8 @@ train_gpt2.c ParameterTensors.
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 
 import numpy as np
@@ -107,6 +109,26 @@ class AttnConfig:
         return 4.0 * self.hd * self.NH * self.T * (self.T + 1) / 2 * self.B
 
 
+@dataclass(frozen=True)
+class DecodeConfig:
+    """One decode step of attention: one new query per sequence against a KV
+    cache of capacity Tmax whose rows 0 .. len-1 are in use, lengths drawn
+    uniformly from [len_lo, len_hi]."""
+    name: str
+    B: int
+    Tmax: int
+    NH: int
+    NKV: int
+    hd: int
+    dtype: str
+    seed: int
+    len_lo: int = 1
+    len_hi: int = 0  # 0: Tmax
+
+    def replace(self, **kw) -> "DecodeConfig":
+        return dataclasses.replace(self, **kw)
+
+
 MICROGPT = BlockConfig("microgpt", L=1, B=1, T=16, C=16, NH=4, NKV=4, H=64,
                        norm="rms_nogamma", mlp="relu", rope="none", rope_base=0.0,
                        eps=1e-5, qkv_bias=False, o_bias=False, mlp_bias=False,
@@ -127,6 +149,12 @@ LLAMA_GQA = BlockConfig("llama_gqa", L=4, B=8, T=2048, C=2048, NH=32, NKV=8, H=5
                         dtype="bf16", vocab=32000, std=0.02, seed=0xD7B0 + 4)
 ATTN_LONG = AttnConfig("attn_long", B=1, T=16384, NH=32, NKV=8, hd=128, dtype="bf16",
                        seed=0xD7B0 + 5)
+
+# decode over the Llama-GQA attention geometry: 256 sequences with cache
+# lengths uniform in [1, 4096] (about 537 MB of bf16 keys and values in use,
+# twice the last-level cache)
+DECODE_LLAMA_GQA = DecodeConfig("decode_llama_gqa", B=256, Tmax=4096, NH=32, NKV=8, hd=64, dtype="bf16",
+                                seed=0xD7B0 + 6)
 
 BLOCK_CONFIGS = {c.name: c for c in (MICROGPT, MINI_QWEN2, GPT2_SMALL, LLAMA_GQA)}
 ALL_CONFIGS = dict(BLOCK_CONFIGS, attn_long=ATTN_LONG)
@@ -226,3 +254,31 @@ def attn_inputs(cfg: AttnConfig):
     qkv = inputs.tensor(cfg.seed, "qkv", (cfg.B, cfg.T, cfg.QKV), dtype=cfg.dtype)
     dout = inputs.tensor(cfg.seed, "dout", (cfg.B, cfg.T, cfg.C), dtype=cfg.dtype)
     return qkv, dout
+
+
+def decode_lens(cfg: DecodeConfig) -> np.ndarray:
+    """Cache lengths [B] (int32), uniform in [len_lo, len_hi]."""
+    hi = cfg.len_hi or cfg.Tmax
+    return (cfg.len_lo + inputs.ids(cfg.seed, "lens", cfg.B, hi - cfg.len_lo + 1)).astype(np.int32)
+
+
+def decode_inputs(cfg: DecodeConfig, fill: float = 0.0):
+    """q [B, NH*hd] and k / v caches [B, Tmax, NKV*hd] ~ N(0, 1) in the rows in
+    use; rows past a sequence's length hold `fill`.  Returns (q, k, v, lens)."""
+    lens = decode_lens(cfg)
+    KV = cfg.NKV * cfg.hd
+    q = inputs.tensor(cfg.seed, "q", (cfg.B, cfg.NH * cfg.hd), dtype=cfg.dtype)
+    caches = []
+    for name in ("k_cache", "v_cache"):
+        c = np.full((cfg.B, cfg.Tmax, KV), fill, dtype=np.float32)
+
+        def seq(b, c=c, name=name):
+            n = int(lens[b])
+            if n:
+                v = inputs.normal(cfg.seed, name, n * KV, start=b * cfg.Tmax * KV).astype(np.float32)
+                c[b, :n] = (inputs.round_bf16(v) if cfg.dtype == "bf16" else v).reshape(n, KV)
+
+        with ThreadPoolExecutor(max(1, min(16, len(os.sched_getaffinity(0))))) as ex:
+            list(ex.map(seq, range(cfg.B)))
+        caches.append(c)
+    return q, caches[0], caches[1], lens

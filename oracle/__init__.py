@@ -186,6 +186,21 @@ def attn_tail(q_tail, k, v, dout_tail, T, R, NH, NKV, hd):
     return o, lse, dq, dk, dv
 
 
+def attn_decode(q, k_cache, v_cache, lens, NH, NKV, hd):
+    """One query per sequence against its KV cache: q [B, NH*hd], caches
+    [B, Tmax, NKV*hd], lens [B] (cache rows in use).  Returns out [B, NH*hd]
+    and lse [B, NH] (-inf for an empty cache)."""
+    q, k_cache, v_cache = _d(q), _d(k_cache), _d(v_cache)
+    B, Tmax = k_cache.shape[0], k_cache.shape[1]
+    lens = np.ascontiguousarray(lens, dtype=np.int32)
+    assert q.shape == (B, NH * hd) and v_cache.shape == k_cache.shape and lens.shape == (B,)
+    assert k_cache.shape[2] == NKV * hd and int(lens.max(initial=0)) <= Tmax and int(lens.min(initial=0)) >= 0
+    out = np.empty((B, NH * hd))
+    lse = np.empty((B, NH))
+    lib().orc_attn_decode(_p(q), _p(k_cache), _p(v_cache), _ip(lens), B, NH, NKV, hd, Tmax, _p(out), _p(lse))
+    return out, lse
+
+
 def act_forward(mlp: str, up, H):
     up = _d(up)
     W = up.shape[-1]

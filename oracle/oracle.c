@@ -528,6 +528,58 @@ void orc_attn_tail(const double *q_tail, const double *k, const double *v, const
     }
 }
 
+/* Decode attention ("microgpt.cu": attention_forward_kernel as called from
+ * forward_position, where the keys / values of every position so far sit in
+ * a per-layer cache and the query of the newest position reads cache rows
+ * 0 .. pos_id).  One query per sequence against the first lens[b] rows of
+ * its cache:
+ *   q [B][NH*hd];  k_cache, v_cache [B][Tmax][NKV*hd] (row t holds kv head
+ *   kh at columns kh*hd, as the microgpt cache rows hold all heads of one
+ *   position);  s_j = q_h . k_j / sqrt(hd) for j < lens[b] with kh =
+ *   h / (NH/NKV);  out [B][NH*hd] = sum_j softmax(s)_j v_j;  lse [B][NH] =
+ *   m + ln sum_j exp(s_j - m).
+ * An empty cache (lens[b] = 0) gives out = 0 and lse = -inf (an empty sum).
+ * Rows at or beyond lens[b] are never read. */
+void orc_attn_decode(const double *q, const double *kc, const double *vc, const int *lens, int B,
+                     int NH, int NKV, int hd, int Tmax, double *out, double *lse)
+{
+    int grp = NH / NKV, KV = NKV * hd;
+    double scale = 1.0 / sqrt((double)hd);
+    #pragma omp parallel if(ORC_PARALLEL((double)B * NH * Tmax * hd))
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Tmax > 0 ? Tmax : 1));
+        #pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int b = 0; b < B; b++)
+            for (int h = 0; h < NH; h++) {
+                int kh = h / grp, n = lens[b];
+                const double *qh = q + ((long)b * NH + h) * hd;
+                const double *kb = kc + (long)b * Tmax * KV + (long)kh * hd;
+                const double *vb = vc + (long)b * Tmax * KV + (long)kh * hd;
+                double *o = out + ((long)b * NH + h) * hd;
+                for (int d = 0; d < hd; d++) o[d] = 0.0;
+                if (n <= 0) {
+                    lse[(long)b * NH + h] = -INFINITY;
+                    continue;
+                }
+                for (int j = 0; j < n; j++) {
+                    double acc = 0.0;
+                    for (int d = 0; d < hd; d++) acc += qh[d] * kb[(long)j * KV + d];
+                    s[j] = acc * scale;
+                }
+                double m = s[0];
+                for (int j = 1; j < n; j++) if (s[j] > m) m = s[j];
+                double l = 0.0;
+                for (int j = 0; j < n; j++) l += exp(s[j] - m);
+                for (int j = 0; j < n; j++) {
+                    double p = exp(s[j] - m) / l;
+                    for (int d = 0; d < hd; d++) o[d] += p * vb[(long)j * KV + d];
+                }
+                lse[(long)b * NH + h] = m + log(l);
+            }
+        free(s);
+    }
+}
+
 /* ------------------------------------------------------------------------ */
 /* MLP activations                                                            */
 /* ------------------------------------------------------------------------ */

@@ -62,6 +62,8 @@ void orc_attn_backward_materialized(const double *qkv, const double *att, const 
 void orc_attn_tail(const double *q_tail, const double *k, const double *v, const double *dout_tail,
                    int T, int R, int NH, int NKV, int hd, double *o_tail, double *lse_tail,
                    double *dq_tail, double *dk_tail, double *dv_tail);
+void orc_attn_decode(const double *q, const double *kc, const double *vc, const int *lens, int B,
+                     int NH, int NKV, int hd, int Tmax, double *out, double *lse);
 void orc_act_forward(int mlp, const double *up, long R, int H, double *h);
 void orc_act_backward(int mlp, const double *dh, const double *up, long R, int H, double *dup);
 void orc_block_forward(const orc_cfg *c, const orc_weights *w, const double *x, double *y,
