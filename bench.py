@@ -113,7 +113,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_gqa",
                     choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw",
-                             "head_ce"])
+                             "head_ce", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -308,6 +308,51 @@ def bench_head_ce(args):
     return out, R, C, V, ws.numel(), logits.numel() * 2
 
 
+def bench_decode(args):
+    """Decode attention over the Llama-GQA heads: 256 sequences, cache lengths
+    uniform in [1, 4096] (capacity 4096), one new query per sequence, bf16.
+    The caches stay resident; a step is one attn_decode call (the chunked
+    attention kernel and its merge)."""
+    import numpy as np
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    from decoder_only_transformer_block_amd.runtime import DecodeAttention, to_device
+    cfg = configs.DECODE_LLAMA_GQA
+    q, kc, vc, lens = configs.decode_inputs(cfg)
+    dq, dk, dv = to_device(q, cfg.dtype), to_device(kc, cfg.dtype), to_device(vc, cfg.dtype)
+    dl = torch.from_numpy(lens).cuda()
+    dec = DecodeAttention(cfg.B, cfg.NH, cfg.NKV, cfg.hd, cfg.Tmax, cfg.dtype)
+    for _ in range(args.warmup):
+        dec(dq, dk, dv, dl)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dec(dq, dk, dv, dl)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    tim = None
+    if not args.no_timing:
+        binding.timing_enable(True)
+        binding.timing_collect()
+        for _ in range(args.steps):
+            dec(dq, dk, dv, dl)
+        tim = binding.timing_collect()
+        binding.timing_enable(False)
+    es = 2
+    kv_bytes = float(lens.astype(np.int64).sum()) * cfg.NKV * cfg.hd * es * 2
+    q_bytes = cfg.B * cfg.NH * cfg.hd * es
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        t0 = time.perf_counter()
+        oracle.attn_decode(q, kc, vc, lens, cfg.NH, cfg.NKV, cfg.hd)
+        dt = time.perf_counter() - t0
+        cpu = {"value": round(cfg.B / dt, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+               "sample": f"the whole workload ({cfg.B} sequences) in fp64, {dt:.2f} s"}
+    return cfg, ms, tim, kv_bytes, q_bytes, int(lens.sum()), dec.ws.numel(), cpu
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -370,6 +415,34 @@ def main():
             "unfused_tflops_3gemm": round(3 * fl / (t["unfused"] * 1e-3) / 1e12, 2),
             "workspace_bytes_fused": ws_bytes, "logits_bytes_unfused": logit_bytes,
             "cpu_baseline": None}), flush=True)
+        return
+    if args.workload == "decode":
+        cfg, ms, tim, kv_bytes, q_bytes, ntok, ws_bytes, cpu = bench_decode(args)
+        roof = None
+        brk = {}
+        if tim:
+            for k in ("attn_decode", "decode_merge"):
+                v = tim.get(k)
+                if v and v["launches"]:
+                    brk[k] = {"ms_per_step": round(v["ms"] / args.steps, 4),
+                              "launches_per_step": v["launches"] // args.steps}
+            d = tim.get("attn_decode")
+            if d and d["launches"]:
+                avg = d["ms"] / d["launches"]
+                per = kv_bytes + q_bytes
+                gb = per / (avg * 1e-3) / 1e9
+                roof = {"kernel": "decode_bf16_kernel<64, 4> (chunked decode attention)", "bound": "hbm",
+                        "achieved": round(gb, 1), "peak": HBM_PEAK, "unit": "GB/s", "frac": round(gb / HBM_PEAK, 4),
+                        "traffic": None, "avg_launch_ms": round(avg, 4), "algorithmic_bytes_per_launch": per}
+        print(json.dumps({
+            "metric": "decode attention tokens/s (one new query per sequence against its KV cache)",
+            "value": round(cfg.B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) q / caches, uniform lengths)",
+            "config": {"workload": "decode attention, Llama-GQA heads: B=256 sequences, cache lengths uniform "
+                                   "in [1, 4096], NH=32, NKV=8, hd=64", "cached_positions": ntok,
+                       "kv_bytes": kv_bytes, "workspace_bytes": ws_bytes},
+            "roofline": roof, "breakdown": brk, "cpu_baseline": cpu}), flush=True)
         return
     cfg = configs.ALL_CONFIGS[args.workload]
 

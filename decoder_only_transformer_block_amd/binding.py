@@ -68,6 +68,9 @@ def lib() -> ctypes.CDLL:
         L.attn_backward.argtypes = [v, v, v, v, v, i, i, i, i, i, i, v, v]
         L.attn_workspace_bytes.argtypes = [i, i, i]
         L.attn_workspace_bytes.restype = z
+        L.attn_decode.argtypes = [v, v, v, v, v, v, i, i, i, i, i, i, i, v, v]
+        L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+        L.attn_decode_workspace_bytes.restype = z
         cp = ctypes.POINTER(BlockCfg)
         L.block_saved_bytes.argtypes = [cp]
         L.block_saved_bytes.restype = z
@@ -154,6 +157,15 @@ def attn_workspace_bytes(B, T, NH) -> int:
 def attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, workspace, stream=None):
     check(lib().attn_backward(_ptr(dqkv), _ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, T, C, NH, NKV,
                               DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_backward")
+
+
+def attn_decode_workspace_bytes(B, NH, NKV, hd, Tmax, chunk, dtype) -> int:
+    return lib().attn_decode_workspace_bytes(B, NH, NKV, hd, Tmax, chunk, DTYPE[dtype])
+
+
+def attn_decode(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, chunk, dtype, workspace, stream=None):
+    check(lib().attn_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), B, NH, NKV,
+                            hd, Tmax, chunk, DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_decode")
 
 
 def linear_forward(out, inp, w, bias, res, R, K, N, dtype, stream=None):
@@ -262,7 +274,7 @@ def timing_enable(on: bool) -> None:
 
 
 def timing_collect():
-    names = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw"]
+    names = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw", "attn_decode", "decode_merge"]
     arr = (Timing * len(names))()
     n = lib().dtb_timing_collect(arr, len(names))
     return {names[i]: {"ms": arr[i].ms, "flops": arr[i].flops, "bytes": arr[i].bytes,

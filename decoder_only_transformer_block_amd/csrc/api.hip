@@ -267,6 +267,37 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
                                 (hipStream_t)stream);
 }
 
+static int check_decode(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (B < 0 || Tmax < 0 || NH <= 0 || NKV <= 0 || NH % NKV || chunk < 0 || chunk % 32) return DTB_EINVAL_SHAPE;
+    if (!hd_ok(hd, dtype)) return DTB_EINVAL_SHAPE;
+    const long long es = dtype == DTB_BF16 ? 2 : 4;
+    if ((long long)Tmax * NKV * hd * es >= (1LL << 31) || (long long)B * NH * hd >= (1LL << 31))
+        return DTB_EINVAL_SHAPE;
+    if ((long long)B * NKV * ((Tmax + 31) / 32) * NH >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+size_t attn_decode_workspace_bytes(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype) {
+    if (check_decode(B, NH, NKV, hd, Tmax, chunk, dtype)) return 0;
+    size_t n = decode_geometry(B, NH, NKV, hd, Tmax, chunk, dtype).ws_bytes;
+    return n ? al(n) : 256;
+}
+
+int attn_decode(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache, const int *lens,
+                int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype, void *workspace, void *stream) {
+    int e = check_decode(B, NH, NKV, hd, Tmax, chunk, dtype);
+    if (e) return e;
+    if (B == 0) return DTB_OK;
+    if (!ptr_ok(out) || !ptr_ok(lse) || !ptr_ok(q) || !ptr_ok(lens) || !ptr_ok(workspace)) return DTB_EINVAL_PTR;
+    if (Tmax > 0 && (!ptr_ok(k_cache) || !ptr_ok(v_cache))) return DTB_EINVAL_PTR;
+    const DecodeGeom g = decode_geometry(B, NH, NKV, hd, Tmax, chunk, dtype);
+    hipError_t he = attn_decode_launch(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, g, dtype,
+                                       workspace, (hipStream_t)stream);
+    if (he != hipSuccess) return set_launch_error(he, "attn_decode");
+    return DTB_OK;
+}
+
 static int check_linear(int R, int K, int N, int dtype) {
     if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
     if (R < 0 || K <= 0 || N <= 0 || K % 8 || N % 8) return DTB_EINVAL_SHAPE;

@@ -176,7 +176,10 @@ struct Launch {
 // timing classes: GEMMs by role (forward projections: both operands k-major,
 // output in the storage dtype; input gradients: B m/n-major; weight gradients:
 // fp32 accumulation), attention, everything else
-enum KClass { K_GEMM_FWD = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_GEMM_DINP = 4, K_GEMM_DW = 5, K_NCLASS = 6 };
+enum KClass {
+    K_GEMM_FWD = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_GEMM_DINP = 4, K_GEMM_DW = 5,
+    K_ATTN_DEC = 6, K_DEC_MERGE = 7, K_NCLASS = 8
+};
 void timing_begin(hipStream_t s);
 void timing_end(hipStream_t s, int cls, double flops, double bytes);
 extern bool g_timing_on;
@@ -232,6 +235,16 @@ int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, in
 int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout,
                          const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
                          float *D, const float *rope_cs, hipStream_t s);
+
+// decode attention: chunking of the cache and the workspace it needs
+struct DecodeGeom {
+    int chunk, nsplit, ngrp;
+    size_t ws_bytes;
+};
+DecodeGeom decode_geometry(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype);
+hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *kc, const void *vc, const int *lens,
+                              int B, int NH, int NKV, int hd, int Tmax, const DecodeGeom &g, int dtype,
+                              void *workspace, hipStream_t s);
 
 // elementwise / reductions
 int norm_forward(int mode, int dtype, const void *x, const void *g, const void *b, float eps, long R, int C,

@@ -260,3 +260,24 @@ class Model:
         o["t"] += 1
         binding.adamw_update(o["params"], self.gbuf.flat, o["m"], o["v"], o["lowp"], o["n"], lr, beta1, beta2, eps,
                              weight_decay, o["t"], "bf16", True, stream)
+
+
+class DecodeAttention:
+    """Buffers of one decode-attention call (one new query per sequence
+    against a KV cache of capacity Tmax): the output, the lse and the chunk
+    workspace are allocated once; __call__ enqueues attn_decode."""
+
+    def __init__(self, B, NH, NKV, hd, Tmax, dtype, chunk=0, device="cuda"):
+        import torch
+        self.B, self.NH, self.NKV, self.hd, self.Tmax, self.dtype, self.chunk = B, NH, NKV, hd, Tmax, dtype, chunk
+        self.out = torch.empty((B, NH * hd), dtype=torch_dtype(dtype), device=device)
+        self.lse = torch.empty((B, NH), dtype=torch.float32, device=device)
+        nb = binding.attn_decode_workspace_bytes(B, NH, NKV, hd, Tmax, chunk, dtype)
+        if nb == 0:
+            raise ValueError("attn_decode: unsupported shape")
+        self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
+
+    def __call__(self, q, k_cache, v_cache, lens):
+        binding.attn_decode(self.out, self.lse, q, k_cache, v_cache, lens, self.B, self.NH, self.NKV, self.hd,
+                            self.Tmax, self.chunk, self.dtype, self.ws)
+        return self.out, self.lse

@@ -95,6 +95,38 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
                   void *workspace, void *stream);
 size_t attn_workspace_bytes(int B, int T, int NH);
 
+/* ---- decode attention ---------------------------------------------------
+ * One new query per sequence against that sequence's KV cache, forward only
+ * ("microgpt.cu": attention_forward_kernel as forward_position calls it, the
+ * newest position's query reading the cached keys and values of positions
+ * 0 .. pos_id):
+ *   out[b, h] = sum_{j < lens[b]} softmax_j(q[b, h] . k[b, j, kh] / sqrt(hd)) v[b, j, kh]
+ *   lse[b, h] = natural-log logsumexp_j of the same scores,  kh = h / (NH/NKV)
+ * The caller has already rotated q (RoPE at position lens[b]-1) and written
+ * the newest position's key and value into row lens[b]-1 of the caches.
+ *   out      [B][NH*hd] of dtype (written)
+ *   lse      [B][NH] fp32 (written)
+ *   q        [B][NH*hd] of dtype
+ *   k_cache, v_cache  [B][Tmax][NKV*hd] of dtype: row t of sequence b holds
+ *            kv head kh at columns kh*hd (a row holds every kv head of one
+ *            position, as the microgpt cache rows do).  Rows at or past
+ *            lens[b] are never read and may hold anything.
+ *   lens     [B] int32 in device memory: cache rows in use, 0 .. Tmax.
+ *            lens[b] = 0 gives out = 0 and lse = -inf (an empty softmax);
+ *            a length outside [0, Tmax] gives NaN in that sequence's out and
+ *            lse (the lengths are not visible to the host; nothing outside
+ *            the caches is read)
+ *   chunk    cache positions per workgroup, a multiple of 32, or 0 for the
+ *            library's choice (sized from B, NKV and Tmax)
+ *   workspace  attn_decode_workspace_bytes(...) bytes of device scratch
+ *            (per-chunk partial results); contents on entry are ignored
+ * dtype DTB_F32 or DTB_BF16 for q, the caches and out; hd as for
+ * attn_forward; Tmax * NKV * hd * sizeof(dtype) below 2^31.  Deterministic. */
+size_t attn_decode_workspace_bytes(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype);
+int attn_decode(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache,
+                const int *lens, int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype,
+                void *workspace, void *stream);
+
 /* ---- the block --------------------------------------------------------- */
 typedef struct {
     int B, T, C, NH, NKV, H; /* H = MLP hidden width */
@@ -298,8 +330,10 @@ const char *dtb_version(void);
 /* Optional per-kernel timing for measurement: while enabled, every kernel the
  * library enqueues is bracketed by HIP events on its stream, grouped by kernel
  * class (0 forward-projection GEMMs, 1 attn_fwd, 2 attn_bwd, 3 elementwise,
- * 4 input-gradient GEMMs, 5 weight-gradient GEMMs), together with the
- * algorithmic flops / bytes of each launch.  dtb_timing_collect() waits for
+ * 4 input-gradient GEMMs, 5 weight-gradient GEMMs, 6 the decode-attention
+ * kernel, 7 its chunk merge), together with the algorithmic flops / bytes of
+ * each launch (0 for the decode-attention kernel, whose bytes depend on the
+ * cache lengths in device memory).  dtb_timing_collect() waits for
  * the recorded events, adds the elapsed times to the running totals and
  * returns the number of classes filled (at most max_classes).  Not for use
  * under graph capture. */
