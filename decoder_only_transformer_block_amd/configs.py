@@ -52,6 +52,8 @@ class BlockConfig:
     embed_norm: bool = False
     final_norm: bool = True
     tied_head: bool = False
+    # K prediction heads: head j at position t predicts token t+1+j
+    mtp: int = 1
 
     @property
     def hd(self) -> int:
@@ -212,8 +214,10 @@ def block_weights(cfg: BlockConfig, layer: int, perturb: bool = False) -> dict:
 
 
 def token_ids(cfg: BlockConfig) -> np.ndarray:
-    """T+1 ids per sequence (the last one is only a shifted target)."""
-    return inputs.ids(cfg.seed, "ids", cfg.B * (cfg.T + 1), cfg.vocab).reshape(cfg.B, cfg.T + 1)
+    """T+K ids per sequence for K = cfg.mtp prediction heads (the last K are
+    only targets)."""
+    n = cfg.T + cfg.mtp
+    return inputs.ids(cfg.seed, "ids", cfg.B * n, cfg.vocab).reshape(cfg.B, n)
 
 
 def block_input(cfg: BlockConfig) -> np.ndarray:
@@ -232,8 +236,8 @@ def block_dout(cfg: BlockConfig, std: float = 1.0) -> np.ndarray:
 def harness_weights(cfg: BlockConfig, perturb: bool = False) -> dict:
     """Seeded harness parameters: token embedding 'wte' [vocab, C] (the same
     seeded matrix whose rows block_input picks), position table 'wpe' [T, C],
-    final-norm 'gf' / 'bf' and LM head 'head' [vocab, C] as the configuration
-    has them.  Matrices ~ N(0, std^2); gamma 1 and beta 0 unless perturb."""
+    final-norm 'gf' / 'bf' and LM head 'head' [mtp*vocab, C] (head j = rows
+    j*vocab ..) as the configuration has them.  Matrices ~ N(0, std^2); gamma 1 and beta 0 unless perturb."""
     V, C = cfg.vocab, cfg.C
     out = {"wte": inputs.tensor(cfg.seed, "E", (V, C), std=cfg.std, dtype=cfg.dtype)}
     if cfg.wpe:
@@ -245,7 +249,7 @@ def harness_weights(cfg: BlockConfig, perturb: bool = False) -> dict:
         out["bf"] = (inputs.tensor(cfg.seed, "bf", (C,), std=0.02, dtype=cfg.dtype)
                      if perturb else inputs.const((C,), 0.0))
     if not cfg.tied_head:
-        out["head"] = inputs.tensor(cfg.seed, "head", (V, C), std=cfg.std, dtype=cfg.dtype)
+        out["head"] = inputs.tensor(cfg.seed, "head", (cfg.mtp * V, C), std=cfg.std, dtype=cfg.dtype)
     return out
 
 

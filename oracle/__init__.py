@@ -339,6 +339,33 @@ def softmax_ce(logits, targets, scale):
     return loss, dl, rl
 
 
+def mtp_targets(ids, T, K):
+    """Targets of K prediction heads ("nanoeuler — CUDA kernels": the batch
+    fills K targets per position): head j at position t predicts token t+1+j.
+    ids [B, T+K] -> [B, T, K] int32."""
+    ids = np.asarray(ids)
+    return np.stack([ids[:, 1 + j:T + 1 + j] for j in range(K)], axis=-1).astype(np.int32)
+
+
+def mtp_head_ce(inp, w, targets, K, scale):
+    """The LM head with K prediction heads and its softmax cross-entropy
+    ("nanoeuler — CUDA kernels": the head GEMM with K*V output columns, the
+    softmax_ce kernel over every (position, head) row of V logits, the head's
+    matmul backward).  inp [R, C]; w [K*V, C] (head j = rows j*V .. j*V+V-1);
+    targets [R, K] (negative: masked); loss = scale * sum of the unmasked row
+    losses.  Returns (loss, row_loss [R, K], dinp [R, C], dw [K*V, C],
+    dlogits [R, K*V])."""
+    inp, w = _d(inp), _d(w)
+    R = inp.shape[0]
+    V = w.shape[0] // K
+    assert w.shape[0] == K * V
+    logits = linear_forward(inp, w)
+    loss, dl, rl = softmax_ce(logits.reshape(R * K, V), np.asarray(targets).reshape(R * K), scale)
+    dl = dl.reshape(R, K * V)
+    dinp, dw, _ = linear_backward(dl, inp, w)
+    return loss, rl.reshape(R, K), dinp, dw, dl
+
+
 def model_step(cfg, layer_weights, hw: dict, ids):
     """Loss and every gradient of the whole model for one batch.
 
@@ -348,11 +375,15 @@ def model_step(cfg, layer_weights, hw: dict, ids):
     the blocks' kind (gamma hw['gf'], beta hw['bf']) if cfg.final_norm, the LM
     head hw['head'] [V, C] (hw['wte'] itself if cfg.tied_head) and the mean
     softmax cross-entropy over the B*T positions with targets ids[:, t+1].
-    Returns (loss, grads: dict of harness gradients, per-layer block gradients,
+    With cfg.mtp = K > 1 prediction heads, hw['head'] is [K*V, C], ids are
+    [B, T+K], head j predicts ids[:, t+1+j] and the mean runs over the B*T*K
+    (position, head) pairs.  Returns (loss, grads: dict of harness gradients, per-layer block gradients,
     extras: logits, dlogits, row losses and the final hidden state)."""
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     B, T = cfg.B, cfg.T
-    inp, tgt = ids[:, :T], ids[:, 1:T + 1]
+    K = getattr(cfg, "mtp", 1)
+    assert K == 1 or not cfg.tied_head
+    inp, tgt = ids[:, :T], mtp_targets(ids, T, K)
     V = hw["wte"].shape[0]
     x = embed_forward(inp, hw["wte"], hw.get("wpe") if cfg.wpe else None)
     if cfg.embed_norm:
@@ -370,9 +401,10 @@ def model_step(cfg, layer_weights, hw: dict, ids):
     else:
         nf = h
     head = hw["wte"] if cfg.tied_head else hw["head"]
+    loss, rows, dnf, dhead, dlogits = mtp_head_ce(nf.reshape(B * T, -1), head, tgt.reshape(B * T, K), K,
+                                                  1.0 / (B * T * K))
     logits = linear_forward(nf, head)
-    loss, dlogits, rows = softmax_ce(logits.reshape(B * T, V), tgt, 1.0 / (B * T))
-    dnf, dhead, _ = linear_backward(dlogits.reshape(B, T, V), nf, head)
+    dnf = dnf.reshape(nf.shape)
     grads = {}
     if cfg.final_norm:
         g, dgf, dbf = norm_backward(cfg.norm, dnf, h, hw.get("gf"), rf, mf)
@@ -395,7 +427,8 @@ def model_step(cfg, layer_weights, hw: dict, ids):
     grads["wte"] = dwte
     if cfg.wpe:
         grads["wpe"] = dwpe
-    extras = SimpleNamespace(logits=logits.reshape(B * T, V), dlogits=dlogits, rows=rows, nf=nf.reshape(B * T, -1))
+    extras = SimpleNamespace(logits=logits.reshape(B * T, K * V), dlogits=dlogits, rows=rows.reshape(-1),
+                             nf=nf.reshape(B * T, -1))
     return loss, grads, bgrads, extras
 
 

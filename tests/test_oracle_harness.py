@@ -124,13 +124,13 @@ FAMILIES = {
 }
 
 
-def make_model(fam, L=2, B=2, T=6, C=8, NH=2, NKV=1, H=12, V=13):
+def make_model(fam, L=2, B=2, T=6, C=8, NH=2, NKV=1, H=12, V=13, K=1):
     f = FAMILIES[fam]
     c = SimpleNamespace(B=B, T=T, C=C, NH=NH, NKV=NKV, H=H, norm=f["norm"], mlp=f["mlp"], rope=f["rope"],
                         rope_base=1e4 if f["rope"] == "neox" else 0.0, eps=1e-5, qkv_bias=f["bias"],
                         o_bias=f["bias"] and fam == "gpt2", mlp_bias=f["bias"] and fam == "gpt2",
                         wpe=f["wpe"], embed_norm=f["embed_norm"], final_norm=f["final_norm"],
-                        tied_head=f["tied"])
+                        tied_head=f["tied"], mtp=K)
     lw = [make_weights(c, scale=0.5) for _ in range(L)]
     hw = {"wte": rng.standard_normal((V, C))}
     if c.wpe:
@@ -140,17 +140,18 @@ def make_model(fam, L=2, B=2, T=6, C=8, NH=2, NKV=1, H=12, V=13):
         if c.norm == "layer":
             hw["bf"] = 0.2 * rng.standard_normal(C)
     if not c.tied_head:
-        hw["head"] = rng.standard_normal((V, C))
-    ids = rng.integers(0, V, (B, T + 1)).astype(np.int32)
+        hw["head"] = rng.standard_normal((K * V, C))
+    ids = rng.integers(0, V, (B, T + K)).astype(np.int32)
     return c, lw, hw, ids
 
 
 def torch_model(c, lw, hw, ids):
     """Independent float64 model: torch embedding, the torch block, norms,
     linear head, mean cross_entropy."""
-    T = c.T
+    T, K = c.T, getattr(c, "mtp", 1)
     inp = torch.tensor(ids[:, :T], dtype=torch.long)
-    tgt = torch.tensor(ids[:, 1:], dtype=torch.long)
+    # head j at position t predicts token t + 1 + j
+    tgt = torch.stack([torch.tensor(ids[:, 1 + j:T + 1 + j], dtype=torch.long) for j in range(K)], dim=-1)
     x = F.embedding(inp, hw["wte"])
     if c.wpe:
         x = x + hw["wpe"][None]
@@ -162,7 +163,8 @@ def torch_model(c, lw, hw, ids):
         x = F.layer_norm(x, (c.C,), hw["gf"], hw.get("bf"), c.eps) if c.norm == "layer" else \
             F.rms_norm(x, (c.C,), hw.get("gf"), c.eps)
     logits = F.linear(x, hw["wte"] if c.tied_head else hw["head"])
-    return F.cross_entropy(logits.reshape(-1, logits.shape[-1]), tgt.reshape(-1))
+    V = logits.shape[-1] // K
+    return F.cross_entropy(logits.reshape(-1, V), tgt.reshape(-1))
 
 
 @pytest.mark.parametrize("fam", list(FAMILIES))
@@ -180,6 +182,57 @@ def test_model_vs_torch_autograd(orc, fam):
     for l in range(len(lw)):
         for k in lw[l]:
             assert rel(bgrads[l][k], lwt[l][k].grad.numpy()) < 1e-10, (l, k)
+
+
+@pytest.mark.parametrize("fam", ["qwen2", "llama"])
+def test_model_mtp_vs_torch_autograd(orc, fam):
+    """Three prediction heads: the loss is the mean over (position, head)
+    pairs, head j predicting token t + 1 + j."""
+    c, lw, hw, ids = make_model(fam, K=3)
+    loss, grads, bgrads, ex = orc.model_step(c, lw, hw, ids)
+    lwt = [{k: torch.tensor(v, requires_grad=True) for k, v in w.items()} for w in lw]
+    hwt = {k: torch.tensor(v, requires_grad=True) for k, v in hw.items()}
+    lt = torch_model(c, lwt, hwt, ids)
+    lt.backward()
+    assert abs(loss - lt.item()) < 1e-12 * max(1.0, abs(loss))
+    for k in hw:
+        assert rel(grads[k], hwt[k].grad.numpy()) < 1e-10, k
+    for l in range(len(lw)):
+        for k in lw[l]:
+            assert rel(bgrads[l][k], lwt[l][k].grad.numpy()) < 1e-10, (l, k)
+
+
+def test_mtp_targets_definition(orc):
+    ids = np.arange(2 * 9, dtype=np.int32).reshape(2, 9)
+    t = orc.mtp_targets(ids, 6, 3)
+    for b in range(2):
+        for pos in range(6):
+            for j in range(3):
+                assert t[b, pos, j] == ids[b, pos + 1 + j]
+
+
+def test_mtp_head_ce_sft_masking_and_closed_form(orc):
+    """Masked (position, head) pairs as in supervised fine-tuning (prompt and
+    padding targets -1, scale 1 / number of supervised targets) against torch
+    float64 autograd; zero head weights give ln V per supervised target."""
+    R, C, V, K = 7, 5, 11, 4
+    inp = rng.standard_normal((R, C))
+    w = rng.standard_normal((K * V, C))
+    tgt = rng.integers(0, V, (R, K)).astype(np.int32)
+    tgt[:2] = -1          # prompt positions
+    tgt[5:, 2:] = -1      # targets past the end of the example
+    nsup = int((tgt >= 0).sum())
+    loss, rows, dinp, dw, dl = orc.mtp_head_ce(inp, w, tgt, K, 1.0 / nsup)
+    it = torch.tensor(inp, requires_grad=True)
+    wt = torch.tensor(w, requires_grad=True)
+    lg = F.linear(it, wt).reshape(R * K, V)
+    ref = F.cross_entropy(lg, torch.tensor(tgt.reshape(-1), dtype=torch.long), ignore_index=-1, reduction="sum") / nsup
+    ref.backward()
+    assert abs(loss - ref.item()) < 1e-13
+    assert rel(dinp, it.grad.numpy()) < 1e-12 and rel(dw, wt.grad.numpy()) < 1e-12
+    assert np.all(rows[tgt < 0] == 0)
+    loss0, _, dinp0, _, _ = orc.mtp_head_ce(inp, np.zeros_like(w), tgt, K, 1.0 / nsup)
+    assert abs(loss0 - np.log(V)) < 1e-14 and not dinp0.any()
 
 
 @pytest.mark.parametrize("fam", ["microgpt", "gpt2"])
