@@ -113,7 +113,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_gqa",
                     choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw",
-                             "head_ce", "decode"])
+                             "head_ce", "decode", "mtp_head"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -308,6 +308,37 @@ def bench_head_ce(args):
     return out, R, C, V, ws.numel(), logits.numel() * 2
 
 
+def bench_mtp_head(args, K=4):
+    """Four prediction heads on the Llama-GQA head (R = 16384 positions,
+    C = 2048, V = 32000 per head, bf16) through the fused, vocabulary-chunked
+    head + cross-entropy (4096-row chunks): loss, dinp and the head gradient."""
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    cfg = configs.LLAMA_GQA
+    R, C, V = cfg.B * cfg.T, cfg.C, cfg.vocab
+    g = torch.Generator(device="cuda").manual_seed(5)
+    inp = torch.randn(R, C, device="cuda", generator=g).bfloat16()
+    w = (torch.randn(K * V, C, device="cuda", generator=g) * 0.02).bfloat16()
+    tgt = torch.randint(0, V, (R, K), device="cuda", generator=g, dtype=torch.int32)
+    loss = torch.empty(1, device="cuda")
+    rows = torch.empty(R * K, device="cuda")
+    dinp = torch.empty(R, C, device="cuda", dtype=torch.bfloat16)
+    dw = torch.zeros(K * V, C, device="cuda")
+    ws = torch.empty(binding.lm_head_ce_workspace_bytes(R, C, V, 4096, "bf16"), dtype=torch.uint8, device="cuda")
+
+    def one():
+        binding.lm_head_mtp_ce(loss, rows, dinp, dw, inp, w, tgt, R, C, V, K, 4096, 1.0 / (R * K), "bf16", ws)
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) / args.steps * 1e3, R, C, V, K, ws.numel()
+
+
 def bench_decode(args):
     """Decode attention over the Llama-GQA heads: 256 sequences, cache lengths
     uniform in [1, 4096] (capacity 4096), one new query per sequence, bf16.
@@ -415,6 +446,22 @@ def main():
             "unfused_tflops_3gemm": round(3 * fl / (t["unfused"] * 1e-3) / 1e12, 2),
             "workspace_bytes_fused": ws_bytes, "logits_bytes_unfused": logit_bytes,
             "cpu_baseline": None}), flush=True)
+        return
+    if args.workload == "mtp_head":
+        ms, R, C, V, K, ws_bytes = bench_mtp_head(args)
+        fl = 4 * 2.0 * R * C * V * K  # four head-sized GEMMs per head (two passes, dinp, dW)
+        tf = fl / (ms * 1e-3) / 1e12
+        print(json.dumps({
+            "metric": "multi-token-prediction head + cross-entropy forward and backward tokens/s (fused, chunked)",
+            "value": round(R / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"Llama-GQA head with K={K} prediction heads: R=16384 positions, C=2048, "
+                                   "V=32000 per head, chunk 4096"},
+            "roofline": {"kernel": "lm_head_mtp_ce (four GEMMs of one head's size per head)", "bound": "mfma",
+                         "achieved": round(tf, 2), "peak": 2500.0, "unit": "TFLOP/s", "frac": round(tf / 2500.0, 4),
+                         "traffic": None},
+            "workspace_bytes": ws_bytes, "cpu_baseline": None}), flush=True)
         return
     if args.workload == "decode":
         cfg, ms, tim, kv_bytes, q_bytes, ntok, ws_bytes, cpu = bench_decode(args)

@@ -95,6 +95,7 @@ def lib() -> ctypes.CDLL:
         L.lm_head_workspace_bytes.restype = z
         L.softmax_ce.argtypes = [v, v, v, v, i, v, i, i, f, i, v]
         L.lm_head_ce.argtypes = [v, v, v, v, v, v, v, i, i, i, i, f, i, v, v]
+        L.lm_head_mtp_ce.argtypes = [v, v, v, v, v, v, v, i, i, i, i, i, f, i, v, v]
         L.lm_head_ce_workspace_bytes.argtypes = [i, i, i, i, i]
         L.lm_head_ce_workspace_bytes.restype = z
         L.adamw_update.argtypes = [v, v, v, v, v, ctypes.c_longlong, f, f, f, f, f, i, i, i, v]
@@ -229,6 +230,13 @@ def softmax_ce(loss, row_loss, dlogits, logits, ldl, targets, R, V, scale, dtype
 def lm_head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, vchunk, scale, dtype, workspace, stream=None):
     check(lib().lm_head_ce(_ptr(loss), _ptr(row_loss), _ptr(dinp), _ptr(dw), _ptr(inp), _ptr(w), _ptr(targets), R, C,
                            V, vchunk, float(scale), DTYPE[dtype], _ptr(workspace), _stream(stream)), "lm_head_ce")
+
+
+def lm_head_mtp_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, K, vchunk, scale, dtype, workspace,
+                   stream=None):
+    check(lib().lm_head_mtp_ce(_ptr(loss), _ptr(row_loss), _ptr(dinp), _ptr(dw), _ptr(inp), _ptr(w), _ptr(targets),
+                               R, C, V, K, vchunk, ctypes.c_float(scale), DTYPE[dtype], _ptr(workspace),
+                               _stream(stream)), "lm_head_mtp_ce")
 
 
 def lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype) -> int:

@@ -509,8 +509,24 @@ int lm_head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *
     if (R > 0 && (!ptr_ok(row_loss) || !ptr_ok(inp) || !ptr_ok(w) || !aligned4(targets) || !ptr_ok(workspace)))
         return DTB_EINVAL_PTR;
     if ((dinp && !aligned(dinp)) || (dw && !aligned(dw))) return DTB_EINVAL_PTR;
-    return head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, head_chunk(V, vchunk), scale, dtype, workspace,
-                   (hipStream_t)stream);
+    return head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, 1, head_chunk(V, vchunk), scale, dtype,
+                   workspace, (hipStream_t)stream);
+}
+
+int lm_head_mtp_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w,
+                   const int *targets, int R, int C, int V, int K, int vchunk, float scale, int dtype, void *workspace,
+                   void *stream) {
+    int e = check_head_ce(R, C, V, vchunk, dtype);
+    if (e) return e;
+    if (K < 1 || (long long)K * V >= (1LL << 31) || (long long)K * V * C >= (1LL << 40) ||
+        (long long)R * K >= (1LL << 31))
+        return DTB_EINVAL_SHAPE;
+    if (!ptr_ok(loss)) return DTB_EINVAL_PTR;
+    if (R > 0 && (!ptr_ok(row_loss) || !ptr_ok(inp) || !ptr_ok(w) || !aligned4(targets) || !ptr_ok(workspace)))
+        return DTB_EINVAL_PTR;
+    if ((dinp && !aligned(dinp)) || (dw && !aligned(dw))) return DTB_EINVAL_PTR;
+    return head_ce(loss, row_loss, dinp, dw, inp, w, targets, R, C, V, K, head_chunk(V, vchunk), scale, dtype,
+                   workspace, (hipStream_t)stream);
 }
 
 int adamw_update(float *params, float *grads, float *m, float *v, void *params_lowp, long long n, float lr,

@@ -270,8 +270,9 @@ int embed_fwd(int dtype, const int *ids, const void *wte, const void *wpe, long 
 int embed_bwd(int dtype, const int *ids, const void *dx, int B, int T, int C, int V, float *dwte, float *dwpe,
               hipStream_t s);
 size_t head_ce_ws_bytes(int R, int C, int V, int vc, int dtype);
+// K prediction heads: w [K*V, C], targets and row_loss [R][K]
 int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w, const int *targets,
-            int R, int C, int V, int vc, float scale, int dtype, void *workspace, hipStream_t s);
+            int R, int C, int V, int K, int vc, float scale, int dtype, void *workspace, hipStream_t s);
 int adamw(float *p, float *g, float *m, float *v, void *lowp, long long n, float lr, float b1, float b2, float eps,
           float wd, int t, int zero_g, hipStream_t s);
 int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *targets, long R, int V, float scale,

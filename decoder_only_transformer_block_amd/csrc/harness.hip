@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void loss_sum_kernel(const float *rows, long R
 // pass 1: one workgroup per row
 template <typename T>
 __global__ __launch_bounds__(256) void ce_chunk_stats_kernel(const T *lg, long ldc, int vc, int v0, const int *targets,
-                                                             float *rm, float *rs, float *tl, int first) {
+                                                             int ts, float *rm, float *rs, float *tl, int first) {
     constexpr int EPC = 16 / sizeof(T);
     const long r = blockIdx.x;
     const T *l = lg + r * ldc;
@@ -232,34 +232,36 @@ __global__ __launch_bounds__(256) void ce_chunk_stats_kernel(const T *lg, long l
         if (!first) lse_merge(m, s, rm[r], rs[r]);
         rm[r] = m;
         rs[r] = s;
-        const int tg = targets[r];
+        const int tg = targets[r * ts];
         if (tg >= v0 && tg < v0 + vc) tl[r] = to_f32(l[tg - v0]);
     }
 }
 
 // after pass 1: lse (+inf for a masked row, so its gradient comes out zero)
-// and the row losses
+// and the row losses (targets and row losses at stride ts: one prediction
+// head of several)
 __global__ __launch_bounds__(256) void ce_finish_kernel(const float *rm, const float *rs, const float *tl,
-                                                        const int *targets, long R, int V, float *lse, float *row_loss) {
+                                                        const int *targets, int ts, long R, int V, float *lse,
+                                                        float *row_loss) {
     const long r = (long)blockIdx.x * 256 + threadIdx.x;
     if (r >= R) return;
-    const int tg = targets[r];
+    const int tg = targets[r * ts];
     const bool masked = tg < 0 || tg >= V;
     const float l = rm[r] + logf(rs[r]);
     lse[r] = masked ? INFINITY : l;
-    row_loss[r] = masked ? 0.f : l - tl[r];
+    row_loss[r * ts] = masked ? 0.f : l - tl[r];
 }
 
 // pass 2: the chunk's logits become scale * (exp(l - lse) - onehot) in place,
 // zeros in the padded columns; one workgroup per row
 template <typename T>
 __global__ __launch_bounds__(256) void ce_chunk_grad_kernel(T *lg, long ldc, int vc, int v0, const int *targets,
-                                                            const float *lse, float scale) {
+                                                            int ts, const float *lse, float scale) {
     constexpr int EPC = 16 / sizeof(T);
     const long r = blockIdx.x;
     T *l = lg + r * ldc;
     const float ls = lse[r];
-    const int tg = targets[r] - v0;
+    const int tg = targets[r * ts] - v0;
     const int nvl = (int)(ldc / EPC);
     for (int c = threadIdx.x; c < nvl; c += 256) {
         float v[EPC], o[EPC];
@@ -423,7 +425,7 @@ size_t head_ce_ws_bytes(int R, int C, int V, int vc, int dtype) {
 }
 
 int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w, const int *targets,
-            int R, int C, int V, int vc, float scale, int dtype, void *workspace, hipStream_t s) {
+            int R, int C, int V, int K, int vc, float scale, int dtype, void *workspace, hipStream_t s) {
     const size_t es = dtype == DTB_BF16 ? 2 : 4;
     const long ldc = ((long)vc + 7) / 8 * 8;
     char *ws = static_cast<char *>(workspace);
@@ -445,75 +447,81 @@ int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp
         DTB_LAUNCH_CHECK("lm_head_ce loss");
         return DTB_OK;
     }
-    const bf16 *wb = static_cast<const bf16 *>(w);
-    const float *wf = static_cast<const float *>(w);
-    auto wchunk = [&](int v0) -> const void * {
-        return dtype == DTB_BF16 ? static_cast<const void *>(wb + (long)v0 * C) : static_cast<const void *>(wf + (long)v0 * C);
-    };
-    auto logits = [&](int v0, int n) {
-        GemmArgs g{};
-        g.dtype = dtype;
-        g.a_kmajor = g.b_kmajor = true;
-        g.A = inp; g.lda = C; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = n; g.K = C;
-        g.out = chunk; g.ldo = ldc;
-        return gemm(g, nullptr, 0, s);
-    };
-    // pass 1
-    for (int v0 = 0, i = 0; v0 < V; v0 += vc, i++) {
-        const int n = V - v0 < vc ? V - v0 : vc;
-        int r = logits(v0, n);
-        if (r) return r;
-        if (dtype == DTB_BF16)
-            hipLaunchKernelGGL(ce_chunk_stats_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)chunk, ldc,
-                               n, v0, targets, rm, rs, tl, i == 0);
-        else
-            hipLaunchKernelGGL(ce_chunk_stats_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (const float *)chunk,
-                               ldc, n, v0, targets, rm, rs, tl, i == 0);
-        DTB_LAUNCH_CHECK("lm_head_ce stats");
-    }
-    hipLaunchKernelGGL(ce_finish_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, rm, rs, tl, targets,
-                       (long)R, V, lse, row_loss);
-    DTB_LAUNCH_CHECK("lm_head_ce finish");
-    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, (long)R, scale, loss);
-    DTB_LAUNCH_CHECK("lm_head_ce loss");
-    if (!dinp && !dw) return DTB_OK;
+    const bool grads = dinp || dw;
     if (dacc) {
         const long long n4 = (long long)R * C / 4;
         hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc, n4);
         DTB_LAUNCH_CHECK("lm_head_ce zero");
     }
-    // pass 2
-    for (int v0 = 0; v0 < V; v0 += vc) {
-        const int n = V - v0 < vc ? V - v0 : vc;
-        int r = logits(v0, n);
-        if (r) return r;
-        if (dtype == DTB_BF16)
-            hipLaunchKernelGGL(ce_chunk_grad_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (bf16 *)chunk, ldc, n,
-                               v0, targets, lse, scale);
-        else
-            hipLaunchKernelGGL(ce_chunk_grad_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (float *)chunk, ldc, n,
-                               v0, targets, lse, scale);
-        DTB_LAUNCH_CHECK("lm_head_ce gradient");
-        if (dacc) {  // dinp += dlogits_chunk W_chunk
+    // head j: vocabulary rows j*V .. j*V+V-1 of w, targets[r*K + j], row_loss[r*K + j]
+    for (int j = 0; j < K; j++) {
+        const long long w0 = (long long)j * V;
+        const int *tj = targets + j;
+        auto wchunk = [&](int v0) -> const void * {
+            const long long off = (w0 + v0) * C;
+            return dtype == DTB_BF16 ? static_cast<const void *>(static_cast<const bf16 *>(w) + off)
+                                     : static_cast<const void *>(static_cast<const float *>(w) + off);
+        };
+        auto logits = [&](int v0, int n) {
             GemmArgs g{};
             g.dtype = dtype;
-            g.a_kmajor = true;
-            g.b_kmajor = false;
-            g.A = chunk; g.lda = ldc; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = C; g.K = n;
-            g.out = dacc; g.ldo = C; g.out_f32 = g.accumulate = true;
-            r = gemm(g, gws, gws_bytes, s);
+            g.a_kmajor = g.b_kmajor = true;
+            g.A = inp; g.lda = C; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = n; g.K = C;
+            g.out = chunk; g.ldo = ldc;
+            return gemm(g, nullptr, 0, s);
+        };
+        // pass 1: running max / sum of exp over the head's vocabulary chunks
+        for (int v0 = 0, i = 0; v0 < V; v0 += vc, i++) {
+            const int n = V - v0 < vc ? V - v0 : vc;
+            int r = logits(v0, n);
             if (r) return r;
+            if (dtype == DTB_BF16)
+                hipLaunchKernelGGL(ce_chunk_stats_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)chunk,
+                                   ldc, n, v0, tj, K, rm, rs, tl, i == 0);
+            else
+                hipLaunchKernelGGL(ce_chunk_stats_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
+                                   (const float *)chunk, ldc, n, v0, tj, K, rm, rs, tl, i == 0);
+            DTB_LAUNCH_CHECK("lm_head_ce stats");
         }
-        if (dw) {  // dw[v0 .. v0+n) += dlogits_chunk^T inp
-            GemmArgs g{};
-            g.dtype = dtype;
-            g.a_kmajor = g.b_kmajor = false;
-            g.A = chunk; g.lda = ldc; g.B = inp; g.ldb = C; g.M = n; g.N = C; g.K = R;
-            g.out = dw + (long)v0 * C; g.ldo = C; g.out_f32 = g.accumulate = true;
-            r = gemm(g, gws, gws_bytes, s);
+        hipLaunchKernelGGL(ce_finish_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, rm, rs, tl, tj, K,
+                           (long)R, V, lse, row_loss + j);
+        DTB_LAUNCH_CHECK("lm_head_ce finish");
+        if (!grads) continue;
+        // pass 2: recompute each chunk, turn it into the gradient, apply it
+        for (int v0 = 0; v0 < V; v0 += vc) {
+            const int n = V - v0 < vc ? V - v0 : vc;
+            int r = logits(v0, n);
             if (r) return r;
+            if (dtype == DTB_BF16)
+                hipLaunchKernelGGL(ce_chunk_grad_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (bf16 *)chunk, ldc,
+                                   n, v0, tj, K, lse, scale);
+            else
+                hipLaunchKernelGGL(ce_chunk_grad_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (float *)chunk,
+                                   ldc, n, v0, tj, K, lse, scale);
+            DTB_LAUNCH_CHECK("lm_head_ce gradient");
+            if (dacc) {  // dinp += dlogits_chunk W_chunk
+                GemmArgs g{};
+                g.dtype = dtype;
+                g.a_kmajor = true;
+                g.b_kmajor = false;
+                g.A = chunk; g.lda = ldc; g.B = wchunk(v0); g.ldb = C; g.M = R; g.N = C; g.K = n;
+                g.out = dacc; g.ldo = C; g.out_f32 = g.accumulate = true;
+                r = gemm(g, gws, gws_bytes, s);
+                if (r) return r;
+            }
+            if (dw) {  // dw[j*V + v0 ..) += dlogits_chunk^T inp
+                GemmArgs g{};
+                g.dtype = dtype;
+                g.a_kmajor = g.b_kmajor = false;
+                g.A = chunk; g.lda = ldc; g.B = inp; g.ldb = C; g.M = n; g.N = C; g.K = R;
+                g.out = dw + (w0 + v0) * C; g.ldo = C; g.out_f32 = g.accumulate = true;
+                r = gemm(g, gws, gws_bytes, s);
+                if (r) return r;
+            }
         }
     }
+    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, (long)R * K, scale, loss);
+    DTB_LAUNCH_CHECK("lm_head_ce loss");
     if (dinp && dtype == DTB_BF16) {
         const long long n4 = (long long)R * C / 4;
         hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc,

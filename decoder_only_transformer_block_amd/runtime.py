@@ -127,8 +127,10 @@ class Model:
     position) embedding, the embedding RMSNorm (cfg.embed_norm), the block
     stack, the final norm (cfg.final_norm), the LM head (tied to the token
     table if cfg.tied_head) and the mean softmax cross-entropy over the B*T
-    positions with targets ids[:, t+1].  Every step runs in libdtb through the
-    C ABI; torch only holds the buffers."""
+    positions with targets ids[:, t+1] (with cfg.mtp = K > 1 prediction
+    heads: head j predicts ids[:, t+1+j], mean over the B*T*K pairs, through
+    the fused head).  Every step runs in libdtb through the C ABI; torch only
+    holds the buffers."""
 
     def __init__(self, cfg, layer_weights, harness_weights: dict, device="cuda", vchunk=None):
         """vchunk None: the head's logits for the whole vocabulary are
@@ -137,6 +139,9 @@ class Model:
         (lm_head_ce) with chunks of vchunk rows (0: the library's default)."""
         import torch
         self.cfg = cfg
+        self.K = getattr(cfg, "mtp", 1)
+        if self.K > 1 and vchunk is None:
+            vchunk = 0  # several heads: the fused head + cross-entropy
         self.vchunk = vchunk
         td = torch_dtype(cfg.dtype)
         # every parameter (block layers, then the harness) is a view of one
@@ -171,7 +176,7 @@ class Model:
         self.mf = torch.empty(R, dtype=torch.float32, device=device)
         self.logits = (torch.empty((R, self.ldl), dtype=td, device=device) if vchunk is None  # dlogits in place
                        else None)
-        self.rows = torch.empty(R, dtype=torch.float32, device=device)
+        self.rows = torch.empty(R * self.K, dtype=torch.float32, device=device)
         self.loss = torch.empty(1, dtype=torch.float32, device=device)
         self.dnf = torch.empty((B, T, C), dtype=td, device=device)
         self.dtop = torch.empty((B, T, C), dtype=td, device=device)
@@ -185,13 +190,16 @@ class Model:
         return self.hw["wte"] if self.cfg.tied_head else self.hw["head"]
 
     def step(self, ids, stream=None):
-        """ids: int32 device tensor [B, T+1].  Forward and backward of the
-        whole model; returns the loss tensor [1] (gradients accumulate)."""
+        """ids: int32 device tensor [B, T+K] (K = cfg.mtp).  Forward and
+        backward of the whole model; returns the loss tensor [1] (gradients
+        accumulate)."""
+        import torch
         cfg, s = self.cfg, self.stack
-        B, T, C, V, dt = cfg.B, cfg.T, cfg.C, self.V, cfg.dtype
+        B, T, C, V, dt, K = cfg.B, cfg.T, cfg.C, self.V, cfg.dtype, self.K
         R = B * T
         inp = ids[:, :T].contiguous()
-        tgt = ids[:, 1:T + 1].contiguous()
+        # targets [B, T, K]: head j at position t predicts token t+1+j
+        tgt = torch.stack([ids[:, 1 + j:T + 1 + j] for j in range(K)], dim=-1).contiguous()
         self._inp = inp
         binding.encoder_forward(self.x, inp, self.hw["wte"], self.hw.get("wpe") if cfg.wpe else None,
                                 B, T, C, V, dt, stream)
@@ -214,9 +222,12 @@ class Model:
             # backward (self.logits now holds dlogits)
             binding.lm_head_backward(self.dnf, dhead, self.logits, self.ldl, nf, self._head_w(), R, C, V, dt,
                                      self.ws, stream)
-        else:
+        elif K == 1:
             binding.lm_head_ce(self.loss, self.rows, self.dnf, dhead, nf, self._head_w(), tgt, R, C, V, self.vchunk,
                                1.0 / R, dt, self.ws, stream)
+        else:
+            binding.lm_head_mtp_ce(self.loss, self.rows, self.dnf, dhead, nf, self._head_w(), tgt, R, C, V, K,
+                                   self.vchunk, 1.0 / (R * K), dt, self.ws, stream)
         dtop = self.dnf
         if cfg.final_norm:
             binding.norm_backward(self.dtop, self.hgrads.get("gf"), self.hgrads.get("bf"), self.dnf, h,

@@ -309,6 +309,23 @@ int lm_head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *
                int R, int C, int V, int vchunk, float scale, int dtype, void *workspace, void *stream);
 size_t lm_head_ce_workspace_bytes(int R, int C, int V, int vchunk, int dtype);
 
+/* lm_head_mtp_ce: lm_head_ce with K prediction heads ("nanoeuler — CUDA
+ * kernels": the head GEMM with K*V output columns and softmax_ce_kernel over
+ * every (position, head) row; its batches give head j at position t the token
+ * t+1+j as target, and supervised fine-tuning masks targets with -1):
+ *   w [K*V, C] dtype, head j = rows j*V .. j*V+V-1
+ *   targets [R][K] int32 (outside [0, V): masked), row_loss [R][K] fp32
+ *   loss[0] = scale * sum over (r, j) of row_loss   (1/(R K) for pretraining,
+ *             1/(number of unmasked targets) for fine-tuning)
+ *   dinp [R, C] = sum over heads of dlogits_j W_j   (dtype, OVERWRITTEN)
+ *   dw [K*V, C] += dlogits_j^T inp per head         (fp32, ACCUMULATED)
+ * The heads run one after another through the same workspace, so
+ * lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype) sizes it for any K.
+ * K = 1 is lm_head_ce. */
+int lm_head_mtp_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp, const void *w,
+                   const int *targets, int R, int C, int V, int K, int vchunk, float scale, int dtype,
+                   void *workspace, void *stream);
+
 /* ---- optimizer ----------------------------------------------------------------
  * adamw_update: one AdamW step over a flat buffer of n parameters ("nanoeuler —
  * CUDA kernels" adamw_kernel; llm.c gpt2_update; microgpt adam_update_param):

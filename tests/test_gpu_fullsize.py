@@ -195,3 +195,54 @@ def test_llama_gqa_model_full_size_chunked_head():
     a ragged last chunk of 3328)."""
     require_gpu()
     _model_full_size("llama_gqa", rows=[0, 1, 2047, 2048, 9000, 16383], vchunk=4096)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_mtp_head_full_size_sampled(dtype):
+    """Four prediction heads on the Llama-GQA head's full size (R = 16384
+    positions, C = 2048, V = 32000) through the fused head in the benchmark's
+    launch configuration (4096-row chunks): sampled rows of every head's loss
+    and of dinp against the oracle and the mean-loss identity.  In fp32 also
+    the property that each head's weight-gradient rows sum to zero over its
+    vocabulary (every softmax-gradient row sums to zero); in bf16 the stored
+    gradient chunk carries the rounding of its target entry, which breaks the
+    property at the 1e-3 level, so the small-size parity tests cover dW."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, configs, inputs
+    from decoder_only_transformer_block_amd.runtime import to_device, to_numpy, torch_dtype
+    cfg = configs.LLAMA_GQA
+    R, C, V, K = cfg.B * cfg.T, cfg.C, cfg.vocab, 4
+    announce(f"mtp head full size R={R} C={C} V={V} K={K} {dtype}")
+    inp = inputs.tensor(cfg.seed, "mtp_inp", (R, C), dtype=dtype)
+    w = inputs.tensor(cfg.seed, "mtp_head", (K * V, C), std=cfg.std, dtype=dtype)
+    tgt = inputs.ids(cfg.seed, "mtp_tgt", R * K, V).reshape(R, K)
+    inpd, wd = to_device(inp, dtype), to_device(w, dtype)
+    loss = torch.empty(1, device="cuda")
+    rows = torch.empty(R * K, device="cuda")
+    dinp = torch.empty((R, C), dtype=torch_dtype(dtype), device="cuda")
+    dw = torch.zeros((K * V, C), device="cuda")
+    ws = torch.empty(binding.lm_head_ce_workspace_bytes(R, C, V, 4096, dtype), dtype=torch.uint8, device="cuda")
+    scale = 1.0 / (R * K)
+    binding.lm_head_mtp_ce(loss, rows, dinp, dw, inpd, wd,
+                           torch.from_numpy(np.ascontiguousarray(tgt)).cuda(), R, C, V, K, 4096, scale, dtype, ws)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    got_rows = to_numpy(rows).reshape(R, K)
+    lossv = float(to_numpy(loss)[0])
+    check("mean rows", np.array([lossv]), np.array([got_rows.astype(np.float64).mean()]), tol)
+    pick = [0, 1, 4095, 4096, 9000, R - 1]
+    rl, rrows, rdinp, _, _ = oracle.mtp_head_ce(inp[pick], w, tgt[pick], K, scale)
+    check("row loss", got_rows[pick], rrows, tol)
+    check("dinp[rows]", to_numpy(dinp[pick]), rdinp, tol)
+    if dtype == "f32":
+        # Each gradient row sums to scale * (e^-d - 1) ~ -scale * d, d the fp32
+        # error of its lse (about 1e-5 at V = 32000); a column sum adds R such
+        # rows times N(0, 1) inputs: ~ scale * sqrt(R) * 1e-5 ~ 1.3e-3 scale,
+        # against max |dW| ~ 4 scale: a ratio near 3e-4.  A dropped or
+        # misplaced chunk gives O(0.1).
+        colsum = dw.reshape(K, V, C).double().sum(1)
+        ratio = (colsum.abs().max() / dw.abs().max()).item()
+        print(f"    max |sum_v dW| / max |dW| = {ratio:.2e}", flush=True)
+        assert ratio < 1e-3

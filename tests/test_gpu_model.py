@@ -169,6 +169,48 @@ def test_lm_head_ce_chunked(dtype, V, vchunk):
     check("dw", to_numpy(dw), rdw, tol)
 
 
+@pytest.mark.parametrize("dtype,V,K,vchunk,sft", [("f32", 1003, 3, 256, False), ("bf16", 997, 4, 256, True),
+                                                   ("bf16", 2048, 2, 512, False), ("f32", 300, 4, 0, True)])
+def test_lm_head_mtp_ce(dtype, V, K, vchunk, sft):
+    """K prediction heads through the fused, vocabulary-chunked head against
+    the oracle's definition (one head GEMM with K*V columns, the softmax
+    cross-entropy of every (position, head) row, the head's matmul backward).
+    Pretraining: every target live, scale 1/(R K).  Fine-tuning: prompt and
+    past-the-end targets masked with -1, scale 1/(supervised targets)."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_numpy
+    R, C = 300, 256
+    announce(f"lm_head_mtp_ce R={R} C={C} V={V} K={K} vchunk={vchunk} {dtype} sft={sft}")
+    inp = inputs.tensor(5, "inp", (R, C), dtype=dtype)
+    w = inputs.tensor(5, "w", (K * V, C), std=0.1, dtype=dtype)
+    tgt = inputs.ids(5, "tgt", R * K, V).reshape(R, K)
+    if sft:
+        tgt[:40] = -1                   # prompt positions
+        tgt[250:, 1:] = -1              # targets past the end of the example
+        tgt[123, 2] = -1
+    scale = 1.0 / max(int((tgt >= 0).sum()), 1) if sft else 1.0 / (R * K)
+    inpd, wd = _dev(inp, dtype), _dev(w, dtype)
+    loss = torch.empty(1, device="cuda")
+    rows = torch.empty(R * K, device="cuda")
+    dinp = torch.empty((R, C), dtype=inpd.dtype, device="cuda")
+    dw = torch.zeros((K * V, C), device="cuda")
+    ws = torch.empty(binding.lm_head_ce_workspace_bytes(R, C, V, vchunk, dtype), dtype=torch.uint8, device="cuda")
+    binding.lm_head_mtp_ce(loss, rows, dinp, dw, inpd, wd, _ids_dev(np.ascontiguousarray(tgt)), R, C, V, K, vchunk,
+                           scale, dtype, ws)
+    torch.cuda.synchronize()
+    rloss, rrows, rdinp, rdw, _ = oracle.mtp_head_ce(inp, w, tgt, K, scale)
+    tol = TOL[dtype]
+    got_rows = to_numpy(rows).reshape(R, K)
+    assert np.all(got_rows[tgt < 0] == 0)
+    check("row loss", got_rows, rrows, tol)
+    check("loss", to_numpy(loss), np.array([rloss]), tol)
+    check("dinp", to_numpy(dinp), rdinp, tol)
+    check("dw", to_numpy(dw), rdw, tol)
+
+
 def _models():
     from decoder_only_transformer_block_amd import configs as K
     return {
@@ -176,12 +218,17 @@ def _models():
         "mini_qwen2": K.MINI_QWEN2,
         "gpt2_reduced": K.GPT2_SMALL.replace(L=2, B=2, T=100, C=256, NH=4, NKV=4, H=1024, vocab=1003),
         "llama_gqa_reduced": K.LLAMA_GQA.replace(L=2, B=2, T=130, C=512, NH=8, NKV=2, H=1408, vocab=997),
+        # multi-token prediction: four heads (nanoeuler's K)
+        "mini_qwen2_mtp4": K.MINI_QWEN2.replace(mtp=4),
+        "llama_gqa_reduced_mtp3": K.LLAMA_GQA.replace(L=2, B=2, T=130, C=512, NH=8, NKV=2, H=1408, vocab=997,
+                                                      mtp=3),
     }
 
 
 @pytest.mark.parametrize("case,vchunk", [(c, None) for c in ("microgpt", "mini_qwen2", "gpt2_reduced",
                                                                "llama_gqa_reduced")] +
-                         [("gpt2_reduced", 256), ("llama_gqa_reduced", 256)])
+                         [("gpt2_reduced", 256), ("llama_gqa_reduced", 256), ("mini_qwen2_mtp4", None),
+                          ("llama_gqa_reduced_mtp3", 256)])
 def test_model_parity(case, vchunk):
     require_gpu()
     import torch
