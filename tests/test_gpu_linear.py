@@ -17,6 +17,9 @@ SHAPES = [
     ("dinp256", 1100, 6144, 136),           # input gradient on 5 x 24 tiles
     ("dw256_split", 600, 520, 776),         # weight gradient M=776, N=520 with split-K
     ("dw256_nosplit", 64, 1024, 2048),      # weight gradient M=2048, N=1024, K=64: one split
+    # more than one round of 256 x 256 tiles (ragged rows and columns, 17 x 17 tiles)
+    ("rounds_fwd", 4100, 384, 4352),        # forward on 289 tiles
+    ("rounds_dinp", 4100, 4352, 384),       # input gradient on 289 tiles
     ("generic_mid", 333, 264, 328),
     ("tiny", 7, 8, 16),
     ("one_row", 1, 64, 8),
@@ -66,3 +69,27 @@ def test_linear_rejects_bad_shapes():
     assert L.linear_forward(None, None, None, None, None, 4, 12, 16, 1, None) == -1   # K % 8
     assert L.linear_forward(None, None, None, None, None, 0, 16, 16, 1, None) == 0    # empty
     assert L.linear_workspace_bytes(4, 16, 16, 7) == 0
+
+
+def test_weight_grad_split8():
+    """The weight gradient of a 2048 x 2048 layer over 8192 rows: 64 tiles x 8
+    K splits of 1024 rows = 512 workgroups, then the split reduction.  Checked on a spread of output rows (dW[n] = sum_r
+    dy[r, n] x[r]) against the oracle's linear backward of those columns."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_device, to_numpy
+    R, K, N = 8192, 2048, 2048
+    announce(f"linear weight gradient (8 K splits) R={R} K={K} N={N} bf16")
+    x = inputs.tensor(11, "pw.x", (R, K), dtype="bf16")
+    w = inputs.tensor(11, "pw.w", (N, K), std=0.05, dtype="bf16")
+    dy = inputs.tensor(11, "pw.dy", (R, N), dtype="bf16")
+    X, W, DY = (to_device(a, "bf16") for a in (x, w, dy))
+    dw = torch.full((N, K), 0.5, dtype=torch.float32, device="cuda")
+    ws = torch.empty(binding.linear_workspace_bytes(R, K, N, "bf16"), dtype=torch.uint8, device="cuda")
+    binding.linear_backward(None, dw, None, DY, X, W, R, K, N, "bf16", ws)
+    torch.cuda.synchronize()
+    cols = np.array([0, 1, 255, 256, 511, 777, 1024, 1500, 2047])
+    _, r_dw, _ = oracle.linear_backward(dy[:, cols], x, w[cols])
+    check("dW[cols]", to_numpy(dw)[cols] - 0.5, r_dw, TOL["bf16"])
