@@ -553,7 +553,8 @@ template <bool AK, bool BKM, int MODE, int NW>
 __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
     constexpr int BM = 256, BN = 256, BK = 32;
     constexpr int WGN = 2, WGM = NW / WGN, TM = BM / WGM, FI = TM / 32, FJ = 4;
-    constexpr int BPW = 16 / NW;          // DMA blocks per operand per wave
+    constexpr int NDW = NW / 2;           // waves that issue the DMA (one per SIMD)
+    constexpr int BPD = 16 / NDW;         // DMA blocks per operand per DMA wave
     const int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
     int tm, tn;
     tile_coords(nm, nn, tm, tn);
@@ -577,10 +578,13 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
 
     // mode 5: B rows 0..127 of the tile are gate rows tn*128.., rows 128..255
     // the up rows act_H + tn*128.. (each wave's DMA blocks lie in one half)
-    const int nb0 = MODE == 5 ? (wave < NW / 2 ? tn * 128 : p.act_H + tn * 128 - 128) : n0;
+    const bool dmaw = wave < NDW;
+    const int nb0 = MODE == 5 ? (wave < NDW / 2 ? tn * 128 : p.act_H + tn * 128 - 128) : n0;
     auto issue = [&](char *st, int k0) {
-        dma_slab<AK, BPW>(st, gA, p.lda, m0, p.M, k0, kend, wave, lane);
-        dma_slab<BKM, BPW>(st + 16384, gB, p.ldb, nb0, p.N, k0, kend, wave, lane);
+        if (dmaw) {
+            dma_slab<AK, BPD>(st, gA, p.lda, m0, p.M, k0, kend, wave, lane);
+            dma_slab<BKM, BPD>(st + 16384, gB, p.ldb, nb0, p.N, k0, kend, wave, lane);
+        }
     };
     auto frags = [&](const char *st, int sidx, bf16x8 *af, bf16x8 *bfr) {
         const char *As = st, *Bs = st + 16384;
@@ -602,8 +606,12 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
         frags(st, 1, af, bfr);
         mma(af, bfr);
     };
-    // Main loop: whole groups of four slabs.  Step k waits until this wave's
-    // DMA of slab k+1 has landed (only slab k+2 may still be in flight), and
+    // Main loop: whole groups of four slabs.  One wave per SIMD (waves
+    // 0 .. NW/2-1) issues the whole operand DMA and the other wave of the SIMD
+    // none, so that one never stalls on a full texture-address FIFO and keeps
+    // the MFMAs fed (measured 1-3 % faster than every wave issuing a share).
+    // Step k waits until the DMA of slab k+1 has landed (only slab k+2 may
+    // still be in flight), and
     // the barrier makes that true for every wave and retires every wave's
     // reads of slab k-1, whose stage the step then refills with slab k+3.
     // The fragments of slab k's first k16 step were read during step k-1, so
@@ -613,53 +621,64 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
     // texture-address FIFO and stalled the issuing waves: measured 5-13 %
     // slower).  Past the end of K the loads are out of range and write zeros
     // into a stage that is no longer read, so every step has the same count.
-    constexpr int WAIT1 = wait_vm_lgkm0(2 * BPW);  // one younger slab in flight
+    constexpr int WAIT1 = wait_vm_lgkm0(2 * BPD);  // one younger slab in flight
     bf16x8 fa[FI], fb[FJ];
     // LDS reads of one k16 step and DMA instructions of one operand slab,
     // spread evenly over the 8 MFMAs of the other fragment set
     constexpr int NRD = FI * (AK ? 1 : 2) + FJ * (BKM ? 1 : 2);
     constexpr int NMM = FI * FJ;
-#define PIPE_PATTERN()                                                          \
+#define PIPE_PATTERN(NVM)                                                       \
     {                                                                           \
         _Pragma("unroll") for (int q = 0; q < NMM; q++) {                       \
             const int nr = ((q + 1) * NRD) / NMM - (q * NRD) / NMM;              \
             if (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      \
             if (nr > 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      \
-            const int nv = ((q + 1) * BPW) / NMM - (q * BPW) / NMM;              \
+            const int nv = ((q + 1) * (NVM)) / NMM - (q * (NVM)) / NMM;          \
             if (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  \
         }                                                                       \
     }
-#define DMA_STEP(S)                                                             \
+#define DMA_STEP(S, D)                                                          \
     {                                                                           \
         __builtin_amdgcn_s_waitcnt(WAIT1);                                      \
         asm volatile("s_barrier" ::: "memory");                                 \
         __builtin_amdgcn_sched_barrier(0);                                      \
         bf16x8 ga[FI], gb[FJ];                                                  \
         const int k3 = kbeg + (kt + S + 3) * BK;                                \
-        dma_slab<AK, BPW>(dma_stage<(S + 3) & 3>(), gA, p.lda, m0, p.M, k3, kend, wave, lane); \
+        if (D) dma_slab<AK, BPD>(dma_stage<(S + 3) & 3>(), gA, p.lda, m0, p.M, k3, kend, wave, lane); \
         frags(dma_stage<S>(), 1, ga, gb);                                       \
         mma(fa, fb);                                                            \
-        PIPE_PATTERN()                                                          \
+        PIPE_PATTERN((D) ? BPD : 0)                                             \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        dma_slab<BKM, BPW>(dma_stage<(S + 3) & 3>() + 16384, gB, p.ldb, nb0, p.N, k3, kend, wave, lane); \
+        if (D) dma_slab<BKM, BPD>(dma_stage<(S + 3) & 3>() + 16384, gB, p.ldb, nb0, p.N, k3, kend, wave, lane); \
         frags(dma_stage<(S + 1) & 3>(), 0, fa, fb);                             \
         mma(ga, gb);                                                            \
-        PIPE_PATTERN()                                                          \
+        PIPE_PATTERN((D) ? BPD : 0)                                             \
         __builtin_amdgcn_sched_barrier(0);                                      \
     }
     issue(dma_stage<0>(), kbeg);
     issue(dma_stage<1>(), kbeg + BK);
     issue(dma_stage<2>(), kbeg + 2 * BK);
-    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * BPW));
+    __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(4 * BPD));
     asm volatile("s_barrier" ::: "memory");
     frags(dma_stage<0>(), 0, fa, fb);
+    // one wave per SIMD issues the whole DMA, so the other wave of the SIMD
+    // never stalls on the texture-address FIFO and keeps the MFMAs fed
     int kt = 0;
-    for (; kt + 4 <= nk; kt += 4) {
-        DMA_STEP(0)
-        DMA_STEP(1)
-        DMA_STEP(2)
-        DMA_STEP(3)
+    if (dmaw) {
+        for (; kt + 4 <= nk; kt += 4) {
+            DMA_STEP(0, true)
+            DMA_STEP(1, true)
+            DMA_STEP(2, true)
+            DMA_STEP(3, true)
+        }
+    } else {
+        for (; kt + 4 <= nk; kt += 4) {
+            DMA_STEP(0, false)
+            DMA_STEP(1, false)
+            DMA_STEP(2, false)
+            DMA_STEP(3, false)
+        }
     }
 #undef DMA_STEP
 #undef PIPE_PATTERN
