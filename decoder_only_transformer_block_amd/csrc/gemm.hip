@@ -717,18 +717,36 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
     }
 }
 
-// out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0)
-__global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *out, long long ldo, int M, int N,
-                                                      int splits) {
-    long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
-    long long total4 = (long long)M * N / 4;
+// out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0), z in order.  The
+// split count is a template argument so that every partial's load is issued
+// before the first add; partials are read exactly once (non-temporal).
+template <int S>
+__global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *out, long long ldo, int M, int N) {
+    const long long i4 = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long total4 = (long long)M * N / 4;
     if (i4 >= total4) return;
-    long long e = i4 * 4;
-    int m = (int)(e / N), n = (int)(e % N);
-    f32x4 s = *reinterpret_cast<const f32x4 *>(part + e);
-    for (int z = 1; z < splits; z++) s += *reinterpret_cast<const f32x4 *>(part + (long long)z * M * N + e);
+    const long long e = i4 * 4;
+    const int m = (int)(e / N), n = (int)(e % N);
+    const long long MN = (long long)M * N;
+    f32x4 v[S];
+#pragma unroll
+    for (int z = 0; z < S; z++) v[z] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(part + z * MN + e));
     f32x4 *o = reinterpret_cast<f32x4 *>(out + (long long)m * ldo + n);
-    *o = *o + s;
+    f32x4 acc = v[0];
+#pragma unroll
+    for (int z = 1; z < S; z++) acc += v[z];
+    *o = *o + acc;
+}
+static hipError_t launch_reduce(const float *part, float *out, long long ldo, int M, int N, int splits, hipStream_t s) {
+    const long long total4 = (long long)M * N / 4;
+    const dim3 grid((unsigned)((total4 + 255) / 256));
+    switch (splits) {
+    case 2: hipLaunchKernelGGL(splitk_reduce<2>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 4: hipLaunchKernelGGL(splitk_reduce<4>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 8: hipLaunchKernelGGL(splitk_reduce<8>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    default: hipLaunchKernelGGL(splitk_reduce<16>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    }
+    return hipGetLastError();
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -852,12 +870,9 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         else e = launch_layout<float, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
     }
     if (e != hipSuccess) return set_launch_error(e, "gemm");
-    if (splits > 1) {
-        long long total4 = (long long)g.M * g.N / 4;
-        hipLaunchKernelGGL(splitk_reduce, dim3((unsigned)((total4 + 255) / 256)), dim3(256), 0, s,
-                           reinterpret_cast<const float *>(ws), reinterpret_cast<float *>(g.out), g.ldo, g.M,
-                           g.N, splits);
-        e = hipGetLastError();
+    if (splits > 1) {  // splits is a power of two in [2, 16] (choose_splits)
+        e = launch_reduce(reinterpret_cast<const float *>(ws), reinterpret_cast<float *>(g.out), g.ldo, g.M, g.N,
+                          splits, s);
         if (e != hipSuccess) return set_launch_error(e, "splitk_reduce");
     }
     if (g_timing_on) {
