@@ -135,3 +135,34 @@ def test_decode_full_size_sampled():
     check("out", out[pick], ro, TOL["bf16"])
     check("lse", lse[pick], rl, TOL["bf16"])
     assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+def test_decode_workspace_reuse():
+    """One workspace (and output buffers) for two calls in a row: 64 long
+    ragged sequences, then three short ones (padded to the same buffers with
+    empty caches): the second call must read none of the first call's
+    leftover chunk partials."""
+    require_gpu()
+    import torch
+    from decoder_only_transformer_block_amd import configs
+    from decoder_only_transformer_block_amd.runtime import DecodeAttention, to_device, to_numpy
+    big = configs.DECODE_LLAMA_GQA.replace(B=64, Tmax=2048)
+    small = configs.DecodeConfig("small", B=3, Tmax=2048, NH=32, NKV=8, hd=64, dtype="bf16", seed=0xD7B0 + 20,
+                                 len_hi=70)
+    dec = DecodeAttention(64, 32, 8, 64, 2048, "bf16")
+    for cfg in (big, small):
+        q, kc, vc, lens = configs.decode_inputs(cfg)
+        announce(f"decode reuse B={cfg.B} lens={lens.tolist() if cfg.B <= 8 else '...'}")
+        qq = np.zeros((64, 32 * 64), np.float32)
+        qq[:cfg.B] = q
+        kk = np.zeros((64, 2048, 8 * 64), np.float32)
+        vv = np.zeros_like(kk)
+        kk[:cfg.B], vv[:cfg.B] = kc, vc
+        ll = np.zeros(64, np.int32)
+        ll[:cfg.B] = lens
+        out, lse = dec(to_device(qq, "bf16"), to_device(kk, "bf16"), to_device(vv, "bf16"), torch.from_numpy(ll).cuda())
+        torch.cuda.synchronize()
+        ro, rl = _oracle(q, kc, vc, lens, cfg)
+        check("out", to_numpy(out)[:cfg.B], ro, TOL["bf16"])
+        check("lse", to_numpy(lse)[:cfg.B], rl, TOL["bf16"])
+        assert np.all(to_numpy(out)[cfg.B:] == 0) and np.all(np.isneginf(to_numpy(lse)[cfg.B:]))
