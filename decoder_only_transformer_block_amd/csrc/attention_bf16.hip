@@ -139,7 +139,15 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
     for (int d = 0; d < L::ND; d++)
 #pragma unroll
         for (int r = 0; r < 16; r++) O[d][r] = 0.f;
-    float m = -1e30f, lsum = 0.f;
+    float m = -1e30f;
+    // the softmax row sums ride on the P V product: an A operand that is 1 in
+    // row 0 and 0 elsewhere gives row 0 of Ls = sum over keys of the (bf16) P
+    // of each query column, in the accumulator of lanes 0..31 (no VALU adds)
+    f32x16 Ls;
+#pragma unroll
+    for (int r = 0; r < 16; r++) Ls[r] = 0.f;
+    const bf16x8 ones = __builtin_bit_cast(
+        bf16x8, (l32 == 0) ? u32x4{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u} : u32x4{0u, 0u, 0u, 0u});
 
     auto compute = [&](const char *st, int kt) {
         const char *Ks = st, *Vs = st + L::TILE;
@@ -165,25 +173,24 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
         for (int j = 0; j < 2; j++)
 #pragma unroll
             for (int r = 0; r < 16; r++) mt = fmaxf(mt, S[j][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;  // running max in log2 units
-        const float mn = fmaxf(m, mt);
-        if (!__all(mn == m)) {
+        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;  // tile max in log2 units
+        // the reference max m moves only when a column's scores exceed it by
+        // more than 2^8 (then O and the sums are rescaled); otherwise the
+        // exponentials below stay under 256 and no rescale is spent
+        if (!__all(mt <= m + 8.f)) {
+            const float mn = fmaxf(m, mt);
             const float alpha = fast_exp2(m - mn);
-            lsum *= alpha;
+            Ls[0] *= alpha;
 #pragma unroll
             for (int d = 0; d < L::ND; d++)
 #pragma unroll
                 for (int r = 0; r < 16; r++) O[d][r] *= alpha;
+            m = mn;
         }
-        m = mn;
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) {
-                const float e = fast_exp2(fmaf(S[j][r], p.sl2, -mn));
-                S[j][r] = e;
-                lsum += e;
-            }
+            for (int r = 0; r < 16; r++) S[j][r] = fast_exp2(fmaf(S[j][r], p.sl2, -m));
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
@@ -195,6 +202,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
 #pragma unroll
                 for (int db = 0; db < L::ND; db++)
                     O[db] = mfma32(lds_tr8<RB>(Vs + vofs[db] + (32 * j + 16 * hh) * RB), xb, O[db]);
+                Ls = mfma32(ones, xb, Ls);
             }
     };
 
@@ -217,7 +225,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
 #undef STG
     __builtin_amdgcn_s_waitcnt(0);
 
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    // row 0 of Ls sits in register 0 of lanes 0..31; lanes 32..63 take it from their partner
+    const float ltot = __shfl(Ls[0], l32, 64);
     if (qi < p.T) {
         bf16 *orow = reinterpret_cast<bf16 *>(p.o) + ((long long)b * p.T + qi) * p.C + h * p.hd;
         store_rows_bf16<HD>(orow, O, 1.f / ltot, p.hd, lane);
