@@ -327,9 +327,14 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
         const int kv0 = kt * BKV;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
+            // dP starts from -D of this lane's query (every element of the
+            // lane's column shares it), so dS = P * dP needs no add
             f32x16 S, dP;
 #pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+            for (int r = 0; r < 16; r++) {
+                S[r] = 0.f;
+                dP[r] = nDq;
+            }
 #pragma unroll
             for (int c = 0; c < L::NC; c++) {
                 S = mfma32(lds_row16(Ks + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, qf[c]), S);
@@ -344,7 +349,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                     if (kv0 + j * 32 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
 #pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * (dP[r] + nDq);
+            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * dP[r];
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 u32x4 xw;
