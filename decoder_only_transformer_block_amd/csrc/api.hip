@@ -196,7 +196,7 @@ static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
     W->dO = take((size_t)d.BT * c->C * d.es);
     W->dqkv = take((size_t)d.BT * d.QKV * d.es);
     W->dn1 = take((size_t)d.BT * c->C * d.es);
-    W->D = take((size_t)c->B * c->NH * c->T * 4 * 2);  // D and lse * log2(e)
+    W->D = take((size_t)c->B * c->NH * c->T * 4 * 2);  // -D and -lse / scale
     W->nparts = norm_backward_parts(d.BT);
     W->npart = take((size_t)W->nparts * 2 * c->C * 4);
     W->bparts = bias_grad_parts(d.BT);
@@ -243,7 +243,7 @@ size_t block_workspace_bytes(const dtb_block_cfg *cfg) {
 
 size_t attn_workspace_bytes(int B, int T, int NH) {
     if (B < 0 || T < 0 || NH <= 0) return 0;
-    size_t n = (size_t)B * T * NH * 4 * 2;  // D and lse * log2(e)
+    size_t n = (size_t)B * T * NH * 4 * 2;  // -D and -lse / scale
     return n ? al(n) : 256;
 }
 

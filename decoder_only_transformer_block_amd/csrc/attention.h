@@ -12,7 +12,7 @@ struct AttnP {
     float *lse;     // forward output
     const float *lse_in;
     const float *D;     // backward: rowsum(dO o)   [B][NH][T]
-    const float *L2;    // backward: lse * log2(e)  [B][NH][T]
+    const float *lsn;   // backward: -lse / scale, lse in raw score units  [B][NH][T]
     const float2 *rope_cs;  // backward: NeoX (cos, sin) table [T][hd/2] to rotate dq, dk back, or null
     int B, T, C, NH, NKV, hd, QKV;
     float sl2;      // log2(e) / sqrt(hd)
@@ -73,7 +73,7 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // bf16 kernels (head width padded to HD in {16, 32, 64, 128})
 hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s);
-// dQ and dK/dV; p.D and p.L2 must already hold -rowsum(dO o) (negated) and lse * log2(e)
+// dQ and dK/dV; p.D and p.lsn must already hold -rowsum(dO o) (negated) and -lse / scale
 hipError_t attn_bwd_bf16(const AttnP &p, int HD, hipStream_t s);
 
 }  // namespace dtb

@@ -273,12 +273,13 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
 
 // ---------------------------------------------------------------------------
 // backward: D = rowsum(dO * O)   [B][NH][T] fp32, one wave per (b, t) row;
-// optionally L2 = lse * log2(e) in the same layout
+// optionally lsn = -lse / scale in the same layout
 // ---------------------------------------------------------------------------
 template <typename T>
 // D = rowsum(dO o) per (b, h, t), written times dsign (the bf16 kernels take
-// -D); with L2, also lse * log2(e)
-__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *L2, float dsign) {
+// -D); with lsn, also -lse / scale (the bf16 kernels start their score
+// accumulators from it, so the exponent is one multiply)
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *lsn, float dsign) {
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= (long long)p.B * p.T) return;
@@ -308,7 +309,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, fl
             int h = c / hch;
             const long long i = ((long long)b * p.NH + h) * p.T + tq;
             D[i] = dsign * s;
-            if (L2) L2[i] = p.lse_in[i] * LOG2E;
+            if (lsn) lsn[i] = -p.lse_in[i] / p.scale;
         }
     }
 }
@@ -634,18 +635,18 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     return hipGetLastError();
 }
 
-// bf16: D and lse * log2(e) by the row kernel, then the dQ and dK/dV kernels
+// bf16: -D and -lse / scale by the row kernel, then the dQ and dK/dV kernels
 static hipError_t bwd_bf16(const AttnP &p, int hdp, float *D, hipStream_t s) {
-    float *L2 = D + (long long)p.B * p.NH * p.T;
+    float *lsn = D + (long long)p.B * p.NH * p.T;
     long long rows = (long long)p.B * p.T;
     // the bf16 kernels take -D: the dK/dV kernel starts its dP accumulation from it
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, L2,
+    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, lsn,
                        -1.f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
     q.D = D;
-    q.L2 = L2;
+    q.lsn = lsn;
     return attn_bwd_bf16(q, hdp, s);
 }
 

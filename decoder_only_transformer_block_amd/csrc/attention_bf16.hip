@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
 
     u32x4 qf[L::NC], df[L::NC];
     const long long li = ((long long)b * p.NH + h) * p.T + qi;
-    float l2 = 0.f, nDq = 0.f;  // lse * log2(e) and -D of this lane's query
+    float nls = 0.f, nDq = 0.f;  // -lse / scale and -D of this lane's query
     {
         const Buf bq(base + h * p.hd);
         const Buf bd(reinterpret_cast<const bf16 *>(p.dout) + (long long)b * p.T * p.C + h * p.hd);
@@ -295,7 +295,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
             df[c] = bd.ld16((int)(((long long)qi * p.C + ch * 8) * 2), ok);
         }
         if (qi < p.T) {
-            l2 = p.L2[li];
+            nls = p.lsn[li];
             nDq = p.D[li];
         }
     }
@@ -327,12 +327,13 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
         const int kv0 = kt * BKV;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
-            // dP starts from -D of this lane's query (every element of the
-            // lane's column shares it), so dS = P * dP needs no add
+            // S starts from -lse / scale and dP from -D of this lane's query
+            // (every element of the lane's column shares them): P = 2^(S sl2)
+            // is one multiply and an exp, dS = P * dP one multiply
             f32x16 S, dP;
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                S[r] = 0.f;
+                S[r] = nls;
                 dP[r] = nDq;
             }
 #pragma unroll
@@ -349,7 +350,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                     if (kv0 + j * 32 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
 #pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = fast_exp2(fmaf(S[r], p.sl2, -l2)) * dP[r];
+            for (int r = 0; r < 16; r++) S[r] = fast_exp2(S[r] * p.sl2) * dP[r];
 #pragma unroll
             for (int hh = 0; hh < 2; hh++) {
                 u32x4 xw;
@@ -395,12 +396,16 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
 // dK^T += Q^T dS with dO^T and Q^T through transposing reads.  A stage holds
 // the Q tile, the dO tile and the 64 lse*log2(e) and D values of its queries.
 // ---------------------------------------------------------------------------
+// Register target: 3 waves per SIMD at HD <= 64 (the LDS of three workgroups
+// fits), 2 at HD = 128, where the compiler alone chose 268 registers (one
+// wave) and 2 waves with 13 spilled registers measured 6 % faster.
 template <int HD, int NS>
-__global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ? 2 : 3, 8))) void dkv_bf16_kernel(
+    AttnP p) {
     using L = TL<HD>;
     constexpr int BK = 128, BQ = 64, RB = L::RB;
     constexpr int DPW = L::NDMA / 2 + 1;   // tile share plus one 256-byte vector
-    constexpr int AUX = 2 * L::TILE;       // [lse2 64][D 64][unused 128 floats]
+    constexpr int AUX = 2 * L::TILE;       // [-lse/scale 64][-D 64][unused 128 floats]
     constexpr int STB = 2 * L::TILE + 1024;
     __shared__ __attribute__((aligned(1024))) char s0[STB];
     __shared__ __attribute__((aligned(1024))) char s1[STB];
@@ -434,7 +439,7 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
 #pragma unroll
         for (int i = 0; i < DPW - 1; i++)
             dma_tile<HD, true>(st + (isQ ? 0 : L::TILE), src, st_, q0, live ? p.T : 0, p.hd, qsub + i, lane);
-        const float *vec = (wave == 0 ? p.L2 : p.D) + ((long long)b * p.NH + h) * p.T;
+        const float *vec = (wave == 0 ? p.lsn : p.D) + ((long long)b * p.NH + h) * p.T;
         dma_vec64(st + AUX + wave * 256, vec, q0, p.T, live && wave < 2, lane);
     };
 
@@ -475,25 +480,27 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
 
     auto compute = [&](const char *st, int it) {
         const char *Qs = st, *dOs = st + L::TILE;
-        const float *l2s = reinterpret_cast<const float *>(st + AUX), *Ds = l2s + BQ;
+        const float *lss = reinterpret_cast<const float *>(st + AUX), *Ds = lss + BQ;
         const int q0 = (qt0 + it % nqt) * BQ;
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             // the 16 query rows of this lane: 4 groups of 4 consecutive rows;
-            // Ds holds -D, in the accumulator's row order, so the dP = dO V^T
-            // accumulation starts from it and ends as dP - D
-            f32x4 lq[4];
+            // lss holds -lse / scale and Ds -D, read in the accumulator's row
+            // order, so S = Q K^T accumulates from the first (P = 2^(S sl2))
+            // and dP = dO V^T from the second (it ends as dP - D); no per-row
+            // value stays live across the MFMAs
             f32x16 S, dP;
 #pragma unroll
             for (int r4 = 0; r4 < 4; r4++) {
                 const int ql = j * 32 + 8 * r4 + 4 * g;
-                lq[r4] = *reinterpret_cast<const f32x4 *>(l2s + ql);
+                const f32x4 ls = *reinterpret_cast<const f32x4 *>(lss + ql);
                 const f32x4 nd = *reinterpret_cast<const f32x4 *>(Ds + ql);
 #pragma unroll
-                for (int e = 0; e < 4; e++) dP[4 * r4 + e] = nd[e];
+                for (int e = 0; e < 4; e++) {
+                    S[4 * r4 + e] = ls[e];
+                    dP[4 * r4 + e] = nd[e];
+                }
             }
-#pragma unroll
-            for (int r = 0; r < 16; r++) S[r] = 0.f;
 #pragma unroll
             for (int c = 0; c < L::NC; c++) {
                 S = mfma32(lds_row16(Qs + kofs[c] + j * 32 * RB), __builtin_bit_cast(bf16x8, kf[c]), S);
@@ -509,7 +516,7 @@ __global__ __launch_bounds__(256) void dkv_bf16_kernel(AttnP p) {
             }
 #pragma unroll
             for (int r = 0; r < 16; r++) {
-                const float pr = fast_exp2(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
+                const float pr = fast_exp2(S[r] * p.sl2);
                 S[r] = pr;
                 dP[r] = pr * dP[r];
             }
