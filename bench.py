@@ -160,6 +160,38 @@ def cpu_baseline_attn(cfg, tokens):
                       f"in fp64, {dt:.2f} s"}
 
 
+def timed_steps(args, step, roof_classes):
+    """Time args.steps steps.  Inside the timed region only the roofline
+    kernel's class carries HIP events (on the kernels' own dispatch packets);
+    a second, untimed pass of the same steps with every class enabled gives
+    the per-class breakdown.  Returns (seconds, timings), where timings maps
+    each class to its event totals and the roofline classes' entries come
+    from the timed region."""
+    import torch
+    from decoder_only_transformer_block_amd import binding
+    torch.cuda.synchronize()
+    if not args.no_timing:
+        binding.timing_enable(classes=roof_classes)
+        binding.timing_collect()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    tim = {}
+    if not args.no_timing:
+        roof = binding.timing_collect()
+        binding.timing_enable(True)
+        for _ in range(args.steps):
+            step()
+        tim = binding.timing_collect()
+        binding.timing_enable(False)
+        for c in roof_classes:
+            tim[c] = roof[c]
+    return dt, tim
+
+
 def bench_block(args, cfg):
     import torch
     from decoder_only_transformer_block_amd import binding, configs
@@ -177,20 +209,7 @@ def bench_block(args, cfg):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    if not args.no_timing:
-        binding.timing_enable(True)
-        binding.timing_collect()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    tim = {}
-    if not args.no_timing:
-        tim = binding.timing_collect()
-        binding.timing_enable(False)
+    dt, tim = timed_steps(args, step, ["gemm_fwd"])
     ms = dt * 1e3 / args.steps
     tokens = cfg.B * cfg.T
     value = tokens * cfg.L / (dt / args.steps)
@@ -216,19 +235,7 @@ def bench_attn(args, cfg):
 
     for _ in range(args.warmup):
         step()
-    torch.cuda.synchronize()
-    if not args.no_timing:
-        binding.timing_enable(True)
-        binding.timing_collect()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t0
-    tim = {}
-    if not args.no_timing:
-        tim = binding.timing_collect()
-        binding.timing_enable(False)
+    dt, tim = timed_steps(args, step, ["attn_bwd"])
     return dt * 1e3 / args.steps, B * T / (dt / args.steps), tim
 
 

@@ -277,12 +277,22 @@ def block_backward(cfg: BlockCfg, weights: dict, x_in, saved, dx_out, dx_in, gra
                                _ptr(dx_in), ctypes.byref(g), _ptr(workspace), _stream(stream)), "block_backward")
 
 
-def timing_enable(on: bool) -> None:
-    lib().dtb_timing_enable(int(on))
+TIMING_CLASSES = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw", "attn_decode",
+                  "decode_merge"]
+
+
+def timing_enable(on: bool = True, classes=None) -> None:
+    """Per-class kernel timing: every class (on), none (not on), or only the
+    named classes."""
+    if classes is not None:
+        mask = sum(1 << TIMING_CLASSES.index(c) for c in classes)
+    else:
+        mask = -1 if on else 0
+    lib().dtb_timing_enable(mask)
 
 
 def timing_collect():
-    names = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw", "attn_decode", "decode_merge"]
+    names = TIMING_CLASSES
     arr = (Timing * len(names))()
     n = lib().dtb_timing_collect(arr, len(names))
     return {names[i]: {"ms": arr[i].ms, "flops": arr[i].flops, "bytes": arr[i].bytes,

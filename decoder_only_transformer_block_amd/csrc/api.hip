@@ -22,6 +22,7 @@ int set_launch_error(hipError_t e, const char *what) {
 
 // ---------------------------------------------------------------- timing ---
 bool g_timing_on = false;
+static unsigned g_timing_mask = 0;  // bit c: class c is timed
 struct TRec {
     hipEvent_t a, b;
     int cls;
@@ -30,7 +31,9 @@ struct TRec {
 static std::mutex g_tmu;
 static std::vector<TRec> g_trec;
 static std::vector<hipEvent_t> g_pool;
-static hipEvent_t g_pending = nullptr;
+static std::vector<hipEvent_t> g_retired;  // stop events a later launch of their unit superseded
+static bool g_unit_open = false;
+static hipEvent_t g_unit_a = nullptr, g_unit_b = nullptr;
 static dtb_timing g_tot[K_NCLASS];
 
 static hipEvent_t ev_get() {
@@ -44,20 +47,46 @@ static hipEvent_t ev_get() {
     return e;
 }
 
-void timing_begin(hipStream_t s) {
+// A timed unit is one or more launches on one stream (a GEMM and its split-K
+// reduction, say).  Its start is the start of its first kernel and its end the
+// end of its last, both taken from the kernels' own dispatch packets.
+void timing_begin(hipStream_t, int cls) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    g_pending = ev_get();
-    if (g_pending) (void)hipEventRecord(g_pending, s);
+    g_unit_open = ((g_timing_mask >> cls) & 1u) != 0;
+    g_unit_a = g_unit_b = nullptr;
 }
 
-void timing_end(hipStream_t s, int cls, double flops, double bytes) {
+void timing_launch_events(hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_tmu);
-    if (!g_pending) return;
+    *start = *stop = nullptr;
+    if (!g_unit_open) return;
     hipEvent_t b = ev_get();
     if (!b) return;
-    (void)hipEventRecord(b, s);
-    g_trec.push_back(TRec{g_pending, b, cls, flops, bytes});
-    g_pending = nullptr;
+    if (!g_unit_a) {
+        g_unit_a = ev_get();
+        if (!g_unit_a) {
+            g_pool.push_back(b);
+            return;
+        }
+        *start = g_unit_a;
+    }
+    // an earlier stop event of this unit may still be pending on the device:
+    // it is only reused after the next collection has waited for it
+    if (g_unit_b) g_retired.push_back(g_unit_b);
+    g_unit_b = b;
+    *stop = b;
+}
+
+void timing_end(hipStream_t, int cls, double flops, double bytes) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    if (g_unit_open && g_unit_a && g_unit_b) {
+        g_trec.push_back(TRec{g_unit_a, g_unit_b, cls, flops, bytes});
+    } else {
+        if (g_unit_a) g_retired.push_back(g_unit_a);
+        if (g_unit_b) g_retired.push_back(g_unit_b);
+    }
+    g_unit_open = false;
+    g_unit_a = g_unit_b = nullptr;
 }
 
 }  // namespace dtb
@@ -80,8 +109,18 @@ const char *dtb_strerror(int code) {
     }
 }
 
-int dtb_timing_enable(int on) {
-    g_timing_on = on != 0;
+int dtb_timing_enable(int class_mask) {
+    std::lock_guard<std::mutex> lk(g_tmu);
+    g_timing_mask = class_mask < 0 ? ~0u : (unsigned)class_mask;
+    g_timing_on = g_timing_mask != 0;
+    // events are created here, not on the launch path: creating them while
+    // kernels are being enqueued made the host fall behind the GPU
+    constexpr size_t kPool = 4096;
+    while (g_timing_on && g_pool.size() + g_trec.size() * 2 + g_retired.size() < kPool) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) break;
+        g_pool.push_back(e);
+    }
     return DTB_OK;
 }
 
@@ -100,6 +139,11 @@ int dtb_timing_collect(dtb_timing *out, int max_classes) {
         g_pool.push_back(r.b);
     }
     g_trec.clear();
+    for (hipEvent_t e : g_retired) {
+        (void)hipEventSynchronize(e);
+        g_pool.push_back(e);
+    }
+    g_retired.clear();
     int n = max_classes < K_NCLASS ? max_classes : K_NCLASS;
     for (int i = 0; i < n; i++) out[i] = g_tot[i];
     for (int i = 0; i < K_NCLASS; i++) g_tot[i] = dtb_timing{0, 0, 0, 0};

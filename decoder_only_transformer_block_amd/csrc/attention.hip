@@ -604,7 +604,7 @@ template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_
         init = true;
     }
     int nqb = (p.T + FC::BQ - 1) / FC::BQ;
-    hipLaunchKernelGGL((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
+    DTB_LAUNCH((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
     return hipGetLastError();
 }
 
@@ -620,18 +620,18 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
         init = true;
     }
     long long rows = (long long)p.B * p.T;
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D,
+    DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D,
                        (float *)nullptr, 1.f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
     q.D = D;
     int nqb = (p.T + QC::BQ - 1) / QC::BQ;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * QC::STAGE, s, q);
+    DTB_LAUNCH((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * QC::STAGE, s, q);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     int nkb = (p.T + KC::BK - 1) / KC::BK;
-    hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
+    DTB_LAUNCH((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
     return hipGetLastError();
 }
 
@@ -640,7 +640,7 @@ static hipError_t bwd_bf16(const AttnP &p, int hdp, float *D, hipStream_t s) {
     float *lsn = D + (long long)p.B * p.NH * p.T;
     long long rows = (long long)p.B * p.T;
     // the bf16 kernels take -D: the dK/dV kernel starts its dP accumulation from it
-    hipLaunchKernelGGL((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, lsn,
+    DTB_LAUNCH((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, lsn,
                        -1.f);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -675,7 +675,7 @@ int launch_attn_forward(void *out, float *lse, const void *qkv, int B, int T, in
     p.o = out;
     p.lse = lse;
     int hdp = pad_hd(p.hd, dtype);
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ATTN_FWD);
     hipError_t e = dtype == DTB_BF16 ? attn_fwd_bf16(p, hdp, s) : DTB_HD_DISPATCH(fwd_t, float, hdp, p, s);
     if (e != hipSuccess) return set_launch_error(e, "attn_forward");
     if (g_timing_on) {
@@ -697,7 +697,7 @@ int launch_attn_backward(void *dqkv, const void *qkv, const void *out, const voi
     p.dout = dout;
     p.lse_in = lse;
     int hdp = pad_hd(p.hd, dtype);
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ATTN_BWD);
     hipError_t e = dtype == DTB_BF16 ? bwd_bf16(p, hdp, D, s) : DTB_HD_DISPATCH(bwd_t, float, hdp, p, D, s);
     if (e != hipSuccess) return set_launch_error(e, "attn_backward");
     if (g_timing_on) {

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
 template <int HD> hipError_t fwd_launch(const AttnP &p, hipStream_t s) {
     constexpr int NS = HD >= 128 ? 2 : 3;
     const int nqb = (p.T + 127) / 128;
-    hipLaunchKernelGGL((fwd_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
+    DTB_LAUNCH((fwd_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -566,11 +566,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ?
 template <int HD> hipError_t bwd_launch(const AttnP &p, hipStream_t s) {
     constexpr int NS = HD >= 128 ? 2 : 3;
     const int nqb = (p.T + 127) / 128;
-    hipLaunchKernelGGL((dq_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
+    DTB_LAUNCH((dq_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int nkb = (p.T + 127) / 128;
-    hipLaunchKernelGGL((dkv_bf16_kernel<HD, NS>), dim3(nkb * p.B * p.NKV), dim3(256), 0, s, p);
+    DTB_LAUNCH((dkv_bf16_kernel<HD, NS>), dim3(nkb * p.B * p.NKV), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

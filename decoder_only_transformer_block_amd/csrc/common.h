@@ -1,6 +1,7 @@
 // Internal header of libdtb: element types, vector loads, MFMA wrappers and
 // the launch bookkeeping shared by the kernel files.  gfx950 (CDNA4) only.
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
@@ -180,9 +181,21 @@ enum KClass {
     K_GEMM_FWD = 0, K_ATTN_FWD = 1, K_ATTN_BWD = 2, K_ELEM = 3, K_GEMM_DINP = 4, K_GEMM_DW = 5,
     K_ATTN_DEC = 6, K_DEC_MERGE = 7, K_NCLASS = 8
 };
-void timing_begin(hipStream_t s);
+void timing_begin(hipStream_t s, int cls);  // opens a unit only if cls is enabled
 void timing_end(hipStream_t s, int cls, double flops, double bytes);
+void timing_launch_events(hipEvent_t *start, hipEvent_t *stop);
 extern bool g_timing_on;
+
+// Every kernel launch of the library.  While a timed unit is open (between
+// timing_begin and timing_end) the launch carries the unit's start event (on
+// its first launch) and a stop event on its own dispatch packet, so timing
+// adds no marker packets, and no idle time, between kernels.
+#define DTB_LAUNCH(kernel, grid, block, shmem, stream, ...)                                        \
+    do {                                                                                           \
+        hipEvent_t dtb_ev0_ = nullptr, dtb_ev1_ = nullptr;                                         \
+        if (g_timing_on) timing_launch_events(&dtb_ev0_, &dtb_ev1_);                               \
+        hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, dtb_ev0_, dtb_ev1_, 0u, __VA_ARGS__); \
+    } while (0)
 
 int set_launch_error(hipError_t e, const char *what);
 

@@ -387,15 +387,15 @@ int pow2_at_least(int v, int lo) {
 
 template <int HD> hipError_t bf16_launch(const DecP &p, int nblk, hipStream_t s) {
     constexpr int NS = HD >= 128 ? 3 : 4;
-    hipLaunchKernelGGL((decode_bf16_kernel<HD, NS>), dim3(nblk), dim3(64), 0, s, p);
+    DTB_LAUNCH((decode_bf16_kernel<HD, NS>), dim3(nblk), dim3(64), 0, s, p);
     return hipGetLastError();
 }
 template <int HD> hipError_t f32_launch(const DecP &p, int HG, int nblk, hipStream_t s) {
     switch (HG) {
-    case 1: hipLaunchKernelGGL((decode_f32_kernel<HD, 1>), dim3(nblk), dim3(64), 0, s, p); break;
-    case 2: hipLaunchKernelGGL((decode_f32_kernel<HD, 2>), dim3(nblk), dim3(64), 0, s, p); break;
-    case 4: hipLaunchKernelGGL((decode_f32_kernel<HD, 4>), dim3(nblk), dim3(64), 0, s, p); break;
-    default: hipLaunchKernelGGL((decode_f32_kernel<HD, 8>), dim3(nblk), dim3(64), 0, s, p); break;
+    case 1: DTB_LAUNCH((decode_f32_kernel<HD, 1>), dim3(nblk), dim3(64), 0, s, p); break;
+    case 2: DTB_LAUNCH((decode_f32_kernel<HD, 2>), dim3(nblk), dim3(64), 0, s, p); break;
+    case 4: DTB_LAUNCH((decode_f32_kernel<HD, 4>), dim3(nblk), dim3(64), 0, s, p); break;
+    default: DTB_LAUNCH((decode_f32_kernel<HD, 8>), dim3(nblk), dim3(64), 0, s, p); break;
     }
     return hipGetLastError();
 }
@@ -447,7 +447,7 @@ hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *
     const long long nblk = (long long)g.nsplit * B * NKV * g.ngrp;
     hipError_t e = hipSuccess;
     if (nblk > 0) {
-        if (g_timing_on) timing_begin(s);
+        if (g_timing_on) timing_begin(s, K_ATTN_DEC);
         if (dtype == DTB_BF16) {
             switch (pow2_at_least(hd, 16)) {
             case 16: e = bf16_launch<16>(p, (int)nblk, s); break;
@@ -472,9 +472,9 @@ hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *
     }
     const int mblk = (B * NH + 3) / 4;
     if (mblk > 0) {
-        if (g_timing_on) timing_begin(s);
-        if (dtype == DTB_BF16) hipLaunchKernelGGL(decode_merge_kernel<bf16>, dim3(mblk), dim3(256), 0, s, p);
-        else hipLaunchKernelGGL(decode_merge_kernel<float>, dim3(mblk), dim3(256), 0, s, p);
+        if (g_timing_on) timing_begin(s, K_DEC_MERGE);
+        if (dtype == DTB_BF16) DTB_LAUNCH(decode_merge_kernel<bf16>, dim3(mblk), dim3(256), 0, s, p);
+        else DTB_LAUNCH(decode_merge_kernel<float>, dim3(mblk), dim3(256), 0, s, p);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         if (g_timing_on) timing_end(s, K_DEC_MERGE, 0.0, (double)B * NH * (hd * 2 + 4));

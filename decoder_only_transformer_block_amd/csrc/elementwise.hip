@@ -208,13 +208,13 @@ static hipError_t norm_fwd_t(int mode, const void *x, const void *g, const void 
     const T *xx = (const T *)x, *gg = (const T *)g, *bb = (const T *)b;
     T *oo = (T *)out;
     if (mode == DTB_NORM_RMS)
-        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C, oo,
+        DTB_LAUNCH((norm_fwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C, oo,
                            rstd, mean);
     else if (mode == DTB_NORM_RMS_NOGAMMA)
-        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, xx, gg, bb, eps,
+        DTB_LAUNCH((norm_fwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, xx, gg, bb, eps,
                            R, C, oo, rstd, mean);
     else
-        hipLaunchKernelGGL((norm_fwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C,
+        DTB_LAUNCH((norm_fwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C,
                            oo, rstd, mean);
     return hipGetLastError();
 }
@@ -230,7 +230,7 @@ int norm_forward(int mode, int dtype, const void *x, const void *g, const void *
                  void *out, float *rstd, float *mean, hipStream_t s) {
     if (R <= 0) return DTB_OK;
     int npl = npl_for(C, dtype);
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     hipError_t e = dtype == DTB_BF16 ? NPL_DISPATCH(norm_fwd_t, bf16, npl, mode, x, g, b, eps, R, C, out, rstd, mean, s)
                                      : NPL_DISPATCH(norm_fwd_t, float, npl, mode, x, g, b, eps, R, C, out, rstd, mean, s);
     if (e != hipSuccess) return set_launch_error(e, "norm_forward");
@@ -254,13 +254,13 @@ static hipError_t norm_bwd_t(int mode, const void *dy, const void *x, const void
     const T *a = (const T *)dy, *xx = (const T *)x, *gg = (const T *)g, *rr = (const T *)dres;
     T *o = (T *)dx;
     if (mode == DTB_NORM_RMS)
-        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean, rr,
+        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean, rr,
                            R, C, o, part);
     else if (mode == DTB_NORM_RMS_NOGAMMA)
-        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, a, xx, gg, rstd,
+        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, a, xx, gg, rstd,
                            mean, rr, R, C, o, part);
     else
-        hipLaunchKernelGGL((norm_bwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean,
+        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean,
                            rr, R, C, o, part);
     return hipGetLastError();
 }
@@ -270,15 +270,15 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
                   int npart, hipStream_t s) {
     if (R <= 0) return DTB_OK;
     int npl = npl_for(C, dtype);
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     hipError_t e = dtype == DTB_BF16
                        ? NPL_DISPATCH(norm_bwd_t, bf16, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s)
                        : NPL_DISPATCH(norm_bwd_t, float, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s);
     if (e != hipSuccess) return set_launch_error(e, "norm_backward");
     if (mode != DTB_NORM_RMS_NOGAMMA) {
-        hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C, dg);
+        DTB_LAUNCH(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C, dg);
         if (mode == DTB_NORM_LAYER)
-            hipLaunchKernelGGL(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part + C, npart, 2L * C,
+            DTB_LAUNCH(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part + C, npart, 2L * C,
                                C, db);
         e = hipGetLastError();
         if (e != hipSuccess) return set_launch_error(e, "norm_backward reduce");
@@ -306,7 +306,7 @@ int rope_table(float *cs, int T, int hd, float base, hipStream_t s) {
     int half = hd / 2;
     long n = (long)T * half;
     if (n <= 0) return DTB_OK;
-    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float2 *)cs, T, half,
+    DTB_LAUNCH(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (float2 *)cs, T, half,
                        hd, (double)base);
     DTB_LAUNCH_CHECK("rope_table");
     return DTB_OK;
@@ -339,13 +339,13 @@ int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int
     long BT = (long)B * T;
     long total = BT * (NH + NKV) * (hd / 2);
     if (total <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     dim3 grid((unsigned)((total + 255) / 256));
     if (dtype == DTB_BF16)
-        hipLaunchKernelGGL(rope_kernel<bf16>, grid, dim3(256), 0, s, (bf16 *)qkv, (const float2 *)cs, BT, T, QKV, NH,
+        DTB_LAUNCH(rope_kernel<bf16>, grid, dim3(256), 0, s, (bf16 *)qkv, (const float2 *)cs, BT, T, QKV, NH,
                            NKV, hd, inverse);
     else
-        hipLaunchKernelGGL(rope_kernel<float>, grid, dim3(256), 0, s, (float *)qkv, (const float2 *)cs, BT, T, QKV,
+        DTB_LAUNCH(rope_kernel<float>, grid, dim3(256), 0, s, (float *)qkv, (const float2 *)cs, BT, T, QKV,
                            NH, NKV, hd, inverse);
     DTB_LAUNCH_CHECK("rope");
     if (g_timing_on) timing_end(s, K_ELEM, 0, 2.0 * (dtype == DTB_BF16 ? 2 : 4) * total * 2);
@@ -408,11 +408,11 @@ static hipError_t act_fwd_t(int mlp, const void *up, long R, int H, void *h, hip
     long n = R * (H / EPC);
     dim3 grid((unsigned)((n + 255) / 256));
     if (mlp == DTB_MLP_SWIGLU)
-        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+        DTB_LAUNCH((act_fwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
     else if (mlp == DTB_MLP_RELU)
-        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+        DTB_LAUNCH((act_fwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
     else
-        hipLaunchKernelGGL((act_fwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
+        DTB_LAUNCH((act_fwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
     return hipGetLastError();
 }
 template <typename T>
@@ -421,20 +421,20 @@ static hipError_t act_bwd_t(int mlp, const void *dh, const void *up, long R, int
     long n = R * (H / EPC);
     dim3 grid((unsigned)((n + 255) / 256));
     if (mlp == DTB_MLP_SWIGLU)
-        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R,
+        DTB_LAUNCH((act_bwd_kernel<T, DTB_MLP_SWIGLU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R,
                            H, (T *)dup);
     else if (mlp == DTB_MLP_RELU)
-        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R, H,
+        DTB_LAUNCH((act_bwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)dh, (const T *)up, R, H,
                            (T *)dup);
     else
-        hipLaunchKernelGGL((act_bwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)dh,
+        DTB_LAUNCH((act_bwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)dh,
                            (const T *)up, R, H, (T *)dup);
     return hipGetLastError();
 }
 
 int act_forward(int mlp, int dtype, const void *up, long R, int H, void *h, hipStream_t s) {
     if (R <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     hipError_t e = dtype == DTB_BF16 ? act_fwd_t<bf16>(mlp, up, R, H, h, s) : act_fwd_t<float>(mlp, up, R, H, h, s);
     if (e != hipSuccess) return set_launch_error(e, "act_forward");
     if (g_timing_on) {
@@ -446,7 +446,7 @@ int act_forward(int mlp, int dtype, const void *up, long R, int H, void *h, hipS
 
 int act_backward(int mlp, int dtype, const void *dh, const void *up, long R, int H, void *dup, hipStream_t s) {
     if (R <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     hipError_t e = dtype == DTB_BF16 ? act_bwd_t<bf16>(mlp, dh, up, R, H, dup, s)
                                      : act_bwd_t<float>(mlp, dh, up, R, H, dup, s);
     if (e != hipSuccess) return set_launch_error(e, "act_backward");
@@ -476,14 +476,14 @@ int bias_grad_parts(long R) {
 
 int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, int npart, hipStream_t s) {
     if (R <= 0 || N <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     long rows_per = (R + npart - 1) / npart;
     dim3 grid((N + 255) / 256, npart);
     if (dtype == DTB_BF16)
-        hipLaunchKernelGGL(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
+        DTB_LAUNCH(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
     else
-        hipLaunchKernelGGL(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
-    hipLaunchKernelGGL(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, npart, (long)N, N, db);
+        DTB_LAUNCH(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
+    DTB_LAUNCH(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, npart, (long)N, N, db);
     DTB_LAUNCH_CHECK("bias_grad");
     if (g_timing_on) timing_end(s, K_ELEM, 0, (double)R * N * (dtype == DTB_BF16 ? 2 : 4));
     return DTB_OK;

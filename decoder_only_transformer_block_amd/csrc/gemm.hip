@@ -975,10 +975,10 @@ static hipError_t launch_reduce(const float *part, float *out, long long ldo, in
     const long long total4 = (long long)M * N / 4;
     const dim3 grid((unsigned)((total4 + 255) / 256));
     switch (splits) {
-    case 2: hipLaunchKernelGGL(splitk_reduce<2>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 4: hipLaunchKernelGGL(splitk_reduce<4>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 8: hipLaunchKernelGGL(splitk_reduce<8>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    default: hipLaunchKernelGGL(splitk_reduce<16>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 2: DTB_LAUNCH(splitk_reduce<2>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 4: DTB_LAUNCH(splitk_reduce<4>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 8: DTB_LAUNCH(splitk_reduce<8>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    default: DTB_LAUNCH(splitk_reduce<16>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
     }
     return hipGetLastError();
 }
@@ -996,7 +996,7 @@ static hipError_t launch_t(const KParams &p, int splits, hipStream_t s) {
     }
     int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
     dim3 grid(nm * nn, 1, splits);
-    hipLaunchKernelGGL((gemm_kernel<T, BM, BN, AK, BKM>), grid, dim3(256), 2 * STAGE, s, p);
+    DTB_LAUNCH((gemm_kernel<T, BM, BN, AK, BKM>), grid, dim3(256), 2 * STAGE, s, p);
     return hipGetLastError();
 }
 
@@ -1015,8 +1015,8 @@ static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
     // 64-k slabs whenever an operand is k-major (its rows then fill whole
     // cache lines); both operands m/n-major (the weight gradients) already
     // stream whole lines on 32-k slabs, and the 32-k ring measured the same
-    if constexpr (AK || BKM) hipLaunchKernelGGL((gemm_k64_kernel<AK, BKM, MODE>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
+    if constexpr (AK || BKM) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE>), grid, dim3(512), 0, s, p);
+    else DTB_LAUNCH((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1096,7 +1096,8 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
                               g.a_kmajor && g.b_kmajor && splits == 1 && !g.out_f32 && !g.res && !g.rope_cs;
     if (swiglu_fused) p.out_mode = 5;
     double flops = 2.0 * g.M * g.N * (double)g.K;
-    if (g_timing_on) timing_begin(s);
+    const int cls = g.out_f32 ? K_GEMM_DW : (g.b_kmajor ? K_GEMM_FWD : K_GEMM_DINP);
+    if (g_timing_on) timing_begin(s, cls);
     hipError_t e;
     if (g.dtype == DTB_BF16) {
         if (tc.bm == 256 && tc.bn == 256) e = launch256(p, g.a_kmajor, g.b_kmajor, splits, s);
@@ -1118,7 +1119,6 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         double bytes = es * ((double)g.M * g.K + (double)g.N * g.K) +
                        (g.out_f32 ? 4.0 * (g.accumulate ? 2.0 : 1.0) : es) * g.M * g.N;
         if (swiglu_fused) bytes += es * (double)g.M * g.act_H;          // write the activation output
-        const int cls = g.out_f32 ? K_GEMM_DW : (g.b_kmajor ? K_GEMM_FWD : K_GEMM_DINP);
         timing_end(s, cls, flops, bytes);
     }
     // passes the epilogue could not take (timed as their own launches)

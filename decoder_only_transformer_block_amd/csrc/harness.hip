@@ -346,13 +346,13 @@ __global__ __launch_bounds__(256) void adamw_kernel(AdamArgs a) {
 int embed_fwd(int dtype, const int *ids, const void *wte, const void *wpe, long BT, int Tn, int C, int V, void *x,
               hipStream_t s) {
     if (BT <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     dim3 grid((unsigned)((BT + 3) / 4));
     if (dtype == DTB_BF16)
-        hipLaunchKernelGGL(embed_fwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)wte, (const bf16 *)wpe,
+        DTB_LAUNCH(embed_fwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)wte, (const bf16 *)wpe,
                            BT, Tn, C, V, (bf16 *)x);
     else
-        hipLaunchKernelGGL(embed_fwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)wte,
+        DTB_LAUNCH(embed_fwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)wte,
                            (const float *)wpe, BT, Tn, C, V, (float *)x);
     DTB_LAUNCH_CHECK("encoder_forward");
     if (g_timing_on) {
@@ -366,22 +366,22 @@ int embed_bwd(int dtype, const int *ids, const void *dx, int B, int Tn, int C, i
               hipStream_t s) {
     const long BT = (long)B * Tn;
     if (BT <= 0) return DTB_OK;
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     if (dwte) {
         dim3 grid((unsigned)((BT + 3) / 4));
         if (dtype == DTB_BF16)
-            hipLaunchKernelGGL(embed_bwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)dx, BT, C, V, dwte);
+            DTB_LAUNCH(embed_bwd_kernel<bf16>, grid, dim3(256), 0, s, ids, (const bf16 *)dx, BT, C, V, dwte);
         else
-            hipLaunchKernelGGL(embed_bwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)dx, BT, C, V,
+            DTB_LAUNCH(embed_bwd_kernel<float>, grid, dim3(256), 0, s, ids, (const float *)dx, BT, C, V,
                                dwte);
         DTB_LAUNCH_CHECK("encoder_backward");
     }
     if (dwpe) {
         dim3 grid((unsigned)(((long)Tn * C + 255) / 256));
         if (dtype == DTB_BF16)
-            hipLaunchKernelGGL(embed_pos_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dx, B, Tn, C, dwpe);
+            DTB_LAUNCH(embed_pos_bwd_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dx, B, Tn, C, dwpe);
         else
-            hipLaunchKernelGGL(embed_pos_bwd_kernel<float>, grid, dim3(256), 0, s, (const float *)dx, B, Tn, C,
+            DTB_LAUNCH(embed_pos_bwd_kernel<float>, grid, dim3(256), 0, s, (const float *)dx, B, Tn, C,
                                dwpe);
         DTB_LAUNCH_CHECK("encoder_backward (positions)");
     }
@@ -394,17 +394,17 @@ int embed_bwd(int dtype, const int *ids, const void *dx, int B, int Tn, int C, i
 
 int softmax_xent_rows(int dtype, const void *logits, long ldl, const int *targets, long R, int V, float scale,
                       float *row_loss, void *dlogits, float *loss, hipStream_t s) {
-    if (g_timing_on) timing_begin(s);
+    if (g_timing_on) timing_begin(s, K_ELEM);
     if (R > 0) {
         if (dtype == DTB_BF16)
-            hipLaunchKernelGGL(softmax_xent_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)logits,
+            DTB_LAUNCH(softmax_xent_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)logits,
                                ldl, targets, V, scale, row_loss, (bf16 *)dlogits);
         else
-            hipLaunchKernelGGL(softmax_xent_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
+            DTB_LAUNCH(softmax_xent_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
                                (const float *)logits, ldl, targets, V, scale, row_loss, (float *)dlogits);
         DTB_LAUNCH_CHECK("softmax_ce");
     }
-    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, R, scale, loss);
+    DTB_LAUNCH(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, R, scale, loss);
     DTB_LAUNCH_CHECK("softmax_ce loss");
     if (g_timing_on) {
         const double es = dtype == DTB_BF16 ? 2 : 4;
@@ -443,14 +443,14 @@ int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp
     size_t g1 = gemm_ws_bytes(vc, C, R, dtype), g2 = gemm_ws_bytes(R, C, vc, dtype);
     const size_t gws_bytes = g1 > g2 ? g1 : g2;
     if (R <= 0) {  // no rows: the loss is zero
-        hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, 0L, scale, loss);
+        DTB_LAUNCH(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, 0L, scale, loss);
         DTB_LAUNCH_CHECK("lm_head_ce loss");
         return DTB_OK;
     }
     const bool grads = dinp || dw;
     if (dacc) {
         const long long n4 = (long long)R * C / 4;
-        hipLaunchKernelGGL(zero4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc, n4);
+        DTB_LAUNCH(zero4_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc, n4);
         DTB_LAUNCH_CHECK("lm_head_ce zero");
     }
     // head j: vocabulary rows j*V .. j*V+V-1 of w, targets[r*K + j], row_loss[r*K + j]
@@ -476,14 +476,14 @@ int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp
             int r = logits(v0, n);
             if (r) return r;
             if (dtype == DTB_BF16)
-                hipLaunchKernelGGL(ce_chunk_stats_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)chunk,
+                DTB_LAUNCH(ce_chunk_stats_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (const bf16 *)chunk,
                                    ldc, n, v0, tj, K, rm, rs, tl, i == 0);
             else
-                hipLaunchKernelGGL(ce_chunk_stats_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
+                DTB_LAUNCH(ce_chunk_stats_kernel<float>, dim3((unsigned)R), dim3(256), 0, s,
                                    (const float *)chunk, ldc, n, v0, tj, K, rm, rs, tl, i == 0);
             DTB_LAUNCH_CHECK("lm_head_ce stats");
         }
-        hipLaunchKernelGGL(ce_finish_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, rm, rs, tl, tj, K,
+        DTB_LAUNCH(ce_finish_kernel, dim3((unsigned)((R + 255) / 256)), dim3(256), 0, s, rm, rs, tl, tj, K,
                            (long)R, V, lse, row_loss + j);
         DTB_LAUNCH_CHECK("lm_head_ce finish");
         if (!grads) continue;
@@ -493,10 +493,10 @@ int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp
             int r = logits(v0, n);
             if (r) return r;
             if (dtype == DTB_BF16)
-                hipLaunchKernelGGL(ce_chunk_grad_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (bf16 *)chunk, ldc,
+                DTB_LAUNCH(ce_chunk_grad_kernel<bf16>, dim3((unsigned)R), dim3(256), 0, s, (bf16 *)chunk, ldc,
                                    n, v0, tj, K, lse, scale);
             else
-                hipLaunchKernelGGL(ce_chunk_grad_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (float *)chunk,
+                DTB_LAUNCH(ce_chunk_grad_kernel<float>, dim3((unsigned)R), dim3(256), 0, s, (float *)chunk,
                                    ldc, n, v0, tj, K, lse, scale);
             DTB_LAUNCH_CHECK("lm_head_ce gradient");
             if (dacc) {  // dinp += dlogits_chunk W_chunk
@@ -520,11 +520,11 @@ int head_ce(float *loss, float *row_loss, void *dinp, float *dw, const void *inp
             }
         }
     }
-    hipLaunchKernelGGL(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, (long)R * K, scale, loss);
+    DTB_LAUNCH(loss_sum_kernel, dim3(1), dim3(256), 0, s, row_loss, (long)R * K, scale, loss);
     DTB_LAUNCH_CHECK("lm_head_ce loss");
     if (dinp && dtype == DTB_BF16) {
         const long long n4 = (long long)R * C / 4;
-        hipLaunchKernelGGL(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc,
+        DTB_LAUNCH(f32_to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dacc,
                            (bf16 *)dinp, n4);
         DTB_LAUNCH_CHECK("lm_head_ce convert");
     }
@@ -546,8 +546,8 @@ int adamw(float *p, float *g, float *m, float *v, void *lowp, long long n, float
     long long blocks = (n4 + 255) / 256;
     if (blocks > (1LL << 20)) blocks = 1LL << 20;
     if (blocks < 1) blocks = 1;
-    if (g_timing_on) timing_begin(s);
-    hipLaunchKernelGGL(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    if (g_timing_on) timing_begin(s, K_ELEM);
+    DTB_LAUNCH(adamw_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
     DTB_LAUNCH_CHECK("adamw_update");
     if (g_timing_on) timing_end(s, K_ELEM, 0, (double)n * (28 + (lowp ? 2 : 0) + (zero_g ? 4 : 0)));
     return DTB_OK;

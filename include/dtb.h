@@ -345,7 +345,9 @@ const char *dtb_strerror(int code);
 const char *dtb_version(void);
 
 /* Optional per-kernel timing for measurement: while enabled, every kernel the
- * library enqueues is bracketed by HIP events on its stream, grouped by kernel
+ * library enqueues in an enabled class carries HIP start / stop events on its
+ * own dispatch packet (hipExtLaunchKernelGGL, so no marker packets are added
+ * between kernels), grouped by kernel
  * class (0 forward-projection GEMMs, 1 attn_fwd, 2 attn_bwd, 3 elementwise,
  * 4 input-gradient GEMMs, 5 weight-gradient GEMMs, 6 the decode-attention
  * kernel, 7 its chunk merge), together with the algorithmic flops / bytes of
@@ -360,7 +362,9 @@ typedef struct {
     double bytes;       /* summed algorithmic HBM bytes */
     long long launches; /* number of launches */
 } dtb_timing;
-int dtb_timing_enable(int on);
+/* class_mask: bit c enables class c; a negative value enables every class,
+ * 0 disables timing. */
+int dtb_timing_enable(int class_mask);
 int dtb_timing_collect(dtb_timing *out, int max_classes);
 
 #ifdef __cplusplus
