@@ -71,25 +71,32 @@ def test_linear_rejects_bad_shapes():
     assert L.linear_workspace_bytes(4, 16, 16, 7) == 0
 
 
-def test_weight_grad_split8():
-    """The weight gradient of a 2048 x 2048 layer over 8192 rows: 64 tiles x 8
-    K splits of 1024 rows = 512 workgroups, then the split reduction.  Checked on a spread of output rows (dW[n] = sum_r
-    dy[r, n] x[r]) against the oracle's linear backward of those columns."""
+@pytest.mark.parametrize("R,K,N,splits", [(8192, 2048, 4096, 2), (8192, 2048, 2048, 4), (4096, 512, 512, 8),
+                                           (65536, 256, 256, 16)])
+def test_weight_grad_splits(R, K, N, splits):
+    """Weight gradients whose row count is split over several workgroups per
+    output tile (fp32 partials, then the split reduction into dW, which starts
+    at 0.5): shapes on which the split choice takes 2, 4, 8 and 16 splits (read
+    back from the workspace size).  Checked on a spread of output rows (dW[n] = sum_r
+    dy[r, n] x[r]) against the oracle's linear backward of those rows."""
     require_gpu()
     import torch
     import oracle
     from decoder_only_transformer_block_amd import binding, inputs
     from decoder_only_transformer_block_amd.runtime import to_device, to_numpy
-    R, K, N = 8192, 2048, 2048
-    announce(f"linear weight gradient (8 K splits) R={R} K={K} N={N} bf16")
+    wsb = binding.linear_workspace_bytes(R, K, N, "bf16")
+    # the partials take splits x N x K floats; the bias-gradient partials and
+    # alignment add less than one more N x K share on these shapes
+    assert (wsb - 256) // (4 * N * K) in (splits, splits + 1), (wsb, splits)
+    announce(f"linear weight gradient ({splits} splits) R={R} K={K} N={N} bf16")
     x = inputs.tensor(11, "pw.x", (R, K), dtype="bf16")
     w = inputs.tensor(11, "pw.w", (N, K), std=0.05, dtype="bf16")
     dy = inputs.tensor(11, "pw.dy", (R, N), dtype="bf16")
     X, W, DY = (to_device(a, "bf16") for a in (x, w, dy))
     dw = torch.full((N, K), 0.5, dtype=torch.float32, device="cuda")
-    ws = torch.empty(binding.linear_workspace_bytes(R, K, N, "bf16"), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
     binding.linear_backward(None, dw, None, DY, X, W, R, K, N, "bf16", ws)
     torch.cuda.synchronize()
-    cols = np.array([0, 1, 255, 256, 511, 777, 1024, 1500, 2047])
+    cols = np.unique(np.array([0, 1, 255, 256, 511, 777, 1024, 1500, 2047, 3000, N - 1]) % N)
     _, r_dw, _ = oracle.linear_backward(dy[:, cols], x, w[cols])
     check("dW[cols]", to_numpy(dw)[cols] - 0.5, r_dw, TOL["bf16"])
