@@ -225,6 +225,34 @@ struct WsLayout {
     size_t gemm_bytes;
 };
 
+// A second stream per device for the weight-gradient GEMMs of block_backward:
+// each runs beside the input-gradient GEMM of the same projection (the two
+// only read the same gradient), so either fills the other's last partial
+// round of workgroups and the split-K reduction overlaps matrix work.  Created
+// once per device at default priority, with two events that carry no timing;
+// null when creation fails (everything then runs on the caller's stream).
+struct SideStream {
+    hipStream_t s;
+    hipEvent_t fork, join;
+};
+static SideStream *side_stream() {
+    static std::mutex mu;
+    static SideStream ss[64];
+    static int state[64];  // 0 untried, 1 ready, 2 failed
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lk(mu);
+    if (state[dev] == 0) {
+        SideStream t{};
+        bool ok = hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) == hipSuccess;
+        ok = ok && hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess;
+        ss[dev] = t;
+        state[dev] = ok ? 1 : 2;
+    }
+    return state[dev] == 1 ? &ss[dev] : nullptr;
+}
+
 static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -707,32 +735,63 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     dw.out_f32 = true;
     dw.accumulate = true;
 
+    // weight gradients on the side stream: each forks after the main stream
+    // has produced its inputs and reads only buffers that nothing later in
+    // this call writes, except dy, which the last kernel may overwrite (dx_in
+    // may be dx_out): the main stream joins before that kernel
+    SideStream *side = side_stream();
+    hipStream_t s2 = side ? side->s : s;
+    bool forked = false;
+    auto fork = [&]() -> int {
+        if (!side) return DTB_OK;
+        forked = true;
+        hipError_t e = hipEventRecord(side->fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s2, side->fork, 0);
+        return e == hipSuccess ? DTB_OK : set_launch_error(e, "block_backward fork");
+    };
+    auto join = [&]() -> int {
+        if (!side || !forked) return DTB_OK;
+        forked = false;
+        hipError_t e = hipEventRecord(side->join, s2);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, side->join, 0);
+        return e == hipSuccess ? DTB_OK : set_launch_error(e, "block_backward join");
+    };
+    // an early return (a launch error) still leaves the caller's stream
+    // waiting for everything already enqueued on the side stream
+    struct JoinOnExit {
+        decltype(join) &j;
+        ~JoinOnExit() { (void)j(); }
+    } join_on_exit{join};
+
     // down projection: dh = dy Wdown; dWdown += dy^T h; db_down
     // (the activation backward stays a kernel of its own: in the GEMM epilogue
     // its 8 bytes per element of extra HBM traffic, which no MFMA work hides,
     // measured slower than the separate streaming pass)
     dinp.A = dy; dinp.lda = C; dinp.B = w->w_down; dinp.ldb = H; dinp.M = BT; dinp.N = H; dinp.K = C;
     dinp.out = dh; dinp.ldo = H;
+    TRY(fork());
     TRY(gemm(dinp, nullptr, 0, s));
     dw.A = dy; dw.lda = C; dw.B = h; dw.ldb = H; dw.M = C; dw.N = H; dw.K = BT; dw.out = gr->w_down; dw.ldo = H;
-    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    TRY(gemm(dw, gws, W.gemm_bytes, s2));
     if (c->mlp_bias) TRY(bias_grad(dt, dy, BT, C, gr->b_down, bpart, W.bparts, s));
     TRY(act_backward(c->mlp, dt, dh, up, BT, H, dup, s));
     // up projection: dn2 = dup Wup; dWup += dup^T n2
     dinp.A = dup; dinp.lda = d.W; dinp.B = w->w_up; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.W;
     dinp.out = dn2; dinp.ldo = C;
+    TRY(fork());
     TRY(gemm(dinp, nullptr, 0, s));
     dw.A = dup; dw.lda = d.W; dw.B = n2; dw.ldb = C; dw.M = d.W; dw.N = C; dw.K = BT; dw.out = gr->w_up; dw.ldo = C;
-    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    TRY(gemm(dw, gws, W.gemm_bytes, s2));
     if (c->mlp_bias) TRY(bias_grad(dt, dup, BT, d.W, gr->b_up, bpart, W.bparts, s));
     // norm2 backward + residual: dx2 = dy + Norm2^T(dn2)
     TRY(norm_backward(c->norm, dt, dn2, x2, w->g2, r2, mu2, dy, BT, C, dx2, gr->g2, gr->b2, npart, W.nparts, s));
     // output projection: dO = dx2 Wo; dWo += dx2^T o
     dinp.A = dx2; dinp.lda = C; dinp.B = w->wo; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = C;
     dinp.out = dO; dinp.ldo = C;
+    TRY(fork());
     TRY(gemm(dinp, nullptr, 0, s));
     dw.A = dx2; dw.lda = C; dw.B = o; dw.ldb = C; dw.M = C; dw.N = C; dw.K = BT; dw.out = gr->wo; dw.ldo = C;
-    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    TRY(gemm(dw, gws, W.gemm_bytes, s2));
     if (c->o_bias) TRY(bias_grad(dt, dx2, BT, C, gr->bo, bpart, W.bparts, s));
     // attention (dq and dk leave the kernels already rotated back by the transposed RoPE)
     float *cs = nullptr;
@@ -744,12 +803,15 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     // qkv projection: dn1 = dqkv Wqkv; dWqkv += dqkv^T n1
     dinp.A = dqkv; dinp.lda = d.QKV; dinp.B = w->wqkv; dinp.ldb = C; dinp.M = BT; dinp.N = C; dinp.K = d.QKV;
     dinp.out = dn1; dinp.ldo = C;
+    TRY(fork());
     TRY(gemm(dinp, nullptr, 0, s));
     dw.A = dqkv; dw.lda = d.QKV; dw.B = n1; dw.ldb = C; dw.M = d.QKV; dw.N = C; dw.K = BT; dw.out = gr->wqkv;
     dw.ldo = C;
-    TRY(gemm(dw, gws, W.gemm_bytes, s));
+    TRY(gemm(dw, gws, W.gemm_bytes, s2));
     if (c->qkv_bias) TRY(bias_grad(dt, dqkv, BT, d.QKV, gr->bqkv, bpart, W.bparts, s));
-    // norm1 backward + residual: dx_in = dx2 + Norm1^T(dn1)
+    // norm1 backward + residual: dx_in = dx2 + Norm1^T(dn1); every weight
+    // gradient has finished first (dx_in may be dy)
+    TRY(join());
     TRY(norm_backward(c->norm, dt, dn1, x_in, w->g1, r1, mu1, dx2, BT, C, dx_in, gr->g1, gr->b1, npart, W.nparts,
                       s));
     return DTB_OK;
