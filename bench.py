@@ -164,7 +164,8 @@ def timed_steps(args, step, roof_classes):
     """Time args.steps steps.  Inside the timed region only the roofline
     kernel's class carries HIP events (on the kernels' own dispatch packets);
     a second, untimed pass of the same steps with every class enabled gives
-    the per-class breakdown.  Returns (seconds, timings), where timings maps
+    the per-class breakdown (the library then runs the block backward on one
+    stream, so the classes' times do not overlap).  Returns (seconds, timings), where timings maps
     each class to its event totals and the roofline classes' entries come
     from the timed region."""
     import torch

@@ -56,6 +56,14 @@ void timing_begin(hipStream_t, int cls) {
     g_unit_a = g_unit_b = nullptr;
 }
 
+// While a class that block_backward launches is being timed, it runs on the
+// caller's stream only, so the per-class times are not inflated by kernels of
+// the side stream sharing the GPU.
+static bool timing_serializes_backward() {
+    const unsigned bwd = (1u << K_GEMM_DINP) | (1u << K_GEMM_DW) | (1u << K_ATTN_BWD) | (1u << K_ELEM);
+    return g_timing_on && (g_timing_mask & bwd) != 0;
+}
+
 void timing_launch_events(hipEvent_t *start, hipEvent_t *stop) {
     std::lock_guard<std::mutex> lk(g_tmu);
     *start = *stop = nullptr;
@@ -739,7 +747,7 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     // has produced its inputs and reads only buffers that nothing later in
     // this call writes, except dy, which the last kernel may overwrite (dx_in
     // may be dx_out): the main stream joins before that kernel
-    SideStream *side = side_stream();
+    SideStream *side = timing_serializes_backward() ? nullptr : side_stream();
     hipStream_t s2 = side ? side->s : s;
     bool forked = false;
     auto fork = [&]() -> int {
