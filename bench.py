@@ -96,7 +96,7 @@ def traffic_summary(root: str, cmds: dict) -> str:
          "copy_bytes": known, "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
          "traffic_bytes_per_launch": round(traffic)}
     lines = ["# HBM traffic of the forward-projection GEMM (%s, Llama-GQA 4-layer stack)" % GEMM_FWD_KERNEL, "",
-             "Counter runs (repository root on the GPU box, one counter per run):", "", "```"]
+             "Counter runs (from the repository root on an MI355X, one counter per run):", "", "```"]
     lines += cmds["commands"] + ["```", "",
               "FETCH_SIZE / WRITE_SIZE are read in KiB per dispatch and averaged over the kernel's dispatches "
               "(QKV, O, MLP up and MLP down projections of every layer).  Each is scaled by known bytes / "
@@ -395,7 +395,7 @@ def bench_decode(args):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this build has no multi-GPU "
+        print(f"bench.py runs on exactly one GPU (asked for --gpus {args.gpus}); this library has no multi-GPU "
               "path: the block shards over sequences with one gradient all-reduce per layer, described in the "
               "design notes but not built.", file=sys.stderr)
         sys.exit(2)
