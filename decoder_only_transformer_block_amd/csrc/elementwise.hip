@@ -353,7 +353,9 @@ int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int
 }
 
 // ------------------------------------------------------------ activations ---
-__device__ __forceinline__ float sigm(float x) { return 1.f / (1.f + __expf(-x)); }
+// logistic sigmoid with the hardware reciprocal (1 ulp; an IEEE division
+// here is a ten-instruction sequence); 1 + e^-x = inf gives 0
+__device__ __forceinline__ float sigm(float x) { return __builtin_amdgcn_rcpf(1.f + __expf(-x)); }
 template <typename T, int MLP>
 __global__ __launch_bounds__(256) void act_fwd_kernel(const T *up, long R, int H, T *h) {
     constexpr int EPC = 16 / sizeof(T);

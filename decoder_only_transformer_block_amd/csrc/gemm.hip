@@ -362,7 +362,8 @@ __device__ __forceinline__ void epilogue_swiglu(const f32x16 *acc, float *lw, co
             const f32x4 gv = gate_wave ? v : w, uv = gate_wave ? w : v;
             f32x4 h;
 #pragma unroll
-            for (int e = 0; e < 4; e++) h[e] = gv[e] / (1.f + __expf(-gv[e])) * uv[e];
+            for (int e = 0; e < 4; e++)  // silu(g) u, sigmoid by the hardware reciprocal (1 ulp)
+                h[e] = gv[e] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[e])) * uv[e];
             store_row4<bf16>(p.act_h, (long long)m * p.act_H + n, h);
         }
     }
