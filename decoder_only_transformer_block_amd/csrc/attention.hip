@@ -290,26 +290,35 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, fl
     const int hd = p.hd;
     // lanes sweep the row in 16-byte chunks; a head spans hd/EPC chunks
     const int nch = p.C / EPC, hch = hd / EPC;
-    for (int c0 = 0; c0 < nch; c0 += 64) {
-        int c = c0 + lane;
-        float s = 0.f;
-        if (c < nch) {
-            float fo[EPC], fd[EPC];
-            unpack16<T>(ld16(o + c * EPC), fo);
-            unpack16<T>(ld16(d + c * EPC), fd);
+    // four sweeps of loads in flight before any reduction (a row is 4 sweeps
+    // at C = 2048 in bf16)
+    const Buf bo(o), bdd(d);
+    for (int c00 = 0; c00 < nch; c00 += 4 * 64) {
+        u32x4 ov[4], dv[4];
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int c = c00 + 64 * u + lane;
+            ov[u] = bo.ld16(c * 16, c < nch);
+            dv[u] = bdd.ld16(c * 16, c < nch);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const int c = c00 + 64 * u + lane;
+            if (c00 + 64 * u >= nch) break;  // uniform
+            float fo[EPC], fd[EPC], s = 0.f;
+            unpack16<T>(ov[u], fo);
+            unpack16<T>(dv[u], fd);
 #pragma unroll
             for (int e = 0; e < EPC; e++) s += fo[e] * fd[e];
-        }
-        // reduce over the hch consecutive lanes of each head (hch is a power of 2)
-        for (int off = 1; off < hch && off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
-        if (hch > 64) {
-            // head wider than one sweep: not reached for hd <= 128 (hch <= 32)
-        }
-        if (c < nch && (c % hch) == 0) {
-            int h = c / hch;
-            const long long i = ((long long)b * p.NH + h) * p.T + tq;
-            D[i] = dsign * s;
-            if (lsn) lsn[i] = -p.lse_in[i] / p.scale;
+            // reduce over the hch consecutive lanes of each head (hch is a
+            // power of 2, at most 32 for hd <= 128)
+            for (int off = 1; off < hch && off < 64; off <<= 1) s += __shfl_xor(s, off, 64);
+            if (c < nch && (c % hch) == 0) {
+                int h = c / hch;
+                const long long i = ((long long)b * p.NH + h) * p.T + tq;
+                D[i] = dsign * s;
+                if (lsn) lsn[i] = -p.lse_in[i] / p.scale;
+            }
         }
     }
 }

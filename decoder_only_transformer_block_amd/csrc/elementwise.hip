@@ -108,17 +108,39 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         for (int e = 0; e < EPC; e++) gv[k][e] = 1.f;
         if (HAS_G && c < nch) unpack16<T>(ld16(g + c * EPC), gv[k]);
     }
-    for (long row = (long)blockIdx.x * 4 + wave; row < R; row += nwaves) {
+    // Each wave walks its rows with the next row's x, dy and residual
+    // gradient already loading while it reduces and stores the current one
+    // (two waves per SIMD leave no other latency hiding).
+    u32x4 qx[NPL], qd[NPL], qr[NPL];
+    auto fetch = [&](long rw) {
+        const bool live = rw < R;
+        const long rr = live ? rw : 0;
+        const Buf bx(x + rr * C), bd(dy + rr * C), br(dres ? dres + rr * C : dy + rr * C);
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
+            const int c = lane + 64 * k;
+            qx[k] = bx.ld16(c * 16, live && c < nch);
+            qd[k] = bd.ld16(c * 16, live && c < nch);
+            qr[k] = br.ld16(c * 16, live && dres != nullptr && c < nch);
+        }
+    };
+    long row = (long)blockIdx.x * 4 + wave;
+    fetch(row);
+    for (; row < R; row += nwaves) {
         const float r = rstd[row];
         const float mu = LN ? mean[row] : 0.f;
         float xh[NPL][EPC], d[NPL][EPC];
-        float s1 = 0.f, s2 = 0.f;
-        const Buf bx(x + row * C), bd(dy + row * C);
+        u32x4 rsv[NPL];
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
-            int c = lane + 64 * k;
-            unpack16<T>(bx.ld16(c * 16, c < nch), xh[k]);
-            unpack16<T>(bd.ld16(c * 16, c < nch), d[k]);
+            unpack16<T>(qx[k], xh[k]);
+            unpack16<T>(qd[k], d[k]);
+            rsv[k] = qr[k];
+        }
+        fetch(row + nwaves);
+        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+        for (int k = 0; k < NPL; k++) {
 #pragma unroll
             for (int e = 0; e < EPC; e++) {
                 xh[k][e] = (xh[k][e] - mu) * r;        // normalised input
@@ -129,11 +151,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         }
         s2 = wave_sum(s2) / C;
         if (LN) s1 = wave_sum(s1) / C;
-        // residual gradient added to the result (none when dres is null)
-        const Buf br(dres ? dres + row * C : dy + row * C);
-        u32x4 rsv[NPL];
-#pragma unroll
-        for (int k = 0; k < NPL; k++) rsv[k] = br.ld16((lane + 64 * k) * 16, dres != nullptr && lane + 64 * k < nch);
+        // residual gradient (rsv) added to the result (zeros when dres is null)
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
             int c = lane + 64 * k;
