@@ -15,6 +15,11 @@ pytestmark = pytest.mark.gpu
 SHAPES = [
     ("fwd256_ragged", 1100, 136, 6144),     # forward on 5 x 24 tiles of 256 (ragged rows, ragged K slab)
     ("dinp256", 1100, 6144, 136),           # input gradient on 5 x 24 tiles
+    # 64-k slabs: three whole groups of five slabs, a tail of one and a ragged
+    # last slab (1000 = 15 x 64 + 40); and K shorter than one slab
+    ("fwd256_longk", 1100, 1000, 6144),
+    ("dinp256_longk", 1100, 6144, 1000),
+    ("fwd256_shortk", 1100, 40, 6144),
     ("dw256_split", 600, 520, 776),         # weight gradient M=776, N=520 with split-K
     ("dw256_nosplit", 64, 1024, 2048),      # weight gradient M=2048, N=1024, K=64: one split
     # more than one round of 256 x 256 tiles (ragged rows and columns, 17 x 17 tiles)
