@@ -11,8 +11,8 @@ struct AttnP {
     void *o;        // forward output / dqkv for the backward
     float *lse;     // forward output
     const float *lse_in;
-    const float *D;     // backward: rowsum(dO o)   [B][NH][T]
-    const float *lsn;   // backward: -lse / scale, lse in raw score units  [B][NH][T]
+    float *D;           // backward: -rowsum(dO o)   [B][NH][T]
+    float *lsn;         // backward: -lse / scale, lse in raw score units  [B][NH][T]
     const float2 *rope_cs;  // backward: NeoX (cos, sin) table [T][hd/2] to rotate dq, dk back, or null
     int B, T, C, NH, NKV, hd, QKV;
     float sl2;      // log2(e) / sqrt(hd)
@@ -73,7 +73,8 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // bf16 kernels (head width padded to HD in {16, 32, 64, 128})
 hipError_t attn_fwd_bf16(const AttnP &p, int HD, hipStream_t s);
-// dQ and dK/dV; p.D and p.lsn must already hold -rowsum(dO o) (negated) and -lse / scale
+// dQ and dK/dV; the dQ kernel writes p.D = -rowsum(dO o) and p.lsn = -lse / scale
+// (from p.out, p.dout and p.lse_in) for the dK/dV kernel that follows it
 hipError_t attn_bwd_bf16(const AttnP &p, int HD, hipStream_t s);
 
 }  // namespace dtb

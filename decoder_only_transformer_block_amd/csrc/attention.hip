@@ -272,14 +272,11 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: D = rowsum(dO * O)   [B][NH][T] fp32, one wave per (b, t) row;
-// optionally lsn = -lse / scale in the same layout
+// backward of the fp32 kernels: D = rowsum(dO * O)   [B][NH][T] fp32, one wave
+// per (b, t) row (the bf16 dQ kernel computes its own D)
 // ---------------------------------------------------------------------------
 template <typename T>
-// D = rowsum(dO o) per (b, h, t), written times dsign (the bf16 kernels take
-// -D); with lsn, also -lse / scale (the bf16 kernels start their score
-// accumulators from it, so the exponent is one multiply)
-__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, float *lsn, float dsign) {
+__global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
     const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     if (row >= (long long)p.B * p.T) return;
@@ -316,8 +313,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D, fl
             if (c < nch && (c % hch) == 0) {
                 int h = c / hch;
                 const long long i = ((long long)b * p.NH + h) * p.T + tq;
-                D[i] = dsign * s;
-                if (lsn) lsn[i] = -p.lse_in[i] / p.scale;
+                D[i] = s;
             }
         }
     }
@@ -629,8 +625,7 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
         init = true;
     }
     long long rows = (long long)p.B * p.T;
-    DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D,
-                       (float *)nullptr, 1.f);
+    DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
@@ -644,15 +639,10 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     return hipGetLastError();
 }
 
-// bf16: -D and -lse / scale by the row kernel, then the dQ and dK/dV kernels
+// bf16: the dQ kernel computes -D and -lse / scale per query (it holds the
+// query's dO row) and stores them for the dK/dV kernel
 static hipError_t bwd_bf16(const AttnP &p, int hdp, float *D, hipStream_t s) {
     float *lsn = D + (long long)p.B * p.NH * p.T;
-    long long rows = (long long)p.B * p.T;
-    // the bf16 kernels take -D: the dK/dV kernel starts its dP accumulation from it
-    DTB_LAUNCH((attn_bwd_dot_kernel<bf16>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D, lsn,
-                       -1.f);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     AttnP q = p;
     q.D = D;
     q.lsn = lsn;

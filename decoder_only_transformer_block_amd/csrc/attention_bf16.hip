@@ -287,16 +287,31 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
     {
         const Buf bq(base + h * p.hd);
         const Buf bd(reinterpret_cast<const bf16 *>(p.dout) + (long long)b * p.T * p.C + h * p.hd);
+        const Buf bo(reinterpret_cast<const bf16 *>(p.out) + (long long)b * p.T * p.C + h * p.hd);
+        // D = rowsum(dO o) of this lane's query: the lane holds chunks 2c + g
+        // of the row, its partner (lane ^ 32) the others
+        float dot = 0.f;
 #pragma unroll
         for (int c = 0; c < L::NC; c++) {
             const int ch = 2 * c + g;
             const bool ok = qi < p.T && ch * 8 < p.hd;
             qf[c] = bq.ld16((int)(((long long)qi * stride + ch * 8) * 2), ok);
             df[c] = bd.ld16((int)(((long long)qi * p.C + ch * 8) * 2), ok);
+            const u32x4 of = bo.ld16((int)(((long long)qi * p.C + ch * 8) * 2), ok);
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                dot += __uint_as_float(df[c][e] << 16) * __uint_as_float(of[e] << 16) +
+                       __uint_as_float(df[c][e] & 0xffff0000u) * __uint_as_float(of[e] & 0xffff0000u);
         }
+        dot += __shfl_xor(dot, 32, 64);
         if (qi < p.T) {
-            nls = p.lsn[li];
-            nDq = p.D[li];
+            // also kept for the dK/dV kernel, which runs after this one
+            nls = -p.lse_in[li] / p.scale;
+            nDq = -dot;
+            if (g == 0) {
+                p.lsn[li] = nls;
+                p.D[li] = nDq;
+            }
         }
     }
     issue(s0, 0);
