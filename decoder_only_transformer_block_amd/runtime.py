@@ -81,6 +81,7 @@ class BlockStack:
         shape = (cfg.B, cfg.T, cfg.C)
         td = torch_dtype(cfg.dtype)
         self.acts = [torch.empty(shape, dtype=td, device=device) for _ in range(len(layer_weights) + 1)]
+        self.inp = self.acts[0]   # the first block's input (acts[0] unless forward was given x)
         self.dx = torch.empty(shape, dtype=td, device=device)
 
     @property
@@ -88,21 +89,26 @@ class BlockStack:
         return len(self.weights)
 
     def forward(self, x=None, stream=None):
-        """x (device tensor [B,T,C]) -> output of the last block."""
-        if x is not None:
-            self.acts[0].copy_(x)
+        """x (device tensor [B,T,C]) -> output of the last block.  x is read
+        where it is (not copied) and is the input the backward uses: it must
+        stay unchanged until then.  Without x, acts[0] is the input."""
+        self.inp = x if x is not None else self.acts[0]
         for i in range(self.L):
-            binding.block_forward(self.c, self.weights[i], self.acts[i], self.acts[i + 1], self.saved[i],
-                                  self.workspace, stream)
+            xin = self.inp if i == 0 else self.acts[i]
+            binding.block_forward(self.c, self.weights[i], xin, self.acts[i + 1], self.saved[i], self.workspace,
+                                  stream)
         return self.acts[self.L]
 
     def backward(self, dy, stream=None):
-        """dy: gradient w.r.t. the last output; returns dx of the first input.
-        Parameter gradients accumulate into self.grads."""
-        self.dx.copy_(dy)
+        """dy: gradient w.r.t. the last output (only read); returns dx of the
+        first input (self.dx).  The top block reads dy and writes self.dx, every
+        block below it works in place on self.dx.  Parameter gradients
+        accumulate into self.grads."""
         for i in reversed(range(self.L)):
-            binding.block_backward(self.c, self.weights[i], self.acts[i], self.saved[i], self.dx, self.dx,
-                                   self.grads[i], self.workspace, stream)
+            xin = self.inp if i == 0 else self.acts[i]
+            dout = dy if i == self.L - 1 else self.dx
+            binding.block_backward(self.c, self.weights[i], xin, self.saved[i], dout, self.dx, self.grads[i],
+                                   self.workspace, stream)
         return self.dx
 
     def zero_grads(self):

@@ -76,23 +76,28 @@ def test_block_stack_parity(case):
 
 
 def test_block_backward_in_place_and_accumulate():
-    """dx_in may alias dx_out, and a second backward adds to the gradients."""
+    """dx_in may alias dx_out (the lower of the two blocks runs in place on
+    the stack's dx), dy is only read, and a second backward adds to the
+    gradients."""
     require_gpu()
     import torch
     from decoder_only_transformer_block_amd import configs
     from decoder_only_transformer_block_amd.runtime import BlockStack, to_device, to_numpy
-    cfg = configs.MINI_QWEN2.replace(L=1)
-    ws = [configs.block_weights(cfg, 0, perturb=True)]
-    announce("block in-place / accumulate (mini_qwen2, 1 layer)")
+    cfg = configs.MINI_QWEN2.replace(L=2)
+    ws = [configs.block_weights(cfg, l, perturb=True) for l in range(cfg.L)]
+    announce("block in-place / accumulate (mini_qwen2, 2 layers)")
     st = BlockStack(cfg, ws)
     x = to_device(configs.block_input(cfg), cfg.dtype)
     dy = to_device(configs.block_dout(cfg), cfg.dtype)
+    dy0 = to_numpy(dy).copy()
     st.forward(x)
     st.backward(dy)
-    g1 = {k: v.clone() for k, v in st.grads[0].items()}
+    g1 = [{k: v.clone() for k, v in g.items()} for g in st.grads]
     dx1 = st.dx.clone()
     st.backward(dy)
     torch.cuda.synchronize()
-    for k in g1:
-        np.testing.assert_allclose(to_numpy(st.grads[0][k]), 2 * to_numpy(g1[k]), rtol=1e-5, atol=1e-7)
+    for l in range(cfg.L):
+        for k in g1[l]:
+            np.testing.assert_allclose(to_numpy(st.grads[l][k]), 2 * to_numpy(g1[l][k]), rtol=1e-5, atol=1e-7)
     np.testing.assert_array_equal(to_numpy(st.dx), to_numpy(dx1))
+    np.testing.assert_array_equal(to_numpy(dy), dy0)
