@@ -87,7 +87,8 @@ int attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, in
  *   dqkv [B, T, QKV]  output, dtype, OVERWRITTEN (every element written)
  *   qkv, out, dout    inputs as in attn_forward (out and lse from attn_forward)
  *   workspace attn_workspace_bytes(B, T, NH) bytes of device scratch (holds
- *             D = rowsum(dO o) and lse * log2(e), each [B, NH, T] fp32);
+ *             -D = -rowsum(dO o) and -lse / scale, each [B, NH, T]
+ *             fp32, written and read by the backward's own kernels);
  *             contents on entry are ignored
  * Deterministic (no atomics). */
 int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout,
