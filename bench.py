@@ -545,8 +545,9 @@ def main():
         if dom == "gemm_fwd":
             st = stored_traffic(args.workload) if cfg.dtype == "bf16" else None
             traffic = st["traffic_bytes_per_launch"] if st else None
+        gemm_name = GEMM_FWD_KERNEL if cfg.dtype == "bf16" else "gemm_kernel<float, 128|64, 128|64, true, true>"
         roof = {"kernel": "attention backward (dq + dk/dv kernels)" if dom == "attn_bwd" else
-                f"forward-projection GEMM {GEMM_FWD_KERNEL} (QKV, O, MLP up, MLP down)",
+                f"forward-projection GEMM {gemm_name} (QKV, O, MLP up, MLP down)",
                 "bound": "mfma", "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": traffic,
                 "avg_launch_ms": round(d["ms"] / d["launches"], 4),
