@@ -1,7 +1,8 @@
 """attn_decode (HIP, through the C ABI) against the oracle: one query per
 sequence against a KV cache with ragged lengths, element by element, in both
 dtypes, at every supported head width, for MHA / GQA / MQA groups (including
-groups wider than one wave's 32 head columns), at chunk boundaries, with empty
+groups wider than one wave's 32 head columns, and more kv heads than a
+workgroup's eight waves), at chunk boundaries, with empty
 caches, and with the rows past each length filled with NaN (they must never
 be read).  The full-size case is the benchmark's own workload and launch
 configuration, checked on sampled sequences."""
@@ -52,6 +53,8 @@ def _cases():
         out.append((DecodeConfig(f"mqa_{dt}", B=3, Tmax=257, NH=12, NKV=1, hd=64, dtype=dt, **base), 32))
         out.append((DecodeConfig(f"grp40_{dt}", B=2, Tmax=150, NH=80, NKV=2, hd=32, dtype=dt, **base), 64))
         out.append((DecodeConfig(f"grp3_{dt}", B=4, Tmax=333, NH=12, NKV=4, hd=64, dtype=dt, **base), 0))
+        # more kv heads than one workgroup's waves: two groups of eight per position
+        out.append((DecodeConfig(f"kv16_{dt}", B=3, Tmax=300, NH=32, NKV=16, hd=64, dtype=dt, **base), 64))
         out.append((DecodeConfig(f"one_chunk_{dt}", B=4, Tmax=1000, NH=8, NKV=2, hd=64, dtype=dt, **base), 1024))
     return out
 
