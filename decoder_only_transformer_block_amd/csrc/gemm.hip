@@ -59,7 +59,7 @@ struct KParams {
     const void *bias;
     const void *res;
     long long ldr;
-    float *part;   // split partials [splits][M][N]
+    float *part;   // split partials of splits 1 .. S-1: [S-1][M][N] (split 0 accumulates into out)
     const float2 *rope_cs;  // NeoX RoPE of the output columns [0, rope_cols) (mode 0), or null
     int rope_T, rope_hd, rope_cols;
     // mode 5: SwiGLU forward (256 x 256 kernel) -- tile column block tn holds
@@ -274,7 +274,9 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
             const int row = q * RPP + rr;
             in[q] = load_row4<T>(rb, (long long)row * p.ldr + n, nok && m_base + row < p.M);
         }
-    } else if (mode == 2) {
+    } else if (mode == 2 || (mode == 3 && blockIdx.z == 0)) {
+        // accumulate (split 0 of a split-K launch adds its partial into the
+        // output here; the reduction adds splits 1 .. S-1 afterwards)
         const char *ob = static_cast<const char *>(p.out) + (long long)m_base * p.ldo * 4;
 #pragma unroll
         for (int q = 0; q < PASSES; q++) {
@@ -317,10 +319,10 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
             }
         } else if (mode == 1) {
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + bv;
-        } else if (mode == 2) {
+        } else if (mode == 2 || blockIdx.z == 0) {
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + (long long)m * p.ldo + n) = v + in[q];
         } else {
-            *reinterpret_cast<f32x4 *>(p.part + ((long long)blockIdx.z * p.M + m) * p.N + n) = v;
+            *reinterpret_cast<f32x4 *>(p.part + ((long long)(blockIdx.z - 1) * p.M + m) * p.N + n) = v;
         }
     }
 }
@@ -952,8 +954,9 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
     }
 }
 
-// out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0), z in order.  The
-// split count is a template argument so that every partial's load is issued
+// out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0), z in order: the
+// partials of splits 1 .. S-1 (split 0 has already added its own into out).
+// The count is a template argument so that every partial's load is issued
 // before the first add; partials are read exactly once (non-temporal).
 template <int S>
 __global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *out, long long ldo, int M, int N) {
@@ -975,11 +978,11 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *o
 static hipError_t launch_reduce(const float *part, float *out, long long ldo, int M, int N, int splits, hipStream_t s) {
     const long long total4 = (long long)M * N / 4;
     const dim3 grid((unsigned)((total4 + 255) / 256));
-    switch (splits) {
-    case 2: DTB_LAUNCH(splitk_reduce<2>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 4: DTB_LAUNCH(splitk_reduce<4>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 8: DTB_LAUNCH(splitk_reduce<8>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    default: DTB_LAUNCH(splitk_reduce<16>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    switch (splits - 1) {  // partial slots
+    case 1: DTB_LAUNCH(splitk_reduce<1>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 3: DTB_LAUNCH(splitk_reduce<3>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    case 7: DTB_LAUNCH(splitk_reduce<7>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    default: DTB_LAUNCH(splitk_reduce<15>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
     }
     return hipGetLastError();
 }
@@ -1098,7 +1101,7 @@ size_t gemm_ws_bytes(int M, int N, int K, int dtype) {
     g.M = M; g.N = N; g.K = K; g.dtype = dtype; g.out_f32 = true; g.accumulate = true;
     TileChoice tc = choose_tile(M, N, dtype, true);
     int sp = choose_splits(g, tc);
-    return sp > 1 ? (size_t)sp * M * N * sizeof(float) : 0;
+    return sp > 1 ? (size_t)(sp - 1) * M * N * sizeof(float) : 0;  // split 0 needs no partial
 }
 
 int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
@@ -1107,7 +1110,7 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
     TileChoice tc = choose_tile(g.M, g.N, g.dtype, splittable);
     if (tc.bm == 256 && tc.bn == 256 && g.out_f32 && !g.accumulate) tc = {128, 128};
     int splits = choose_splits(g, tc);
-    if (splits > 1 && (!ws || ws_bytes < (size_t)splits * g.M * g.N * sizeof(float))) splits = 1;
+    if (splits > 1 && (!ws || ws_bytes < (size_t)(splits - 1) * g.M * g.N * sizeof(float))) splits = 1;
     const int BK = g.dtype == DTB_BF16 ? 64 : 32;
     KParams p{};
     p.A = g.A; p.B = g.B; p.lda = g.lda; p.ldb = g.ldb;

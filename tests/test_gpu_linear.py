@@ -90,9 +90,10 @@ def test_weight_grad_splits(R, K, N, splits):
     from decoder_only_transformer_block_amd import binding, inputs
     from decoder_only_transformer_block_amd.runtime import to_device, to_numpy
     wsb = binding.linear_workspace_bytes(R, K, N, "bf16")
-    # the partials take splits x N x K floats; the bias-gradient partials and
-    # alignment add less than one more N x K share on these shapes
-    assert (wsb - 256) // (4 * N * K) in (splits, splits + 1), (wsb, splits)
+    # the partials of splits 1 .. S-1 take (splits - 1) x N x K floats (split 0
+    # adds into dW directly); the bias-gradient partials and alignment add less
+    # than one more N x K share on these shapes
+    assert (wsb - 256) // (4 * N * K) in (splits - 1, splits), (wsb, splits)
     announce(f"linear weight gradient ({splits} splits) R={R} K={K} N={N} bf16")
     x = inputs.tensor(11, "pw.x", (R, K), dtype="bf16")
     w = inputs.tensor(11, "pw.w", (N, K), std=0.05, dtype="bf16")
