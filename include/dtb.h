@@ -206,7 +206,13 @@ int block_forward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const vo
  *   dx_in  [B, T, C] dtype: gradient w.r.t. x_in (output, OVERWRITTEN);
  *          may alias dx_out (the residual gradient is updated in place)
  *   g      parameter gradients, fp32, ACCUMULATED
- *   workspace block_workspace_bytes(cfg) bytes, scratch */
+ *   workspace block_workspace_bytes(cfg) bytes, scratch
+ * The weight-gradient GEMMs run on a second stream that the library creates
+ * once per device (default priority), forked from `stream` after each
+ * gradient is produced and joined back before the call's last kernel: all of
+ * the call's work is ordered before anything enqueued on `stream` afterwards.
+ * That stream and its two events are shared by every call on a device, so
+ * calls on one device must not be issued from several host threads at once. */
 int block_backward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const void *x_in,
                    const void *saved, const void *dx_out, void *dx_in,
                    const dtb_block_grads *g, void *workspace, void *stream);
