@@ -71,6 +71,25 @@ __device__ __forceinline__ void store_rows_bf16(bf16 *row, const f32x16 *acc, fl
 // forward: one workgroup = 4 waves x 32 queries of one (b, h); key tiles of 64;
 // last query blocks launched first (causal load balance)
 // ---------------------------------------------------------------------------
+// (query block, b*NH + h) of a query-owning workgroup.  Workgroups go to the
+// eight XCDs round robin; when the B*NKV head groups split evenly over them,
+// the G = NH/NKV query heads of a group (which read the same K / V tiles) are
+// placed on one XCD one after another, so that XCD's L2 serves all of them.
+// Heaviest query blocks still come first.
+__device__ __forceinline__ void qowner_coords(int x, int nqb, int B, int NH, int NKV, int &qb, int &bh) {
+    const int BH = B * NH, NG = B * NKV, G = NH / NKV;
+    if (NG % 8 != 0) {
+        qb = nqb - 1 - x / BH;
+        bh = x % BH;
+        return;
+    }
+    const int xcd = x & 7, r = x >> 3;
+    const int hg = r % G, t = r / G;
+    const int g = (t % (NG / 8)) * 8 + xcd;
+    qb = nqb - 1 - t / (NG / 8);
+    bh = g * G + hg;
+}
+
 template <int HD, int NS>
 __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
     using L = TL<HD>;
@@ -83,7 +102,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
 #define STG(S) ((S) == 0 ? s0 : (S) == 1 ? s1 : s2)
 
     const int nqb = (p.T + BQ - 1) / BQ, BH = p.B * p.NH;
-    const int qb = nqb - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    int qb, bh;
+    qowner_coords((int)blockIdx.x, nqb, p.B, p.NH, p.NKV, qb, bh);
     const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
     const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -259,7 +279,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
 #define STG(S) ((S) == 0 ? s0 : (S) == 1 ? s1 : s2)
 
     const int nqb = (p.T + BQ - 1) / BQ, BH = p.B * p.NH;
-    const int qb = nqb - 1 - (int)(blockIdx.x / BH), bh = blockIdx.x % BH;
+    int qb, bh;
+    qowner_coords((int)blockIdx.x, nqb, p.B, p.NH, p.NKV, qb, bh);
     const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
     const int t = threadIdx.x, lane = t & 63, g = lane >> 5, l32 = lane & 31;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
