@@ -122,7 +122,7 @@ def parse():
     ap.add_argument("--traffic-summary", default="",
                     help="only write the forward-GEMM traffic summary from the rocprofv3 runs under this "
                          "directory (subdirectories fetch, write, copy_fetch, copy_write) and exit")
-    ap.add_argument("--cpu-tokens", type=int, default=256,
+    ap.add_argument("--cpu-tokens", type=int, default=512,
                     help="tokens of the oracle's bounded sample (one sequence, one layer)")
     return ap.parse_args()
 
