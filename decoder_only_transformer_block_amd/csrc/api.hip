@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <new>
 #include <vector>
 
 #include "common.h"
@@ -175,6 +176,10 @@ static int check_attn_shape(int B, int T, int C, int NH, int NKV, int dtype) {
     if (!hd_ok(C / NH, dtype)) return DTB_EINVAL_SHAPE;
     long long QKV = (long long)C + 2LL * NKV * (C / NH);
     if ((long long)B * T * QKV >= (1LL << 40) || (long long)B * T >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    // the attention kernels address a sequence's rows by 32-bit byte offsets
+    // from the sequence base (qkv rows of QKV elements, out / dout rows of C)
+    const long long es = dtype == DTB_BF16 ? 2 : 4;
+    if ((long long)T * QKV * es >= (1LL << 31)) return DTB_EINVAL_SHAPE;
     return DTB_OK;
 }
 
@@ -233,33 +238,14 @@ struct WsLayout {
     size_t gemm_bytes;
 };
 
-// A second stream per device for the weight-gradient GEMMs of block_backward:
-// each runs beside the input-gradient GEMM of the same projection (the two
-// only read the same gradient), so either fills the other's last partial
-// round of workgroups and the split-K reduction overlaps matrix work.  Created
-// once per device at default priority, with two events that carry no timing;
-// null when creation fails (everything then runs on the caller's stream).
-struct SideStream {
+// The second stream of block_backward_overlap, owned by the caller (created
+// and destroyed through dtb_overlap_create / dtb_overlap_destroy): the
+// library itself keeps no stream or event between calls.
+struct dtb_overlap_s {
+    int device;
     hipStream_t s;
     hipEvent_t fork, join;
 };
-static SideStream *side_stream() {
-    static std::mutex mu;
-    static SideStream ss[64];
-    static int state[64];  // 0 untried, 1 ready, 2 failed
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lk(mu);
-    if (state[dev] == 0) {
-        SideStream t{};
-        bool ok = hipStreamCreateWithFlags(&t.s, hipStreamNonBlocking) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&t.fork, hipEventDisableTiming) == hipSuccess;
-        ok = ok && hipEventCreateWithFlags(&t.join, hipEventDisableTiming) == hipSuccess;
-        ss[dev] = t;
-        state[dev] = ok ? 1 : 2;
-    }
-    return state[dev] == 1 ? &ss[dev] : nullptr;
-}
 
 static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
     size_t o = 0;
@@ -703,8 +689,56 @@ int block_forward(const dtb_block_cfg *c, const dtb_block_weights *w, const void
     return DTB_OK;
 }
 
+int dtb_overlap_create(dtb_overlap *out) {
+    if (!out) return DTB_EINVAL_PTR;
+    *out = nullptr;
+    dtb_overlap h = new (std::nothrow) dtb_overlap_s{};
+    if (!h) return set_launch_error(hipErrorOutOfMemory, "dtb_overlap_create");
+    hipError_t e = hipGetDevice(&h->device);
+    // default priority (a stream of another priority is never created)
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&h->s, hipStreamNonBlocking);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->fork, hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&h->join, hipEventDisableTiming);
+    if (e != hipSuccess) {
+        (void)dtb_overlap_destroy(h);
+        return set_launch_error(e, "dtb_overlap_create");
+    }
+    *out = h;
+    return DTB_OK;
+}
+
+int dtb_overlap_destroy(dtb_overlap h) {
+    if (!h) return DTB_OK;
+    // no wait: HIP releases a stream or an event with pending work once that
+    // work has completed
+    if (h->join) (void)hipEventDestroy(h->join);
+    if (h->fork) (void)hipEventDestroy(h->fork);
+    if (h->s) (void)hipStreamDestroy(h->s);
+    delete h;
+    return DTB_OK;
+}
+
+static int block_backward_impl(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in,
+                               const void *saved, const void *dx_out, void *dx_in, const dtb_block_grads *gr,
+                               void *workspace, void *stream, dtb_overlap side_h);
+
 int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in, const void *saved,
                    const void *dx_out, void *dx_in, const dtb_block_grads *gr, void *workspace, void *stream) {
+    return block_backward_impl(c, w, x_in, saved, dx_out, dx_in, gr, workspace, stream, nullptr);
+}
+
+int block_backward_overlap(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in, const void *saved,
+                           const void *dx_out, void *dx_in, const dtb_block_grads *gr, void *workspace, void *stream,
+                           dtb_overlap side) {
+    if (!side) return DTB_EINVAL_PTR;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev != side->device) return DTB_EINVAL_PTR;
+    return block_backward_impl(c, w, x_in, saved, dx_out, dx_in, gr, workspace, stream, side);
+}
+
+static int block_backward_impl(const dtb_block_cfg *c, const dtb_block_weights *w, const void *x_in,
+                               const void *saved, const void *dx_out, void *dx_in, const dtb_block_grads *gr,
+                               void *workspace, void *stream, dtb_overlap side_h) {
     Dims d;
     TRY(check_cfg(c, &d));
     if (d.BT == 0) return DTB_OK;
@@ -747,7 +781,7 @@ int block_backward(const dtb_block_cfg *c, const dtb_block_weights *w, const voi
     // has produced its inputs and reads only buffers that nothing later in
     // this call writes, except dy, which the last kernel may overwrite (dx_in
     // may be dx_out): the main stream joins before that kernel
-    SideStream *side = timing_serializes_backward() ? nullptr : side_stream();
+    dtb_overlap side = timing_serializes_backward() ? nullptr : side_h;
     hipStream_t s2 = side ? side->s : s;
     bool forked = false;
     auto fork = [&]() -> int {

@@ -24,6 +24,9 @@
  * - The caller owns every buffer.  The library never allocates, frees or
  *   synchronises: each call validates its arguments on the host, enqueues
  *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
+ *   It keeps no state between calls apart from its kernels (the opt-in
+ *   measurement timing aside); the one second stream, of
+ *   block_backward_overlap, is a handle the caller creates and destroys.
  * - Errors: 0 on success, a negative DTB_E* code otherwise (no kernel is
  *   enqueued when validation fails; the library never calls exit()).
  *   dtb_strerror() gives a message; for DTB_ELAUNCH it includes the HIP error.
@@ -74,7 +77,11 @@ extern "C" {
  *   qkv  [B, T, QKV]  input, dtype
  *   out  [B, T, C]    output, dtype; head h at columns h*hd .. h*hd+hd-1
  *   lse  [B, NH, T]   output, fp32
- * B == 0 or T == 0 is a no-op.  No workspace. */
+ * B == 0 or T == 0 is a no-op.  No workspace.
+ * One sequence must stay below 2^31 bytes of qkv: T * QKV * sizeof(dtype)
+ * < 2^31 (rows are addressed by 32-bit offsets from the sequence's first
+ * row), else DTB_EINVAL_SHAPE; the same limit holds for attn_backward and
+ * for the block calls. */
 int attn_forward(void *out, float *lse, const void *qkv, int B, int T, int C, int NH, int NKV,
                  int dtype, void *stream);
 
@@ -207,15 +214,33 @@ int block_forward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const vo
  *          may alias dx_out (the residual gradient is updated in place)
  *   g      parameter gradients, fp32, ACCUMULATED
  *   workspace block_workspace_bytes(cfg) bytes, scratch
- * The weight-gradient GEMMs run on a second stream that the library creates
- * once per device (default priority), forked from `stream` after each
- * gradient is produced and joined back before the call's last kernel: all of
- * the call's work is ordered before anything enqueued on `stream` afterwards.
- * That stream and its two events are shared by every call on a device, so
- * calls on one device must not be issued from several host threads at once. */
+ * Every kernel runs on `stream`, one after another. */
 int block_backward(const dtb_block_cfg *cfg, const dtb_block_weights *w, const void *x_in,
                    const void *saved, const void *dx_out, void *dx_in,
                    const dtb_block_grads *g, void *workspace, void *stream);
+
+/* block_backward_overlap: block_backward with its four weight-gradient GEMMs
+ * (dWdown, dWup, dWo, dWqkv) on a second stream that the caller owns: each
+ * forks from `stream` once its output gradient exists and runs beside the
+ * input-gradient GEMM of the same projection (the pages run them one after
+ * another; both only read that gradient).  The second stream joins `stream`
+ * before the call's last kernel, so all of the call's work is ordered before
+ * anything enqueued on `stream` afterwards.  Results are bit-identical to
+ * block_backward.  Arguments as block_backward, plus
+ *   side  a handle from dtb_overlap_create on the current device
+ *         (DTB_EINVAL_PTR if NULL or made on another device).
+ * One handle holds one stream and two events: calls that share a handle
+ * must be issued from one host thread at a time; calls with separate handles
+ * are independent.  While a backward kernel class is timed
+ * (dtb_timing_enable) everything runs on `stream`. */
+typedef struct dtb_overlap_s *dtb_overlap;
+int dtb_overlap_create(dtb_overlap *out); /* on the current device: a non-blocking stream of
+                                             default priority and two events without timing */
+int dtb_overlap_destroy(dtb_overlap h);   /* NULL is a no-op; pending work still completes */
+int block_backward_overlap(const dtb_block_cfg *cfg, const dtb_block_weights *w, const void *x_in,
+                           const void *saved, const void *dx_out, void *dx_in,
+                           const dtb_block_grads *g, void *workspace, void *stream,
+                           dtb_overlap side);
 
 /* ---- component: one linear layer ------------------------------------------
  * The GEMMs block_forward / block_backward run, exposed on their own

@@ -76,6 +76,25 @@ def test_enum_dtype_pointer_validation(B):
     assert L.attn_backward(None, None, None, None, None, 1, 16, 64, 3, 1, 0, None, None) == -1
 
 
+def test_sequence_offset_limit(B):
+    # a sequence of 2^31 bytes or more of qkv is refused before any launch
+    L = B.lib()
+    # fp32, C = 4096, 32 + 2 x 32 heads of 128: QKV = 12288, T = 65536 -> 3.2 GB per sequence
+    assert L.attn_forward(None, None, None, 1, 65536, 4096, 32, 32, 0, None) == -1
+    assert L.attn_backward(None, None, None, None, None, 1, 65536, 4096, 32, 32, 0, None, None) == -1
+    # bf16, C = 8192, 64 heads, 8 kv heads: QKV = 10240, T = 131072 -> 2.7 GB
+    assert L.attn_forward(None, None, None, 1, 131072, 8192, 64, 8, 1, None) == -1
+    # just below the limit passes validation (and then fails on the NULL pointers)
+    # bf16 QKV = 6144: T = 174762 -> 2^31 - 2048 bytes
+    assert L.attn_forward(None, None, None, 1, 174762, 4096, 32, 8, 1, None) == -2
+    assert L.attn_forward(None, None, None, 1, 174763, 4096, 32, 8, 1, None) == -1
+    # a Llama-GQA block (bf16, QKV = 3072) at T = 2^19: 3.2 GB of qkv in one sequence
+    c = _cfg(B, T=1 << 19, B=1)
+    assert L.block_saved_bytes(ctypes.byref(c)) == 0
+    c = _cfg(B, T=1 << 18, B=1)   # 1.6 GB: accepted
+    assert L.block_saved_bytes(ctypes.byref(c)) > 0
+
+
 def test_empty_problem_is_ok_without_pointers(B):
     L = B.lib()
     assert L.attn_forward(None, None, None, 0, 16, 64, 4, 2, 0, None) == 0
