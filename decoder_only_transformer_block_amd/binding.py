@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         L.block_saved_layout.argtypes = [cp, ctypes.POINTER(SavedLayout)]
         L.block_forward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, v]
         L.block_backward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, ctypes.POINTER(BlockGrads), v, v]
+        L.block_backward_overlap.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v,
+                                             ctypes.POINTER(BlockGrads), v, v, v]
+        L.dtb_overlap_create.argtypes = [ctypes.POINTER(_VP)]
+        L.dtb_overlap_destroy.argtypes = [v]
         L.linear_forward.argtypes = [v, v, v, v, v, i, i, i, i, v]
         L.linear_backward.argtypes = [v, v, v, v, v, v, i, i, i, i, v, v]
         L.linear_workspace_bytes.argtypes = [i, i, i, i]
@@ -275,6 +279,27 @@ def block_backward(cfg: BlockCfg, weights: dict, x_in, saved, dx_out, dx_in, gra
     g = grads_struct(grads)
     check(lib().block_backward(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_in), _ptr(saved), _ptr(dx_out),
                                _ptr(dx_in), ctypes.byref(g), _ptr(workspace), _stream(stream)), "block_backward")
+
+
+def dtb_overlap_create():
+    """A caller-owned second stream (and its two events) on the current
+    device, for block_backward_overlap; release it with dtb_overlap_destroy."""
+    h = _VP()
+    check(lib().dtb_overlap_create(ctypes.byref(h)), "dtb_overlap_create")
+    return h
+
+
+def dtb_overlap_destroy(h) -> None:
+    check(lib().dtb_overlap_destroy(h), "dtb_overlap_destroy")
+
+
+def block_backward_overlap(cfg: BlockCfg, weights: dict, x_in, saved, dx_out, dx_in, grads: dict, workspace, side,
+                           stream=None):
+    w = weights_struct(weights)
+    g = grads_struct(grads)
+    check(lib().block_backward_overlap(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_in), _ptr(saved), _ptr(dx_out),
+                                       _ptr(dx_in), ctypes.byref(g), _ptr(workspace), _stream(stream), side),
+          "block_backward_overlap")
 
 
 TIMING_CLASSES = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw", "attn_decode",

@@ -602,12 +602,9 @@ static int pad_hd(int hd, int dtype) {
 
 template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_t s) {
     using FC = FwdCfg<T, HD>;
-    static bool init = false;
-    if (!init) {
-        hipError_t e = set_lds(attn_fwd_kernel<T, HD>, 2 * FC::STAGE);
-        if (e != hipSuccess) return e;
-        init = true;
-    }
+    // set on every launch (per device), no first-device-only flag
+    hipError_t e = set_lds(attn_fwd_kernel<T, HD>, 2 * FC::STAGE);
+    if (e != hipSuccess) return e;
     int nqb = (p.T + FC::BQ - 1) / FC::BQ;
     DTB_LAUNCH((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
     return hipGetLastError();
@@ -616,17 +613,13 @@ template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_
 template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, hipStream_t s) {
     using QC = DqCfg<T, HD>;
     using KC = DkvCfg<T, HD>;
-    static bool init = false;
-    if (!init) {
-        hipError_t e = set_lds(attn_bwd_dq_kernel<T, HD>, 2 * QC::STAGE);
-        if (e != hipSuccess) return e;
-        e = set_lds(attn_bwd_dkv_kernel<T, HD>, 2 * KC::STAGE);
-        if (e != hipSuccess) return e;
-        init = true;
-    }
+    hipError_t e = set_lds(attn_bwd_dq_kernel<T, HD>, 2 * QC::STAGE);
+    if (e != hipSuccess) return e;
+    e = set_lds(attn_bwd_dkv_kernel<T, HD>, 2 * KC::STAGE);
+    if (e != hipSuccess) return e;
     long long rows = (long long)p.B * p.T;
     DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     AttnP q = p;
     q.D = D;

@@ -991,13 +991,11 @@ static hipError_t launch_reduce(const float *part, float *out, long long ldo, in
 template <typename T, int BM, int BN, bool AK, bool BKM>
 static hipError_t launch_t(const KParams &p, int splits, hipStream_t s) {
     constexpr int STAGE = (BM + BN) * 128;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<T, BM, BN, AK, BKM>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    // set on every launch (a host-side attribute, per device): no flag that
+    // would only remember the first device is kept
+    hipError_t e = hipFuncSetAttribute((const void *)gemm_kernel<T, BM, BN, AK, BKM>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 2 * STAGE);
+    if (e != hipSuccess) return e;
     int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
     dim3 grid(nm * nn, 1, splits);
     DTB_LAUNCH((gemm_kernel<T, BM, BN, AK, BKM>), grid, dim3(256), 2 * STAGE, s, p);
@@ -1054,17 +1052,14 @@ static TileChoice choose_tile(int M, int N, int dtype, bool splittable) {
     return {64, 64};
 }
 
+// compute units of the current device (asked each time: the answer depends
+// on the device, and the runtime answers from its own cache)
 static int device_cus() {
-    static int n = 0;
-    if (!n) {
-        int dev = 0, cus = 0;
-        if (hipGetDevice(&dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-            n = cus;
-        else
-            n = 256;
-    }
-    return n;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+        return cus;
+    return 256;
 }
 
 static int choose_splits(const GemmArgs &g, TileChoice tc) {

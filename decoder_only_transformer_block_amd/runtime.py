@@ -54,9 +54,14 @@ class BlockStack:
     caller owns (e.g. views of one flat buffer); otherwise they are allocated
     here."""
 
-    def __init__(self, cfg, layer_weights, device="cuda", weight_views=None, grad_views=None):
+    def __init__(self, cfg, layer_weights, device="cuda", weight_views=None, grad_views=None, overlap=True):
         import torch
         self.cfg = cfg
+        # overlap: the backward's weight-gradient GEMMs run on a second stream
+        # this stack owns (block_backward_overlap); otherwise block_backward
+        # runs everything on the caller's stream
+        self.overlap = overlap
+        self._side = None
         self.c = binding.make_cfg(cfg)
         self.device = device
         if weight_views is None:
@@ -104,12 +109,30 @@ class BlockStack:
         first input (self.dx).  The top block reads dy and writes self.dx, every
         block below it works in place on self.dx.  Parameter gradients
         accumulate into self.grads."""
+        if self.overlap and self._side is None:
+            self._side = binding.dtb_overlap_create()
         for i in reversed(range(self.L)):
             xin = self.inp if i == 0 else self.acts[i]
             dout = dy if i == self.L - 1 else self.dx
-            binding.block_backward(self.c, self.weights[i], xin, self.saved[i], dout, self.dx, self.grads[i],
-                                   self.workspace, stream)
+            if self.overlap:
+                binding.block_backward_overlap(self.c, self.weights[i], xin, self.saved[i], dout, self.dx,
+                                               self.grads[i], self.workspace, self._side, stream)
+            else:
+                binding.block_backward(self.c, self.weights[i], xin, self.saved[i], dout, self.dx, self.grads[i],
+                                       self.workspace, stream)
         return self.dx
+
+    def close(self):
+        """Release the second stream (its pending work still completes)."""
+        if self._side is not None:
+            binding.dtb_overlap_destroy(self._side)
+            self._side = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
     def zero_grads(self):
         for g in self.grads:

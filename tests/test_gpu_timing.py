@@ -67,9 +67,11 @@ def test_timing_classes_and_units():
 
 
 def test_block_backward_same_with_and_without_side_stream():
-    """Weight gradients of a block backward with the side stream in use
-    (timing off) and with everything on the caller's stream (the elementwise
-    class timed) are bit-identical, as are dx and the other gradients."""
+    """Weight gradients of a block backward with the caller-owned second
+    stream in use (block_backward_overlap, timing off), with everything on
+    the caller's stream because a backward class is timed, and through the
+    single-stream block_backward are bit-identical, as are dx and the other
+    gradients."""
     require_gpu()
     import torch
     from decoder_only_transformer_block_amd import binding, configs
@@ -80,8 +82,8 @@ def test_block_backward_same_with_and_without_side_stream():
     x = to_device(configs.block_input(cfg), cfg.dtype)
     dy = to_device(configs.block_dout(cfg), cfg.dtype)
     res = []
-    for timed in (False, True):
-        st = BlockStack(cfg, ws)
+    for timed, overlap in ((False, True), (True, True), (False, False)):
+        st = BlockStack(cfg, ws, overlap=overlap)
         try:
             if timed:
                 binding.timing_enable(classes=["elementwise"])
@@ -93,8 +95,26 @@ def test_block_backward_same_with_and_without_side_stream():
             binding.timing_collect()
         res.append((dx.float().cpu().numpy(),
                     [{k: v.cpu().numpy() for k, v in g.items()} for g in st.grads]))
-    (dx0, g0), (dx1, g1) = res
-    assert np.array_equal(dx0, dx1)
-    for a, b in zip(g0, g1):
-        for k in a:
-            assert np.array_equal(a[k], b[k]), k
+        st.close()
+    dx0, g0 = res[0]
+    for dx1, g1 in res[1:]:
+        assert np.array_equal(dx0, dx1)
+        for a, b in zip(g0, g1):
+            for k in a:
+                assert np.array_equal(a[k], b[k]), k
+
+
+def test_overlap_handle_checks():
+    """block_backward_overlap refuses a NULL handle; a handle is created on the
+    current device and destroyed without waiting for the host."""
+    require_gpu()
+    import ctypes
+    from decoder_only_transformer_block_amd import binding, configs
+    announce("overlap handle checks")
+    L = binding.lib()
+    c = binding.make_cfg(configs.LLAMA_GQA.replace(B=1, T=64, L=1))
+    assert L.block_backward_overlap(ctypes.byref(c), None, None, None, None, None, None, None, None, None) == -2
+    h = binding.dtb_overlap_create()
+    assert h.value
+    binding.dtb_overlap_destroy(h)
+    assert L.dtb_overlap_destroy(None) == 0
