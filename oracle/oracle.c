@@ -84,47 +84,40 @@ void orc_norm_forward(int mode, const double *x, const double *g, const double *
     }
 }
 
-/* Backward of the norms; dx, dg, db are ACCUMULATED (+=), as the pages do.
- * RMS (nanoeuler rmsnorm_cpu_bwd):
- *   q = (sum_j dy_j g_j x_j) r^3 / C;  dx_i += g_i dy_i r - x_i q;  dg_i += dy_i x_i r.
- * LayerNorm (llm.c layernorm_backward), with xhat = (x - mu) r, dn = w dy:
- *   dx_i += r (dn_i - mean(dn) - xhat_i mean(dn xhat));  dw_i += xhat_i dy_i;  db_i += dy_i. */
+/* Backward of the norms; dx, dg, db are ACCUMULATED (+=), as the pages do
+ * (nanoeuler rmsnorm_cpu_bwd, llm.c layernorm_backward).  Both norms are
+ * n = xhat g (+ b) with xhat = (x - mu) r, r = (var + eps)^(-1/2): for RMS,
+ * mu = 0 and var = mean(x^2); for LayerNorm, mu = mean(x) and var the biased
+ * variance.  With dxhat = g dy (g = 1 without gamma), the chain rule through
+ * r (and mu) gives
+ *   RMS:        dx_i += r (dxhat_i - xhat_i mean_j(dxhat_j xhat_j))
+ *   LayerNorm:  dx_i += r (dxhat_i - mean_j(dxhat_j) - xhat_i mean_j(dxhat_j xhat_j))
+ * (d r / d x_j = -r^3 (x_j - mu) / C; for LayerNorm d mu / d x_j = 1/C adds the
+ * mean(dxhat) term), and dg_i += sum over rows of dy_i xhat_i, db_i += sum dy_i. */
 void orc_norm_backward(int mode, const double *dy, const double *x, const double *g,
                        const double *rstd, const double *mean, long R, int C,
                        double *dx, double *dg, double *db)
 {
+    const int layer = mode == ORC_NORM_LAYER, has_g = mode != ORC_NORM_RMS_NOGAMMA;
     #pragma omp parallel for schedule(static) if(ORC_PARALLEL((double)R * C))
     for (long r = 0; r < R; r++) {
         const double *xr = x + r * C, *dyr = dy + r * C;
         double *dxr = dx + r * C;
-        double rs = rstd[r];
-        if (mode == ORC_NORM_LAYER) {
-            double mu = mean[r];
-            double sdn = 0.0, sdnx = 0.0;
-            for (int i = 0; i < C; i++) {
-                double xh = (xr[i] - mu) * rs;
-                double dn = g[i] * dyr[i];
-                sdn += dn;
-                sdnx += dn * xh;
-            }
-            sdn /= C;
-            sdnx /= C;
-            for (int i = 0; i < C; i++) {
-                double xh = (xr[i] - mu) * rs;
-                double dn = g[i] * dyr[i];
-                dxr[i] += rs * (dn - sdn - xh * sdnx);
-            }
-        } else {
-            double q = 0.0;
-            for (int i = 0; i < C; i++) {
-                double gi = (mode == ORC_NORM_RMS) ? g[i] : 1.0;
-                q += dyr[i] * gi * xr[i];
-            }
-            q *= rs * rs * rs / C;
-            for (int i = 0; i < C; i++) {
-                double gi = (mode == ORC_NORM_RMS) ? g[i] : 1.0;
-                dxr[i] += gi * dyr[i] * rs - xr[i] * q;
-            }
+        const double rs = rstd[r], mu = layer ? mean[r] : 0.0;
+        double m_dxh = 0.0, m_dxh_xh = 0.0;    /* mean(dxhat), mean(dxhat xhat) */
+        for (int i = 0; i < C; i++) {
+            double xh = (xr[i] - mu) * rs;
+            double dxh = (has_g ? g[i] : 1.0) * dyr[i];
+            m_dxh += dxh;
+            m_dxh_xh += dxh * xh;
+        }
+        m_dxh /= C;
+        m_dxh_xh /= C;
+        if (!layer) m_dxh = 0.0;    /* RMS: no mean is subtracted */
+        for (int i = 0; i < C; i++) {
+            double xh = (xr[i] - mu) * rs;
+            double dxh = (has_g ? g[i] : 1.0) * dyr[i];
+            dxr[i] += rs * (dxh - m_dxh - xh * m_dxh_xh);
         }
     }
     if (mode == ORC_NORM_RMS_NOGAMMA) return;
@@ -787,20 +780,25 @@ double orc_softmax_ce(const double *logits, const int *targets, long R, int V, d
 /* ------------------------------------------------------------------------ */
 
 /* One AdamW step at step number t >= 1 ("nanoeuler — CUDA kernels"
- * adamw_cpu; llm.c gpt2_update; microgpt adam_update_param without decay):
- *   m = b1 m + (1 - b1) g;   v = b2 v + (1 - b2) g^2
- *   mh = m / (1 - b1^t);     vh = v / (1 - b2^t)
- *   p = p - lr (mh / (sqrt(vh) + eps) + wd p)     (wd on the old p)
+ * adamw_cpu; llm.c gpt2_update; microgpt adam_update_param without decay).
+ * The moments are exponential moving averages of g and g^2, each moved a
+ * fraction (1 - beta) of the way toward the new value; dividing by
+ * 1 - beta^t removes the bias of their zero start; the decay is decoupled
+ * (it shrinks the parameter by lr*wd, independently of the moments):
+ *   m' = m + (1 - b1)(g - m),   v' = v + (1 - b2)(g^2 - v)
+ *   p' = (1 - lr wd) p - lr (m' / (1 - b1^t)) / (sqrt(v' / (1 - b2^t)) + eps)
  * In place on p, m, v. */
 void orc_adamw(double *p, const double *g, double *m, double *v, long n, double lr, double b1,
                double b2, double eps, double wd, int t)
 {
-    double c1 = 1.0 - pow(b1, t), c2 = 1.0 - pow(b2, t);
+    const double bias1 = 1.0 - pow(b1, t), bias2 = 1.0 - pow(b2, t);
+    const double shrink = 1.0 - lr * wd;
     for (long i = 0; i < n; i++) {
-        m[i] = b1 * m[i] + (1.0 - b1) * g[i];
-        v[i] = b2 * v[i] + (1.0 - b2) * g[i] * g[i];
-        double mh = m[i] / c1, vh = v[i] / c2;
-        p[i] -= lr * (mh / (sqrt(vh) + eps) + wd * p[i]);
+        const double gi = g[i];
+        m[i] += (1.0 - b1) * (gi - m[i]);
+        v[i] += (1.0 - b2) * (gi * gi - v[i]);
+        const double step = (m[i] / bias1) / (sqrt(v[i] / bias2) + eps);
+        p[i] = shrink * p[i] - lr * step;
     }
 }
 
