@@ -311,13 +311,25 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
 // ------------------------------------------------------------------ RoPE ---
 // cs[t][i] = (cos(t theta_i), sin(t theta_i)), theta_i = base^(-2i/hd), computed
 // in double and rounded to fp32 (fp32 angles lose ~1e-4 rad at t ~ 1e3-1e4)
+// cos / sin of the angle t * base^(-2k/hd), in fp64, rounded to fp32.  The
+// angle (up to T radians) is first reduced by whole turns, a - n 2pi with 2pi
+// split into two doubles (Cody-Waite; each fma is exact up to one rounding of
+// a result below pi, so the reduced angle is good to ~1e-15), which keeps
+// cos and sin on their short-argument path.
 __global__ void rope_table_kernel(float2 *cs, int T, int half, int hd, double base) {
     long i = (long)blockIdx.x * 256 + threadIdx.x;
     if (i >= (long)T * half) return;
     int t = (int)(i / half), k = (int)(i % half);
-    double theta = pow(base, -2.0 * k / hd);
-    double a = t * theta;
-    cs[i] = make_float2((float)cos(a), (float)sin(a));
+    const double theta = pow(base, -2.0 * k / hd);
+    const double a = t * theta;
+    constexpr double TWO_PI_HI = 6.283185307179586232e+00;   // 2pi rounded to double
+    constexpr double TWO_PI_LO = 2.449293598294706354e-16;   // 2pi - TWO_PI_HI
+    constexpr double INV_TWO_PI = 1.591549430918953358e-01;
+    const double n = rint(a * INV_TWO_PI);
+    const double r = fma(-n, TWO_PI_LO, fma(-n, TWO_PI_HI, a));
+    double sn, c;
+    sincos(r, &sn, &c);
+    cs[i] = make_float2((float)c, (float)sn);
 }
 
 int rope_table(float *cs, int T, int hd, float base, hipStream_t s) {
