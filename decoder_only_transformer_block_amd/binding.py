@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
         i, v, f, z = ctypes.c_int, _VP, ctypes.c_float, ctypes.c_size_t
         L.attn_forward.argtypes = [v, v, v, i, i, i, i, i, i, v]
         L.attn_backward.argtypes = [v, v, v, v, v, i, i, i, i, i, i, v, v]
+        L.attn_backward_noalloc.argtypes = [v, v, v, v, v, i, i, i, i, i, i, v]
         L.attn_workspace_bytes.argtypes = [i, i, i]
         L.attn_workspace_bytes.restype = z
         L.attn_decode.argtypes = [v, v, v, v, v, v, i, i, i, i, i, i, i, v, v]
@@ -162,6 +163,11 @@ def attn_workspace_bytes(B, T, NH) -> int:
 def attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, workspace, stream=None):
     check(lib().attn_backward(_ptr(dqkv), _ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, T, C, NH, NKV,
                               DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_backward")
+
+
+def attn_backward_noalloc(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, stream=None):
+    check(lib().attn_backward_noalloc(_ptr(dqkv), _ptr(qkv), _ptr(out), _ptr(dout), _ptr(lse), B, T, C, NH, NKV,
+                                      DTYPE[dtype], _stream(stream)), "attn_backward_noalloc")
 
 
 def attn_decode_workspace_bytes(B, NH, NKV, hd, Tmax, chunk, dtype) -> int:

@@ -333,6 +333,54 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
                                 (hipStream_t)stream);
 }
 
+// ---- attn_backward without a workspace argument ------------------------------
+// The scratch of attn_backward_noalloc (-D and -lse / scale, [B][NH][T] fp32
+// each) lives in this file-scope device array: every device the library runs
+// on holds its own copy from module load until the process ends.  Host code
+// never uses the array's name as an address (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, asked once per device with that device current, and
+// is kept per device.
+static __device__ __align__(256) char scratch[DTB_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+static void *g_scratch_ptr[kMaxDevices];
+
+static int scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_launch_error(e, "attn_backward_noalloc (hipGetDevice)");
+    if (dev < 0 || dev >= kMaxDevices) return set_launch_error(hipErrorInvalidDevice, "attn_backward_noalloc");
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress((void **)&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) return set_launch_error(e != hipSuccess ? e : hipErrorInvalidSymbol,
+                                                             "attn_backward_noalloc (hipGetSymbolAddress)");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return DTB_OK;
+}
+
+int attn_backward_noalloc(void *dqkv, const void *qkv, const void *out, const void *dout, const float *lse, int B,
+                          int T, int C, int NH, int NKV, int dtype, void *stream) {
+    int e = check_attn_shape(B, T, C, NH, NKV, dtype);
+    if (e) return e;
+    if ((long long)B * T == 0) return DTB_OK;
+    // -D and -lse / scale, each [B][NH][T] fp32, must fit the array
+    if ((long long)B * NH * T * 4 * 2 > (long long)DTB_NOALLOC_SCRATCH_BYTES) return DTB_EINVAL_SHAPE;
+    if (!ptr_ok(dqkv) || !ptr_ok(qkv) || !ptr_ok(out) || !ptr_ok(dout) || !ptr_ok(lse)) return DTB_EINVAL_PTR;
+    void *ws = nullptr;
+    e = scratch_address(&ws);
+    if (e) return e;
+    // the backward's kernels write every scratch value they read (nothing has
+    // to start at zero), so no clearing pass is needed
+    return launch_attn_backward(dqkv, qkv, out, dout, lse, B, T, C, NH, NKV, dtype, (float *)ws, nullptr,
+                                (hipStream_t)stream);
+}
+
 static int check_decode(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype) {
     if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
     if (B < 0 || Tmax < 0 || NH <= 0 || NKV <= 0 || NH % NKV || chunk < 0 || chunk % 32) return DTB_EINVAL_SHAPE;

@@ -25,8 +25,9 @@
  *   synchronises: each call validates its arguments on the host, enqueues
  *   kernels on `stream` (a hipStream_t; NULL = the null stream) and returns.
  *   It keeps no state between calls apart from its kernels (the opt-in
- *   measurement timing aside); the one second stream, of
- *   block_backward_overlap, is a handle the caller creates and destroys.
+ *   measurement timing and the per-device address of attn_backward_noalloc's
+ *   scratch array aside); the one second stream, of block_backward_overlap,
+ *   is a handle the caller creates and destroys.
  * - Errors: 0 on success, a negative DTB_E* code otherwise (no kernel is
  *   enqueued when validation fails; the library never calls exit()).
  *   dtb_strerror() gives a message; for DTB_ELAUNCH it includes the HIP error.
@@ -102,6 +103,25 @@ int attn_backward(void *dqkv, const void *qkv, const void *out, const void *dout
                   const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
                   void *workspace, void *stream);
 size_t attn_workspace_bytes(int B, int T, int NH);
+
+/* attn_backward_noalloc: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as attn_backward (the same
+ * kernels), without the workspace argument: its scratch (-D and -lse / scale,
+ * 8 * B * NH * T bytes) lives in a device array inside the library,
+ * DTB_NOALLOC_SCRATCH_BYTES (8 MiB) on each device it runs on, held until the
+ * process ends.  8 * B * NH * T above that size is DTB_EINVAL_SHAPE (B * NH * T
+ * up to 2^20: one 16384-token sequence of 64 heads, say).  The call allocates
+ * and frees nothing (the array's device address is looked up once per device,
+ * on the first call there) and clears nothing: every scratch value the
+ * kernels read, they have written in the same call.  Every call on one
+ * device shares that device's array, which keeps the last call's contents:
+ * calls on one stream are ordered, but calls that can overlap in time on one
+ * device (other streams, other host threads) race on it. */
+#define DTB_NOALLOC_SCRATCH_BYTES (8u << 20)
+int attn_backward_noalloc(void *dqkv, const void *qkv, const void *out, const void *dout,
+                          const float *lse, int B, int T, int C, int NH, int NKV, int dtype,
+                          void *stream);
 
 /* ---- decode attention ---------------------------------------------------
  * One new query per sequence against that sequence's KV cache, forward only
