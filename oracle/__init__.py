@@ -124,13 +124,19 @@ def linear_forward(inp, w, bias=None):
     return out
 
 
-def linear_backward(dout, inp, w):
-    dout, inp, w = _d(dout), _d(inp), _d(w)
-    N, K = w.shape
-    R = inp.size // K
-    dinp = np.zeros_like(inp)
-    dw = np.zeros_like(w)
-    db = np.zeros(N)
+def linear_backward(dout, inp, w, parts=("dinp", "dw", "db")):
+    """dinp, dw, db of a linear layer; a product left out of `parts` is not
+    computed and comes back as None (w may then be None for dinp, or inp
+    for dw)."""
+    dout = _d(dout)
+    N = dout.shape[-1]
+    R = dout.size // N
+    inp = _d(inp) if inp is not None else None
+    w = _d(w) if w is not None else None
+    K = w.shape[1] if w is not None else inp.shape[-1]
+    dinp = np.zeros((R, K)).reshape(dout.shape[:-1] + (K,)) if "dinp" in parts else None
+    dw = np.zeros((N, K)) if "dw" in parts else None
+    db = np.zeros(N) if "db" in parts else None
     lib().orc_linear_backward(_p(dout), _p(inp), _p(w), ctypes.c_long(R), K, N,
                               _p(dinp), _p(dw), _p(db))
     return dinp, dw, db
