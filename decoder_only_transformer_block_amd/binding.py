@@ -43,6 +43,10 @@ class SavedLayout(ctypes.Structure):
                 ("n1", "r1", "mu1", "qkv", "o", "lse", "x2", "n2", "r2", "mu2", "up", "h", "total")]
 
 
+class WorkspaceLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_longlong) for n in ("dh", "dup", "dn2", "dx2", "dO", "dqkv", "dn1", "total")]
+
+
 class Timing(ctypes.Structure):
     _fields_ = [("ms", ctypes.c_double), ("flops", ctypes.c_double), ("bytes", ctypes.c_double),
                 ("launches", ctypes.c_longlong)]
@@ -78,6 +82,7 @@ def lib() -> ctypes.CDLL:
         L.block_workspace_bytes.argtypes = [cp]
         L.block_workspace_bytes.restype = z
         L.block_saved_layout.argtypes = [cp, ctypes.POINTER(SavedLayout)]
+        L.block_workspace_layout.argtypes = [cp, ctypes.POINTER(WorkspaceLayout)]
         L.block_forward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, v]
         L.block_backward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, ctypes.POINTER(BlockGrads), v, v]
         L.block_backward_overlap.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v,
@@ -271,6 +276,12 @@ def block_workspace_bytes(cfg: BlockCfg) -> int:
 def block_saved_layout(cfg: BlockCfg) -> SavedLayout:
     L = SavedLayout()
     check(lib().block_saved_layout(ctypes.byref(cfg), ctypes.byref(L)), "block_saved_layout")
+    return L
+
+
+def block_workspace_layout(cfg: BlockCfg) -> WorkspaceLayout:
+    L = WorkspaceLayout()
+    check(lib().block_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)), "block_workspace_layout")
     return L
 
 

@@ -307,6 +307,24 @@ size_t block_workspace_bytes(const dtb_block_cfg *cfg) {
     return W.total;
 }
 
+int block_workspace_layout(const dtb_block_cfg *cfg, dtb_workspace_layout *layout) {
+    Dims d;
+    int e = check_cfg(cfg, &d);
+    if (e) return e;
+    if (!layout) return DTB_EINVAL_PTR;
+    WsLayout W;
+    ws_layout(cfg, d, &W);
+    layout->dh = (long long)W.dh;
+    layout->dup = (long long)W.dup;
+    layout->dn2 = (long long)W.dn2;
+    layout->dx2 = (long long)W.dx2;
+    layout->dO = (long long)W.dO;
+    layout->dqkv = (long long)W.dqkv;
+    layout->dn1 = (long long)W.dn1;
+    layout->total = (long long)W.total;
+    return DTB_OK;
+}
+
 size_t attn_workspace_bytes(int B, int T, int NH) {
     if (B < 0 || T < 0 || NH <= 0) return 0;
     size_t n = (size_t)B * T * NH * 4 * 2;  // -D and -lse / scale

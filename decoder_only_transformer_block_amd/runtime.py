@@ -139,6 +139,17 @@ class BlockStack:
             for t in g.values():
                 t.zero_()
 
+    def workspace_tensor(self, name: str, shape):
+        """View of one intermediate gradient the last block_backward left in the
+        shared workspace (see dtb_workspace_layout): dh, dup, dn2, dx2, dO,
+        dqkv, dn1."""
+        import torch
+        off = getattr(binding.block_workspace_layout(self.c), name)
+        dt = torch_dtype(self.cfg.dtype)
+        n = int(np.prod(shape))
+        es = torch.tensor([], dtype=dt).element_size()
+        return self.workspace[off:off + n * es].view(dt).view(*shape)
+
     def saved_tensor(self, layer: int, name: str, shape, dtype=None):
         """View of one saved activation (see dtb_saved_layout)."""
         import torch

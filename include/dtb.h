@@ -207,6 +207,22 @@ size_t block_saved_bytes(const dtb_block_cfg *cfg);
 size_t block_workspace_bytes(const dtb_block_cfg *cfg);
 int block_saved_layout(const dtb_block_cfg *cfg, dtb_saved_layout *layout);
 
+/* Byte offsets, inside `workspace`, of the intermediate gradients that
+ * block_backward leaves there (valid once its work on the stream has
+ * completed, until the next call that uses the same workspace), for
+ * inspection and testing; all dtype, row-major:
+ *   dh [BT, H]          dy Wdown                       (activation output)
+ *   dup [BT, 2H or H]   gradient of the MLP pre-activation ([gate | up])
+ *   dn2 [BT, C]         dup Wup                        (norm2 output)
+ *   dx2 [BT, C]         dy + Norm2^T(dn2)              (residual stream)
+ *   dO [BT, C]          dx2 Wo                         (attention output)
+ *   dqkv [BT, QKV]      attention backward, after the inverse RoPE of dq, dk
+ *   dn1 [BT, C]         dqkv Wqkv                      (norm1 output) */
+typedef struct {
+    long long dh, dup, dn2, dx2, dO, dqkv, dn1, total;
+} dtb_workspace_layout;
+int block_workspace_layout(const dtb_block_cfg *cfg, dtb_workspace_layout *layout);
+
 /* block_forward: the pre-norm block of "nanoeuler — CUDA kernels" run_train /
  * forward_gpu (RMSNorm, QKV GEMM, RoPE, flash attention, O GEMM + residual,
  * RMSNorm, MLP GEMMs, down GEMM + residual), generalised by the mini-Qwen2

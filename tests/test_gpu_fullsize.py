@@ -10,17 +10,16 @@ compute one by one, plus properties that hold at any size.
   - sum over keys of dk is 0 and sum over keys of dv is the sum of dO over the
     group's query rows (every row of dS sums to zero), checked on the whole
     GPU result.
-* Llama-GQA block (B=8, T=2048, C=2048, bf16) and GPT-2-small block
-  (B=4, T=1024, C=768, fp32), one layer each: the forward output and the
-  input gradient of the last rows of two sequences, composed from the
-  oracle's per-op functions (the last rows' dk/dv are exact as above), and a
-  random-projection check that dW_down = dy^T h on the full gradient.
+* GPT-2-small block (B=4, T=1024, C=768, fp32), one layer: every output,
+  saved activation and parameter gradient against the oracle's whole block.
+* Llama-GQA block (B=8, T=2048, C=2048, bf16), one layer: every step on every
+  row of two sequences, each from the GPU's own inputs to that step, and
+  every parameter gradient from the GPU's own full upstream tensors.
 """
 import numpy as np
 import pytest
 
 from gpu_util import TOL, announce, check, require_gpu
-from oracle_compose import block_tail_reference
 
 pytestmark = pytest.mark.gpu
 
@@ -79,45 +78,145 @@ def test_attn_long_full_size_sampled():
     check("sum dv", dv.sum(0), dO_group.sum(0), tol)
 
 
-def _block_full_size(cfg_name, batches, R):
+def _gpu_block(cfg, w, x, dy):
+    """One block forward + backward at full size; the saved activations, the
+    backward's intermediate gradients (from the workspace) and every parameter
+    gradient, as float64-comparable numpy arrays keyed by name."""
     import torch
+    from decoder_only_transformer_block_amd.runtime import BlockStack, to_device, to_numpy
+    B, T, C, H, NH = cfg.B, cfg.T, cfg.C, cfg.H, cfg.NH
+    BT = B * T
+    hd = C // NH
+    QKV = C + 2 * cfg.NKV * hd
+    W = 2 * H if cfg.mlp == "swiglu" else H
+    st = BlockStack(cfg, [w])
+    y = to_numpy(st.forward(to_device(x, cfg.dtype))).reshape(BT, C)
+    dx = to_numpy(st.backward(to_device(dy, cfg.dtype))).reshape(BT, C)
+    torch.cuda.synchronize()
+    shapes = {"n1": (BT, C), "r1": (BT,), "mu1": (BT,), "qkv": (BT, QKV), "o": (BT, C), "lse": (B, NH, T),
+              "x2": (BT, C), "n2": (BT, C), "r2": (BT,), "mu2": (BT,), "up": (BT, W), "h": (BT, H)}
+    sv = {}
+    for n, shp in shapes.items():
+        t = st.saved_tensor(0, n, shp)
+        if t is not None:
+            sv[n] = to_numpy(t)
+    wshapes = {"dh": (BT, H), "dup": (BT, W), "dn2": (BT, C), "dx2": (BT, C), "dO": (BT, C),
+               "dqkv": (BT, QKV), "dn1": (BT, C)}
+    wk = {n: to_numpy(st.workspace_tensor(n, shp)) for n, shp in wshapes.items()}
+    grads = {k: v.cpu().numpy() for k, v in st.grads[0].items()}
+    st.close()
+    del st
+    torch.cuda.empty_cache()
+    return y, dx, sv, wk, grads
+
+
+def test_gpt2_small_block_full_size_every_tensor():
+    """One GPT-2-small block (fp32, B=4, T=1024, C=768, 12 heads, LayerNorm,
+    GELU-tanh, every bias; perturbed gammas, betas and biases) at full size,
+    in the benchmark's kernels and launch configuration, against the oracle's
+    whole block forward and backward: the output, the input gradient, every
+    saved activation and every parameter gradient, element by element."""
+    require_gpu()
     import oracle
     from decoder_only_transformer_block_amd import configs
-    from decoder_only_transformer_block_amd.runtime import BlockStack, to_device, to_numpy
-    cfg = configs.BLOCK_CONFIGS[cfg_name].replace(L=1)
+    cfg = configs.GPT2_SMALL.replace(L=1)
     w = configs.block_weights(cfg, 0, perturb=True)
     x = configs.block_input(cfg)
     dy = configs.block_dout(cfg)
-    announce(f"block full size {cfg.name} B={cfg.B} T={cfg.T} C={cfg.C} H={cfg.H} {cfg.dtype}")
-    st = BlockStack(cfg, [w])
-    y = to_numpy(st.forward(to_device(x, cfg.dtype)))
-    dx = to_numpy(st.backward(to_device(dy, cfg.dtype)))
-    lse = to_numpy(st.saved_tensor(0, "lse", (cfg.B, cfg.NH, cfg.T)))
+    BT, C = cfg.B * cfg.T, cfg.C
+    announce(f"block full size, every tensor: {cfg.name} B={cfg.B} T={cfg.T} C={C} H={cfg.H} {cfg.dtype}")
+    y, dx, sv, _, grads = _gpu_block(cfg, w, x, dy)
+    announce("  oracle block forward + backward (fp64, host cores)")
+    ry, rsv = oracle.block_forward(cfg, w, x)
+    rdx, rg = oracle.block_backward(cfg, w, x, rsv, dy)
     tol = TOL[cfg.dtype]
-    for b in batches:
-        ry, rdx, rl = block_tail_reference(oracle, cfg, w, x[b], dy[b], R)
-        check(f"y[b{b},tail]", y[b, cfg.T - R:], ry, tol)
-        check(f"lse[b{b},tail]", lse[b][:, cfg.T - R:], rl, tol)
-        check(f"dx[b{b},tail]", dx[b, cfg.T - R:], rdx, tol)
-    # dW_down = dy^T h on the whole gradient (random projection, fp32 on the GPU)
-    h = st.saved_tensor(0, "h", (cfg.B * cfg.T, cfg.H)).float()
-    dyt = to_device(dy, cfg.dtype).float().reshape(-1, cfg.C)
-    gen = torch.Generator(device="cuda").manual_seed(5)
-    vv = torch.randn(cfg.H, 1, device="cuda", generator=gen)
-    lhs = (st.grads[0]["w_down"] @ vv).double().cpu().numpy()
-    rhs = (dyt.t() @ (h @ vv)).double().cpu().numpy()
-    check("dWdown.v", lhs, rhs, tol)
-    torch.cuda.synchronize()
+    check("y", y, ry.reshape(BT, C), tol)
+    check("dx", dx, rdx.reshape(BT, C), tol)
+    for n, got in sv.items():
+        check(n, got, getattr(rsv, n).reshape(got.shape), tol)
+    for k in rg:
+        check("d" + k, grads[k], rg[k], tol)
 
 
-def test_llama_gqa_block_full_size_sampled():
+def test_llama_gqa_block_full_size_every_gradient():
+    """One Llama-GQA block (bf16, B=8, T=2048, C=2048, 32/8 heads, SwiGLU 5632,
+    RMSNorm with perturbed gammas, NeoX RoPE) at full size, in the benchmark's
+    kernels, tile shapes and split-K counts.  The whole oracle block would
+    take minutes here, so each step is checked on the GPU's own inputs to that
+    step: every row of the first and the last sequence through every step of
+    the forward and the backward (norms, projections with RoPE, the whole
+    attention of the sequence, SwiGLU, residuals), then every parameter
+    gradient element by element from the GPU's own full upstream tensors (the
+    weight-gradient GEMMs contract over all B*T = 16384 rows; the gamma
+    gradients sum the norm backward's per-workgroup partials)."""
     require_gpu()
-    _block_full_size("llama_gqa", batches=(0, 7), R=16)
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    cfg = configs.LLAMA_GQA.replace(L=1)
+    B, T, C, H, NH, NKV = cfg.B, cfg.T, cfg.C, cfg.H, cfg.NH, cfg.NKV
+    BT, hd = B * T, C // NH
+    KV = NKV * hd
+    w = configs.block_weights(cfg, 0, perturb=True)
+    x = configs.block_input(cfg).reshape(BT, C)
+    dy = configs.block_dout(cfg).reshape(BT, C)
+    announce(f"block full size, every gradient: {cfg.name} B={B} T={T} C={C} H={H} {cfg.dtype}")
+    y, dx, sv, wk, grads = _gpu_block(cfg, w, x.reshape(B, T, C), dy.reshape(B, T, C))
+    tol = TOL[cfg.dtype]
+    g1, g2 = w["g1"], w["g2"]
 
+    def rope(buf, off, nheads, inverse=False):
+        return oracle.rope(buf, 1, T, buf.shape[1], off, nheads, hd, cfg.rope_base, inverse=inverse)
 
-def test_gpt2_small_block_full_size_sampled():
-    require_gpu()
-    _block_full_size("gpt2_small", batches=(0, 3), R=16)
+    for b in (0, B - 1):
+        r = slice(b * T, (b + 1) * T)
+        announce(f"  sequence {b}: every row through every step")
+        n1, r1, _ = oracle.norm_forward(cfg.norm, x[r], g1, None, cfg.eps)
+        check(f"n1[b{b}]", sv["n1"][r], n1, tol)
+        check(f"r1[b{b}]", sv["r1"][r], r1, tol)
+        qkv = oracle.linear_forward(sv["n1"][r], w["wqkv"])
+        qkv = rope(rope(qkv, 0, NH), C, NKV)
+        check(f"qkv[b{b}]", sv["qkv"][r], qkv, tol)
+        o, lse = oracle.attn_forward(sv["qkv"][r][None], 1, T, C, NH, NKV)
+        check(f"o[b{b}]", sv["o"][r], o.reshape(T, C), tol)
+        check(f"lse[b{b}]", sv["lse"][b], lse.reshape(NH, T), tol)
+        x2 = x[r] + oracle.linear_forward(sv["o"][r], w["wo"])
+        check(f"x2[b{b}]", sv["x2"][r], x2, tol)
+        n2, r2, _ = oracle.norm_forward(cfg.norm, sv["x2"][r], g2, None, cfg.eps)
+        check(f"n2[b{b}]", sv["n2"][r], n2, tol)
+        check(f"r2[b{b}]", sv["r2"][r], r2, tol)
+        up = oracle.linear_forward(sv["n2"][r], w["w_up"])
+        check(f"up[b{b}]", sv["up"][r], up, tol)
+        check(f"h[b{b}]", sv["h"][r], oracle.act_forward(cfg.mlp, sv["up"][r], H), tol)
+        check(f"y[b{b}]", y[r], sv["x2"][r] + oracle.linear_forward(sv["h"][r], w["w_down"]), tol)
+        # backward
+        dh, _, _ = oracle.linear_backward(dy[r], None, w["w_down"], parts=("dinp",))
+        check(f"dh[b{b}]", wk["dh"][r], dh, tol)
+        check(f"dup[b{b}]", wk["dup"][r], oracle.act_backward(cfg.mlp, wk["dh"][r], sv["up"][r], H), tol)
+        dn2, _, _ = oracle.linear_backward(wk["dup"][r], None, w["w_up"], parts=("dinp",))
+        check(f"dn2[b{b}]", wk["dn2"][r], dn2, tol)
+        dn, _, _ = oracle.norm_backward(cfg.norm, wk["dn2"][r], sv["x2"][r], g2, sv["r2"][r], None)
+        check(f"dx2[b{b}]", wk["dx2"][r], dy[r] + dn, tol)
+        dO, _, _ = oracle.linear_backward(wk["dx2"][r], None, w["wo"], parts=("dinp",))
+        check(f"dO[b{b}]", wk["dO"][r], dO, tol)
+        dqkv = oracle.attn_backward(sv["qkv"][r][None], wk["dO"][r][None], 1, T, C, NH, NKV).reshape(T, -1)
+        dqkv = rope(rope(dqkv, 0, NH, inverse=True), C, NKV, inverse=True)
+        check(f"dq[b{b}]", wk["dqkv"][r][:, :C], dqkv[:, :C], tol)
+        check(f"dk[b{b}]", wk["dqkv"][r][:, C:C + KV], dqkv[:, C:C + KV], tol)
+        check(f"dv[b{b}]", wk["dqkv"][r][:, C + KV:], dqkv[:, C + KV:], tol)
+        dn1, _, _ = oracle.linear_backward(wk["dqkv"][r], None, w["wqkv"], parts=("dinp",))
+        check(f"dn1[b{b}]", wk["dn1"][r], dn1, tol)
+        dn, _, _ = oracle.norm_backward(cfg.norm, wk["dn1"][r], x[r], g1, sv["r1"][r], None)
+        check(f"dx[b{b}]", dx[r], wk["dx2"][r] + dn, tol)
+
+    announce("  every parameter gradient from the GPU's own full upstream tensors")
+    for name, dout, inp in (("w_down", dy, sv["h"]), ("w_up", wk["dup"], sv["n2"]),
+                            ("wo", wk["dx2"], sv["o"]), ("wqkv", wk["dqkv"], sv["n1"])):
+        _, dw, _ = oracle.linear_backward(dout, inp, None, parts=("dw",))
+        check("d" + name, grads[name], dw, tol)
+    _, dg2, _ = oracle.norm_backward(cfg.norm, wk["dn2"], sv["x2"], g2, sv["r2"], None)
+    check("dg2", grads["g2"], dg2, tol)
+    _, dg1, _ = oracle.norm_backward(cfg.norm, wk["dn1"], x, g1, sv["r1"], None)
+    check("dg1", grads["g1"], dg1, tol)
 
 
 def _model_full_size(cfg_name, rows, vchunk=None):

@@ -49,20 +49,29 @@ def test_encoder_forward_backward(dtype):
     check("dwpe", to_numpy(dwpe), rp, tol)
 
 
+NORM_SHAPES = [(333, 520, False),     # two chunks per lane in bf16, a ragged last chunk
+               (2500, 2048, True),    # the Llama-GQA width (4 chunks per lane in bf16) with the residual gradient
+               (700, 768, True),      # the GPT-2-small width
+               (257, 4096, True)]     # the widest fp32 rows (8192 for bf16 below)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("norm", ["rms", "rms_nogamma", "layer"])
-def test_norm_standalone(dtype, norm):
+@pytest.mark.parametrize("R,C,with_res", NORM_SHAPES + [(129, 8192, True)])
+def test_norm_standalone(dtype, norm, R, C, with_res):
     require_gpu()
     import torch
     import oracle
     from decoder_only_transformer_block_amd import binding, inputs
     from decoder_only_transformer_block_amd.runtime import to_numpy
-    R, C = 333, 520
-    announce(f"norm {norm} R={R} C={C} {dtype}")
-    x = inputs.tensor(5, "x", (R, C), std=2.0, mean=0.3, dtype=dtype)
-    g = inputs.tensor(5, "g", (C,), std=0.1, mean=1.0, dtype=dtype)
-    b = inputs.tensor(5, "b", (C,), std=0.1, dtype=dtype)
-    dy = inputs.tensor(5, "dy", (R, C), dtype=dtype)
+    if C > (8192 if dtype == "bf16" else 4096):
+        pytest.skip("wider than the norm kernels' row limit for this dtype")
+    announce(f"norm {norm} R={R} C={C} {dtype} residual={with_res}")
+    x = inputs.tensor(5, f"x{R}.{C}", (R, C), std=2.0, mean=0.3, dtype=dtype)
+    g = inputs.tensor(5, f"g{C}", (C,), std=0.1, mean=1.0, dtype=dtype)
+    b = inputs.tensor(5, f"b{C}", (C,), std=0.1, dtype=dtype)
+    dy = inputs.tensor(5, f"dy{R}.{C}", (R, C), dtype=dtype)
+    res = inputs.tensor(5, f"res{R}.{C}", (R, C), dtype=dtype) if with_res else None
     gd = None if norm == "rms_nogamma" else _dev(g, dtype)
     bd = _dev(b, dtype) if norm == "layer" else None
     out = torch.empty((R, C), dtype=_dev(x, dtype).dtype, device="cuda")
@@ -75,12 +84,15 @@ def test_norm_standalone(dtype, norm):
     db = torch.zeros(C, device="cuda")
     ws = torch.empty(binding.norm_workspace_bytes(R, C), dtype=torch.uint8, device="cuda")
     binding.norm_backward(dx, dg if gd is not None else None, db if bd is not None else None, _dev(dy, dtype), xd,
-                          gd, rstd, mean if norm == "layer" else None, None, R, C, norm, dtype, ws)
+                          gd, rstd, mean if norm == "layer" else None, None if res is None else _dev(res, dtype),
+                          R, C, norm, dtype, ws)
     torch.cuda.synchronize()
     tol = TOL[dtype]
     ro, rr, rm = oracle.norm_forward(norm, x, None if gd is None else g, b if bd is not None else None)
     check("out", to_numpy(out), ro, tol)
     rdx, rdg, rdb = oracle.norm_backward(norm, dy, x, None if gd is None else g, rr, rm)
+    if res is not None:
+        rdx = rdx + res.astype(np.float64)
     check("dx", to_numpy(dx), rdx, tol)
     if gd is not None:
         check("dg", to_numpy(dg), rdg, tol)
