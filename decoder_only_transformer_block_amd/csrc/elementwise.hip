@@ -196,19 +196,28 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
 // dst[i] += sum_p part[p][i] for i < n (part row stride ld).  A workgroup
 // covers 32 columns; its 8 groups of 32 threads sum the parts p = pg, pg+8, ...
 // (independent loads, issued back to back), then combine in a fixed order.
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst) {
+// dst[i] += sum over p of part[p][i] for the n columns of part; with dst1,
+// columns n .. 2n-1 of part go to dst1 (the gamma and beta partials of a
+// LayerNorm, side by side in part, in one launch).  Fixed order: eight
+// strided part groups, then a fixed tree.
+__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst,
+                                                           float *dst1) {
     __shared__ float red[8][32];
     const int c = threadIdx.x & 31, pg = threadIdx.x >> 5;
     const int i = blockIdx.x * 32 + c;
+    const int ncols = dst1 ? 2 * n : n;
     float s = 0.f;
-    if (i < n) {
+    if (i < ncols) {
 #pragma unroll 8
         for (int p = pg; p < np; p += 8) s += part[(long)p * ld + i];
     }
     red[pg][c] = s;
     __syncthreads();
-    if (pg == 0 && i < n)
-        dst[i] += ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) + ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
+    if (pg == 0 && i < ncols) {
+        const float t = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) + ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
+        if (i < n) dst[i] += t;
+        else dst1[i - n] += t;
+    }
 }
 
 static int npl_for(int C, int dtype) {
@@ -234,7 +243,7 @@ static hipError_t norm_fwd_t(int mode, const void *x, const void *g, const void 
     else
         DTB_LAUNCH((norm_fwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, xx, gg, bb, eps, R, C,
                            oo, rstd, mean);
-    return hipGetLastError();
+    return last_error();
 }
 
 #define NPL_DISPATCH(FN, T, npl, ...)                                                   \
@@ -280,7 +289,7 @@ static hipError_t norm_bwd_t(int mode, const void *dy, const void *x, const void
     else
         DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean,
                            rr, R, C, o, part);
-    return hipGetLastError();
+    return last_error();
 }
 
 int norm_backward(int mode, int dtype, const void *dy, const void *x, const void *g, const float *rstd,
@@ -294,11 +303,11 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
                        : NPL_DISPATCH(norm_bwd_t, float, npl, mode, dy, x, g, rstd, mean, dres, R, C, dx, part, npart, s);
     if (e != hipSuccess) return set_launch_error(e, "norm_backward");
     if (mode != DTB_NORM_RMS_NOGAMMA) {
-        DTB_LAUNCH(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C, dg);
-        if (mode == DTB_NORM_LAYER)
-            DTB_LAUNCH(reduce_parts_kernel, dim3((C + 31) / 32), dim3(256), 0, s, part + C, npart, 2L * C,
-                               C, db);
-        e = hipGetLastError();
+        // LayerNorm: the gamma (columns 0 .. C-1) and beta (C .. 2C-1) partials in one launch
+        const bool ln = mode == DTB_NORM_LAYER;
+        DTB_LAUNCH(reduce_parts_kernel, dim3(((ln ? 2 : 1) * C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C,
+                   dg, ln ? db : (float *)nullptr);
+        e = last_error();
         if (e != hipSuccess) return set_launch_error(e, "norm_backward reduce");
     }
     if (g_timing_on) {
@@ -445,7 +454,7 @@ static hipError_t act_fwd_t(int mlp, const void *up, long R, int H, void *h, hip
         DTB_LAUNCH((act_fwd_kernel<T, DTB_MLP_RELU>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
     else
         DTB_LAUNCH((act_fwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)up, R, H, (T *)h);
-    return hipGetLastError();
+    return last_error();
 }
 template <typename T>
 static hipError_t act_bwd_t(int mlp, const void *dh, const void *up, long R, int H, void *dup, hipStream_t s) {
@@ -461,7 +470,7 @@ static hipError_t act_bwd_t(int mlp, const void *dh, const void *up, long R, int
     else
         DTB_LAUNCH((act_bwd_kernel<T, DTB_MLP_GELU_TANH>), grid, dim3(256), 0, s, (const T *)dh,
                            (const T *)up, R, H, (T *)dup);
-    return hipGetLastError();
+    return last_error();
 }
 
 int act_forward(int mlp, int dtype, const void *up, long R, int H, void *h, hipStream_t s) {
@@ -490,32 +499,74 @@ int act_backward(int mlp, int dtype, const void *dh, const void *up, long R, int
 }
 
 // --------------------------------------------------------- bias gradient ---
-// part[p][n] = sum over the p-th row range of dy[r][n]
+// part[p][n] = sum over the p-th range of rows of dy[r][n].  A workgroup owns
+// 64 column chunks of 16 bytes (one per lane) and one row range; its four
+// waves take every fourth row of the range, and their sums are combined in
+// LDS in a fixed order (deterministic).
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_kernel(const T *dy, long R, int N, long rows_per, float *part) {
-    int n = blockIdx.x * 256 + threadIdx.x;
-    if (n >= N) return;
-    long r0 = (long)blockIdx.y * rows_per, r1 = min(R, r0 + rows_per);
-    float s = 0.f;
-    for (long r = r0; r < r1; r++) s += to_f32(dy[r * N + n]);
-    part[(long)blockIdx.y * N + n] = s;
+    constexpr int EPV = 16 / sizeof(T);
+    __shared__ float red[3][64 * EPV];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n0 = (blockIdx.x * 64 + lane) * EPV;
+    const long r0 = (long)blockIdx.y * rows_per, r1 = min(R, r0 + rows_per);
+    const bool ok = n0 < N;
+    float acc[EPV];
+#pragma unroll
+    for (int e = 0; e < EPV; e++) acc[e] = 0.f;
+    if (ok) {
+#pragma unroll 4
+        for (long r = r0 + wv; r < r1; r += 4) {
+            float f[EPV];
+            unpack16<T>(ld16(dy + r * N + n0), f);
+#pragma unroll
+            for (int e = 0; e < EPV; e++) acc[e] += f[e];
+        }
+    }
+    if (wv > 0) {
+#pragma unroll
+        for (int e = 0; e < EPV; e++) red[wv - 1][lane * EPV + e] = acc[e];
+    }
+    __syncthreads();
+    if (wv == 0 && ok) {
+        float *dst = part + (long)blockIdx.y * N + n0;
+#pragma unroll
+        for (int e4 = 0; e4 < EPV; e4 += 4) {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; e++)
+                v[e] = (acc[e4 + e] + red[0][lane * EPV + e4 + e]) +
+                       (red[1][lane * EPV + e4 + e] + red[2][lane * EPV + e4 + e]);
+            *reinterpret_cast<f32x4 *>(dst + e4) = v;
+        }
+    }
 }
 
+// the most row ranges a bias gradient of R rows uses (sizes the partials)
 int bias_grad_parts(long R) {
-    long p = (R + 63) / 64;
-    return (int)(p < 256 ? (p > 0 ? p : 1) : 256);
+    long p = (R + 15) / 16;
+    return (int)(p < 512 ? (p > 0 ? p : 1) : 512);
 }
 
 int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, int npart, hipStream_t s) {
     if (R <= 0 || N <= 0) return DTB_OK;
     if (g_timing_on) timing_begin(s, K_ELEM);
-    long rows_per = (R + npart - 1) / npart;
-    dim3 grid((N + 255) / 256, npart);
+    // about 1024 workgroups: the column blocks times as many row ranges as
+    // that takes (at most npart, at least 16 rows each)
+    const int epv = dtype == DTB_BF16 ? 8 : 4;
+    const int cblocks = (N / epv + 63) / 64;
+    int np = (1024 + cblocks - 1) / cblocks;
+    if (np > npart) np = npart;
+    if (np < 1) np = 1;
+    const long rows_per = (R + np - 1) / np;
+    np = (int)((R + rows_per - 1) / rows_per);
+    dim3 grid(cblocks, np);
     if (dtype == DTB_BF16)
         DTB_LAUNCH(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
     else
         DTB_LAUNCH(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
-    DTB_LAUNCH(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, npart, (long)N, N, db);
+    DTB_LAUNCH(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, np, (long)N, N, db,
+               (float *)nullptr);
     DTB_LAUNCH_CHECK("bias_grad");
     if (g_timing_on) timing_end(s, K_ELEM, 0, (double)R * N * (dtype == DTB_BF16 ? 2 : 4));
     return DTB_OK;
