@@ -984,7 +984,7 @@ static hipError_t launch_reduce(const float *part, float *out, long long ldo, in
     case 7: DTB_LAUNCH(splitk_reduce<7>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
     default: DTB_LAUNCH(splitk_reduce<15>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
     }
-    return hipGetLastError();
+    return last_error();
 }
 
 // ---- host side ---------------------------------------------------------------
@@ -999,7 +999,7 @@ static hipError_t launch_t(const KParams &p, int splits, hipStream_t s) {
     int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
     dim3 grid(nm * nn, 1, splits);
     DTB_LAUNCH((gemm_kernel<T, BM, BN, AK, BKM>), grid, dim3(256), 2 * STAGE, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 
 template <typename T, int BM, int BN>
@@ -1019,7 +1019,7 @@ static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
     // stream whole lines on 32-k slabs, and the 32-k ring measured the same
     if constexpr (AK || BKM) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE>), grid, dim3(512), 0, s, p);
     else DTB_LAUNCH((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 
 template <int MODE>
@@ -1048,6 +1048,11 @@ static TileChoice choose_tile(int M, int N, int dtype, bool splittable) {
         if (tiles(128, 128) >= 256) return {128, 128};
         return {64, 64};
     }
+    // fp32: weight gradients (split over K when their tiles are few) on
+    // 128 x 128 tiles, measured 8-10% faster than 64 x 64 on the GPT-2-small
+    // shapes; the forward and input-gradient GEMMs keep 64 x 64 below 256
+    // tiles of 128 x 128 (128 x 128 there measured slower)
+    if (splittable && M >= 128 && N >= 128) return {128, 128};
     if (tiles(128, 128) >= 256) return {128, 128};
     return {64, 64};
 }
