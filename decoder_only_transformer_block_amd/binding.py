@@ -99,6 +99,8 @@ def lib() -> ctypes.CDLL:
         L.norm_backward.argtypes = [v, v, v, v, v, v, v, v, v, i, i, i, i, v, v]
         L.norm_workspace_bytes.argtypes = [i, i]
         L.norm_workspace_bytes.restype = z
+        L.activation_forward.argtypes = [v, v, i, i, i, i, v]
+        L.activation_backward.argtypes = [v, v, v, i, i, i, i, v]
         L.lm_head_forward.argtypes = [v, i, v, v, i, i, i, i, v]
         L.lm_head_backward.argtypes = [v, v, v, i, v, v, i, i, i, i, v, v]
         L.lm_head_workspace_bytes.argtypes = [i, i, i, i]
@@ -112,6 +114,7 @@ def lib() -> ctypes.CDLL:
         L.dtb_strerror.argtypes = [i]
         L.dtb_strerror.restype = ctypes.c_char_p
         L.dtb_version.restype = ctypes.c_char_p
+        L.dtb_debug_enable.argtypes = [i]
         L.dtb_timing_enable.argtypes = [i]
         L.dtb_timing_collect.argtypes = [ctypes.POINTER(Timing), i]
         _lib = L
@@ -223,6 +226,16 @@ def norm_backward(dx, dg, db, dy, x, g, rstd, mean, dres, R, C, norm, dtype, wor
           "norm_backward")
 
 
+def activation_forward(h, up, R, H, mlp, dtype, stream=None):
+    check(lib().activation_forward(_ptr(h), _ptr(up), R, H, MLP[mlp], DTYPE[dtype], _stream(stream)),
+          "activation_forward")
+
+
+def activation_backward(dup, dh, up, R, H, mlp, dtype, stream=None):
+    check(lib().activation_backward(_ptr(dup), _ptr(dh), _ptr(up), R, H, MLP[mlp], DTYPE[dtype], _stream(stream)),
+          "activation_backward")
+
+
 def lm_head_forward(logits, ldl, inp, w, R, C, V, dtype, stream=None):
     check(lib().lm_head_forward(_ptr(logits), ldl, _ptr(inp), _ptr(w), R, C, V, DTYPE[dtype], _stream(stream)),
           "lm_head_forward")
@@ -317,6 +330,11 @@ def block_backward_overlap(cfg: BlockCfg, weights: dict, x_in, saved, dx_out, dx
     check(lib().block_backward_overlap(ctypes.byref(cfg), ctypes.byref(w), _ptr(x_in), _ptr(saved), _ptr(dx_out),
                                        _ptr(dx_in), ctypes.byref(g), _ptr(workspace), _stream(stream), side),
           "block_backward_overlap")
+
+
+def dtb_debug_enable(level: int) -> None:
+    """0: off; 1: check and wait after every kernel; 2: also log each kernel."""
+    check(lib().dtb_debug_enable(int(level)), "dtb_debug_enable")
 
 
 TIMING_CLASSES = ["gemm_fwd", "attn_fwd", "attn_bwd", "elementwise", "gemm_dinp", "gemm_dw", "attn_decode",

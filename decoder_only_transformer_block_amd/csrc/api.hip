@@ -16,9 +16,43 @@ namespace dtb {
 // ---------------------------------------------------------------- errors ---
 static thread_local char g_msg[256];
 
+static thread_local hipError_t t_debug_err = hipSuccess;
+static thread_local char t_debug_kernel[160];
+
 int set_launch_error(hipError_t e, const char *what) {
-    snprintf(g_msg, sizeof g_msg, "kernel launch failed in %s: %s", what, hipGetErrorString(e));
+    if (t_debug_kernel[0])
+        snprintf(g_msg, sizeof g_msg, "kernel launch failed in %s (kernel %s): %s", what, t_debug_kernel,
+                 hipGetErrorString(e));
+    else
+        snprintf(g_msg, sizeof g_msg, "kernel launch failed in %s: %s", what, hipGetErrorString(e));
+    t_debug_kernel[0] = 0;
     return DTB_ELAUNCH;
+}
+
+// ---------------------------------------------------------------- debug ---
+int g_debug_level = 0;
+
+void debug_after_launch(hipStream_t s, const char *kernel) {
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        fprintf(stderr, "[dtb debug] %s failed: %s\n", kernel, hipGetErrorString(e));
+        if (t_debug_err == hipSuccess) {
+            t_debug_err = e;
+            snprintf(t_debug_kernel, sizeof t_debug_kernel, "%s", kernel);
+        }
+    } else if (g_debug_level >= 2) {
+        fprintf(stderr, "[dtb debug] %s ok\n", kernel);
+    }
+}
+
+hipError_t last_error() {
+    hipError_t e = hipGetLastError();
+    if (t_debug_err != hipSuccess) {
+        e = t_debug_err;
+        t_debug_err = hipSuccess;
+    }
+    return e;
 }
 
 // ---------------------------------------------------------------- timing ---
@@ -116,6 +150,12 @@ const char *dtb_strerror(int code) {
     case DTB_ELAUNCH: return g_msg[0] ? g_msg : "kernel launch failed";
     default: return "unknown error code";
     }
+}
+
+int dtb_debug_enable(int level) {
+    if (level < 0 || level > 2) return DTB_EINVAL_ENUM;
+    g_debug_level = level;
+    return DTB_OK;
 }
 
 int dtb_timing_enable(int class_mask) {
@@ -553,6 +593,29 @@ int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x,
     if (norm == DTB_NORM_LAYER && (!ptr_ok(db) || !ptr_ok(mean))) return DTB_EINVAL_PTR;
     return dtb::norm_backward(norm, dtype, dy, x, g, rstd, mean, dres, R, C, dx, dg, db, (float *)workspace,
                               norm_backward_parts(R), (hipStream_t)stream);
+}
+
+static int check_act(int R, int H, int mlp, int dtype) {
+    if (dtype != DTB_F32 && dtype != DTB_BF16) return DTB_EDTYPE;
+    if (mlp < 0 || mlp > 2) return DTB_EINVAL_ENUM;
+    if (R < 0 || H <= 0 || H % 8 || (long long)R * H >= (1LL << 40)) return DTB_EINVAL_SHAPE;
+    return DTB_OK;
+}
+
+int activation_forward(void *h, const void *up, int R, int H, int mlp, int dtype, void *stream) {
+    int e = check_act(R, H, mlp, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(h) || !ptr_ok(up)) return DTB_EINVAL_PTR;
+    return dtb::act_forward(mlp, dtype, up, R, H, h, (hipStream_t)stream);
+}
+
+int activation_backward(void *dup, const void *dh, const void *up, int R, int H, int mlp, int dtype, void *stream) {
+    int e = check_act(R, H, mlp, dtype);
+    if (e) return e;
+    if (R == 0) return DTB_OK;
+    if (!ptr_ok(dup) || !ptr_ok(dh) || !ptr_ok(up)) return DTB_EINVAL_PTR;
+    return dtb::act_backward(mlp, dtype, dh, up, R, H, dup, (hipStream_t)stream);
 }
 
 static int check_head(int R, int C, int V, int ldl, int dtype) {

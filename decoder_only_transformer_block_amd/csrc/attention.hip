@@ -607,7 +607,7 @@ template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_
     if (e != hipSuccess) return e;
     int nqb = (p.T + FC::BQ - 1) / FC::BQ;
     DTB_LAUNCH((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 
 template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, hipStream_t s) {
@@ -619,17 +619,17 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     if (e != hipSuccess) return e;
     long long rows = (long long)p.B * p.T;
     DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
-    e = hipGetLastError();
+    e = last_error();
     if (e != hipSuccess) return e;
     AttnP q = p;
     q.D = D;
     int nqb = (p.T + QC::BQ - 1) / QC::BQ;
     DTB_LAUNCH((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * QC::STAGE, s, q);
-    e = hipGetLastError();
+    e = last_error();
     if (e != hipSuccess) return e;
     int nkb = (p.T + KC::BK - 1) / KC::BK;
     DTB_LAUNCH((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
-    return hipGetLastError();
+    return last_error();
 }
 
 // bf16: the dQ kernel computes -D and -lse / scale per query (it holds the

@@ -258,7 +258,7 @@ template <int HD> hipError_t fwd_launch(const AttnP &p, hipStream_t s) {
     constexpr int NS = HD >= 128 ? 2 : 3;
     const int nqb = (p.T + 127) / 128;
     DTB_LAUNCH((fwd_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 
 
@@ -603,11 +603,11 @@ template <int HD> hipError_t bwd_launch(const AttnP &p, hipStream_t s) {
     constexpr int NS = HD >= 128 ? 2 : 3;
     const int nqb = (p.T + 127) / 128;
     DTB_LAUNCH((dq_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
-    hipError_t e = hipGetLastError();
+    hipError_t e = last_error();
     if (e != hipSuccess) return e;
     const int nkb = (p.T + 127) / 128;
     DTB_LAUNCH((dkv_bf16_kernel<HD, NS>), dim3(nkb * p.B * p.NKV), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 
 }  // namespace

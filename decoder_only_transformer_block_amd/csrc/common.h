@@ -190,18 +190,27 @@ extern bool g_timing_on;
 // timing_begin and timing_end) the launch carries the unit's start event (on
 // its first launch) and a stop event on its own dispatch packet, so timing
 // adds no marker packets, and no idle time, between kernels.
+// Opt-in debugging (dtb_debug_enable): with a level above 0, every launch is
+// followed by a check of the launch and a wait for the stream, and the first
+// failure of the calling thread is kept for last_error() with the kernel's name.
+extern int g_debug_level;
+void debug_after_launch(hipStream_t s, const char *kernel);
+
 #define DTB_LAUNCH(kernel, grid, block, shmem, stream, ...)                                        \
     do {                                                                                           \
         hipEvent_t dtb_ev0_ = nullptr, dtb_ev1_ = nullptr;                                         \
         if (g_timing_on) timing_launch_events(&dtb_ev0_, &dtb_ev1_);                               \
         hipExtLaunchKernelGGL(kernel, grid, block, shmem, stream, dtb_ev0_, dtb_ev1_, 0u, __VA_ARGS__); \
+        if (g_debug_level) ::dtb::debug_after_launch(stream, #kernel);                             \
     } while (0)
 
 int set_launch_error(hipError_t e, const char *what);
+// hipGetLastError(), or (debug mode) the first failure a debug check saw
+hipError_t last_error();
 
 #define DTB_LAUNCH_CHECK(what)                                           \
     do {                                                                  \
-        hipError_t _e = hipGetLastError();                                \
+        hipError_t _e = ::dtb::last_error();                              \
         if (_e != hipSuccess) return ::dtb::set_launch_error(_e, what);   \
     } while (0)
 

@@ -407,7 +407,7 @@ template <int HD> hipError_t bf16_launch(const DecP &p, long long nwave, hipStre
     // nwave counts (split, b, kv head, head group) waves; a workgroup takes W kv heads
     const long long nblk = nwave / p.NKV * ((p.NKV + W - 1) / W);
     DTB_LAUNCH((decode_bf16_kernel<HD, NS, W>), dim3((unsigned)nblk), dim3(64 * W), 0, s, p);
-    return hipGetLastError();
+    return last_error();
 }
 template <int HD> hipError_t f32_launch(const DecP &p, int HG, int nblk, hipStream_t s) {
     switch (HG) {
@@ -416,7 +416,7 @@ template <int HD> hipError_t f32_launch(const DecP &p, int HG, int nblk, hipStre
     case 4: DTB_LAUNCH((decode_f32_kernel<HD, 4>), dim3(nblk), dim3(64), 0, s, p); break;
     default: DTB_LAUNCH((decode_f32_kernel<HD, 8>), dim3(nblk), dim3(64), 0, s, p); break;
     }
-    return hipGetLastError();
+    return last_error();
 }
 
 }  // namespace
@@ -494,7 +494,7 @@ hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *
         if (g_timing_on) timing_begin(s, K_DEC_MERGE);
         if (dtype == DTB_BF16) DTB_LAUNCH(decode_merge_kernel<bf16>, dim3(mblk), dim3(256), 0, s, p);
         else DTB_LAUNCH(decode_merge_kernel<float>, dim3(mblk), dim3(256), 0, s, p);
-        e = hipGetLastError();
+        e = last_error();
         if (e != hipSuccess) return e;
         if (g_timing_on) timing_end(s, K_DEC_MERGE, 0.0, (double)B * NH * (hd * 2 + 4));
     }

@@ -331,6 +331,19 @@ int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x,
                   void *stream);
 size_t norm_workspace_bytes(int R, int C);
 
+/* activation_forward / activation_backward: the block's MLP activation on its
+ * own (DTB_MLP_*; "nanoeuler — CUDA kernels" swiglu_forward_kernel /
+ * swiglu_backward_kernel, "microgpt.cu" relu_forward_kernel /
+ * relu_backward_kernel, llm.c gelu_forward / gelu_backward, tanh form).
+ *   up  [R, 2H] for SwiGLU (gate columns 0..H-1, then up columns), else [R, H]
+ *   h   [R, H]  = silu(gate) * up, relu(up) or gelu_tanh(up)  (OVERWRITTEN)
+ *   dup [R, 2H or H] = gradient of up from dh [R, H]         (OVERWRITTEN)
+ * All dtype; H a multiple of 8.  (In block_forward the SwiGLU forward runs in
+ * the up projection's GEMM epilogue where the tiling allows.) */
+int activation_forward(void *h, const void *up, int R, int H, int mlp, int dtype, void *stream);
+int activation_backward(void *dup, const void *dh, const void *up, int R, int H, int mlp, int dtype,
+                        void *stream);
+
 /* lm_head_forward: logits[R, :V] = inp[R, C] W[V, C]^T ("nanoeuler — CUDA
  *   kernels" forward_gpu's head matmul; llm.c gpt2_forward, where W is wte when
  *   the head is tied).  logits rows have stride ldl >= V, ldl a multiple of 8
@@ -411,6 +424,16 @@ int adamw_update(float *params, float *grads, float *m, float *v, void *params_l
 /* ---- misc ---------------------------------------------------------------- */
 const char *dtb_strerror(int code);
 const char *dtb_version(void);
+
+/* Opt-in debugging, in the spirit of the CHECK_CUDA discipline of "nanoeuler —
+ * CUDA kernels" (every call checked): level 1 makes the library check each
+ * kernel launch and wait for its stream right after it, so a failing kernel
+ * is caught at once; the entry point that launched it returns DTB_ELAUNCH and
+ * dtb_strerror names that kernel.  Level 2 also prints one line per kernel to
+ * stderr as it completes.  0 (the default) turns it off.  Process-wide; it
+ * slows every call and must not be on under graph capture.  A level outside
+ * 0..2 gives DTB_EINVAL_ENUM. */
+int dtb_debug_enable(int level);
 
 /* Optional per-kernel timing for measurement: while enabled, every kernel the
  * library enqueues in an enabled class carries HIP start / stop events on its

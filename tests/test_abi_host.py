@@ -141,3 +141,10 @@ def test_saved_layout_consistent(B):
         assert (lay.mu1 >= 0) == (cfg.norm == "layer")
         assert B.block_workspace_bytes(c) > 0
     assert B.attn_workspace_bytes(1, 16384, 32) >= 2 * 16384 * 32 * 4  # D and lse * log2(e)
+
+
+def test_debug_level_validation(B):
+    L = B.lib()
+    assert L.dtb_debug_enable(3) == -4
+    assert L.dtb_debug_enable(-1) == -4
+    assert L.dtb_debug_enable(0) == 0

@@ -100,6 +100,34 @@ def test_norm_standalone(dtype, norm, R, C, with_res):
         check("db", to_numpy(db), rdb, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("mlp", ["swiglu", "relu", "gelu_tanh"])
+@pytest.mark.parametrize("R,H", [(37, 64), (1000, 5632)])
+def test_activation_standalone(dtype, mlp, R, H):
+    """activation_forward / activation_backward through the C ABI against the
+    oracle's activation and its backward."""
+    require_gpu()
+    import torch
+    import oracle
+    from decoder_only_transformer_block_amd import binding, inputs
+    from decoder_only_transformer_block_amd.runtime import to_numpy
+    W = 2 * H if mlp == "swiglu" else H
+    announce(f"activation {mlp} R={R} H={H} {dtype}")
+    up = inputs.tensor(6, f"act.up{R}.{W}", (R, W), std=2.0, dtype=dtype)
+    if mlp == "relu":
+        up[:, :8] = 0.0    # the gradient at exactly 0 is 0 (strict >)
+    dh = inputs.tensor(6, f"act.dh{R}.{H}", (R, H), dtype=dtype)
+    upd = _dev(up, dtype)
+    h = torch.full((R, H), float("nan"), dtype=upd.dtype, device="cuda")
+    dup = torch.full((R, W), float("nan"), dtype=upd.dtype, device="cuda")
+    binding.activation_forward(h, upd, R, H, mlp, dtype)
+    binding.activation_backward(dup, _dev(dh, dtype), upd, R, H, mlp, dtype)
+    torch.cuda.synchronize()
+    tol = TOL[dtype]
+    check("h", to_numpy(h), oracle.act_forward(mlp, up, H), tol)
+    check("dup", to_numpy(dup), oracle.act_backward(mlp, dh, up, H), tol)
+
+
 @pytest.mark.parametrize("dtype,V", [("f32", 1003), ("bf16", 997), ("bf16", 2048)])
 def test_lm_head_and_softmax_ce(dtype, V):
     """Ragged vocabularies (padded row stride), a masked target, the gradient

@@ -118,3 +118,37 @@ def test_overlap_handle_checks():
     assert h.value
     binding.dtb_overlap_destroy(h)
     assert L.dtb_overlap_destroy(None) == 0
+
+
+def test_debug_mode_checks_every_kernel(capfd):
+    """dtb_debug_enable: at level 2 every kernel of an attention forward +
+    backward is checked, waited for and logged by name; the results are the
+    same bits as with debugging off."""
+    require_gpu()
+    import torch
+    from decoder_only_transformer_block_amd import binding
+    announce("debug mode: attention forward + backward")
+    B, T, NH, NKV, hd = 1, 130, 4, 2, 64
+    C, QKV = NH * hd, NH * hd + 2 * NKV * hd
+    g = torch.Generator(device="cuda").manual_seed(1)
+    q = torch.randn(B, T, QKV, device="cuda", generator=g).bfloat16()
+    d = torch.randn(B, T, C, device="cuda", generator=g).bfloat16()
+    ws = torch.empty(binding.attn_workspace_bytes(B, T, NH), dtype=torch.uint8, device="cuda")
+    res = []
+    for level in (0, 2):
+        out = torch.empty(B, T, C, device="cuda", dtype=torch.bfloat16)
+        lse = torch.empty(B, NH, T, device="cuda")
+        dq = torch.empty_like(q)
+        binding.dtb_debug_enable(level)
+        try:
+            binding.attn_forward(out, lse, q, B, T, C, NH, NKV, "bf16")
+            binding.attn_backward(dq, q, out, d, lse, B, T, C, NH, NKV, "bf16", ws)
+        finally:
+            binding.dtb_debug_enable(0)
+        torch.cuda.synchronize()
+        res.append((out.clone(), lse.clone(), dq.clone()))
+    err = capfd.readouterr().err
+    for name in ("fwd_bf16_kernel", "dq_bf16_kernel", "dkv_bf16_kernel"):
+        assert f"{name}" in err and "ok" in err, err[-2000:]
+    for a, b in zip(*res):
+        assert torch.equal(a, b)
