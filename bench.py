@@ -113,7 +113,12 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama_gqa",
                     choices=["llama_gqa", "gpt2_small", "mini_qwen2", "microgpt", "attn_long", "adamw",
-                             "head_ce", "decode", "mtp_head"])
+                             "head_ce", "decode", "mtp_head", "hbm_cold", "oracle_table"])
+    ap.add_argument("--no-overlap", action="store_true",
+                    help="block backward on one stream (block_backward): no weight-gradient GEMM runs beside "
+                         "another kernel, so per-kernel profiles isolate them")
+    ap.add_argument("--attn-long-tokens", type=int, default=4096,
+                    help="oracle_table: sequence length of the long-context attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -122,8 +127,8 @@ def parse():
     ap.add_argument("--traffic-summary", default="",
                     help="only write the forward-GEMM traffic summary from the rocprofv3 runs under this "
                          "directory (subdirectories fetch, write, copy_fetch, copy_write) and exit")
-    ap.add_argument("--cpu-tokens", type=int, default=512,
-                    help="tokens of the oracle's bounded sample (one sequence, one layer)")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens of the oracle's bounded sample (one sequence, one layer); 0: the workload's T")
     return ap.parse_args()
 
 
@@ -158,6 +163,166 @@ def cpu_baseline_attn(cfg, tokens):
     return {"value": round(tokens / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"attention forward+backward B=1, T={tokens}, NH={cfg.NH}, NKV={cfg.NKV}, hd={cfg.hd} "
                       f"in fp64, {dt:.2f} s"}
+
+
+def oracle_table(args):
+    """The oracle timed on the host cores, per configuration: the whole block
+    stack forward + backward (microgpt, mini-Qwen2, GPT-2-small) on every
+    thread and on one thread (GPT-2-small on one thread: one of its twelve
+    layers), one Llama-GQA block on one sequence at the full T = 2048, and
+    long-context attention forward + backward at --attn-long-tokens.  Progress
+    lines go to stderr; a markdown table and one JSON line to stdout."""
+    import numpy as np
+    import oracle
+    from decoder_only_transformer_block_amd import configs
+    oracle.build(force=False)
+    allt = oracle.num_threads()
+    rows = []
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    def stack(cfg, layers, threads):
+        oracle.set_num_threads(threads)
+        x = configs.block_input(cfg)
+        dy = configs.block_dout(cfg)
+        ws = [configs.block_weights(cfg, l) for l in range(layers)]
+        t0 = time.perf_counter()
+        h, saved, xs = x, [], []
+        for l in range(layers):
+            xs.append(h)
+            h, sv = oracle.block_forward(cfg, ws[l], h)
+            saved.append(sv)
+            log(f"  {cfg.name}: layer {l} forward done ({time.perf_counter() - t0:.1f} s, {threads} threads)")
+        g = dy
+        for l in reversed(range(layers)):
+            g, _ = oracle.block_backward(cfg, ws[l], xs[l], saved[l], g)
+            log(f"  {cfg.name}: layer {l} backward done ({time.perf_counter() - t0:.1f} s, {threads} threads)")
+        return time.perf_counter() - t0
+
+    for name in ("microgpt", "mini_qwen2", "gpt2_small"):
+        cfg = configs.BLOCK_CONFIGS[name]
+        tok = cfg.B * cfg.T
+        for threads in (allt, 1):
+            layers = cfg.L if (threads == allt or cfg.L <= 2) else 1
+            dt = stack(cfg, layers, threads)
+            rows.append({"config": name, "shape": f"L={layers} B={cfg.B} T={cfg.T}", "threads": threads,
+                         "seconds": round(dt, 3), "tokens_per_s_per_block": round(tok * layers / dt, 2),
+                         "gflop": round((cfg.gemm_flops_per_layer() + cfg.attn_flops_per_layer()) * layers / 1e9, 4)})
+            log(json.dumps(rows[-1]))
+    cfg = configs.LLAMA_GQA.replace(B=1, L=1)
+    dt = stack(cfg, 1, allt)
+    rows.append({"config": "llama_gqa", "shape": f"L=1 B=1 T={cfg.T} (one of the B=8 sequences of one layer)",
+                 "threads": allt, "seconds": round(dt, 3), "tokens_per_s_per_block": round(cfg.T / dt, 2),
+                 "gflop": round((cfg.gemm_flops_per_layer() + cfg.attn_flops_per_layer()) / 1e9, 4)})
+    log(json.dumps(rows[-1]))
+    oracle.set_num_threads(allt)
+    cfg = configs.ATTN_LONG.replace(T=args.attn_long_tokens)
+    qkv, dout = configs.attn_inputs(cfg)
+    t0 = time.perf_counter()
+    oracle.attn_forward(qkv, cfg.B, cfg.T, cfg.C, cfg.NH, cfg.NKV)
+    log(f"  attn_long T={cfg.T}: forward done ({time.perf_counter() - t0:.1f} s)")
+    oracle.attn_backward(qkv, dout, cfg.B, cfg.T, cfg.C, cfg.NH, cfg.NKV)
+    dt = time.perf_counter() - t0
+    rows.append({"config": "attn_long", "shape": f"B=1 T={cfg.T} NH=32 NKV=8 hd=128 (attention forward+backward)",
+                 "threads": allt, "seconds": round(dt, 3), "tokens_per_s_per_block": round(cfg.T / dt, 2),
+                 "gflop": round(cfg.fwd_flops() * 3.5 / 1e9, 4)})
+    log(json.dumps(rows[-1]))
+    print("| config | oracle run | threads | seconds | tokens/s per block | GFLOP |")
+    print("|---|---|---:|---:|---:|---:|")
+    for r in rows:
+        print(f"| {r['config']} | {r['shape']} | {r['threads']} | {r['seconds']} | {r['tokens_per_s_per_block']} | "
+              f"{r['gflop']} |")
+    print(json.dumps({"oracle_table": rows, "host_threads": allt}))
+
+
+def bench_hbm_cold(args):
+    """The bandwidth-bound kernels of the Llama-GQA layer (RMSNorm forward and
+    backward with the residual gradient, the SwiGLU forward and backward) and
+    of the GPT-2-small layer (LayerNorm forward and backward, GELU forward and
+    backward, the bias gradient), each launched alone through the C ABI on its
+    full-size tensors: hot (the same buffers every launch, so what fits stays
+    in the 256 MB last-level cache) and cold (launches rotate over buffer sets
+    of more than 1.5 GB in all, so every launch reads tensors that left the
+    cache).  GB/s from the algorithmic bytes the library records per launch
+    and the HIP events on each kernel."""
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    out = []
+    for cname in ("llama_gqa", "gpt2_small"):
+        cfg = configs.BLOCK_CONFIGS[cname]
+        R, C, H, dt = cfg.B * cfg.T, cfg.C, cfg.H, cfg.dtype
+        td = torch.bfloat16 if dt == "bf16" else torch.float32
+        es = 2 if dt == "bf16" else 4
+        W = 2 * H if cfg.mlp == "swiglu" else H
+        norm, mlp = cfg.norm, cfg.mlp
+        g = torch.Generator(device="cuda").manual_seed(7)
+
+        def rnd(*shape):
+            return torch.randn(*shape, device="cuda", generator=g).to(td)
+
+        gam, bet = rnd(C), rnd(C)
+        nws = torch.empty(binding.norm_workspace_bytes(R, C), dtype=torch.uint8, device="cuda")
+        lws = torch.empty(binding.linear_workspace_bytes(R, 8, W, dt), dtype=torch.uint8, device="cuda")
+        kernels = {
+            "norm_forward": (lambda b: binding.norm_forward(b["o"], b["rs"], b["mu"], b["x"], gam, bet, R, C, norm,
+                                                            1e-5, dt), ("x", "o"), C),
+            "norm_backward (+ residual)": (
+                lambda b: binding.norm_backward(b["o"], b["dg"], b["db"], b["dy"], b["x"], gam, b["rs"], b["mu"],
+                                                b["r"], R, C, norm, dt, nws), ("x", "o", "dy", "r"), C),
+            f"{mlp} forward": (lambda b: binding.activation_forward(b["h"], b["up"], R, H, mlp, dt), ("up", "h"), 0),
+            f"{mlp} backward": (lambda b: binding.activation_backward(b["dup"], b["h"], b["up"], R, H, mlp, dt),
+                                ("up", "h", "dup"), 0),
+        }
+        if cfg.mlp_bias:
+            kernels["bias gradient (MLP up)"] = (
+                lambda b: binding.linear_backward(None, None, b["db2"], b["up"], None, None, R, 8, W, dt, lws),
+                ("up",), 0)
+        shapes = {"x": (R, C), "o": (R, C), "dy": (R, C), "r": (R, C), "up": (R, W), "h": (R, H), "dup": (R, W)}
+        for kname, (fn, used, _) in kernels.items():
+            set_elems = sum(R * shapes[u][1] for u in used)
+            nsets = max(2, -(-int(1.6e9) // (set_elems * es)))
+            # every set is a view of one allocation (one contiguous range of
+            # device memory), filled with N(0, 1) values
+            flat = torch.empty(nsets * set_elems, dtype=td, device="cuda")
+            for i in range(nsets):
+                flat[i * set_elems:(i + 1) * set_elems].copy_(
+                    torch.randn(set_elems, device="cuda", generator=g))
+            sets = []
+            for i in range(nsets):
+                b, off = {}, i * set_elems
+                for u in used:
+                    n = R * shapes[u][1]
+                    b[u] = flat[off:off + n].view(*shapes[u])
+                    off += n
+                b.update(rs=torch.rand(R, device="cuda", generator=g) + 0.5,
+                         mu=torch.zeros(R, device="cuda"), dg=torch.zeros(C, device="cuda"),
+                         db=torch.zeros(C, device="cuda"), db2=torch.zeros(W, device="cuda"))
+                if "o" not in b:
+                    b["o"] = None
+                sets.append(b)
+            res = {}
+            for mode in ("hot", "cold"):
+                for i in range(3):
+                    fn(sets[0] if mode == "hot" else sets[i % nsets])
+                torch.cuda.synchronize()
+                binding.timing_enable(classes=["elementwise"])
+                binding.timing_collect()
+                n = 4 * nsets if mode == "cold" else 20
+                for i in range(n):
+                    fn(sets[0] if mode == "hot" else sets[(i + 3) % nsets])
+                t = binding.timing_collect()["elementwise"]
+                binding.timing_enable(False)
+                gbps = t["bytes"] / (t["ms"] * 1e-3) / 1e9
+                res[mode] = {"gbps": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK, 4),
+                             "us_per_launch": round(t["ms"] * 1e3 / t["launches"], 2)}
+            row = {"workload": cname, "kernel": kname, "dtype": dt,
+                   "bytes_per_launch": round(t["bytes"] / t["launches"]), "buffer_sets": nsets, **res}
+            out.append(row)
+            print(json.dumps(row), file=sys.stderr, flush=True)
+            del sets, flat
+            torch.cuda.empty_cache()
+    return out
 
 
 def timed_steps(args, step, roof_classes):
@@ -201,7 +366,7 @@ def bench_block(args, cfg):
     ws = [configs.block_weights(cfg, l) for l in range(cfg.L)]
     x = to_device(configs.block_input(cfg), cfg.dtype)
     dy = to_device(configs.block_dout(cfg), cfg.dtype)
-    st = BlockStack(cfg, ws)
+    st = BlockStack(cfg, ws, overlap=not args.no_overlap)
     del ws
 
     def step():
@@ -411,6 +576,9 @@ def main():
         cmds.append(f"python3 bench.py --traffic-summary {root} > profiles/gemm_fwd_llama_gqa_traffic.md")
         print(traffic_summary(root, {"workload": "llama_gqa", "copy_bytes": n, "commands": cmds}))
         return
+    if args.workload == "oracle_table":
+        oracle_table(args)
+        return
     import torch
     from decoder_only_transformer_block_amd import configs
     assert torch.cuda.is_available(), "bench.py needs a GPU"
@@ -422,6 +590,16 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4, "repeats": 3}))
+        return
+    if args.workload == "hbm_cold":
+        rows = bench_hbm_cold(args)
+        print("| workload | kernel | dtype | bytes per launch | hot GB/s (frac) | cold GB/s (frac) | cold us |")
+        print("|---|---|---|---:|---:|---:|---:|")
+        for r in rows:
+            print(f"| {r['workload']} | {r['kernel']} | {r['dtype']} | {r['bytes_per_launch']} | "
+                  f"{r['hot']['gbps']} ({r['hot']['frac_hbm_peak']}) | {r['cold']['gbps']} "
+                  f"({r['cold']['frac_hbm_peak']}) | {r['cold']['us_per_launch']} |")
+        print(json.dumps({"hbm_cold": rows}))
         return
     if args.workload == "adamw":
         ms, n, nbytes = bench_adamw(args)
@@ -556,7 +734,8 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline_attn(cfg, 1024) if args.workload == "attn_long" else cpu_baseline(cfg, args.cpu_tokens)
+        cpu = cpu_baseline_attn(cfg, 1024) if args.workload == "attn_long" else \
+            cpu_baseline(cfg, args.cpu_tokens or cfg.T)
 
     line = {
         "metric": "train tokens/s per block fwd+bwd; attn+GEMM TFLOP/s as % MFMA peak",
