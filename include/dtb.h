@@ -33,6 +33,10 @@
  *   dtb_strerror() gives a message; for DTB_ELAUNCH it includes the HIP error.
  * - Calls on the same stream are ordered; calls on different streams that
  *   touch the same buffers race.
+ * - Graph capture: the block, attention, linear, norm and activation entry
+ *   points enqueue kernels and (block_backward_overlap) event waits only,
+ *   never a memset, copy or host wait, so a stream capture of them replays
+ *   to the same results; not while timing or debug mode is on.
  */
 #ifndef DTB_H
 #define DTB_H
