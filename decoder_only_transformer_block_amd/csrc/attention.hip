@@ -143,6 +143,75 @@ __device__ __forceinline__ void store_rows(T *row, const f32x16 *acc, float s, i
 }
 
 // ---------------------------------------------------------------------------
+// transposed fp32 tiles (head widths >= 32): a natural [64][HD] tile staged as
+// its transpose [HD][64], so that the A operand of a product over positions
+// (V^T, K^T, ...) comes as one 16-byte read of four consecutive positions per
+// lane, i.e. one read per four MFMAs, instead of one 4-byte read per MFMA.
+// Row d holds the 64 positions of column d in 16 chunks; chunk kc (positions
+// 4 kc .. 4 kc + 3) sits at kc ^ (d & 15), so the 16 lanes of a read group
+// (16 consecutive d, one chunk) hit 16 different bank quads.
+// Staging items are 4 x 4 blocks (4 positions x 4 columns): four 16-byte row
+// pieces loaded, transposed in registers, stored as four 16-byte column pieces.
+// ---------------------------------------------------------------------------
+template <int HD, int NT> struct NatT {
+    static constexpr int CB = HD / 4;              // column blocks
+    static constexpr int ITEMS = 16 * CB;          // 16 position blocks of 4
+    static constexpr int P = (ITEMS + NT - 1) / NT;
+    static constexpr int REGS = 4 * P;             // 16-byte registers per thread
+    __device__ static __forceinline__ void load(u32x4 *reg, const float *g, long long stride, int row0, int nrows,
+                                                int hd, int tl) {
+        const Buf buf(g + (long long)row0 * stride);
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            const int idx = tl + NT * p;
+            const int cb = idx % CB, pb = idx / CB;   // neighbouring threads: neighbouring 16-byte pieces of a row
+            const bool live = idx < ITEMS && cb * 4 < hd;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int r = pb * 4 + i;
+                reg[4 * p + i] = buf.ld16((int)(((long long)r * stride + cb * 4) * 4), live && row0 + r < nrows);
+            }
+        }
+    }
+    __device__ static __forceinline__ void store(const u32x4 *reg, char *lds, int tl) {
+#pragma unroll
+        for (int p = 0; p < P; p++) {
+            const int idx = tl + NT * p;
+            if (idx >= ITEMS) continue;
+            const int cb = idx % CB, pb = idx / CB;
+            u32x4 o[4];
+            transpose4x4(reg + 4 * p, o);   // o[e]: column cb*4+e, positions 4 pb .. 4 pb + 3
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                const int d = cb * 4 + e;
+                *reinterpret_cast<u32x4 *>(lds + d * 256 + ((pb ^ (d & 15)) << 4)) = o[e];
+            }
+        }
+    }
+};
+
+// acc (ND blocks over the head dimension, columns = the lane's query or key)
+// += A^T (HD x 32 positions of block j) * X (32 positions x 32 columns, the
+// S^T-layout registers x), A^T read from a transposed tile: chunk
+// j*8 + 2q + g of row d holds positions 32 j + 8 q + 4 g + e, the rows that
+// registers 4q + e of lane half g hold in x
+template <int HD>
+__device__ __forceinline__ void mma_trans_t(f32x16 *acc, const f32x16 &x, const char *tt, int j, int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int db = 0; db < HD / 32; db++) {
+        const int d = db * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int kc = j * 8 + 2 * q + g;
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(tt + d * 256 + ((kc ^ (d & 15)) << 4));
+#pragma unroll
+            for (int e = 0; e < 4; e++) acc[db] = mfma32(__uint_as_float(v[e]), x[4 * q + e], acc[db]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // forward
 // ---------------------------------------------------------------------------
 template <typename T, int HD> struct FwdCfg {
@@ -153,19 +222,33 @@ template <typename T, int HD> struct FwdCfg {
     static constexpr int PREG = Nat<T, HD, BKV, 128>::P;
 };
 
+// V staged transposed (fp32, HD >= 32): the same register count as the natural loader
+template <typename T, int HD> constexpr bool fwd_vt() { return std::is_same<T, float>::value && HD >= 32; }
+
 template <typename T, int HD>
 __device__ __forceinline__ void fwd_stage_load(u32x4 *reg, const T *kb, const T *vb, long long stride, int kv0,
                                                int T_, int hd) {
     const int t = threadIdx.x;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
-    const T *g = lo ? vb : kb;
-    Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    if constexpr (fwd_vt<T, HD>()) {
+        static_assert(NatT<HD, 128>::REGS == Nat<T, HD, 64, 128>::P, "transposed staging must fit the registers");
+        if (lo) NatT<HD, 128>::load(reg, vb, stride, kv0, T_, hd, t & 127);
+        else Nat<T, HD, 64, 128>::load(reg, kb, stride, kv0, T_, hd, t & 127);
+    } else {
+        const T *g = lo ? vb : kb;
+        Nat<T, HD, 64, 128>::load(reg, g, stride, kv0, T_, hd, t & 127);
+    }
 }
 template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(const u32x4 *reg, char *st) {
     const int t = threadIdx.x;
     constexpr int KB = FwdCfg<T, HD>::KB;
     const bool lo = __builtin_amdgcn_readfirstlane(t >> 6) < 2;
-    Nat<T, HD, 64, 128>::store(reg, lo ? st + KB : st, t & 127);
+    if constexpr (fwd_vt<T, HD>()) {
+        if (lo) NatT<HD, 128>::store(reg, st + KB, t & 127);
+        else Nat<T, HD, 64, 128>::store(reg, st, t & 127);
+    } else {
+        Nat<T, HD, 64, 128>::store(reg, lo ? st + KB : st, t & 127);
+    }
 }
 
 template <typename T, int HD>
@@ -257,7 +340,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
                     lsum += e;
                 }
 #pragma unroll
-            for (int j = 0; j < 2; j++) mma_trans<T, HD, BKV>(O, S[j], Vs, j, lane);
+            for (int j = 0; j < 2; j++) {
+                if constexpr (fwd_vt<T, HD>()) mma_trans_t<HD>(O, S[j], Vs, j, lane);
+                else mma_trans<T, HD, BKV>(O, S[j], Vs, j, lane);
+            }
         }
         if (more) fwd_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
         __syncthreads();
