@@ -978,11 +978,14 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *part, float *o
 static hipError_t launch_reduce(const float *part, float *out, long long ldo, int M, int N, int splits, hipStream_t s) {
     const long long total4 = (long long)M * N / 4;
     const dim3 grid((unsigned)((total4 + 255) / 256));
-    switch (splits - 1) {  // partial slots
-    case 1: DTB_LAUNCH(splitk_reduce<1>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 3: DTB_LAUNCH(splitk_reduce<3>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    case 7: DTB_LAUNCH(splitk_reduce<7>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
-    default: DTB_LAUNCH(splitk_reduce<15>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    switch (splits - 1) {  // partial slots (splits is in [2, 16])
+#define DTB_REDUCE_CASE(n) \
+    case n: DTB_LAUNCH(splitk_reduce<n>, grid, dim3(256), 0, s, part, out, ldo, M, N); break;
+    DTB_REDUCE_CASE(1) DTB_REDUCE_CASE(2) DTB_REDUCE_CASE(3) DTB_REDUCE_CASE(4) DTB_REDUCE_CASE(5)
+    DTB_REDUCE_CASE(6) DTB_REDUCE_CASE(7) DTB_REDUCE_CASE(8) DTB_REDUCE_CASE(9) DTB_REDUCE_CASE(10)
+    DTB_REDUCE_CASE(11) DTB_REDUCE_CASE(12) DTB_REDUCE_CASE(13) DTB_REDUCE_CASE(14) DTB_REDUCE_CASE(15)
+#undef DTB_REDUCE_CASE
+    default: return hipErrorInvalidValue;
     }
     return last_error();
 }
@@ -1037,6 +1040,16 @@ static hipError_t launch256(const KParams &p, bool ak, bool bk, int splits, hipS
     return launch256_mode<3>(p, ak, bk, splits, s);
 }
 
+// compute units of the current device (asked each time: the answer depends
+// on the device, and the runtime answers from its own cache)
+static int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+        return cus;
+    return 256;
+}
+
 struct TileChoice {
     int bm, bn;
 };
@@ -1048,23 +1061,16 @@ static TileChoice choose_tile(int M, int N, int dtype, bool splittable) {
         if (tiles(128, 128) >= 256) return {128, 128};
         return {64, 64};
     }
-    // fp32: weight gradients (split over K when their tiles are few) on
-    // 128 x 128 tiles, measured 8-10% faster than 64 x 64 on the GPT-2-small
-    // shapes; the forward and input-gradient GEMMs keep 64 x 64 below 256
-    // tiles of 128 x 128 (128 x 128 there measured slower)
+    // fp32: weight gradients (split over K, see choose_splits) on 128 x 128
+    // tiles.  The forward and input-gradient GEMMs take 64 x 128 tiles when
+    // there are at least four per CU and 64 x 64 otherwise: on the GPT-2-small
+    // projection shapes 64 x 128 ran 101-122 TFLOP/s against 82-97 for
+    // 128 x 128 (two workgroups per CU by LDS against three), and with fewer
+    // tiles 64 x 64 keeps the CUs evenly loaded (384 tiles of 64 x 128 leave
+    // half the CUs with twice the work).
     if (splittable && M >= 128 && N >= 128) return {128, 128};
-    if (tiles(128, 128) >= 256) return {128, 128};
+    if (tiles(64, 128) >= 4LL * device_cus()) return {64, 128};
     return {64, 64};
-}
-
-// compute units of the current device (asked each time: the answer depends
-// on the device, and the runtime answers from its own cache)
-static int device_cus() {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
-        return cus;
-    return 256;
 }
 
 static int choose_splits(const GemmArgs &g, TileChoice tc) {
@@ -1091,9 +1097,33 @@ static int choose_splits(const GemmArgs &g, TileChoice tc) {
         }
         return best;
     }
-    int splits = 1;
-    while (tiles * splits < 512 && (long long)g.K / (splits * 2) >= 8 * BK && splits < 16) splits *= 2;
-    return splits;
+    if (g.dtype == DTB_BF16) {  // bf16 tiles below 256 x 256 (a side under 256)
+        int splits = 1;
+        while (tiles * splits < 512 && (long long)g.K / (splits * 2) >= 8 * BK && splits < 16) splits *= 2;
+        return splits;
+    }
+    // fp32 128 x 128 tiles: the split count with the least estimated time.
+    // The workgroups of S splits x tiles are dealt to the CUs in turn, so the
+    // busiest CU runs ceil(tiles S / CUs) of them, each a fixed cost plus its
+    // k range; the reduction streams (S + 2) M N fp32 values.  Constants
+    // measured on the GPT-2-small weight-gradient shapes: 3 us per workgroup,
+    // 70 ns per k, 6 TB/s.  Any S (not only powers of two): there, 7 splits
+    // of 108, 36 or 144 tiles ran 80-104 TFLOP/s against 65-91 for 4-16.
+    const int cus = device_cus();
+    int best = 1;
+    double best_t = 0.0;
+    for (int sp = 1; sp <= 16; sp++) {
+        const long long kc = ((long long)g.K + sp - 1) / sp;
+        if (sp > 1 && kc < 4 * BK) break;
+        const long long per_cu = (tiles * sp + cus - 1) / cus;
+        double t = (double)per_cu * (3.0 + (double)kc * 0.07 * (tc.bm * tc.bn) / (128.0 * 128.0));
+        if (sp > 1) t += (sp + 2) * 4.0 * g.M * g.N / 6e6;
+        if (sp == 1 || t < best_t) {
+            best = sp;
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 size_t gemm_ws_bytes(int M, int N, int K, int dtype) {
@@ -1143,10 +1173,11 @@ int gemm(const GemmArgs &g, void *ws, size_t ws_bytes, hipStream_t s) {
         else e = launch_layout<bf16, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
     } else {
         if (tc.bm == 128) e = launch_layout<float, 128, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
+        else if (tc.bn == 128) e = launch_layout<float, 64, 128>(p, g.a_kmajor, g.b_kmajor, splits, s);
         else e = launch_layout<float, 64, 64>(p, g.a_kmajor, g.b_kmajor, splits, s);
     }
     if (e != hipSuccess) return set_launch_error(e, "gemm");
-    if (splits > 1) {  // splits is a power of two in [2, 16] (choose_splits)
+    if (splits > 1) {  // splits is in [2, 16] (choose_splits)
         e = launch_reduce(reinterpret_cast<const float *>(ws), reinterpret_cast<float *>(g.out), g.ldo, g.M, g.N,
                           splits, s);
         if (e != hipSuccess) return set_launch_error(e, "splitk_reduce");
