@@ -1081,14 +1081,21 @@ static int choose_splits(const GemmArgs &g, TileChoice tc) {
         // bf16 256 x 256 tiles: the split count with the least estimated time,
         // rounds of workgroups x (per-round cost + k range x per-k cost) plus
         // the reduction's traffic ((S + 2) M N fp32 values), with constants
-        // measured on this kernel: 9 us per round, 27.5 ns per k, 6 TB/s
+        // measured on this kernel: 9 us per round, 27.5 ns per k with every CU
+        // busy, 6 TB/s.  A round that leaves CUs idle runs its k range faster
+        // (the busy ones share L2, HBM and power with fewer others): per-k cost
+        // x (0.45 + 0.55 x busy fraction), fitted to the Llama-GQA
+        // weight-gradient shapes (e.g. the QKV one ran 1061 TFLOP/s on 2 splits,
+        // one round of 192 workgroups, against 908 on 8, three full rounds).
         const int cus = device_cus();
         int best = 1;
         double best_t = 0.0;
         for (int sp = 1; sp <= 16; sp *= 2) {
             if (sp > 1 && (long long)g.K / sp < 8 * BK) break;
-            const long long rounds = (tiles * sp + cus - 1) / cus;
-            double t = (double)rounds * (9.0 + (double)g.K / sp * 0.0275);
+            const long long units = tiles * sp, full = units / cus, rest = units % cus;
+            const double kcost = (double)g.K / sp * 0.0275;
+            double t = (double)full * (9.0 + kcost);
+            if (rest) t += 9.0 + kcost * (0.45 + 0.55 * (double)rest / cus);
             if (sp > 1) t += (sp + 2) * 4.0 * g.M * g.N / 6e6;
             if (sp == 1 || t < best_t) {
                 best = sp;
