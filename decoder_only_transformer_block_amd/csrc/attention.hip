@@ -20,8 +20,9 @@
 //   with (row & 7).  Two LDS stages; the next tile's global loads are issued
 //   before the current tile's MFMAs (one barrier per tile).  Half of the
 //   threads stage one tensor, the other half the other.
-// * forward: one workgroup = 4 waves x 32 queries of one (b, h), key tiles of
-//   64, last query blocks launched first (causal load balance).
+// * forward: one workgroup = 64 queries of one (b, h), key tiles of 64 whose
+//   two 32-key halves go to two waves per 32-query slice (merged at the end),
+//   last query blocks launched first (causal load balance).
 // * backward: D = rowsum(dO o) by a small kernel; dQ by a query-owning kernel
 //   (like the forward: S^T, dP^T = V dO^T, dQ^T += K^T dS^T); dK and dV by a
 //   key-owning kernel (4 waves x 32 keys of one (b, kv head)) that loops over
@@ -215,11 +216,14 @@ __device__ __forceinline__ void mma_trans_t(f32x16 *acc, const f32x16 &x, const 
 // forward
 // ---------------------------------------------------------------------------
 template <typename T, int HD> struct FwdCfg {
-    static constexpr int BQ = 128, BKV = 64;
+    static constexpr int BQ = 64, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);  // K natural tile bytes (= V tile bytes)
     static constexpr int STAGE = 2 * KB;
     // staging: threads [0, 128) load V, [128, 256) load K with the same loader
     static constexpr int PREG = Nat<T, HD, BKV, 128>::P;
+    // end of the kernel: the two slices' (O, m, l) hand-over, in the same LDS
+    static constexpr int MERGE = 2 * (AT<T, HD>::ND * 16 * 64 + 128) * 4;
+    static constexpr int LDS = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
 };
 
 // V staged transposed (fp32, HD >= 32): the same register count as the natural loader
@@ -251,6 +255,14 @@ template <typename T, int HD> __device__ __forceinline__ void fwd_stage_store(co
     }
 }
 
+// One workgroup: 64 queries of one (b, h) as two slices of 32, each slice
+// shared by two waves that split every 64-key tile into its two 32-key halves
+// (wave = slice + 2 * half).  Each wave keeps its own online-softmax state over
+// its keys; at the end the half-1 waves hand (m, l, O) to their half-0
+// partners through LDS, which merge and store.  Splitting the keys halves the
+// serial chain of the slices next to the diagonal's end (the last 32 queries
+// see every key): with one wave per slice that chain alone took longer than
+// the average CU's share of the whole launch.
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
     using A = AT<T, HD>;
@@ -264,7 +276,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
     const int bh = blockIdx.x % BH;
     const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+    const int slice = wave & 1, half = wave >> 1;
+    const int q0 = qb * BQ, qw0 = q0 + slice * 32, qi = qw0 + l32;
+    // last key this slice can see (none if the slice starts past the sequence)
+    const int klast = qw0 < p.T ? min(qw0 + 31, p.T - 1) : -1;
 
     const long long stride = p.QKV;
     const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
@@ -283,7 +298,6 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
 
     const int kv_end = min(p.T, q0 + BQ);
     const int ntiles = (kv_end + BKV - 1) / BKV;
-    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
 
     u32x4 reg[FC::PREG];
     fwd_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
@@ -298,28 +312,21 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
         if (more) fwd_stage_load<T, HD>(reg, kbase, vbase, stride, (kt + 1) * BKV, p.T, p.hd);
         const char *Ks = smem + (kt & 1) * FC::STAGE;
         const char *Vs = Ks + FC::KB;
-        if (kt < wtiles) {
-            const int kv0 = kt * BKV;
-            f32x16 S[2];
+        const int kb0 = kt * BKV + half * 32;   // this wave's 32 keys
+        if (kb0 <= klast) {
+            f32x16 S;
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
+            for (int r = 0; r < 16; r++) S[r] = 0.f;
+            mma_rows<T, HD>(S, Ks, half * 32, qf, lane);
+            // keys above the diagonal only occur in the last blocks of a slice
+            if (kb0 + 31 > qw0) {
 #pragma unroll
-                for (int r = 0; r < 16; r++) S[j][r] = 0.f;
-                mma_rows<T, HD>(S[j], Ks, j * 32, qf, lane);
+                for (int r = 0; r < 16; r++)
+                    if (kb0 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
-            // keys above the diagonal only occur in the last tiles of a wave
-            if (kv0 + BKV - 1 > qw0) {
+            float mt = S[0];
 #pragma unroll
-                for (int j = 0; j < 2; j++)
-#pragma unroll
-                    for (int r = 0; r < 16; r++)
-                        if (kv0 + j * 32 + acc_row(r, lane) > qi) S[j][r] = -INFINITY;
-            }
-            float mt = S[0][0];
-#pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) mt = fmaxf(mt, S[j][r]);
+            for (int r = 1; r < 16; r++) mt = fmaxf(mt, S[r]);
             mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;   // running max in log2 units
             const float mn = fmaxf(m, mt);
             if (!__all(mn == m)) {
@@ -332,23 +339,42 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
             }
             m = mn;
 #pragma unroll
-            for (int j = 0; j < 2; j++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    float e = exp2f(fmaf(S[j][r], p.sl2, -mn));
-                    S[j][r] = e;
-                    lsum += e;
-                }
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                if constexpr (fwd_vt<T, HD>()) mma_trans_t<HD>(O, S[j], Vs, j, lane);
-                else mma_trans<T, HD, BKV>(O, S[j], Vs, j, lane);
+            for (int r = 0; r < 16; r++) {
+                float e = exp2f(fmaf(S[r], p.sl2, -mn));
+                S[r] = e;
+                lsum += e;
             }
+            if constexpr (fwd_vt<T, HD>()) mma_trans_t<HD>(O, S, Vs, half, lane);
+            else mma_trans<T, HD, BKV>(O, S, Vs, half, lane);
         }
         if (more) fwd_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
         __syncthreads();
     }
 
+    // merge the two halves of each slice (the stages are free after the last barrier):
+    // per slice, O as [ND][16][64 lanes] floats, then m and the lane's partial sum
+    float *xo = reinterpret_cast<float *>(smem) + slice * (A::ND * 16 * 64 + 128);
+    if (half == 1) {
+#pragma unroll
+        for (int d = 0; d < A::ND; d++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) xo[(d * 16 + r) * 64 + lane] = O[d][r];
+        xo[A::ND * 16 * 64 + lane] = m;
+        xo[A::ND * 16 * 64 + 64 + lane] = lsum;
+    }
+    __syncthreads();
+    if (half == 1) return;
+    {
+        const float m1 = xo[A::ND * 16 * 64 + lane], l1 = xo[A::ND * 16 * 64 + 64 + lane];
+        const float mm = fmaxf(m, m1);
+        const float a0 = exp2f(m - mm), a1 = exp2f(m1 - mm);
+#pragma unroll
+        for (int d = 0; d < A::ND; d++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) O[d][r] = O[d][r] * a0 + xo[(d * 16 + r) * 64 + lane] * a1;
+        lsum = lsum * a0 + l1 * a1;
+        m = mm;
+    }
     const float ltot = lsum + __shfl_xor(lsum, 32, 64);
     if (qi < p.T) {
         T *orow = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + qi) * p.C + h * p.hd;
@@ -689,10 +715,10 @@ static int pad_hd(int hd, int dtype) {
 template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_t s) {
     using FC = FwdCfg<T, HD>;
     // set on every launch (per device), no first-device-only flag
-    hipError_t e = set_lds(attn_fwd_kernel<T, HD>, 2 * FC::STAGE);
+    hipError_t e = set_lds(attn_fwd_kernel<T, HD>, FC::LDS);
     if (e != hipSuccess) return e;
     int nqb = (p.T + FC::BQ - 1) / FC::BQ;
-    DTB_LAUNCH((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * FC::STAGE, s, p);
+    DTB_LAUNCH((attn_fwd_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), FC::LDS, s, p);
     return last_error();
 }
 
