@@ -25,10 +25,13 @@
 //   last query blocks launched first (causal load balance).
 // * backward: D = rowsum(dO o) by a small kernel; dQ by a query-owning kernel
 //   (like the forward: S^T, dP^T = V dO^T, dQ^T += K^T dS^T); dK and dV by a
-//   key-owning kernel (4 waves x 32 keys of one (b, kv head)) that loops over
+//   key-owning kernel (64 keys of one (b, kv head)) that loops over
 //   the group's query heads and the query tiles at or after its keys
 //   (S = Q K^T, dP = dO V^T, dV^T += dO^T P, dK^T += Q^T dS), so dK/dV are
-//   summed over the group in registers -- no atomics, deterministic.
+//   summed over the group in registers -- no atomics, deterministic.  In both
+//   backward kernels a workgroup holds two 32-row slices of its own rows and
+//   gives each slice two waves that take alternate 32-row halves of the other
+//   side's tiles; the halves' partial sums meet in LDS at the end.
 #include <type_traits>
 
 #include "attention.h"
@@ -435,12 +438,15 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(AttnP p, float *D) {
 // backward: dQ (query-owning)
 // ---------------------------------------------------------------------------
 template <typename T, int HD> struct DqCfg {
-    static constexpr int BQ = 128, BKV = 64;
+    static constexpr int BQ = 64, BKV = 64;
     static constexpr int KB = BKV * HD * (int)sizeof(T);
     // LDS stage: K natural, V natural.  Threads [0, 128) load K, [128, 256)
     // load V with the same loader.
     static constexpr int STAGE = 2 * KB;
     static constexpr int PREG = Nat<T, HD, BKV, 128>::P;
+    // end of the kernel: the half-1 waves' dQ partials, in the same LDS
+    static constexpr int MERGE = 2 * AT<T, HD>::ND * 16 * 64 * 4;
+    static constexpr int LDS = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
 };
 
 template <typename T, int HD>
@@ -471,7 +477,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
     const int bh = blockIdx.x % BH;
     const int b = bh / p.NH, h = bh % p.NH, kh = h / (p.NH / p.NKV);
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-    const int q0 = qb * BQ, qw0 = q0 + wave * 32, qi = qw0 + l32;
+    // two 32-query slices; each 64-key tile's two 32-key halves go to two
+    // waves (wave = slice + 2 * half), whose dQ partials are summed at the end
+    const int slice = wave & 1, half = wave >> 1;
+    const int q0 = qb * BQ, qw0 = q0 + slice * 32, qi = qw0 + l32;
+    const int klast = qw0 < p.T ? min(qw0 + 31, p.T - 1) : -1;
 
     const long long stride = p.QKV;
     const T *base = reinterpret_cast<const T *>(p.qkv) + (long long)b * p.T * stride;
@@ -494,7 +504,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
 
     const int kv_end = min(p.T, q0 + BQ);
     const int ntiles = (kv_end + BKV - 1) / BKV;
-    const int wtiles = qw0 < p.T ? min(qw0 + 31, p.T - 1) / BKV + 1 : 0;
 
     u32x4 reg[FC::PREG];
     dq_stage_load<T, HD>(reg, kbase, vbase, stride, 0, p.T, p.hd);
@@ -510,27 +519,40 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
         const char *Ks = smem + (kt & 1) * FC::STAGE;
         const char *Vs = Ks + FC::KB;
         const char *Kt = Ks;
-        if (kt < wtiles) {
-            const int kv0 = kt * BKV;
+        const int kb0 = kt * BKV + half * 32;   // this wave's 32 keys
+        if (kb0 <= klast) {
+            f32x16 S, dP;
 #pragma unroll
-            for (int j = 0; j < 2; j++) {
-                f32x16 S, dP;
+            for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
+            mma_rows<T, HD>(S, Ks, half * 32, qf, lane);
+            mma_rows<T, HD>(dP, Vs, half * 32, df, lane);
+            const bool diag = kb0 + 31 > qw0;
 #pragma unroll
-                for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
-                mma_rows<T, HD>(S, Ks, j * 32, qf, lane);
-                mma_rows<T, HD>(dP, Vs, j * 32, df, lane);
-                const bool diag = kv0 + j * 32 + 31 > qw0;
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    float pr = exp2f(fmaf(S[r], p.sl2, -lse2));
-                    if (diag && kv0 + j * 32 + acc_row(r, lane) > qi) pr = 0.f;
-                    S[r] = pr * (dP[r] - Dq);
-                }
-                mma_trans<T, HD, BKV>(dQ, S, Kt, j, lane);
+            for (int r = 0; r < 16; r++) {
+                float pr = exp2f(fmaf(S[r], p.sl2, -lse2));
+                if (diag && kb0 + acc_row(r, lane) > qi) pr = 0.f;
+                S[r] = pr * (dP[r] - Dq);
             }
+            mma_trans<T, HD, BKV>(dQ, S, Kt, half, lane);
         }
         if (more) dq_stage_store<T, HD>(reg, smem + ((kt + 1) & 1) * FC::STAGE);
         __syncthreads();
+    }
+    // sum the two halves of each slice (the stages are free after the last barrier)
+    {
+        float *xq = reinterpret_cast<float *>(smem) + slice * (A::ND * 16 * 64);
+        if (half == 1) {
+#pragma unroll
+            for (int d = 0; d < A::ND; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) xq[(d * 16 + r) * 64 + lane] = dQ[d][r];
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int d = 0; d < A::ND; d++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) dQ[d][r] += xq[(d * 16 + r) * 64 + lane];
     }
     if (p.rope_cs) rope_rotate_acc<A::ND>(dQ, p.rope_cs + (long long)min(qi, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (qi < p.T) {
@@ -543,13 +565,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(AttnP p) {
 // backward: dK, dV (key-owning, summed over the query heads of the group)
 // ---------------------------------------------------------------------------
 template <typename T, int HD> struct DkvCfg {
-    static constexpr int BK = 128;   // keys per workgroup (4 waves x 32)
+    static constexpr int BK = 64;    // keys per workgroup (2 slices of 32, two waves each)
     static constexpr int BQ = 64;    // queries per tile
     static constexpr int QB = BQ * HD * (int)sizeof(T);
     // LDS stage: Q natural, dO natural, then lse2[BQ], D[BQ]
     static constexpr int STAGE = 2 * QB + 2 * BQ * 4;
     static constexpr int PQ = Nat<T, HD, BQ, 128>::P;
     static constexpr int PREG = PQ;
+    // end of the kernel: the half-1 waves' dK and dV partials, in the same LDS
+    static constexpr int MERGE = 2 * 2 * AT<T, HD>::ND * 16 * 64 * 4;
+    static constexpr int LDS = 2 * STAGE > MERGE ? 2 * STAGE : MERGE;
 };
 
 template <typename T, int HD>
@@ -600,7 +625,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
     const int b = bk / p.NKV, kh = bk % p.NKV;
     const int grp = p.NH / p.NKV;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6, g = lane >> 5, l32 = lane & 31;
-    const int k0 = kb * BK, kw0 = k0 + wave * 32, ki = kw0 + l32;
+    // two 32-key slices; each 64-query tile's two 32-query halves go to two
+    // waves (wave = slice + 2 * half), whose dK and dV partials are summed at the end
+    const int slice = wave & 1, half = wave >> 1;
+    const int k0 = kb * BK, kw0 = k0 + slice * 32, ki = kw0 + l32;
     (void)nkb;
 
     const long long stride = p.QKV;
@@ -658,9 +686,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
         const float *lse2 = reinterpret_cast<const float *>(st + 2 * FC::QB);
         const float *Dt = lse2 + BQ;
         const int q0 = (qt0 + it % nqt) * BQ;
-        if (q0 + BQ - 1 >= kw0 && kw0 < p.T) {
-#pragma unroll
-            for (int j = 0; j < BQ / 32; j++) {
+        const int j = half;   // this wave's 32 queries of the tile
+        if (q0 + j * 32 + 31 >= kw0 && kw0 < p.T) {
+            {
                 f32x16 S, dP;
 #pragma unroll
                 for (int r = 0; r < 16; r++) S[r] = dP[r] = 0.f;
@@ -689,6 +717,29 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
         }
         if (more) dkv_stage_store<T, HD>(reg, aux, smem + ((it + 1) & 1) * FC::STAGE, (qt0 + (it + 1) % nqt) * BQ, p.T);
         __syncthreads();
+    }
+    // sum the two halves of each slice (the stages are free after the last barrier)
+    {
+        float *xk = reinterpret_cast<float *>(smem) + slice * (2 * A::ND * 16 * 64);
+        float *xv = xk + A::ND * 16 * 64;
+        if (half == 1) {
+#pragma unroll
+            for (int d = 0; d < A::ND; d++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                    xk[(d * 16 + r) * 64 + lane] = dK[d][r];
+                    xv[(d * 16 + r) * 64 + lane] = dV[d][r];
+                }
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int d = 0; d < A::ND; d++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+                dK[d][r] += xk[(d * 16 + r) * 64 + lane];
+                dV[d][r] += xv[(d * 16 + r) * 64 + lane];
+            }
     }
     if (p.rope_cs) rope_rotate_acc<A::ND>(dK, p.rope_cs + (long long)min(ki, p.T - 1) * (p.hd / 2), p.hd, -1.f, lane);
     if (ki < p.T) {
@@ -725,9 +776,9 @@ template <typename T, int HD> static hipError_t fwd_t(const AttnP &p, hipStream_
 template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, hipStream_t s) {
     using QC = DqCfg<T, HD>;
     using KC = DkvCfg<T, HD>;
-    hipError_t e = set_lds(attn_bwd_dq_kernel<T, HD>, 2 * QC::STAGE);
+    hipError_t e = set_lds(attn_bwd_dq_kernel<T, HD>, QC::LDS);
     if (e != hipSuccess) return e;
-    e = set_lds(attn_bwd_dkv_kernel<T, HD>, 2 * KC::STAGE);
+    e = set_lds(attn_bwd_dkv_kernel<T, HD>, KC::LDS);
     if (e != hipSuccess) return e;
     long long rows = (long long)p.B * p.T;
     DTB_LAUNCH((attn_bwd_dot_kernel<T>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s, p, D);
@@ -736,11 +787,11 @@ template <typename T, int HD> static hipError_t bwd_t(const AttnP &p, float *D, 
     AttnP q = p;
     q.D = D;
     int nqb = (p.T + QC::BQ - 1) / QC::BQ;
-    DTB_LAUNCH((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), 2 * QC::STAGE, s, q);
+    DTB_LAUNCH((attn_bwd_dq_kernel<T, HD>), dim3(nqb * p.B * p.NH), dim3(256), QC::LDS, s, q);
     e = last_error();
     if (e != hipSuccess) return e;
     int nkb = (p.T + KC::BK - 1) / KC::BK;
-    DTB_LAUNCH((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), 2 * KC::STAGE, s, q);
+    DTB_LAUNCH((attn_bwd_dkv_kernel<T, HD>), dim3(nkb * p.B * p.NKV), dim3(256), KC::LDS, s, q);
     return last_error();
 }
 
