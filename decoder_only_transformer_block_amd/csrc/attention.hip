@@ -612,7 +612,7 @@ __device__ __forceinline__ void dkv_stage_store(const u32x4 *reg, float aux, cha
 }
 
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
+__global__ __launch_bounds__(256, HD == 64 ? 2 : 1) void attn_bwd_dkv_kernel(AttnP p) {
     using A = AT<T, HD>;
     using FC = DkvCfg<T, HD>;
     constexpr int BK = FC::BK, BQ = FC::BQ;
@@ -696,20 +696,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_kernel(AttnP p) {
                 mma_rows<T, HD>(dP, dOs, j * 32, vf, lane);
                 const bool diag = q0 + j * 32 < kw0 + 31;
                 // the 16 query rows of this lane: 4 groups of 4 consecutive rows
-                f32x4 lq[4], dq4[4];
 #pragma unroll
                 for (int r4 = 0; r4 < 4; r4++) {
-                    const int ql = j * 32 + 8 * r4 + 4 * g;
-                    lq[r4] = *reinterpret_cast<const f32x4 *>(lse2 + ql);
-                    dq4[r4] = *reinterpret_cast<const f32x4 *>(Dt + ql);
-                }
+                    const int qg = j * 32 + 8 * r4 + 4 * g;
+                    const f32x4 lq = *reinterpret_cast<const f32x4 *>(lse2 + qg);
+                    const f32x4 dq4 = *reinterpret_cast<const f32x4 *>(Dt + qg);
 #pragma unroll
-                for (int r = 0; r < 16; r++) {
-                    const int ql = j * 32 + acc_row(r, lane);
-                    float pr = exp2f(fmaf(S[r], p.sl2, -lq[r >> 2][r & 3]));
-                    if (diag && q0 + ql < ki) pr = 0.f;
-                    S[r] = pr;
-                    dP[r] = pr * (dP[r] - dq4[r >> 2][r & 3]);
+                    for (int e = 0; e < 4; e++) {
+                        const int r = 4 * r4 + e;
+                        float pr = exp2f(fmaf(S[r], p.sl2, -lq[e]));
+                        if (diag && q0 + qg + e < ki) pr = 0.f;
+                        S[r] = pr;
+                        dP[r] = pr * (dP[r] - dq4[e]);
+                    }
                 }
                 mma_trans<T, HD, BQ>(dV, S, dOt, j, lane);
                 mma_trans<T, HD, BQ>(dK, dP, Qt, j, lane);
