@@ -193,28 +193,35 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
     }
 }
 
-// dst[i] += sum_p part[p][i] for i < n (part row stride ld).  A workgroup
-// covers 32 columns; its 8 groups of 32 threads sum the parts p = pg, pg+8, ...
-// (independent loads, issued back to back), then combine in a fixed order.
-// dst[i] += sum over p of part[p][i] for the n columns of part; with dst1,
-// columns n .. 2n-1 of part go to dst1 (the gamma and beta partials of a
-// LayerNorm, side by side in part, in one launch).  Fixed order: eight
-// strided part groups, then a fixed tree.
-__global__ __launch_bounds__(256) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst,
-                                                           float *dst1) {
-    __shared__ float red[8][32];
+// dst[i] += sum over p of part[p][i] for the n columns of part (row stride
+// ld); with dst1, columns n .. 2n-1 of part go to dst1 (the gamma and beta
+// partials of a LayerNorm, side by side in part, in one launch).  A workgroup
+// covers 32 columns with 32 groups of 32 threads: group pg sums the parts
+// pg, pg + 32, ... (a few independent loads, issued back to back: the partials
+// are few hundred rows, so the latency of one batch is the kernel's time),
+// then the 32 group sums meet in a fixed tree.  Deterministic.
+__global__ __launch_bounds__(1024) void reduce_parts_kernel(const float *part, int np, long ld, int n, float *dst,
+                                                            float *dst1) {
+    __shared__ float red[32][33];
     const int c = threadIdx.x & 31, pg = threadIdx.x >> 5;
     const int i = blockIdx.x * 32 + c;
     const int ncols = dst1 ? 2 * n : n;
     float s = 0.f;
     if (i < ncols) {
 #pragma unroll 8
-        for (int p = pg; p < np; p += 8) s += part[(long)p * ld + i];
+        for (int p = pg; p < np; p += 32) s += part[(long)p * ld + i];
     }
     red[pg][c] = s;
     __syncthreads();
+    // pairwise tree over the 32 groups: after the step of width w, group g < w
+    // holds the sum of groups g, g + w, g + 2w, ... (a fixed order)
+#pragma unroll
+    for (int w = 16; w >= 1; w >>= 1) {
+        if (pg < w) red[pg][c] += red[pg + w][c];
+        __syncthreads();
+    }
     if (pg == 0 && i < ncols) {
-        const float t = ((red[0][c] + red[1][c]) + (red[2][c] + red[3][c])) + ((red[4][c] + red[5][c]) + (red[6][c] + red[7][c]));
+        const float t = red[0][c];
         if (i < n) dst[i] += t;
         else dst1[i - n] += t;
     }
@@ -305,7 +312,7 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
     if (mode != DTB_NORM_RMS_NOGAMMA) {
         // LayerNorm: the gamma (columns 0 .. C-1) and beta (C .. 2C-1) partials in one launch
         const bool ln = mode == DTB_NORM_LAYER;
-        DTB_LAUNCH(reduce_parts_kernel, dim3(((ln ? 2 : 1) * C + 31) / 32), dim3(256), 0, s, part, npart, 2L * C, C,
+        DTB_LAUNCH(reduce_parts_kernel, dim3(((ln ? 2 : 1) * C + 31) / 32), dim3(1024), 0, s, part, npart, 2L * C, C,
                    dg, ln ? db : (float *)nullptr);
         e = last_error();
         if (e != hipSuccess) return set_launch_error(e, "norm_backward reduce");
@@ -565,7 +572,7 @@ int bias_grad(int dtype, const void *dy, long R, int N, float *db, float *part, 
         DTB_LAUNCH(colsum_kernel<bf16>, grid, dim3(256), 0, s, (const bf16 *)dy, R, N, rows_per, part);
     else
         DTB_LAUNCH(colsum_kernel<float>, grid, dim3(256), 0, s, (const float *)dy, R, N, rows_per, part);
-    DTB_LAUNCH(reduce_parts_kernel, dim3((N + 31) / 32), dim3(256), 0, s, part, np, (long)N, N, db,
+    DTB_LAUNCH(reduce_parts_kernel, dim3((N + 31) / 32), dim3(1024), 0, s, part, np, (long)N, N, db,
                (float *)nullptr);
     DTB_LAUNCH_CHECK("bias_grad");
     if (g_timing_on) timing_end(s, K_ELEM, 0, (double)R * N * (dtype == DTB_BF16 ? 2 : 4));
