@@ -120,6 +120,9 @@ def parse():
     ap.add_argument("--attn-long-tokens", type=int, default=4096,
                     help="oracle_table: sequence length of the long-context attention sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-layout", choices=["position", "head"], default="position",
+                    help="decode workload: position-major caches [B][Tmax][NKV*hd] (attn_decode) or head-major "
+                         "[B][NKV][Tmax][hd] (attn_decode_strided)")
     ap.add_argument("--no-timing", action="store_true", help="skip the per-kernel HIP events")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB three times (the known-size "
@@ -516,7 +519,8 @@ def bench_decode(args):
     """Decode attention over the Llama-GQA heads: 256 sequences, cache lengths
     uniform in [1, 4096] (capacity 4096), one new query per sequence, bf16.
     The caches stay resident; a step is one attn_decode call (the chunked
-    attention kernel and its merge)."""
+    attention kernel and its merge), or with --decode-layout head one
+    attn_decode_strided call on head-major caches holding the same values."""
     import numpy as np
     import torch
     from decoder_only_transformer_block_amd import binding, configs
@@ -524,8 +528,12 @@ def bench_decode(args):
     cfg = configs.DECODE_LLAMA_GQA
     q, kc, vc, lens = configs.decode_inputs(cfg)
     dq, dk, dv = to_device(q, cfg.dtype), to_device(kc, cfg.dtype), to_device(vc, cfg.dtype)
+    if args.decode_layout == "head":   # [B][Tmax][NKV][hd] -> [B][NKV][Tmax][hd]
+        shape = (cfg.B, cfg.Tmax, cfg.NKV, cfg.hd)
+        dk = dk.view(shape).permute(0, 2, 1, 3).contiguous()
+        dv = dv.view(shape).permute(0, 2, 1, 3).contiguous()
     dl = torch.from_numpy(lens).cuda()
-    dec = DecodeAttention(cfg.B, cfg.NH, cfg.NKV, cfg.hd, cfg.Tmax, cfg.dtype)
+    dec = DecodeAttention(cfg.B, cfg.NH, cfg.NKV, cfg.hd, cfg.Tmax, cfg.dtype, layout=args.decode_layout)
     for _ in range(args.warmup):
         dec(dq, dk, dv, dl)
     torch.cuda.synchronize()
@@ -673,7 +681,8 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic (seeded N(0,1) q / caches, uniform lengths)",
             "config": {"workload": "decode attention, Llama-GQA heads: B=256 sequences, cache lengths uniform "
-                                   "in [1, 4096], NH=32, NKV=8, hd=64", "cached_positions": ntok,
+                                   "in [1, 4096], NH=32, NKV=8, hd=64", "cache_layout": args.decode_layout,
+                       "cached_positions": ntok,
                        "kv_bytes": kv_bytes, "workspace_bytes": ws_bytes},
             "roofline": roof, "breakdown": brk, "cpu_baseline": cpu}), flush=True)
         return

@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.attn_workspace_bytes.argtypes = [i, i, i]
         L.attn_workspace_bytes.restype = z
         L.attn_decode.argtypes = [v, v, v, v, v, v, i, i, i, i, i, i, i, v, v]
+        ll = ctypes.c_longlong
+        L.attn_decode_strided.argtypes = [v, v, v, v, v, v, i, i, i, i, i, ll, ll, ll, i, i, v, v]
         L.attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
         L.attn_decode_workspace_bytes.restype = z
         cp = ctypes.POINTER(BlockCfg)
@@ -185,6 +187,13 @@ def attn_decode_workspace_bytes(B, NH, NKV, hd, Tmax, chunk, dtype) -> int:
 def attn_decode(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, chunk, dtype, workspace, stream=None):
     check(lib().attn_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), B, NH, NKV,
                             hd, Tmax, chunk, DTYPE[dtype], _ptr(workspace), _stream(stream)), "attn_decode")
+
+
+def attn_decode_strided(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, stride_b, stride_t, stride_h,
+                        chunk, dtype, workspace, stream=None):
+    check(lib().attn_decode_strided(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(lens), B, NH,
+                                    NKV, hd, Tmax, stride_b, stride_t, stride_h, chunk, DTYPE[dtype],
+                                    _ptr(workspace), _stream(stream)), "attn_decode_strided")
 
 
 def linear_forward(out, inp, w, bias, res, R, K, N, dtype, stream=None):

@@ -456,18 +456,41 @@ size_t attn_decode_workspace_bytes(int B, int NH, int NKV, int hd, int Tmax, int
     return n ? al(n) : 256;
 }
 
-int attn_decode(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache, const int *lens,
-                int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype, void *workspace, void *stream) {
-    int e = check_decode(B, NH, NKV, hd, Tmax, chunk, dtype);
-    if (e) return e;
+static int decode_run(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache,
+                      const int *lens, int B, int NH, int NKV, int hd, int Tmax, long long sb, long long st,
+                      long long sh, int chunk, int dtype, void *workspace, void *stream) {
     if (B == 0) return DTB_OK;
     if (!ptr_ok(out) || !ptr_ok(lse) || !ptr_ok(q) || !ptr_ok(lens) || !ptr_ok(workspace)) return DTB_EINVAL_PTR;
     if (Tmax > 0 && (!ptr_ok(k_cache) || !ptr_ok(v_cache))) return DTB_EINVAL_PTR;
     const DecodeGeom g = decode_geometry(B, NH, NKV, hd, Tmax, chunk, dtype);
-    hipError_t he = attn_decode_launch(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, g, dtype,
-                                       workspace, (hipStream_t)stream);
+    hipError_t he = attn_decode_launch(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, sb, st, sh, g,
+                                       dtype, workspace, (hipStream_t)stream);
     if (he != hipSuccess) return set_launch_error(he, "attn_decode");
     return DTB_OK;
+}
+
+int attn_decode(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache, const int *lens,
+                int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype, void *workspace, void *stream) {
+    int e = check_decode(B, NH, NKV, hd, Tmax, chunk, dtype);
+    if (e) return e;
+    const long long row = (long long)NKV * hd;
+    return decode_run(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, (long long)Tmax * row, row, hd,
+                      chunk, dtype, workspace, stream);
+}
+
+int attn_decode_strided(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache,
+                        const int *lens, int B, int NH, int NKV, int hd, int Tmax, long long stride_b,
+                        long long stride_t, long long stride_h, int chunk, int dtype, void *workspace,
+                        void *stream) {
+    int e = check_decode(B, NH, NKV, hd, Tmax, chunk, dtype);
+    if (e) return e;
+    const long long es = dtype == DTB_BF16 ? 2 : 4;
+    // every head row lies inside its (b, kv head) base's 2^31-byte window, and
+    // the rows of one sequence and kv head do not overlap
+    if (stride_b < 0 || stride_t < hd || stride_h < 0) return DTB_EINVAL_SHAPE;
+    if (Tmax > 0 && ((long long)(Tmax - 1) * stride_t + hd) * es >= (1LL << 31)) return DTB_EINVAL_SHAPE;
+    return decode_run(out, lse, q, k_cache, v_cache, lens, B, NH, NKV, hd, Tmax, stride_b, stride_t, stride_h,
+                      chunk, dtype, workspace, stream);
 }
 
 static int check_linear(int R, int K, int N, int dtype) {

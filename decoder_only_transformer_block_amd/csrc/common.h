@@ -264,9 +264,10 @@ struct DecodeGeom {
     size_t ws_bytes;
 };
 DecodeGeom decode_geometry(int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype);
+// cache head row (b, t, kv head) at element b*sb + t*st + kh*sh of each cache
 hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *kc, const void *vc, const int *lens,
-                              int B, int NH, int NKV, int hd, int Tmax, const DecodeGeom &g, int dtype,
-                              void *workspace, hipStream_t s);
+                              int B, int NH, int NKV, int hd, int Tmax, long long sb, long long st, long long sh,
+                              const DecodeGeom &g, int dtype, void *workspace, hipStream_t s);
 
 // elementwise / reductions
 int norm_forward(int mode, int dtype, const void *x, const void *g, const void *b, float eps, long R, int C,

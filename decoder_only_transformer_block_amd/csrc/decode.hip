@@ -6,8 +6,10 @@
 //   out[b, h] = sum_{j < len_b} softmax_j(q_{b,h} . k_{b,j,kh} / sqrt(hd)) v_{b,j,kh}
 //   lse[b, h] = natural-log logsumexp_j of the same scores,   kh = h / (NH/NKV)
 //
-// Layout: q and out [B][NH*hd]; k_cache and v_cache [B][Tmax][NKV*hd] (a cache
-// row holds every kv head of one position, as the microgpt cache rows do);
+// Layout: q and out [B][NH*hd]; k_cache and v_cache addressed by element
+// strides (b, t, kv head): position-major [B][Tmax][NKV*hd] (a cache row holds
+// every kv head of one position, as the microgpt cache rows do) or any other
+// arrangement of hd-contiguous head rows, e.g. head-major [B][NKV][Tmax][hd];
 // lens [B] int32 in device memory; lse [B][NH] fp32.
 //
 // Design.  The work is bound by HBM: every cached byte is read once and meets
@@ -41,8 +43,9 @@ struct DecP {
     void *o;            // [B][NH*hd]
     float *lse;         // [B][NH]
     const void *q;      // [B][NH*hd]
-    const void *kc;     // [B][Tmax][NKV*hd]
+    const void *kc;     // head row (b, t, kh) at b*sb + t*st + kh*sh elements
     const void *vc;
+    long long sb, st, sh;
     const int *lens;    // [B]
     float *po;          // [nsplit][B][NH][hd] unnormalised chunk outputs
     float2 *pml;        // [nsplit][B][NH] (running max in log2 units, sum)
@@ -91,7 +94,7 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(DecP p) {
     const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
     const int grp = p.NH / p.NKV, hl = hg * 32 + l32, h = kh * grp + hl;
     const bool hv = hl < grp;
-    const long long stride = (long long)p.NKV * p.hd;
+    const long long stride = p.st;
 
     // query fragments: chunks 2c+g of head h (zero for lanes past the group)
     u32x4 qf[L::NC];
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(DecP p) {
         }
     }
 
-    const long long cbase = ((long long)b * p.Tmax * p.NKV + kh) * p.hd;
+    const long long cbase = (long long)b * p.sb + (long long)kh * p.sh;
     const Buf bk(reinterpret_cast<const bf16 *>(p.kc) + cbase);
     const Buf bv(reinterpret_cast<const bf16 *>(p.vc) + cbase);
     // K tiles are read as rows, V tiles transposed: each has its own swizzle.
@@ -260,7 +263,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecP p) {
     const int lane = threadIdx.x, slot = lane / LPK, dl = (lane % LPK) * 4;
     const int grp = p.NH / p.NKV;
     const bool dv = dl < p.hd;
-    const long long stride = (long long)p.NKV * p.hd;
+    const long long stride = p.st;
 
     // the group's queries, pre-scaled so that scores come out in log2 units
     float qv[HG][4];
@@ -274,7 +277,7 @@ __global__ __launch_bounds__(64) void decode_f32_kernel(DecP p) {
             for (int k = 0; k < 4; k++) qv[i][k] = __uint_as_float(v[k]) * p.sl2;
         }
     }
-    const long long cbase = ((long long)b * p.Tmax * p.NKV + kh) * p.hd;
+    const long long cbase = (long long)b * p.sb + (long long)kh * p.sh;
     const Buf bk(reinterpret_cast<const float *>(p.kc) + cbase);
     const Buf bv(reinterpret_cast<const float *>(p.vc) + cbase);
 
@@ -402,12 +405,21 @@ template <int HD> struct DecCfg {
     static constexpr int W = HD >= 128 ? 1 : 8;
     static constexpr int NS = HD >= 128 ? 3 : HD >= 64 ? 2 : 4;
 };
-template <int HD> hipError_t bf16_launch(const DecP &p, long long nwave, hipStream_t s) {
-    constexpr int W = DecCfg<HD>::W, NS = DecCfg<HD>::NS;
+template <int HD, int W, int NS> hipError_t bf16_launch_t(const DecP &p, long long nwave, hipStream_t s) {
     // nwave counts (split, b, kv head, head group) waves; a workgroup takes W kv heads
     const long long nblk = nwave / p.NKV * ((p.NKV + W - 1) / W);
     DTB_LAUNCH((decode_bf16_kernel<HD, NS, W>), dim3((unsigned)nblk), dim3(64 * W), 0, s, p);
     return last_error();
+}
+template <int HD> hipError_t bf16_launch(const DecP &p, long long nwave, hipStream_t s) {
+    // rows of one kv head contiguous (head-major caches): nothing to gain from
+    // grouping a position's heads, so one wave per workgroup (more resident
+    // waves); on the 256-sequence workload at hd 64 two stages measured best
+    // (5.0-5.1 TB/s with the merge, against 4.5-5.1 for 3, 4 or 6 stages or
+    // workgroups of 2 or 4 waves, and 4.6-4.8 for the position-major caches)
+    if (HD == 64 && p.st == p.hd) return bf16_launch_t<HD, 1, 2>(p, nwave, s);
+    if (HD < 64 && p.st == p.hd) return bf16_launch_t<HD, 1, 4>(p, nwave, s);
+    return bf16_launch_t<HD, DecCfg<HD>::W, DecCfg<HD>::NS>(p, nwave, s);
 }
 template <int HD> hipError_t f32_launch(const DecP &p, int HG, int nblk, hipStream_t s) {
     switch (HG) {
@@ -444,14 +456,17 @@ DecodeGeom decode_geometry(int B, int NH, int NKV, int hd, int Tmax, int chunk, 
 }
 
 hipError_t attn_decode_launch(void *out, float *lse, const void *q, const void *kc, const void *vc, const int *lens,
-                              int B, int NH, int NKV, int hd, int Tmax, const DecodeGeom &g, int dtype,
-                              void *workspace, hipStream_t s) {
+                              int B, int NH, int NKV, int hd, int Tmax, long long sb, long long st, long long sh,
+                              const DecodeGeom &g, int dtype, void *workspace, hipStream_t s) {
     DecP p{};
     p.o = out;
     p.lse = lse;
     p.q = q;
     p.kc = kc;
     p.vc = vc;
+    p.sb = sb;
+    p.st = st;
+    p.sh = sh;
     p.lens = lens;
     p.po = reinterpret_cast<float *>(workspace);
     p.pml = reinterpret_cast<float2 *>(reinterpret_cast<char *>(workspace) + (size_t)g.nsplit * B * NH * hd * 4);

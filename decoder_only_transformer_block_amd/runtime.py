@@ -316,10 +316,15 @@ class Model:
 class DecodeAttention:
     """Buffers of one decode-attention call (one new query per sequence
     against a KV cache of capacity Tmax): the output, the lse and the chunk
-    workspace are allocated once; __call__ enqueues attn_decode."""
+    workspace are allocated once; __call__ enqueues attn_decode.  With
+    layout="head" the caches are head-major [B][NKV][Tmax][hd] and the call
+    goes to attn_decode_strided."""
 
-    def __init__(self, B, NH, NKV, hd, Tmax, dtype, chunk=0, device="cuda"):
+    def __init__(self, B, NH, NKV, hd, Tmax, dtype, chunk=0, device="cuda", layout="position"):
         import torch
+        if layout not in ("position", "head"):
+            raise ValueError(f"unknown cache layout {layout!r}")
+        self.layout = layout
         self.B, self.NH, self.NKV, self.hd, self.Tmax, self.dtype, self.chunk = B, NH, NKV, hd, Tmax, dtype, chunk
         self.out = torch.empty((B, NH * hd), dtype=torch_dtype(dtype), device=device)
         self.lse = torch.empty((B, NH), dtype=torch.float32, device=device)
@@ -329,6 +334,11 @@ class DecodeAttention:
         self.ws = torch.empty(nb, dtype=torch.uint8, device=device)
 
     def __call__(self, q, k_cache, v_cache, lens):
-        binding.attn_decode(self.out, self.lse, q, k_cache, v_cache, lens, self.B, self.NH, self.NKV, self.hd,
-                            self.Tmax, self.chunk, self.dtype, self.ws)
+        if self.layout == "head":
+            T, hd = self.Tmax, self.hd
+            binding.attn_decode_strided(self.out, self.lse, q, k_cache, v_cache, lens, self.B, self.NH, self.NKV,
+                                        hd, T, self.NKV * T * hd, hd, T * hd, self.chunk, self.dtype, self.ws)
+        else:
+            binding.attn_decode(self.out, self.lse, q, k_cache, v_cache, lens, self.B, self.NH, self.NKV, self.hd,
+                                self.Tmax, self.chunk, self.dtype, self.ws)
         return self.out, self.lse

@@ -159,6 +159,24 @@ int attn_decode(void *out, float *lse, const void *q, const void *k_cache, const
                 const int *lens, int B, int NH, int NKV, int hd, int Tmax, int chunk, int dtype,
                 void *workspace, void *stream);
 
+/* attn_decode over caches in another arrangement of head rows (the same
+ * computation, the same chunks and the same results bit for bit as attn_decode
+ * on the same values): the hd contiguous elements of kv head kh at position t
+ * of sequence b start at element
+ *   b * stride_b + t * stride_t + kh * stride_h
+ * of each cache (K and V share the strides).  attn_decode is the case
+ * stride_b = Tmax*NKV*hd, stride_t = NKV*hd, stride_h = hd; the head-major
+ * cache [B][NKV][Tmax][hd] is stride_b = NKV*Tmax*hd, stride_t = hd,
+ * stride_h = Tmax*hd, in which one kv head's positions are contiguous and
+ * stream from HBM in whole pages.  Requires stride_t >= hd, stride_b and
+ * stride_h >= 0, and ((Tmax-1)*stride_t + hd) * sizeof(dtype) below 2^31
+ * (DTB_EINVAL_SHAPE otherwise); the other arguments, the workspace and the
+ * errors are those of attn_decode. */
+int attn_decode_strided(void *out, float *lse, const void *q, const void *k_cache, const void *v_cache,
+                        const int *lens, int B, int NH, int NKV, int hd, int Tmax, long long stride_b,
+                        long long stride_t, long long stride_h, int chunk, int dtype, void *workspace,
+                        void *stream);
+
 /* ---- the block --------------------------------------------------------- */
 typedef struct {
     int B, T, C, NH, NKV, H; /* H = MLP hidden width */

@@ -126,6 +126,28 @@ def test_decode_validation(B):
     assert L.attn_decode(None, None, None, None, None, None, 0, 32, 8, 64, 128, 0, 1, None, None) == 0
 
 
+def test_decode_strided_validation(B):
+    """attn_decode_strided: the shape checks of attn_decode, then its own
+    stride checks (a head row narrower than hd, negative strides, and a
+    sequence's rows reaching past 2^31 bytes are refused), before any pointer
+    is looked at."""
+    L = B.lib()
+    f = L.attn_decode_strided
+    T, hd, NKV = 128, 64, 8
+    hm = (NKV * T * hd, hd, T * hd)    # head-major strides
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, *hm, 16, 1, None, None) == -1   # chunk
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, *hm, 0, 4, None, None) == -3    # dtype
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, NKV * T * hd, hd - 8, T * hd, 0, 1, None,
+             None) == -1
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, -1, hd, T * hd, 0, 1, None, None) == -1
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, 0, hd, -1, 0, 1, None, None) == -1
+    # row stride of 2^24 elements: the last row of a sequence starts past 2^31 bytes
+    assert f(None, None, None, None, None, None, 1, 32, NKV, hd, T, 0, 1 << 24, hd, 0, 1, None, None) == -1
+    bad = ctypes.c_void_p(0x1004)
+    assert f(bad, bad, bad, bad, bad, bad, 1, 32, NKV, hd, T, *hm, 0, 1, bad, None) == -2
+    assert f(None, None, None, None, None, None, 0, 32, NKV, hd, T, *hm, 0, 1, None, None) == 0
+
+
 def test_saved_layout_consistent(B):
     from decoder_only_transformer_block_amd import configs
     for cfg in configs.BLOCK_CONFIGS.values():

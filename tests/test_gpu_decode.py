@@ -169,3 +169,59 @@ def test_decode_workspace_reuse():
         check("out", to_numpy(out)[:cfg.B], ro, TOL["bf16"])
         check("lse", to_numpy(lse)[:cfg.B], rl, TOL["bf16"])
         assert np.all(to_numpy(out)[cfg.B:] == 0) and np.all(np.isneginf(to_numpy(lse)[cfg.B:]))
+
+
+def _head_major(cache, cfg):
+    """[B][Tmax][NKV*hd] -> [B][NKV][Tmax][hd] (the same values)."""
+    B, T = cache.shape[0], cache.shape[1]
+    return np.ascontiguousarray(cache.reshape(B, T, cfg.NKV, cfg.hd).transpose(0, 2, 1, 3))
+
+
+HEAD_MAJOR = [("hd64_gqa4_bf16", 64), ("hd64_gqa4_f32", 64), ("hd128_gqa4_bf16", 64), ("hd16_gqa4_f32", 64),
+              ("kv16_bf16", 64), ("mqa_bf16", 32), ("grp40_f32", 64), ("one_chunk_bf16", 1024)]
+
+
+@pytest.mark.parametrize("name,chunk", HEAD_MAJOR, ids=[n for n, _ in HEAD_MAJOR])
+def test_decode_head_major(name, chunk):
+    """attn_decode_strided on head-major caches [B][NKV][Tmax][hd] holding the
+    same values as the position-major caches of attn_decode: the same results
+    bit for bit (same chunks, same arithmetic, other addresses), and the oracle
+    on the position-major values.  Rows past each length hold NaN in both."""
+    require_gpu()
+    import torch
+    from decoder_only_transformer_block_amd.runtime import DecodeAttention, to_device, to_numpy
+    cfg = next(c for c, _ in CASES if c.name == name)
+    q, kc, vc, lens, out_pm, lse_pm = _run(cfg, chunk=chunk)
+    announce(f"decode head-major {cfg.name} chunk={chunk}")
+    dec = DecodeAttention(cfg.B, cfg.NH, cfg.NKV, cfg.hd, cfg.Tmax, cfg.dtype, chunk=chunk, layout="head")
+    out, lse = dec(to_device(q, cfg.dtype), to_device(_head_major(kc, cfg), cfg.dtype),
+                   to_device(_head_major(vc, cfg), cfg.dtype), torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    out, lse = to_numpy(out), to_numpy(lse)
+    assert np.array_equal(out, out_pm) and np.array_equal(lse, lse_pm)
+    ro, rl = _oracle(q, kc, vc, lens, cfg)
+    check("out", out, ro, TOL[cfg.dtype])
+    check("lse", lse, rl, TOL[cfg.dtype])
+
+
+def test_decode_head_major_full_size_sampled():
+    """The benchmark's workload with head-major caches, in its launch
+    configuration: bit-identical to the position-major call, and the oracle on
+    sampled sequences."""
+    require_gpu()
+    import torch
+    from decoder_only_transformer_block_amd import configs
+    from decoder_only_transformer_block_amd.runtime import DecodeAttention, to_device, to_numpy
+    cfg = configs.DECODE_LLAMA_GQA
+    q, kc, vc, lens, out_pm, lse_pm = _run(cfg, fill=0.0)
+    announce("decode head-major full size")
+    dec = DecodeAttention(cfg.B, cfg.NH, cfg.NKV, cfg.hd, cfg.Tmax, cfg.dtype, layout="head")
+    out, lse = dec(to_device(q, cfg.dtype), to_device(_head_major(kc, cfg), cfg.dtype),
+                   to_device(_head_major(vc, cfg), cfg.dtype), torch.from_numpy(lens).cuda())
+    torch.cuda.synchronize()
+    out, lse = to_numpy(out), to_numpy(lse)
+    assert np.array_equal(out, out_pm) and np.array_equal(lse, lse_pm)
+    pick = sorted(set([int(np.argmin(lens)), int(np.argmax(lens))] + list(range(5, cfg.B, 41))))
+    ro, rl = _oracle(q[pick], kc[pick], vc[pick], lens[pick], cfg.replace(B=len(pick)))
+    check("out", out[pick], ro, TOL["bf16"])
+    check("lse", lse[pick], rl, TOL["bf16"])
