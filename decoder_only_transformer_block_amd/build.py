@@ -56,6 +56,14 @@ def build(jobs: int | None = None) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
+    # a kernel whose host-side stub was dropped (a template that did not
+    # instantiate for the host pass) links but leaves an undefined symbol of
+    # our own namespace, and the library then fails to load: refuse it here
+    r = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    own = [l.split()[-1] for l in r.stdout.splitlines() if "_ZN3dtb" in l]
+    if own:
+        os.remove(tmp)
+        raise RuntimeError("libdtb.so would reference undefined symbols of its own: " + ", ".join(own[:8]))
     os.replace(tmp, LIB)
     return LIB
 

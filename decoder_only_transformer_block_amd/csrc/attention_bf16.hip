@@ -30,18 +30,33 @@
 namespace dtb {
 namespace {
 
-// DMA instruction q (1 KB) of a 64-row tile at row0 of a row-major tensor
-template <int HD, bool COLS>
-__device__ __forceinline__ void dma_tile(char *lds, const bf16 *g, long long stride, int row0, int nrows, int hd,
-                                         int q, int lane) {
+// A wave's DMA instructions qsub .. qsub+N-1 of every 64-row tile of one
+// row-major tensor.  The per-lane byte offsets within a tile do not change
+// from tile to tile, so they are computed once (tile_dma_offsets); the rows
+// past the valid range are zero-filled by the buffer's record count (a tile at
+// row0 gets a record of (nrows - row0) rows), and head dims past hd by an
+// out-of-range offset.  Issuing a tile (tile_dma_issue) then costs scalar work
+// only.
+template <int HD, bool COLS, int N>
+__device__ __forceinline__ void tile_dma_offsets(int (&voff)[N], long long stride, int hd, int qsub, int lane) {
     constexpr int RB = TL<HD>::RB;
-    const int off = q * 1024 + lane * 16;
-    const int r = off / RB, pc = (off % RB) >> 4;
-    const int c = pc ^ (COLS ? swz_cols<HD>(r) : swz_rows<HD>(r));
-    const Buf buf(g + (long long)row0 * stride);
-    const bool ok = row0 + r < nrows && c * 8 < hd;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(buf.r, (lds_vptr)(lds + q * 1024), 16,
-                                             ok ? (int)((r * stride + c * 8) * 2) : (int)0x80000000, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < N; i++) {
+        const int off = (qsub + i) * 1024 + lane * 16;
+        const int r = off / RB, pc = (off % RB) >> 4;
+        const int c = pc ^ (COLS ? swz_cols<HD>(r) : swz_rows<HD>(r));
+        voff[i] = c * 8 < hd ? (int)((r * stride + c * 8) * 2) : (int)0x80000000;
+    }
+}
+template <int N>
+__device__ __forceinline__ void tile_dma_issue(char *lds, const bf16 *g, long long stride, int row0, int nrows,
+                                               const int *voff, int qsub) {
+    const long long rows = nrows > row0 ? nrows - row0 : 0;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16 *>(g + (long long)row0 * stride), (short)0, (int)(rows * stride * 2), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(lds + (qsub + i) * 1024), 16, voff[i], 0, 0, 0);
 }
 
 // 64 fp32 values (4 bytes per lane) of a row of a [rows][T] array into LDS
@@ -119,12 +134,11 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
     const bool isK = wave < 2;
     const bf16 *src = isK ? kbase : vbase;
     const int qsub = (wave & 1) * DPW;
+    int voff[DPW];   // K rows and V columns use different swizzles
+    if (isK) tile_dma_offsets<HD, false>(voff, stride, p.hd, qsub, lane);
+    else tile_dma_offsets<HD, true>(voff, stride, p.hd, qsub, lane);
     auto issue = [&](char *st, int kt) {
-#pragma unroll
-        for (int i = 0; i < DPW; i++) {
-            if (isK) dma_tile<HD, false>(st, src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
-            else dma_tile<HD, true>(st + L::TILE, src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
-        }
+        tile_dma_issue<DPW>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, voff, qsub);
     };
 
     // query fragments (chunks 2c+g of row qi), then the first NS-1 tiles
@@ -296,10 +310,10 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
     const bool isK = wave < 2;
     const bf16 *src = isK ? kbase : vbase;
     const int qsub = (wave & 1) * DPW;
+    int voff[DPW];
+    tile_dma_offsets<HD, true>(voff, stride, p.hd, qsub, lane);
     auto issue = [&](char *st, int kt) {
-#pragma unroll
-        for (int i = 0; i < DPW; i++)
-            dma_tile<HD, true>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, p.hd, qsub + i, lane);
+        tile_dma_issue<DPW>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, voff, qsub);
     };
 
     u32x4 qf[L::NC], df[L::NC];
@@ -466,15 +480,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ?
 
     const bool isQ = wave < 2;
     const int qsub = (wave & 1) * (DPW - 1);
+    const long long st_ = isQ ? stride : (long long)p.C;
+    int voff[DPW - 1];
+    tile_dma_offsets<HD, true>(voff, st_, p.hd, qsub, lane);
     auto issue = [&](char *st, int it) {
         const bool live = it < niter;
         const int hh = live ? it / nqt : 0, q0 = (qt0 + (live ? it % nqt : 0)) * BQ;
         const int h = kh * grp + hh;
         const bf16 *src = isQ ? base + h * p.hd : dbase + h * p.hd;
-        const long long st_ = isQ ? stride : (long long)p.C;
-#pragma unroll
-        for (int i = 0; i < DPW - 1; i++)
-            dma_tile<HD, true>(st + (isQ ? 0 : L::TILE), src, st_, q0, live ? p.T : 0, p.hd, qsub + i, lane);
+        tile_dma_issue<DPW - 1>(st + (isQ ? 0 : L::TILE), src, st_, q0, live ? p.T : 0, voff, qsub);
         const float *vec = (wave == 0 ? p.lsn : p.D) + ((long long)b * p.NH + h) * p.T;
         dma_vec64(st + AUX + wave * 256, vec, q0, p.T, live && wave < 2, lane);
     };
