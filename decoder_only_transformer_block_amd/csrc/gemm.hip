@@ -782,6 +782,46 @@ __device__ __forceinline__ void dma_slab64(char *unit, const bf16 *base, long lo
     }
 }
 
+// The same DMA with the per-lane offsets computed once per tile.  When K is a
+// multiple of 64 no slab is cut short in k, so a lane's offset from its slab
+// base depends only on its row (validity included) and never changes from
+// slab to slab; the k limit is left to the buffer's record count: slabs past
+// kend get a record of 0 bytes (every load reads zeros), and for m/n-major
+// operands, whose rows are k, a record of the (kend - k0) rows still in range.
+// Issuing a slab is then scalar work (base, record, LDS address) only.
+template <bool KMAJOR>
+__device__ __forceinline__ void slab64_offsets(int *voff, long long ld, int row0, int nrows, int wave, int lane) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const int blk = wave * 8 + q;
+        int off;
+        bool ok;
+        if constexpr (KMAJOR) {
+            const int r = blk * 8 + (lane >> 3), c = (lane & 7) ^ k64_swz(r);
+            ok = row0 + r < nrows;
+            off = (r * (int)ld + c * 8) * 2;
+        } else {
+            const int kr = blk * 2 + (lane >> 5), c = (lane & 31) ^ mmaj_swz(kr);
+            ok = row0 + c * 8 < nrows;
+            off = (kr * (int)ld + c * 8) * 2;
+        }
+        voff[q] = ok ? off : (int)0x80000000;
+    }
+}
+template <bool KMAJOR, int N>
+__device__ __forceinline__ void dma_slab64_pre(char *unit, const bf16 *base, long long ld, int row0, int k0, int kend,
+                                               const int *voff, int q0, int wave) {
+    const bf16 *g = KMAJOR ? base + (long long)row0 * ld + k0 : base + (long long)k0 * ld + row0;
+    long long nb = 0;
+    if (k0 < kend) nb = KMAJOR ? 0x7fffffffLL : (long long)(kend - k0) * ld * 2;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16 *>(g), (short)0, (int)(nb < 0x7fffffffLL ? nb : 0x7fffffffLL), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < N; i++)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(unit + (wave * 8 + q0 + i) * 1024), 16, voff[q0 + i], 0,
+                                                 0, 0);
+}
+
 // MFMA fragment of row r, k16 step s (0..3) of a 64-k unit
 template <bool KMAJOR>
 __device__ __forceinline__ bf16x8 k64_frag(const char *unit, int r, int s, int lane) {
@@ -792,7 +832,8 @@ __device__ __forceinline__ bf16x8 k64_frag(const char *unit, int r, int s, int l
     }
 }
 
-template <bool AK, bool BKM, int MODE>
+// PRE: K is a multiple of 64 and the DMA offsets are computed once per tile
+template <bool AK, bool BKM, int MODE, bool PRE>
 __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
     constexpr int NW = 8, BM = 256, BN = 256, BK = 64;
     constexpr int WGN = 2, TM = 64, FI = 2, FJ = 4;
@@ -850,6 +891,23 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  \
         }                                                                       \
     }
+    // this DMA wave's per-lane slab offsets (PRE: once per tile)
+    int voffA[PRE ? 8 : 1], voffB[PRE ? 8 : 1];
+    if constexpr (PRE) {
+        slab64_offsets<AK>(voffA, p.lda, m0, p.M, wave, lane);
+        slab64_offsets<BKM>(voffB, p.ldb, nb0, p.N, wave, lane);
+    }
+    // half h of this wave's NV-instruction shares of the B (A) slab at k
+#define DMA_B(unit, k, h)                                                                                        \
+    {                                                                                                            \
+        if constexpr (PRE) dma_slab64_pre<BKM, NV>(unit, gB, p.ldb, nb0, k, kend, voffB, (h) * NV, wave);        \
+        else dma_slab64<BKM, NV>(unit, gB, p.ldb, nb0, p.N, k, kend, 2 * wave + (h), lane);                      \
+    }
+#define DMA_A(unit, k, h)                                                                                        \
+    {                                                                                                            \
+        if constexpr (PRE) dma_slab64_pre<AK, NV>(unit, gA, p.lda, m0, k, kend, voffA, (h) * NV, wave);          \
+        else dma_slab64<AK, NV>(unit, gA, p.lda, m0, p.M, k, kend, 2 * wave + (h), lane);                        \
+    }
     // one 64-k step: J = j mod 5 picks the units at compile time
 #define K64_STEP(J, D)                                                          \
     {                                                                           \
@@ -860,22 +918,22 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
         __builtin_amdgcn_sched_barrier(0);                                      \
         const int kb1 = kbeg + (j + 1) * BK, ka2 = kbeg + (j + 2) * BK;          \
         bf16x8 ga[FI], gb[FJ];                                                  \
-        if (D) dma_slab64<BKM, NV>(k64_unit<NB>(), gB, p.ldb, nb0, p.N, kb1, kend, 2 * wave, lane); \
+        if (D) DMA_B(k64_unit<NB>(), kb1, 0)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 0, ga, gb);                       \
         mma(fa, fb);                                                            \
         K64_PATTERN((D) ? NV : 0)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        if (D) dma_slab64<BKM, NV>(k64_unit<NB>(), gB, p.ldb, nb0, p.N, kb1, kend, 2 * wave + 1, lane); \
+        if (D) DMA_B(k64_unit<NB>(), kb1, 1)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 1, fa, fb);                       \
         mma(ga, gb);                                                            \
         K64_PATTERN((D) ? NV : 0)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        if (D) dma_slab64<AK, NV>(k64_unit<NA>(), gA, p.lda, m0, p.M, ka2, kend, 2 * wave, lane); \
+        if (D) DMA_A(k64_unit<NA>(), ka2, 0)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 2, ga, gb);                       \
         mma(fa, fb);                                                            \
         K64_PATTERN((D) ? NV : 0)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
-        if (D) dma_slab64<AK, NV>(k64_unit<NA>(), gA, p.lda, m0, p.M, ka2, kend, 2 * wave + 1, lane); \
+        if (D) DMA_A(k64_unit<NA>(), ka2, 1)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 3, fa, fb);                       \
         mma(ga, gb);                                                            \
         K64_PATTERN((D) ? NV : 0)                                               \
@@ -886,9 +944,15 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
     // go out in step 0).  The k16 fragments multiplied first in step 0
     // belong to no slab and are zero.
     if (dmaw) {
-        dma_slab64<AK, BPD>(k64_unit<0>(), gA, p.lda, m0, p.M, kbeg, kend, wave, lane);
-        dma_slab64<BKM, BPD>(k64_unit<1>(), gB, p.ldb, nb0, p.N, kbeg, kend, wave, lane);
-        dma_slab64<AK, BPD>(k64_unit<2>(), gA, p.lda, m0, p.M, kbeg + BK, kend, wave, lane);
+        if constexpr (PRE) {
+            dma_slab64_pre<AK, BPD>(k64_unit<0>(), gA, p.lda, m0, kbeg, kend, voffA, 0, wave);
+            dma_slab64_pre<BKM, BPD>(k64_unit<1>(), gB, p.ldb, nb0, kbeg, kend, voffB, 0, wave);
+            dma_slab64_pre<AK, BPD>(k64_unit<2>(), gA, p.lda, m0, kbeg + BK, kend, voffA, 0, wave);
+        } else {
+            dma_slab64<AK, BPD>(k64_unit<0>(), gA, p.lda, m0, p.M, kbeg, kend, wave, lane);
+            dma_slab64<BKM, BPD>(k64_unit<1>(), gB, p.ldb, nb0, p.N, kbeg, kend, wave, lane);
+            dma_slab64<AK, BPD>(k64_unit<2>(), gA, p.lda, m0, p.M, kbeg + BK, kend, wave, lane);
+        }
     }
     bf16x8 fa[FI], fb[FJ];
 #pragma unroll
@@ -929,6 +993,8 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
         mma(fa, fb);  // last k16 step of the last slab
     }
 #undef K64_STEP
+#undef DMA_A
+#undef DMA_B
 #undef K64_PATTERN
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -1020,8 +1086,13 @@ static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
     // 64-k slabs whenever an operand is k-major (its rows then fill whole
     // cache lines); both operands m/n-major (the weight gradients) already
     // stream whole lines on 32-k slabs, and the 32-k ring measured the same
-    if constexpr (AK || BKM) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE>), grid, dim3(512), 0, s, p);
-    else DTB_LAUNCH((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
+    // K a multiple of 64 (one split: kbeg = 0, kend = K): every slab is whole in k
+    if constexpr (AK || BKM) {
+        if (p.K % 64 == 0 && splits == 1) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, true>), grid, dim3(512), 0, s, p);
+        else DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, false>), grid, dim3(512), 0, s, p);
+    } else {
+        DTB_LAUNCH((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
+    }
     return last_error();
 }
 
