@@ -63,6 +63,25 @@ __device__ __forceinline__ bool decode_range(const DecP &p, int b, int split, in
     return kv0 < kv1;
 }
 
+// one 32-position K tile and V tile at row r0 into LDS (st, st + KT): the
+// lanes' offsets within a tile are given, and the rows at or past kv1 are
+// zero-filled by the record count of the tile's buffers
+template <int NDQ, int KT>
+__device__ __forceinline__ void decode_tile_dma(char *st, const bf16 *kc, const bf16 *vc, long long stride, int r0,
+                                                int kv1, const int *okof, const int *ovof) {
+    const long long nb = r0 < kv1 ? (long long)(kv1 - r0) * stride * 2 : 0;
+    const int nrec = (int)(nb < 0x7fffffffLL ? nb : 0x7fffffffLL);
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16 *>(kc + (long long)r0 * stride), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16 *>(vc + (long long)r0 * stride), (short)0, nrec, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < NDQ; i++) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_vptr)(st + i * 1024), 16, okof[i], 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_vptr)(st + KT + i * 1024), 16, ovof[i], 0, 0, 0);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // bf16: one wave = (chunk, b, kv head, up to 32 query heads); a workgroup holds
 // the waves of W consecutive kv heads of the same positions, so that the
@@ -108,26 +127,23 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(DecP p) {
     }
 
     const long long cbase = (long long)b * p.sb + (long long)kh * p.sh;
-    const Buf bk(reinterpret_cast<const bf16 *>(p.kc) + cbase);
-    const Buf bv(reinterpret_cast<const bf16 *>(p.vc) + cbase);
+    const bf16 *kc = reinterpret_cast<const bf16 *>(p.kc) + cbase;
+    const bf16 *vc = reinterpret_cast<const bf16 *>(p.vc) + cbase;
     // K tiles are read as rows, V tiles transposed: each has its own swizzle.
-    // Positions at or past kv1 (and head dims past hd) are filled with zeros.
-    auto issue = [&](char *st, int t) {
-        const int r0 = kv0 + t * 32;
+    // A lane's byte offsets within a tile are the same for every tile (head
+    // dims past hd: out of range); positions at or past kv1 are zero-filled by
+    // the record count of the tile's buffer, (kv1 - r0) rows of the row stride.
+    int okof[NDQ], ovof[NDQ];
 #pragma unroll
-        for (int i = 0; i < NDQ; i++) {
-            const int off = i * 1024 + lane * 16;
-            const int r = off / RB, pc = (off % RB) >> 4;
-            const int ck = pc ^ swz_rows<HD>(r), cv = pc ^ swz_cols<HD>(r);
-            const bool okr = r0 + r < kv1;
-            const long long rowoff = (long long)(r0 + r) * stride;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                bk.r, (lds_vptr)(st + i * 1024), 16,
-                okr && ck * 8 < p.hd ? (int)((rowoff + ck * 8) * 2) : (int)0x80000000, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                bv.r, (lds_vptr)(st + KT + i * 1024), 16,
-                okr && cv * 8 < p.hd ? (int)((rowoff + cv * 8) * 2) : (int)0x80000000, 0, 0, 0);
-        }
+    for (int i = 0; i < NDQ; i++) {
+        const int off = i * 1024 + lane * 16;
+        const int r = off / RB, pc = (off % RB) >> 4;
+        const int ck = pc ^ swz_rows<HD>(r), cv = pc ^ swz_cols<HD>(r);
+        okof[i] = ck * 8 < p.hd ? (int)((r * stride + ck * 8) * 2) : (int)0x80000000;
+        ovof[i] = cv * 8 < p.hd ? (int)((r * stride + cv * 8) * 2) : (int)0x80000000;
+    }
+    auto issue = [&](char *st, int t) {
+        decode_tile_dma<NDQ, KT>(st, kc, vc, stride, kv0 + t * 32, kv1, okof, ovof);
     };
 
     int kofs[L::NC];
