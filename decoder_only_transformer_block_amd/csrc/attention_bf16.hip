@@ -37,14 +37,15 @@ namespace {
 // row0 gets a record of (nrows - row0) rows), and head dims past hd by an
 // out-of-range offset.  Issuing a tile (tile_dma_issue) then costs scalar work
 // only.
-template <int HD, bool COLS, int N>
+enum { SWZ_ROWS, SWZ_COLS, SWZ_DUAL };  // which chunk swizzle a tile is stored with
+template <int HD, int MODE, int N>
 __device__ __forceinline__ void tile_dma_offsets(int (&voff)[N], long long stride, int hd, int qsub, int lane) {
     constexpr int RB = TL<HD>::RB;
 #pragma unroll
     for (int i = 0; i < N; i++) {
         const int off = (qsub + i) * 1024 + lane * 16;
         const int r = off / RB, pc = (off % RB) >> 4;
-        const int c = pc ^ (COLS ? swz_cols<HD>(r) : swz_rows<HD>(r));
+        const int c = pc ^ (MODE == SWZ_COLS ? swz_cols<HD>(r) : MODE == SWZ_DUAL ? swz_dual<HD>(r) : swz_rows<HD>(r));
         voff[i] = c * 8 < hd ? (int)((r * stride + c * 8) * 2) : (int)0x80000000;
     }
 }
@@ -135,8 +136,8 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
     const bf16 *src = isK ? kbase : vbase;
     const int qsub = (wave & 1) * DPW;
     int voff[DPW];   // K rows and V columns use different swizzles
-    if (isK) tile_dma_offsets<HD, false>(voff, stride, p.hd, qsub, lane);
-    else tile_dma_offsets<HD, true>(voff, stride, p.hd, qsub, lane);
+    if (isK) tile_dma_offsets<HD, SWZ_ROWS>(voff, stride, p.hd, qsub, lane);
+    else tile_dma_offsets<HD, SWZ_COLS>(voff, stride, p.hd, qsub, lane);
     auto issue = [&](char *st, int kt) {
         tile_dma_issue<DPW>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, voff, qsub);
     };
@@ -311,7 +312,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
     const bf16 *src = isK ? kbase : vbase;
     const int qsub = (wave & 1) * DPW;
     int voff[DPW];
-    tile_dma_offsets<HD, true>(voff, stride, p.hd, qsub, lane);
+    tile_dma_offsets<HD, SWZ_DUAL>(voff, stride, p.hd, qsub, lane);
     auto issue = [&](char *st, int kt) {
         tile_dma_issue<DPW>(st + (isK ? 0 : L::TILE), src, stride, kt * BKV, kv_end, voff, qsub);
     };
@@ -365,6 +366,9 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
             tofs[db] = xr * RB + ((ch ^ swz_dual<HD>(xr)) << 4) + 8 * (i16 & 1);
         }
     }
+    int tofs8[L::ND];  // the transposing reads' second 8 rows
+#pragma unroll
+    for (int db = 0; db < L::ND; db++) tofs8[db] = tofs[db] ^ dual_x8<HD>();
 
     f32x16 dQ[L::ND];
 #pragma unroll
@@ -409,7 +413,8 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                 const bf16x8 xb = __builtin_bit_cast(bf16x8, xw);
 #pragma unroll
                 for (int db = 0; db < L::ND; db++)
-                    dQ[db] = mfma32(lds_tr8<RB>(Ks + tofs[db] + (32 * j + 16 * hh) * RB), xb, dQ[db]);
+                    dQ[db] = mfma32(lds_tr8x<RB>(Ks + tofs[db] + (32 * j + 16 * hh) * RB,
+                                                 Ks + tofs8[db] + (32 * j + 16 * hh) * RB), xb, dQ[db]);
             }
         }
     };
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ?
     const int qsub = (wave & 1) * (DPW - 1);
     const long long st_ = isQ ? stride : (long long)p.C;
     int voff[DPW - 1];
-    tile_dma_offsets<HD, true>(voff, st_, p.hd, qsub, lane);
+    tile_dma_offsets<HD, SWZ_DUAL>(voff, st_, p.hd, qsub, lane);
     auto issue = [&](char *st, int it) {
         const bool live = it < niter;
         const int hh = live ? it / nqt : 0, q0 = (qt0 + (live ? it % nqt : 0)) * BQ;
@@ -521,6 +526,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ?
             tofs[db] = xr * RB + ((ch ^ swz_dual<HD>(xr)) << 4) + 8 * (i16 & 1);
         }
     }
+    int tofs8[L::ND];  // the transposing reads' second 8 rows
+#pragma unroll
+    for (int db = 0; db < L::ND; db++) tofs8[db] = tofs[db] ^ dual_x8<HD>();
 
     f32x16 dK[L::ND], dV[L::ND];
 #pragma unroll
@@ -580,9 +588,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD >= 128 ?
                 }
 #pragma unroll
                 for (int db = 0; db < L::ND; db++) {
-                    const int o = tofs[db] + (32 * j + 16 * hh) * RB;
-                    dV[db] = mfma32(lds_tr8<RB>(dOs + o), __builtin_bit_cast(bf16x8, xs), dV[db]);
-                    dK[db] = mfma32(lds_tr8<RB>(Qs + o), __builtin_bit_cast(bf16x8, xd), dK[db]);
+                    const int o = tofs[db] + (32 * j + 16 * hh) * RB, o8 = tofs8[db] + (32 * j + 16 * hh) * RB;
+                    dV[db] = mfma32(lds_tr8x<RB>(dOs + o, dOs + o8), __builtin_bit_cast(bf16x8, xs), dV[db]);
+                    dK[db] = mfma32(lds_tr8x<RB>(Qs + o, Qs + o8), __builtin_bit_cast(bf16x8, xd), dK[db]);
                 }
             }
         }
