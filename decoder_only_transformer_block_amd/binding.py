@@ -31,7 +31,7 @@ class BlockCfg(ctypes.Structure):
 
 
 class BlockWeights(ctypes.Structure):
-    _fields_ = [(n, _VP) for n in _WNAMES]
+    _fields_ = [(n, _VP) for n in _WNAMES] + [("rope_cs", _VP)]
 
 
 class BlockGrads(ctypes.Structure):
@@ -86,6 +86,7 @@ def lib() -> ctypes.CDLL:
         L.block_saved_layout.argtypes = [cp, ctypes.POINTER(SavedLayout)]
         L.block_workspace_layout.argtypes = [cp, ctypes.POINTER(WorkspaceLayout)]
         L.block_forward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, v]
+        L.rope_table_build.argtypes = [v, i, i, ctypes.c_float, v]
         L.block_backward.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v, ctypes.POINTER(BlockGrads), v, v]
         L.block_backward_overlap.argtypes = [cp, ctypes.POINTER(BlockWeights), v, v, v, v,
                                              ctypes.POINTER(BlockGrads), v, v, v]
@@ -151,7 +152,9 @@ def make_cfg(c, B=None, T=None) -> BlockCfg:
 
 
 def weights_struct(w: dict) -> BlockWeights:
-    return BlockWeights(**{n: _ptr(w.get(n)) for n in _WNAMES})
+    """The block's weights; the optional key "rope_cs" is a table from
+    rope_table_build (absent: each call computes it)."""
+    return BlockWeights(**{n: _ptr(w.get(n)) for n in _WNAMES + ("rope_cs",)})
 
 
 def grads_struct(g: dict) -> BlockGrads:
@@ -305,6 +308,11 @@ def block_workspace_layout(cfg: BlockCfg) -> WorkspaceLayout:
     L = WorkspaceLayout()
     check(lib().block_workspace_layout(ctypes.byref(cfg), ctypes.byref(L)), "block_workspace_layout")
     return L
+
+
+def rope_table_build(cs, T, hd, base, stream=None):
+    """cs (T * hd fp32, device): the NeoX (cos, sin) table for T positions of head width hd."""
+    check(lib().rope_table_build(_ptr(cs), T, hd, base, _stream(stream)), "rope_table_build")
 
 
 def block_forward(cfg: BlockCfg, weights: dict, x_in, x_out, saved, workspace, stream=None):

@@ -330,6 +330,13 @@ size_t block_saved_bytes(const dtb_block_cfg *cfg) {
     return (size_t)L.total;
 }
 
+int rope_table_build(float *cs, int T, int hd, float base, void *stream) {
+    if (T < 0 || hd < 2 || hd > 256 || hd % 2 || !(base > 0.f)) return DTB_EINVAL_SHAPE;
+    if (T == 0) return DTB_OK;
+    if (!ptr_ok(cs)) return DTB_EINVAL_PTR;
+    return rope_table(cs, T, hd, base, (hipStream_t)stream);
+}
+
 int block_saved_layout(const dtb_block_cfg *cfg, dtb_saved_layout *layout) {
     Dims d;
     int e = check_cfg(cfg, &d);
@@ -768,6 +775,7 @@ static int check_weights(const dtb_block_cfg *c, const dtb_block_weights *w) {
     if (c->qkv_bias && !ptr_ok(w->bqkv)) return DTB_EINVAL_PTR;
     if (c->o_bias && !ptr_ok(w->bo)) return DTB_EINVAL_PTR;
     if (c->mlp_bias && (!ptr_ok(w->b_up) || !ptr_ok(w->b_down))) return DTB_EINVAL_PTR;
+    if (w->rope_cs && !aligned(w->rope_cs)) return DTB_EINVAL_PTR;
     return DTB_OK;
 }
 
@@ -816,8 +824,11 @@ int block_forward(const dtb_block_cfg *c, const dtb_block_weights *w, const void
     g.A = n1; g.lda = C; g.B = w->wqkv; g.ldb = C; g.M = BT; g.N = d.QKV; g.K = C;
     g.out = qkv; g.ldo = d.QKV; g.bias = c->qkv_bias ? w->bqkv : nullptr; g.res = nullptr;
     if (c->rope == DTB_ROPE_NEOX) {
-        float *cs = (float *)(ws + W.cs);
-        TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
+        const float *cs = w->rope_cs;
+        if (!cs) {
+            TRY(rope_table((float *)(ws + W.cs), c->T, d.hd, c->rope_base, s));
+            cs = (const float *)(ws + W.cs);
+        }
         g.rope_cs = cs; g.rope_T = c->T; g.rope_hd = d.hd; g.rope_cols = C + c->NKV * d.hd;
     }
     TRY(gemm(g, nullptr, 0, s));
@@ -988,10 +999,13 @@ static int block_backward_impl(const dtb_block_cfg *c, const dtb_block_weights *
     TRY(gemm(dw, gws, W.gemm_bytes, s2));
     if (c->o_bias) TRY(bias_grad(dt, dx2, BT, C, gr->bo, bpart, W.bparts, s));
     // attention (dq and dk leave the kernels already rotated back by the transposed RoPE)
-    float *cs = nullptr;
+    const float *cs = nullptr;
     if (c->rope == DTB_ROPE_NEOX) {
-        cs = (float *)(ws + W.cs);
-        TRY(rope_table(cs, c->T, d.hd, c->rope_base, s));
+        cs = w->rope_cs;
+        if (!cs) {
+            TRY(rope_table((float *)(ws + W.cs), c->T, d.hd, c->rope_base, s));
+            cs = (const float *)(ws + W.cs);
+        }
     }
     TRY(launch_attn_backward(dqkv, qkv, o, dO, lse, c->B, c->T, C, c->NH, c->NKV, dt, Dbuf, cs, s));
     // qkv projection: dn1 = dqkv Wqkv; dWqkv += dqkv^T n1

@@ -82,6 +82,13 @@ class BlockStack:
             raise binding.DtbError("invalid block configuration")
         self.saved = [torch.empty(nsv, dtype=torch.uint8, device=device) for _ in layer_weights]
         self.workspace = torch.empty(nws, dtype=torch.uint8, device=device)
+        # the NeoX rotation table, built once for every layer and step (the
+        # block calls would otherwise each compute it)
+        self.rope_cs = None
+        if cfg.rope == "neox":
+            hd = cfg.C // cfg.NH
+            self.rope_cs = torch.empty(cfg.T * hd, dtype=torch.float32, device=device)
+            binding.rope_table_build(self.rope_cs, cfg.T, hd, cfg.rope_base)
         self.layout = binding.block_saved_layout(self.c)
         shape = (cfg.B, cfg.T, cfg.C)
         td = torch_dtype(cfg.dtype)
@@ -100,8 +107,7 @@ class BlockStack:
         self.inp = x if x is not None else self.acts[0]
         for i in range(self.L):
             xin = self.inp if i == 0 else self.acts[i]
-            binding.block_forward(self.c, self.weights[i], xin, self.acts[i + 1], self.saved[i], self.workspace,
-                                  stream)
+            binding.block_forward(self.c, self._w(i), xin, self.acts[i + 1], self.saved[i], self.workspace, stream)
         return self.acts[self.L]
 
     def backward(self, dy, stream=None):
@@ -115,12 +121,16 @@ class BlockStack:
             xin = self.inp if i == 0 else self.acts[i]
             dout = dy if i == self.L - 1 else self.dx
             if self.overlap:
-                binding.block_backward_overlap(self.c, self.weights[i], xin, self.saved[i], dout, self.dx,
+                binding.block_backward_overlap(self.c, self._w(i), xin, self.saved[i], dout, self.dx,
                                                self.grads[i], self.workspace, self._side, stream)
             else:
-                binding.block_backward(self.c, self.weights[i], xin, self.saved[i], dout, self.dx, self.grads[i],
+                binding.block_backward(self.c, self._w(i), xin, self.saved[i], dout, self.dx, self.grads[i],
                                        self.workspace, stream)
         return self.dx
+
+    def _w(self, i):
+        """Layer i's weights as the block calls take them (with the shared table)."""
+        return self.weights[i] if self.rope_cs is None else dict(self.weights[i], rope_cs=self.rope_cs)
 
     def close(self):
         """Release the second stream (its pending work still completes)."""

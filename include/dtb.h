@@ -196,10 +196,27 @@ typedef struct {
  *   g2, b2   [C]      norm2 gamma / beta
  *   w_up     SwiGLU: [2H, C], rows 0..H-1 the gate, rows H..2H-1 the up
  *            projection; ReLU / GELU: [H, C].  b_up [2H] or [H]
- *   w_down   [C, H];  b_down [C] */
+ *   w_down   [C, H];  b_down [C]
+ *   rope_cs  optional, DTB_ROPE_NEOX only: the (cos, sin) table that
+ *            rope_table_build writes for this config's T, head width C/NH
+ *            and rope_base (its contents are not checked).
+ *            NULL: block_forward and block_backward compute it in their
+ *            workspace on every call; a table built once serves every layer
+ *            of a stack and every step. */
 typedef struct {
     const void *g1, *b1, *wqkv, *bqkv, *wo, *bo, *g2, *b2, *w_up, *b_up, *w_down, *b_down;
+    const float *rope_cs;
 } dtb_block_weights;
+
+/* rope_table_build: the NeoX rotation table of "nx_f32_qwen2_train_gate.nx
+ * source" build_rope / "nanoeuler — CUDA kernels" rope_kernel:
+ *   cs[2 (t hd/2 + i)] = cos(t theta_i),  cs[2 (t hd/2 + i) + 1] = sin(t theta_i),
+ *   theta_i = base^(-2i/hd),  0 <= t < T, 0 <= i < hd/2,
+ * the angle and its cosine and sine in fp64, rounded to fp32.  cs: T*hd
+ * floats, OVERWRITTEN.  T >= 0; hd even in [2, 256]; base > 0
+ * (DTB_EINVAL_SHAPE otherwise; DTB_EINVAL_PTR for a null or misaligned cs
+ * when T > 0). */
+int rope_table_build(float *cs, int T, int hd, float base, void *stream);
 
 /* Parameter gradients, fp32, same shapes as dtb_block_weights, ACCUMULATED
  * (+=): the caller zeroes them before the first backward of a step (cuBLAS

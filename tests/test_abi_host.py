@@ -170,3 +170,20 @@ def test_debug_level_validation(B):
     assert L.dtb_debug_enable(3) == -4
     assert L.dtb_debug_enable(-1) == -4
     assert L.dtb_debug_enable(0) == 0
+
+
+def test_rope_table_build_validation(B):
+    """rope_table_build rejects bad sizes and pointers before any launch; an
+    empty table needs no buffer.  A misaligned table in the block's weights is
+    refused by block_forward."""
+    L = B.lib()
+    for T, hd, base in [(-1, 64, 1e4), (16, 0, 1e4), (16, 3, 1e4), (16, 258, 1e4), (16, 64, 0.0),
+                        (16, 64, -1.0), (16, 64, float("nan"))]:
+        assert L.rope_table_build(None, T, hd, base, None) == -1, (T, hd, base)
+    assert L.rope_table_build(None, 0, 64, 1e4, None) == 0
+    assert L.rope_table_build(None, 16, 64, 1e4, None) == -2
+    assert L.rope_table_build(ctypes.c_void_p(8), 16, 64, 1e4, None) == -2
+    c = _cfg(B, B=1, T=16)
+    w = B.BlockWeights(**{n: ctypes.c_void_p(256) for n in B._WNAMES}, rope_cs=ctypes.c_void_p(264))
+    p = ctypes.c_void_p(256)
+    assert L.block_forward(ctypes.byref(c), ctypes.byref(w), p, p, p, p, None) == -2

@@ -101,3 +101,46 @@ def test_block_backward_in_place_and_accumulate():
             np.testing.assert_allclose(to_numpy(st.grads[l][k]), 2 * to_numpy(g1[l][k]), rtol=1e-5, atol=1e-7)
     np.testing.assert_array_equal(to_numpy(st.dx), to_numpy(dx1))
     np.testing.assert_array_equal(to_numpy(dy), dy0)
+
+
+@pytest.mark.parametrize("case", ["rope_hd8_f32", "rope_hd128_bf16", "llama_gqa_reduced"])
+def test_block_rope_table_given_or_computed(case):
+    """A RoPE table built once by rope_table_build (the stack's path) and the
+    table each block call computes in its workspace (weights without one)
+    give bit-identical outputs, saved activations, dx and gradients; the built
+    table holds cos / sin of t base^(-2i/hd) to fp32 rounding."""
+    require_gpu()
+    import torch
+    from decoder_only_transformer_block_amd import binding, configs
+    from decoder_only_transformer_block_amd.runtime import BlockStack, to_device, to_numpy
+    cfg = _reduced()[case]
+    ws = [configs.block_weights(cfg, l, perturb=True) for l in range(cfg.L)]
+    announce(f"rope table given / computed ({case})")
+    x = to_device(configs.block_input(cfg), cfg.dtype)
+    dy = to_device(configs.block_dout(cfg), cfg.dtype)
+    st = BlockStack(cfg, ws, overlap=False)
+    assert st.rope_cs is not None
+    hd = cfg.C // cfg.NH
+    t = np.arange(cfg.T, dtype=np.float64)[:, None]
+    ang = t * cfg.rope_base ** (-2.0 * np.arange(hd // 2) / hd)[None, :]
+    cs = to_numpy(st.rope_cs).reshape(cfg.T, hd // 2, 2)
+    np.testing.assert_allclose(cs[..., 0], np.cos(ang), rtol=0, atol=1e-7)
+    np.testing.assert_allclose(cs[..., 1], np.sin(ang), rtol=0, atol=1e-7)
+    runs = []
+    for given in (True, False):
+        st.zero_grads()
+        if not given:
+            st.rope_cs = None
+        y = st.forward(x).clone()
+        dx = st.backward(dy).clone()
+        torch.cuda.synchronize()
+        runs.append((to_numpy(y), to_numpy(dx), [to_numpy(s).copy() for s in st.saved],
+                     [{k: to_numpy(v).copy() for k, v in g.items()} for g in st.grads]))
+    (y1, dx1, s1, g1), (y2, dx2, s2, g2) = runs
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(dx1, dx2)
+    for a, b in zip(s1, s2):
+        np.testing.assert_array_equal(a, b)
+    for l in range(cfg.L):
+        for k in g1[l]:
+            np.testing.assert_array_equal(g1[l][k], g2[l][k])
