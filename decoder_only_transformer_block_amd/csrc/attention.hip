@@ -327,10 +327,10 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
                 for (int r = 0; r < 16; r++)
                     if (kb0 + acc_row(r, lane) > qi) S[r] = -INFINITY;
             }
-            float mt = S[0];
+            float sv[16];
 #pragma unroll
-            for (int r = 1; r < 16; r++) mt = fmaxf(mt, S[r]);
-            mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;   // running max in log2 units
+            for (int r = 0; r < 16; r++) sv[r] = S[r];
+            const float mt = max_xor32(tree_max<16>(sv)) * p.sl2;   // tile max in log2 units
             const float mn = fmaxf(m, mt);
             if (!__all(mn == m)) {
                 const float alpha = exp2f(m - mn);
@@ -378,7 +378,7 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(AttnP p) {
         lsum = lsum * a0 + l1 * a1;
         m = mm;
     }
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const float ltot = sum_xor32(lsum);
     if (qi < p.T) {
         T *orow = reinterpret_cast<T *>(p.o) + ((long long)b * p.T + qi) * p.C + h * p.hd;
         store_rows<T, HD>(orow, O, 1.f / ltot, p.hd, lane);

@@ -203,12 +203,12 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
                 for (int r = 0; r < 16; r++)
                     if (kv0 + j * 32 + acc_row(r, lane) > qi) S[j][r] = -INFINITY;
         }
-        float mt = S[0][0];
+        float sv[32];
 #pragma unroll
         for (int j = 0; j < 2; j++)
 #pragma unroll
-            for (int r = 0; r < 16; r++) mt = fmaxf(mt, S[j][r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;  // tile max in log2 units
+            for (int r = 0; r < 16; r++) sv[16 * j + r] = S[j][r];
+        const float mt = max_xor32(tree_max<32>(sv)) * p.sl2;  // tile max in log2 units
         // the reference max m moves only when a column's scores exceed it by
         // more than 2^8 (then O and the sums are rescaled); otherwise the
         // exponentials below stay under 256 and no rescale is spent
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void dq_bf16_kernel(AttnP p) {
                 dot += __uint_as_float(df[c][e] << 16) * __uint_as_float(of[e] << 16) +
                        __uint_as_float(df[c][e] & 0xffff0000u) * __uint_as_float(of[e] & 0xffff0000u);
         }
-        dot += __shfl_xor(dot, 32, 64);
+        dot = sum_xor32(dot);
         if (qi < p.T) {
             // also kept for the dK/dV kernel, which runs after this one
             nls = -p.lse_in[li] / p.scale;

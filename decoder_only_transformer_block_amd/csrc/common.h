@@ -106,6 +106,37 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// max / sum of the lane's value and that of lane l ^ 32.  v_permlane32_swap
+// exchanges the upper 32 lanes of one register with the lower 32 of another:
+// swapping x with itself leaves the lower half's values in one result and the
+// upper half's in the other, in every lane, so no LDS round trip is needed.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// maximum of N values as a balanced tree of 3-input maxima (dependency depth
+// log3 N instead of a serial chain of N/2)
+template <int N> __device__ __forceinline__ float tree_max(const float *v) {
+    if constexpr (N == 1) {
+        return v[0];
+    } else if constexpr (N == 2) {
+        return fmaxf(v[0], v[1]);
+    } else {
+        constexpr int M = (N + 2) / 3;
+        float w[M];
+#pragma unroll
+        for (int i = 0; i < M; i++) {
+            const int a = 3 * i;
+            w[i] = a + 2 < N ? fmaxf(fmaxf(v[a], v[a + 1]), v[a + 2]) : a + 1 < N ? fmaxf(v[a], v[a + 1]) : v[a];
+        }
+        return tree_max<M>(w);
+    }
+}
+
 // ---------------------------------------------------------------- MFMA ---
 // 32x32 output block: lane l, accumulator r holds row 8*(r/4) + 4*(l/32) + r%4,
 // column l%32.  The A operand lane l supplies row l%32, the B operand lane l

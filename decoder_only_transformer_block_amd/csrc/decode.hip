@@ -181,10 +181,10 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(DecP p) {
             for (int r = 0; r < 16; r++)
                 if (kb0 + acc_row(r, lane) >= kv1) S[r] = -INFINITY;
         }
-        float mt = S[0];
+        float sv[16];
 #pragma unroll
-        for (int r = 1; r < 16; r++) mt = fmaxf(mt, S[r]);
-        mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * p.sl2;
+        for (int r = 0; r < 16; r++) sv[r] = S[r];
+        const float mt = max_xor32(tree_max<16>(sv)) * p.sl2;
         const float mn = fmaxf(m, mt);
         if (!__all(mn == m)) {
             const float alpha = fast_exp2(m - mn);
@@ -225,7 +225,7 @@ __global__ __launch_bounds__(64 * W) void decode_bf16_kernel(DecP p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
 
-    const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+    const float ltot = sum_xor32(lsum);
     if (!hv) return;
     // lane column l32 = head h; accumulator rows = head dims 32 db + 8 (r/4) + 4 g + r%4
     if (kv0 == 0 && kv1 == len) {
