@@ -106,8 +106,12 @@ __device__ __forceinline__ void qowner_coords(int x, int nqb, int B, int NH, int
     bh = g * G + hg;
 }
 
+// Head width 64 runs a two-stage ring (32 KB of LDS, five workgroups' worth
+// per CU) held to 128 VGPRs: four waves per SIMD.  One register spills, kept
+// across the loop only.
 template <int HD, int NS>
-__global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(HD == 64 && NS == 2 ? 4 : 1, 8))) void
+fwd_bf16_kernel(AttnP p) {
     using L = TL<HD>;
     constexpr int BQ = 128, BKV = 64, RB = L::RB;
     constexpr int DPW = L::NDMA / 2;  // DMA instructions per wave per tile (waves 0-1: K, 2-3: V)
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(256) void fwd_bf16_kernel(AttnP p) {
 }
 
 template <int HD> hipError_t fwd_launch(const AttnP &p, hipStream_t s) {
-    constexpr int NS = HD >= 128 ? 2 : 3;
+    constexpr int NS = HD >= 64 ? 2 : 3;
     const int nqb = (p.T + 127) / 128;
     DTB_LAUNCH((fwd_bf16_kernel<HD, NS>), dim3(nqb * p.B * p.NH), dim3(256), 0, s, p);
     return last_error();
