@@ -672,7 +672,8 @@ def main():
                 avg = d["ms"] / d["launches"]
                 per = kv_bytes + q_bytes
                 gb = per / (avg * 1e-3) / 1e9
-                roof = {"kernel": "decode_bf16_kernel<64, 2, 8> (chunked decode attention)", "bound": "hbm",
+                inst = "decode_bf16_kernel<64, 2, 1>" if args.decode_layout == "head" else "decode_bf16_kernel<64, 2, 8>"
+                roof = {"kernel": f"{inst} (chunked decode attention)", "bound": "hbm",
                         "achieved": round(gb, 1), "peak": HBM_PEAK, "unit": "GB/s", "frac": round(gb / HBM_PEAK, 4),
                         "traffic": None, "avg_launch_ms": round(avg, 4), "algorithmic_bytes_per_launch": per}
         print(json.dumps({
