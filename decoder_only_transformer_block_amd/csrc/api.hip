@@ -304,7 +304,7 @@ static void ws_layout(const dtb_block_cfg *c, const Dims &d, WsLayout *W) {
     W->dn1 = take((size_t)d.BT * c->C * d.es);
     W->D = take((size_t)c->B * c->NH * c->T * 4 * 2);  // -D and -lse / scale
     W->nparts = norm_backward_parts(d.BT);
-    W->npart = take((size_t)W->nparts * 2 * c->C * 4);
+    W->npart = take(norm_backward_ws_bytes(d.BT, c->C));
     W->bparts = bias_grad_parts(d.BT);
     int maxn = d.QKV > d.W ? d.QKV : d.W;
     if (c->C > maxn) maxn = c->C;
@@ -608,7 +608,7 @@ int norm_forward(void *out, float *rstd, float *mean, const void *x, const void 
 
 size_t norm_workspace_bytes(int R, int C) {
     if (R < 0 || C <= 0) return 0;
-    return al((size_t)norm_backward_parts(R) * 2 * C * 4);
+    return al(norm_backward_ws_bytes(R, C));
 }
 
 int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x, const void *g, const float *rstd,

@@ -308,6 +308,12 @@ int norm_backward(int mode, int dtype, const void *dy, const void *x, const void
                   const float *mean, const void *dres, long R, int C, void *dx, float *dg, float *db,
                   float *part, int npart, hipStream_t s);
 int norm_backward_parts(long R);
+// the norm backward's workspace: np x 2C fp32 partials, then (wide rows) the
+// row statistics, 2 fp32 per row, from this float offset (64-float aligned)
+inline long norm_backward_stats_offset(int np, int C) { return ((long)np * 2 * C + 63) / 64 * 64; }
+inline size_t norm_backward_ws_bytes(long R, int C) {
+    return (size_t)(norm_backward_stats_offset(norm_backward_parts(R), C) + 2 * R) * 4;
+}
 int rope_table(float *cs, int T, int hd, float base, hipStream_t s);
 int rope_apply(int dtype, void *qkv, const float *cs, int B, int T, int QKV, int NH, int NKV, int hd,
                int inverse, hipStream_t s);

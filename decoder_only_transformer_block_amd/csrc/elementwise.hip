@@ -83,17 +83,62 @@ __global__ __launch_bounds__(256) void norm_fwd_kernel(const T *x, const T *g, c
     }
 }
 
+// Row statistics of the norm backward for rows too wide to hold in a wave's
+// registers: st[2 row] = mean over the row of dn (LayerNorm; 0 otherwise),
+// st[2 row + 1] = mean of dn xhat, with dn = dy gamma and xhat the normalised
+// input.  One wave per row streams it in 16-byte chunks; each lane adds its
+// chunks in the order the register-resident kernel does.
+template <typename T, int MODE>
+__global__ __launch_bounds__(256) void norm_bwd_stats_kernel(const T *dy, const T *x, const T *g, const float *rstd,
+                                                              const float *mean, long R, int C, float *st) {
+    constexpr int EPC = 16 / sizeof(T);
+    constexpr bool HAS_G = MODE != DTB_NORM_RMS_NOGAMMA;
+    constexpr bool LN = MODE == DTB_NORM_LAYER;
+    const int lane = threadIdx.x & 63;
+    const long row = (long)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (row >= R) return;
+    const int nch = C / EPC;
+    const float r = rstd[row];
+    const float mu = LN ? mean[row] : 0.f;
+    float s1 = 0.f, s2 = 0.f;
+    for (int c = lane; c < nch; c += 64) {
+        float xv[EPC], d[EPC], gv[EPC];
+        unpack16<T>(ld16(x + row * C + c * EPC), xv);
+        unpack16<T>(ld16(dy + row * C + c * EPC), d);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) gv[e] = 1.f;
+        if (HAS_G) unpack16<T>(ld16(g + c * EPC), gv);
+#pragma unroll
+        for (int e = 0; e < EPC; e++) {
+            const float xh = (xv[e] - mu) * r;
+            const float dn = d[e] * gv[e];
+            s1 += dn;
+            s2 += dn * xh;
+        }
+    }
+    s2 = wave_sum(s2) / C;
+    if (LN) s1 = wave_sum(s1) / C;
+    if (lane == 0) {
+        st[2 * row] = LN ? s1 : 0.f;
+        st[2 * row + 1] = s2;
+    }
+}
+
 // dx = dres + Norm^T(dy).  Each wave handles rows wave_id, wave_id + nwaves, ...;
 // gamma/beta partials per workgroup -> part[blockIdx.x][0..C) and [C..2C).
-template <typename T, int NPL, int MODE>
+// WIN: the workgroup covers the column window blockIdx.y (64 NPL chunks) of
+// its rows and takes the row statistics from st (norm_bwd_stats_kernel);
+// otherwise one wave holds a whole row and reduces it itself.
+template <typename T, int NPL, int MODE, bool WIN>
 __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, const T *g, const float *rstd,
                                                         const float *mean, const T *dres, long R, int C, T *dx,
-                                                        float *part) {
+                                                        float *part, const float *st) {
     constexpr int EPC = 16 / sizeof(T);
     constexpr bool HAS_G = MODE != DTB_NORM_RMS_NOGAMMA;
     constexpr bool LN = MODE == DTB_NORM_LAYER;
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nch = C / EPC;
+    const int c0 = WIN ? (int)blockIdx.y * 64 * NPL : 0;  // first chunk of the window
     const long nwaves = (long)gridDim.x * 4;
     float ag[NPL][EPC], ab[NPL][EPC];
 #pragma unroll
@@ -103,7 +148,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
     float gv[NPL][EPC];
 #pragma unroll
     for (int k = 0; k < NPL; k++) {
-        int c = lane + 64 * k;
+        int c = c0 + lane + 64 * k;
 #pragma unroll
         for (int e = 0; e < EPC; e++) gv[k][e] = 1.f;
         if (HAS_G && c < nch) unpack16<T>(ld16(g + c * EPC), gv[k]);
@@ -118,7 +163,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
         const Buf bx(x + rr * C), bd(dy + rr * C), br(dres ? dres + rr * C : dy + rr * C);
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
-            const int c = lane + 64 * k;
+            const int c = c0 + lane + 64 * k;
             qx[k] = bx.ld16(c * 16, live && c < nch);
             qd[k] = bd.ld16(c * 16, live && c < nch);
             qr[k] = br.ld16(c * 16, live && dres != nullptr && c < nch);
@@ -149,12 +194,17 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
                 s2 += dn * xh[k][e];
             }
         }
-        s2 = wave_sum(s2) / C;
-        if (LN) s1 = wave_sum(s1) / C;
+        if constexpr (WIN) {
+            s1 = st[2 * row];
+            s2 = st[2 * row + 1];
+        } else {
+            s2 = wave_sum(s2) / C;
+            if (LN) s1 = wave_sum(s1) / C;
+        }
         // residual gradient (rsv) added to the result (zeros when dres is null)
 #pragma unroll
         for (int k = 0; k < NPL; k++) {
-            int c = lane + 64 * k;
+            int c = c0 + lane + 64 * k;
             if (c >= nch) continue;
             float rs[EPC], o[EPC];
             unpack16<T>(rsv[k], rs);
@@ -186,7 +236,7 @@ __global__ __launch_bounds__(256) void norm_bwd_kernel(const T *dy, const T *x, 
                 int i = threadIdx.x;
                 float sum = buf[0][i] + buf[1][i] + buf[2][i] + buf[3][i];
                 int ln = i >> 2, e = i & 3;
-                int c = ln + 64 * k;
+                int c = c0 + ln + 64 * k;
                 if (c < nch) part[(long)blockIdx.x * 2 * C + half * C + c * EPC + e0 + e] = sum;
             }
         }
@@ -280,23 +330,49 @@ int norm_backward_parts(long R) {
     return (int)(waves < 512 ? (waves > 0 ? waves : 1) : 512);
 }
 
+// Rows of 16 chunks per lane (bf16 C > 4096, fp32 C > 2048), whose chunks and
+// gamma / beta partial sums no longer fit a wave's registers (the whole-row
+// kernel spilled hundreds of registers there), take the windowed path: a
+// statistics pass over each row, then workgroups of 4-chunk column windows.
+// R = 16384: bf16 C = 8192 RMS 1393 -> 271 us, LayerNorm 1635 -> 288 us; fp32
+// C = 4096 RMS 264 -> 262 us, LayerNorm 365 -> 272 us.  (The bf16 LayerNorm at
+// 8 chunks spills 67 registers but measured 112 us against 128-137 windowed.)
+template <typename T, int MODE, int NPL> constexpr bool norm_bwd_windowed() { return NPL >= 16; }
+
+template <typename T, int MODE, int NPL, bool WIN>
+static void norm_bwd_launch(dim3 grid, const T *a, const T *xx, const T *gg, const float *rstd, const float *mean,
+                            const T *rr, long R, int C, T *o, float *part, const float *st, hipStream_t s) {
+    DTB_LAUNCH((norm_bwd_kernel<T, NPL, MODE, WIN>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean, rr, R, C, o, part,
+               st);
+}
+
+template <typename T, int MODE, int NPL>
+static hipError_t norm_bwd_mode(const T *a, const T *xx, const T *gg, const float *rstd, const float *mean,
+                                const T *rr, long R, int C, T *o, float *part, int np, float *st, hipStream_t s) {
+    if constexpr (norm_bwd_windowed<T, MODE, NPL>()) {
+        DTB_LAUNCH((norm_bwd_stats_kernel<T, MODE>), dim3((unsigned)((R + 3) / 4)), dim3(256), 0, s, a, xx, gg, rstd,
+                   mean, R, C, st);
+        hipError_t e = last_error();
+        if (e != hipSuccess) return e;
+        norm_bwd_launch<T, MODE, 4, true>(dim3(np, NPL / 4), a, xx, gg, rstd, mean, rr, R, C, o, part, st, s);
+    } else {
+        norm_bwd_launch<T, MODE, NPL, false>(dim3(np), a, xx, gg, rstd, mean, rr, R, C, o, part, nullptr, s);
+    }
+    return last_error();
+}
+
 template <typename T, int NPL>
 static hipError_t norm_bwd_t(int mode, const void *dy, const void *x, const void *g, const float *rstd,
                              const float *mean, const void *dres, long R, int C, void *dx, float *part, int np,
                              hipStream_t s) {
-    dim3 grid(np);
     const T *a = (const T *)dy, *xx = (const T *)x, *gg = (const T *)g, *rr = (const T *)dres;
     T *o = (T *)dx;
+    float *st = part + norm_backward_stats_offset(np, C);
     if (mode == DTB_NORM_RMS)
-        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_RMS>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean, rr,
-                           R, C, o, part);
-    else if (mode == DTB_NORM_RMS_NOGAMMA)
-        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_RMS_NOGAMMA>), grid, dim3(256), 0, s, a, xx, gg, rstd,
-                           mean, rr, R, C, o, part);
-    else
-        DTB_LAUNCH((norm_bwd_kernel<T, NPL, DTB_NORM_LAYER>), grid, dim3(256), 0, s, a, xx, gg, rstd, mean,
-                           rr, R, C, o, part);
-    return last_error();
+        return norm_bwd_mode<T, DTB_NORM_RMS, NPL>(a, xx, gg, rstd, mean, rr, R, C, o, part, np, st, s);
+    if (mode == DTB_NORM_RMS_NOGAMMA)
+        return norm_bwd_mode<T, DTB_NORM_RMS_NOGAMMA, NPL>(a, xx, gg, rstd, mean, rr, R, C, o, part, np, st, s);
+    return norm_bwd_mode<T, DTB_NORM_LAYER, NPL>(a, xx, gg, rstd, mean, rr, R, C, o, part, np, st, s);
 }
 
 int norm_backward(int mode, int dtype, const void *dy, const void *x, const void *g, const float *rstd,

@@ -361,8 +361,10 @@ int encoder_backward(float *dwte, float *dwpe, const int *ids, const void *dx, i
  *   else may be NULL).  g, b [C] dtype (g unused for RMS_NOGAMMA, b LayerNorm only).
  *   norm_backward: dx = dres + Norm^T(dy) (OVERWRITTEN; dres may be NULL, may
  *   alias dx);  dg, db [C] fp32 ACCUMULATED.  workspace norm_workspace_bytes(R, C)
- *   bytes (per-workgroup partial sums; deterministic).  C a multiple of 8, at
- *   most 8192 (bf16) / 4096 (fp32). */
+ *   bytes (per-workgroup partial sums, and for rows wider than a wave holds in
+ *   registers (C above 4096 bf16 / 2048 fp32) the per-row statistics of a
+ *   first pass; deterministic).  C a multiple of
+ *   8, at most 8192 (bf16) / 4096 (fp32). */
 int norm_forward(void *out, float *rstd, float *mean, const void *x, const void *g, const void *b, int R, int C,
                  int norm, float eps, int dtype, void *stream);
 int norm_backward(void *dx, float *dg, float *db, const void *dy, const void *x, const void *g, const float *rstd,
