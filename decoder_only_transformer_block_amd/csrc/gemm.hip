@@ -225,16 +225,18 @@ template <typename T> __device__ __forceinline__ void store_row4(void *base, lon
 // mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial
 template <typename T, int NI>
 __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int m_base, int n_base,
-                                               const KParams &p, int mode, int lane) {
+                                               const KParams &p, int mode, int lane, bool staged = false) {
     constexpr int W = NI * 32;          // floats per row
     constexpr int CPR = W / 4;          // float4 chunks per row
     constexpr int RPP = 64 / CPR;       // rows per pass
     constexpr int PASSES = 32 / RPP;
     const int g = lane >> 5, l32 = lane & 31;
+    if (!staged) {  // else the caller has already written the block into lw
 #pragma unroll
-    for (int j = 0; j < NI; j++)
+        for (int j = 0; j < NI; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+            for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+    }
     const int cc = lane % CPR, rr = lane / CPR;
     const int n = n_base + cc * 4;
     const bool nok = n < p.N;
@@ -334,13 +336,16 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
 // computes h = silu(g) u for half of the rows.  Every wave of the workgroup
 // must call this the same number of times (two barriers per call).
 __device__ __forceinline__ void epilogue_swiglu(const f32x16 *acc, float *lw, const float *lw_partner, int m_base,
-                                                int col_base, bool gate_wave, const KParams &p, int lane) {
+                                                int col_base, bool gate_wave, const KParams &p, int lane,
+                                                bool staged = false) {
     constexpr int W = 128, CPR = 32, RPP = 2, PASSES = 16;
     const int g = lane >> 5, l32 = lane & 31;
+    if (!staged) {
 #pragma unroll
-    for (int j = 0; j < 4; j++)
+        for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+            for (int r = 0; r < 16; r++) lw[(8 * (r >> 2) + 4 * g + (r & 3)) * W + j * 32 + l32] = acc[j][r];
+    }
     __syncthreads();
     const int cc = lane % CPR, rr = lane / CPR;
     const int n = col_base + cc * 4;  // hidden unit (gate column n, up column act_H + n)
@@ -1020,6 +1025,264 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 256x256 kernel for two k-major operands (the forward projections) on
+// v_mfma_f32_16x16x32_bf16.  The tiles, 64-k slabs, five-unit LDS ring, DMA
+// schedule and epilogue are those of gemm_k64_kernel; each wave's 64 x 128
+// block is 4 x 8 MFMA blocks of 16 x 16 and a slab is two k32 steps (12
+// fragment reads, 32 MFMAs).  Measured on the MLP-up shape, the 16x16x32 form
+// lets the chip hold a higher clock under its power limit (the 32x32x16 form
+// moves twice the accumulator registers per flop): sustained 1305-1324
+// against 1248-1260 TFLOP/s, about 1880 against 1690-1730 MHz, and the sums
+// come out bit-identical (each output is the same fp32 chain of 64-k dot
+// products).
+// * Register budget (two waves per SIMD: 256 per wave): 128 accumulators;
+//   fragments of the next k32 step are read while the current one is
+//   multiplied, column pair by column pair (A blocks double-buffered, the B
+//   blocks of the next step only after the same blocks of the current step are
+//   done), 18 fragments at most; the DMA offsets are per-lane pattern values.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Lane offsets of the 16x16x32 fragments of a k-major 64-k unit: the A (B)
+// operand lane l supplies row (column) l % 16 of a 16-row block and k
+// 8 (l / 16) .. + 7 of the k32 step.  Row block b sits at + 2048 b (16 rows of
+// 128 bytes; the chunk swizzle depends on row bits 1-3 only), so a lane needs
+// one offset per k32 step: lc0 for k 0..31, lc1 for k 32..63.
+__device__ __forceinline__ void frag16_lane(int row0, int lane, int &lc0, int &lc1) {
+    const int r = row0 + (lane & 15);  // row0 a multiple of 16
+    lc0 = k64_off(r, lane >> 4);
+    lc1 = k64_off(r, 4 + (lane >> 4));
+}
+__device__ __forceinline__ bf16x8 frag16(const char *unit, int s, int b, int lc0, int lc1) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(unit + b * 2048 + (s ? lc1 : lc0)));
+}
+
+// DMA of one k-major 64-k slab (32 KB, 32 blocks of 1 KB: 8 rows x 128 bytes)
+// by one of four DMA waves (8 blocks each), K a multiple of 64.  A lane's
+// offset in block q is its row-in-block and swizzled chunk, which depend on q
+// only through q mod 2 (the swizzle takes row bits 1-3), plus q's first row:
+// the two pattern values vpat[] are computed once per tile.  Rows past the
+// tile's last valid row (nrows) and slabs past kend are cut off by the
+// buffer's record count (zeros land in LDS).
+__device__ __forceinline__ void slab16_pattern(int *vpat, long long ld, int lane) {
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        const int r = q * 8 + (lane >> 3), c = (lane & 7) ^ k64_swz(r);
+        vpat[q] = ((lane >> 3) * (int)ld + c * 8) * 2;
+    }
+}
+__device__ __forceinline__ void dma_slab16(char *unit, const bf16 *base, long long ld, int row0, int nrows, int k0,
+                                           int kend, const int *vpat, int wave) {
+    const bf16 *g = base + (long long)row0 * ld + k0;
+    // last valid byte: row (min(nrows - row0, 256) - 1), chunk 7, when k0 + 64 <= ld
+    long long nb = 0;
+    if (k0 < kend) nb = (long long)(min(nrows - row0, 256) - 1) * ld * 2 + 128;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<bf16 *>(g), (short)0, (int)(nb < 0x7fffffffLL ? nb : 0x7fffffffLL), 0x00020000);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+        const int blk = wave * 8 + i;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(unit + blk * 1024), 16,
+                                                 vpat[i & 1] + blk * 16 * (int)ld, 0, 0, 0);
+    }
+}
+
+// rows 0..31 x columns 0..127 of a wave's 16x16 accumulators acc[2][8]
+// (lane l, element e: row 4 (l / 16) + e, column l % 16 of its block) into lw [32][128]
+__device__ __forceinline__ void stage16(const f32x4 *acc, float *lw, int lane) {
+    const int g = lane >> 4, c = lane & 15;
+#pragma unroll
+    for (int bi = 0; bi < 2; bi++)
+#pragma unroll
+        for (int bj = 0; bj < 8; bj++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) lw[(bi * 16 + 4 * g + e) * 128 + bj * 16 + c] = acc[bi * 8 + bj][e];
+}
+
+// K a multiple of 64 and one split (kbeg = 0, kend = K)
+template <int MODE>
+__global__ __launch_bounds__(512) void gemm_k64m16_kernel(KParams p) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int WGN = 2, TM = 64, FI = 4, FJ = 8;
+    constexpr int NDW = 4;   // waves that issue the DMA (one per SIMD)
+    constexpr int BPD = 8;   // 1 KB blocks per operand slab per DMA wave
+    const int nm = (p.M + BM - 1) / BM, nn = (p.N + BN - 1) / BN;
+    int tm, tn;
+    tile_coords(nm, nn, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int kbeg = blockIdx.z * p.kchunk;
+    const int kend = min(p.K, kbeg + p.kchunk);
+    const int nk = kend > kbeg ? (kend - kbeg + BK - 1) / BK : 0;
+
+    const int t = threadIdx.x, lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int wm = wave / WGN, wn = wave % WGN;
+    const bf16 *gA = static_cast<const bf16 *>(p.A), *gB = static_cast<const bf16 *>(p.B);
+
+    f32x4 acc[FI][FJ];
+#pragma unroll
+    for (int i = 0; i < FI; i++)
+#pragma unroll
+        for (int j = 0; j < FJ; j++) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const bool dmaw = wave < NDW;
+    // mode 5: B rows 0..127 are gate rows tn*128.., rows 128..255 the up rows
+    // act_H + tn*128.. (DMA waves 0-1 load the first half, 2-3 the second)
+    const int nb0 = MODE == 5 ? (wave < NDW / 2 ? tn * 128 : p.act_H + tn * 128 - 128) : n0;
+    int la0, la1, lb0, lb1;
+    frag16_lane(wm * TM, lane, la0, la1);
+    frag16_lane(wn * 128, lane, lb0, lb1);
+    // the 8 MFMAs of column pair g (B blocks 2g, 2g+1)
+    auto mma_pair = [&](const bf16x8 *af, const bf16x8 *bfr, int g) {
+#pragma unroll
+        for (int i = 0; i < FI; i++) {
+            acc[i][2 * g] = mfma16(af[i], bfr[2 * g], acc[i][2 * g]);
+            acc[i][2 * g + 1] = mfma16(af[i], bfr[2 * g + 1], acc[i][2 * g + 1]);
+        }
+    };
+    // multiply the current k32 step (ca, cb) column pair by column pair while
+    // the next step's fragments (na, nb) are read from units ua / ub
+    auto phase = [&](const bf16x8 *ca, const bf16x8 *cb, bf16x8 *na, bf16x8 *nb, const char *ua, const char *ub,
+                     int sidx) {
+        // the lane offsets pass through an empty asm, so the addresses of the
+        // five units (beyond the 64 KB reach of a read's immediate offset) are
+        // formed here instead of being hoisted out of the loop as live registers
+        asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
+        na[0] = frag16(ua, sidx, 0, la0, la1);
+        na[1] = frag16(ua, sidx, 1, la0, la1);
+        mma_pair(ca, cb, 0);
+        nb[0] = frag16(ub, sidx, 0, lb0, lb1);
+        nb[1] = frag16(ub, sidx, 1, lb0, lb1);
+        na[2] = frag16(ua, sidx, 2, la0, la1);
+        mma_pair(ca, cb, 1);
+        nb[2] = frag16(ub, sidx, 2, lb0, lb1);
+        nb[3] = frag16(ub, sidx, 3, lb0, lb1);
+        na[3] = frag16(ua, sidx, 3, la0, la1);
+        mma_pair(ca, cb, 2);
+        nb[4] = frag16(ub, sidx, 4, lb0, lb1);
+        nb[5] = frag16(ub, sidx, 5, lb0, lb1);
+        nb[6] = frag16(ub, sidx, 6, lb0, lb1);
+        nb[7] = frag16(ub, sidx, 7, lb0, lb1);
+        mma_pair(ca, cb, 3);
+    };
+    // fragment reads per column-pair group (2, 3, 3, 4) and NVM DMA
+    // instructions spread over the 32 MFMAs of a phase
+#define M16_PATTERN(NVM)                                                        \
+    {                                                                           \
+        _Pragma("unroll") for (int g = 0; g < 4; g++) {                         \
+            const int nrg = g == 0 ? 2 : g == 3 ? 4 : 3;                        \
+            _Pragma("unroll") for (int q = 0; q < 8; q++) {                     \
+                const int nr = ((q + 1) * nrg) / 8 - (q * nrg) / 8;             \
+                if (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  \
+                const int qq = g * 8 + q;                                       \
+                const int nv = ((qq + 1) * (NVM)) / 32 - (qq * (NVM)) / 32;     \
+                if (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  \
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);              \
+            }                                                                   \
+        }                                                                       \
+    }
+    int vpA[2], vpB[2];
+    slab16_pattern(vpA, p.lda, lane);
+    slab16_pattern(vpB, p.ldb, lane);
+    // one 64-k step: J = j mod 5 picks the units at compile time (the same
+    // ring as gemm_k64_kernel: B of slab j+1 and A of slab j+2 go into the
+    // units of slab j-1, freed at the barrier that opens step j)
+#define M16_STEP(J, D)                                                                          \
+    {                                                                                           \
+        constexpr int UA = (2 * (J)) % 5, UB = (2 * (J) + 1) % 5;                               \
+        constexpr int NB = (2 * (J) + 3) % 5, NA = (2 * (J) + 4) % 5;                           \
+        __builtin_amdgcn_s_waitcnt(wait_vm_lgkm0(BPD));                                         \
+        asm volatile("s_barrier" ::: "memory");                                                 \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        const int kb1 = kbeg + (j + 1) * BK, ka2 = kbeg + (j + 2) * BK;                          \
+        bf16x8 ga[FI], gb[FJ];                                                                  \
+        if (D) dma_slab16(k64_unit<NB>(), gB, p.ldb, nb0, p.N, kb1, kend, vpB, wave);           \
+        phase(fa, fb, ga, gb, k64_unit<UA>(), k64_unit<UB>(), 0);                               \
+        M16_PATTERN((D) ? BPD : 0)                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        if (D) dma_slab16(k64_unit<NA>(), gA, p.lda, m0, p.M, ka2, kend, vpA, wave);            \
+        phase(ga, gb, fa, fb, k64_unit<UA>(), k64_unit<UB>(), 1);                               \
+        M16_PATTERN((D) ? BPD : 0)                                                              \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+        ++j;                                                                                    \
+    }
+    // prologue: A of slabs 0 and 1, B of slab 0.  The k32 fragments
+    // multiplied first in step 0 belong to no slab and are zero.
+    if (dmaw) {
+        dma_slab16(k64_unit<0>(), gA, p.lda, m0, p.M, kbeg, kend, vpA, wave);
+        dma_slab16(k64_unit<1>(), gB, p.ldb, nb0, p.N, kbeg, kend, vpB, wave);
+        dma_slab16(k64_unit<2>(), gA, p.lda, m0, p.M, kbeg + BK, kend, vpA, wave);
+    }
+    bf16x8 fa[FI], fb[FJ];
+#pragma unroll
+    for (int i = 0; i < FI; i++) fa[i] = bf16x8{};
+#pragma unroll
+    for (int j = 0; j < FJ; j++) fb[j] = bf16x8{};
+    int j = 0;
+    if (nk > 0) {
+        // every step issues the same number of DMA instructions (past the end
+        // of K they load zeros into free units), so the wait count is uniform
+        if (dmaw) {
+            for (; j + 5 <= nk;) {
+                M16_STEP(0, true)
+                M16_STEP(1, true)
+                M16_STEP(2, true)
+                M16_STEP(3, true)
+                M16_STEP(4, true)
+            }
+            if (j < nk) M16_STEP(0, true)
+            if (j < nk) M16_STEP(1, true)
+            if (j < nk) M16_STEP(2, true)
+            if (j < nk) M16_STEP(3, true)
+        } else {
+            for (; j + 5 <= nk;) {
+                M16_STEP(0, false)
+                M16_STEP(1, false)
+                M16_STEP(2, false)
+                M16_STEP(3, false)
+                M16_STEP(4, false)
+            }
+            if (j < nk) M16_STEP(0, false)
+            if (j < nk) M16_STEP(1, false)
+            if (j < nk) M16_STEP(2, false)
+            if (j < nk) M16_STEP(3, false)
+        }
+#pragma unroll
+        for (int g = 0; g < 4; g++) mma_pair(fa, fb, g);  // last k32 step of the last slab
+    }
+#undef M16_STEP
+#undef M16_PATTERN
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+    // ---- epilogue through LDS (16 KB per wave in units 0-3), 32 rows at a time
+    {
+        auto region = [&](int w) {
+            const int u = w >> 1;
+            char *reg = u == 0 ? k64_unit<0>() : u == 1 ? k64_unit<1>() : u == 2 ? k64_unit<2>() : k64_unit<3>();
+            return reinterpret_cast<float *>(reg + (w & 1) * 16384);
+        };
+        float *lw = region(wave);
+        if constexpr (MODE == 5) {
+            const float *lp = region(wave ^ 1);
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                stage16(&acc[2 * i][0], lw, lane);
+                epilogue_swiglu(nullptr, lw, lp, m0 + wm * TM + i * 32, tn * 128, wn == 0, p, lane, true);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                stage16(&acc[2 * i][0], lw, lane);
+                epilogue_block<bf16, 4>(nullptr, lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane, true);
+            }
+        }
+    }
+}
+
 // out[m*ldo + n] += sum_z part[z][m][n]   (N % 4 == 0), z in order: the
 // partials of splits 1 .. S-1 (split 0 has already added its own into out).
 // The count is a template argument so that every partial's load is issued
@@ -1087,8 +1350,12 @@ static hipError_t launch256_t(const KParams &p, int splits, hipStream_t s) {
     // cache lines); both operands m/n-major (the weight gradients) already
     // stream whole lines on 32-k slabs, and the 32-k ring measured the same
     // K a multiple of 64 (one split: kbeg = 0, kend = K): every slab is whole in k
-    if constexpr (AK || BKM) {
-        if (p.K % 64 == 0 && splits == 1) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, true>), grid, dim3(512), 0, s, p);
+    const bool whole = p.K % 64 == 0 && splits == 1;
+    if constexpr (AK && BKM) {
+        if (whole) DTB_LAUNCH((gemm_k64m16_kernel<MODE>), grid, dim3(512), 0, s, p);
+        else DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, false>), grid, dim3(512), 0, s, p);
+    } else if constexpr (AK || BKM) {
+        if (whole) DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, true>), grid, dim3(512), 0, s, p);
         else DTB_LAUNCH((gemm_k64_kernel<AK, BKM, MODE, false>), grid, dim3(512), 0, s, p);
     } else {
         DTB_LAUNCH((gemm_dma_kernel<AK, BKM, MODE, 8>), grid, dim3(512), 0, s, p);
