@@ -27,7 +27,7 @@ PEAK = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA TFLOP/s (MI355X datasheet)
 HBM_PEAK = 8000.0                        # GB/s
 # the bf16 forward-projection GEMM: one main loop, two epilogues (MODE 0: bias /
 # residual / RoPE for QKV, O and down; MODE 5: SwiGLU for the MLP up projection)
-GEMM_FWD_KERNEL = "gemm_k64_kernel<true, true, 0|5, true>"
+GEMM_FWD_KERNEL = "gemm_k64m16_kernel<0|5>"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gemm_fwd_llama_gqa_traffic.md")
 GEMM_SOURCES = [os.path.join(ROOT, "decoder_only_transformer_block_amd", "csrc", f) for f in ("gemm.hip", "common.h")]
 
@@ -77,8 +77,8 @@ def traffic_summary(root: str, cmds: dict) -> str:
                     vals[disp] = vals.get(disp, 0.0) + v
         return vals
 
-    is_gemm = lambda n: any(k in n for k in ("gemm_k64_kernel<true, true, 0,", "gemm_k64_kernel<true, true, 5,",
-                                             "gemm_k64_kernelILb1ELb1ELi0E", "gemm_k64_kernelILb1ELb1ELi5E"))
+    is_gemm = lambda n: any(k in n for k in ("gemm_k64m16_kernel<0>", "gemm_k64m16_kernel<5>",
+                                             "gemm_k64m16_kernelILi0E", "gemm_k64m16_kernelILi5E"))
     is_copy = lambda n: "copy" in n.lower()
     f = per_dispatch("fetch", "FETCH_SIZE", is_gemm)
     w = per_dispatch("write", "WRITE_SIZE", is_gemm)
