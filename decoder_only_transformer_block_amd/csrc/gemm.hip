@@ -1161,21 +1161,28 @@ __global__ __launch_bounds__(512) void gemm_k64m16_kernel(KParams p) {
         nb[2] = frag16(ub, sidx, 2, lb0, lb1);
         nb[3] = frag16(ub, sidx, 3, lb0, lb1);
         na[3] = frag16(ua, sidx, 3, la0, la1);
+        if (sidx) {  // before the barrier: the last pair is read one group early
+            nb[6] = frag16(ub, sidx, 6, lb0, lb1);
+            nb[7] = frag16(ub, sidx, 7, lb0, lb1);
+        }
         mma_pair(ca, cb, 2);
         nb[4] = frag16(ub, sidx, 4, lb0, lb1);
         nb[5] = frag16(ub, sidx, 5, lb0, lb1);
-        nb[6] = frag16(ub, sidx, 6, lb0, lb1);
-        nb[7] = frag16(ub, sidx, 7, lb0, lb1);
+        if (!sidx) {
+            nb[6] = frag16(ub, sidx, 6, lb0, lb1);
+            nb[7] = frag16(ub, sidx, 7, lb0, lb1);
+        }
         mma_pair(ca, cb, 3);
     };
     // fragment reads per column-pair group (2, 3, 3, 4) and NVM DMA
     // instructions spread over the 32 MFMAs of a phase
-#define M16_PATTERN(NVM)                                                        \
+#define M16_PATTERN(NVM, LATE)                                                  \
     {                                                                           \
         _Pragma("unroll") for (int g = 0; g < 4; g++) {                         \
-            const int nrg = g == 0 ? 2 : g == 3 ? 4 : 3;                        \
+            const int nrg = g == 0 ? 2 : g == 1 ? 3 : g == 2 ? ((LATE) ? 3 : 5) : ((LATE) ? 4 : 2); \
             _Pragma("unroll") for (int q = 0; q < 8; q++) {                     \
-                const int nr = ((q + 1) * nrg) / 8 - (q * nrg) / 8;             \
+                const int nr = (!(LATE) && g == 3) ? (q < nrg ? 1 : 0)          \
+                                                   : ((q + 1) * nrg) / 8 - (q * nrg) / 8; \
                 if (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  \
                 const int qq = g * 8 + q;                                       \
                 const int nv = ((qq + 1) * (NVM)) / 32 - (qq * (NVM)) / 32;     \
@@ -1201,11 +1208,11 @@ __global__ __launch_bounds__(512) void gemm_k64m16_kernel(KParams p) {
         bf16x8 ga[FI], gb[FJ];                                                                  \
         if (D) dma_slab16(k64_unit<NB>(), gB, p.ldb, nb0, p.N, kb1, kend, vpB, wave);           \
         phase(fa, fb, ga, gb, k64_unit<UA>(), k64_unit<UB>(), 0);                               \
-        M16_PATTERN((D) ? BPD : 0)                                                              \
+        M16_PATTERN((D) ? BPD : 0, true)                                                        \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         if (D) dma_slab16(k64_unit<NA>(), gA, p.lda, m0, p.M, ka2, kend, vpA, wave);            \
         phase(ga, gb, fa, fb, k64_unit<UA>(), k64_unit<UB>(), 1);                               \
-        M16_PATTERN((D) ? BPD : 0)                                                              \
+        M16_PATTERN((D) ? BPD : 0, false)                                                              \
         __builtin_amdgcn_sched_barrier(0);                                                      \
         ++j;                                                                                    \
     }
