@@ -555,6 +555,8 @@ __device__ __forceinline__ bf16x8 dma_frag(const char *region, int r, int s, int
 // s_waitcnt immediate for vmcnt(n) lgkmcnt(0) (vmcnt bits [3:0] and [15:14],
 // expcnt [6:4] left at its maximum, lgkmcnt [11:8])
 constexpr int wait_vm_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+// the same with lgkmcnt(l) (l <= 15)
+constexpr int wait_vm_lgkm(int n, int l) { return wait_vm_lgkm0(n) | ((l & 15) << 8); }
 
 // NW waves: 8 -> 4 x 2 waves of 64 x 128, 4 -> 2 x 2 waves of 128 x 128.
 template <bool AK, bool BKM, int MODE, int NW>
@@ -629,12 +631,16 @@ __global__ __launch_bounds__(NW * 64) void gemm_dma_kernel(KParams p) {
     // texture-address FIFO and stalled the issuing waves: measured 5-13 %
     // slower).  Past the end of K the loads are out of range and write zeros
     // into a stage that is no longer read, so every step has the same count.
-    constexpr int WAIT1 = wait_vm_lgkm0(2 * BPD);  // one younger slab in flight
     bf16x8 fa[FI], fb[FJ];
     // LDS reads of one k16 step and DMA instructions of one operand slab,
     // spread evenly over the 8 MFMAs of the other fragment set
     constexpr int NRD = FI * (AK ? 1 : 2) + FJ * (BKM ? 1 : 2);
     constexpr int NMM = FI * FJ;
+    // one younger slab in flight; the last NRD LDS reads (the next slab's
+    // first fragments, issued at the end of the previous step) may still be in
+    // flight: the barrier only needs the reads of the stage it frees
+    static_assert(NRD <= 15, "lgkmcnt field");
+    constexpr int WAIT1 = wait_vm_lgkm(2 * BPD, NRD);
 #define PIPE_PATTERN(NVM)                                                       \
     {                                                                           \
         _Pragma("unroll") for (int q = 0; q < NMM; q++) {                       \
@@ -885,10 +891,11 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
     constexpr int NMM = FI * FJ;
     constexpr int NV = BPD / 2;  // DMA instructions per k16 group (one operand over two groups)
     // LDS reads of one k16 step and NVM DMA instructions spread evenly over 8 MFMAs
-#define K64_PATTERN(NVM)                                                        \
+#define K64_PATTERN(NVM, FRONT)                                                 \
     {                                                                           \
         _Pragma("unroll") for (int q = 0; q < NMM; q++) {                       \
-            const int nr = ((q + 1) * NRD) / NMM - (q * NRD) / NMM;              \
+            const int nr = (FRONT) ? (2 * q < NRD ? (2 * q + 1 < NRD ? 2 : 1) : 0) \
+                                   : ((q + 1) * NRD) / NMM - (q * NRD) / NMM;     \
             if (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      \
             if (nr > 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      \
             const int nv = ((q + 1) * (NVM)) / NMM - (q * (NVM)) / NMM;          \
@@ -926,22 +933,22 @@ __global__ __launch_bounds__(512) void gemm_k64_kernel(KParams p) {
         if (D) DMA_B(k64_unit<NB>(), kb1, 0)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 0, ga, gb);                       \
         mma(fa, fb);                                                            \
-        K64_PATTERN((D) ? NV : 0)                                               \
+        K64_PATTERN((D) ? NV : 0, false)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
         if (D) DMA_B(k64_unit<NB>(), kb1, 1)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 1, fa, fb);                       \
         mma(ga, gb);                                                            \
-        K64_PATTERN((D) ? NV : 0)                                               \
+        K64_PATTERN((D) ? NV : 0, false)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
         if (D) DMA_A(k64_unit<NA>(), ka2, 0)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 2, ga, gb);                       \
         mma(fa, fb);                                                            \
-        K64_PATTERN((D) ? NV : 0)                                               \
+        K64_PATTERN((D) ? NV : 0, false)                                               \
         __builtin_amdgcn_sched_barrier(0);                                      \
         if (D) DMA_A(k64_unit<NA>(), ka2, 1)                                    \
         frags(k64_unit<UA>(), k64_unit<UB>(), 3, fa, fb);                       \
         mma(ga, gb);                                                            \
-        K64_PATTERN((D) ? NV : 0)                                               \
+        K64_PATTERN((D) ? NV : 0, true)                                                \
         __builtin_amdgcn_sched_barrier(0);                                      \
         ++j;                                                                    \
     }
