@@ -223,7 +223,7 @@ template <typename T> __device__ __forceinline__ void store_row4(void *base, lon
 // accesses (8 bytes of bf16 or 16 bytes of fp32 per lane) issued without
 // intervening waits.  Requires that no other wave still reads that LDS region.
 // mode: 0 store dtype (+bias, +res), 1 store fp32 (+bias), 2 fp32 +=, 3 fp32 partial
-template <typename T, int NI>
+template <typename T, int NI, bool ROPE_AHEAD = false>
 __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int m_base, int n_base,
                                                const KParams &p, int mode, int lane, bool staged = false) {
     constexpr int W = NI * 32;          // floats per row
@@ -286,8 +286,33 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
             in[q] = load_row4<float>(ob, (long long)row * p.ldo + n, nok && m_base + row < p.M);
         }
     }
+    // RoPE table row of pass q: one modulo per call (a 32-row block wraps past
+    // T at most once when T >= 32; rows past M still index a valid table row)
+    const int rT = p.rope_T > 0 ? p.rope_T : 1;
+    const int pos0 = rope ? (m_base + rr) % rT : 0;
+    auto rpos = [&](int q) {
+        const int x = pos0 + q * RPP;
+        return rT >= 32 ? (x >= rT ? x - rT : x) : x % rT;
+    };
+    // ROPE_AHEAD: the (cos, sin) pairs of a batch of RB passes are loaded
+    // before any of them is used (the output stores in between keep the
+    // compiler from hoisting them itself)
+    constexpr int RB = !ROPE_AHEAD ? PASSES : PASSES < 4 ? PASSES : 4;
 #pragma unroll
-    for (int q = 0; q < PASSES; q++) {
+    for (int qb = 0; qb < PASSES; qb += RB) {
+    float2 rc[ROPE_AHEAD ? RB : 1][4];
+    if constexpr (ROPE_AHEAD) {
+        if (rope && rhalf >= 4) {
+#pragma unroll
+            for (int q = 0; q < RB; q++) {
+                const float2 *cs = p.rope_cs + (long long)rpos(qb + q) * rhalf + rk;
+#pragma unroll
+                for (int e = 0; e < 4; e++) rc[q][e] = cs[e];
+            }
+        }
+    }
+#pragma unroll
+    for (int q = qb; q < qb + RB; q++) {
         const int row = q * RPP + rr;
         const int m = m_base + row;
         f32x4 v = *reinterpret_cast<const f32x4 *>(lw + row * W + cc * 4);
@@ -295,13 +320,13 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
         if (mode == 0) {
             v = v + bv + in[q];
             if (rope) {
-                const float2 *cs = p.rope_cs + (long long)(m % p.rope_T) * rhalf;
+                const float2 *cs = p.rope_cs + (long long)rpos(q) * rhalf;
                 if (rhalf >= 4) {
                     const f32x4 w = *reinterpret_cast<const f32x4 *>(lw + row * W + cc * 4 + roff) + bvp;
                     const float sg = rlow ? -1.f : 1.f;
 #pragma unroll
                     for (int e = 0; e < 4; e++) {
-                        const float2 c = cs[rk + e];
+                        const float2 c = ROPE_AHEAD ? rc[ROPE_AHEAD ? q - qb : 0][e] : cs[rk + e];
                         v[e] = v[e] * c.x + sg * w[e] * c.y;
                     }
                 } else {  // head width 4: pairs (0, 2), (1, 3) of the vector
@@ -326,6 +351,7 @@ __device__ __forceinline__ void epilogue_block(const f32x16 *acc, float *lw, int
         } else {
             *reinterpret_cast<f32x4 *>(p.part + ((long long)(blockIdx.z - 1) * p.M + m) * p.N + n) = v;
         }
+    }
     }
 }
 
@@ -1291,7 +1317,8 @@ __global__ __launch_bounds__(512) void gemm_k64m16_kernel(KParams p) {
 #pragma unroll
             for (int i = 0; i < 2; i++) {
                 stage16(&acc[2 * i][0], lw, lane);
-                epilogue_block<bf16, 4>(nullptr, lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane, true);
+                epilogue_block<bf16, 4, MODE == 0>(nullptr, lw, m0 + wm * TM + i * 32, n0 + wn * 128, p, MODE, lane,
+                                                   true);
             }
         }
     }
