@@ -25,6 +25,12 @@ SHAPES = [
     # more than one round of 256 x 256 tiles (ragged rows and columns, 17 x 17 tiles)
     ("rounds_fwd", 4100, 384, 4352),        # forward on 289 tiles
     ("rounds_dinp", 4100, 4352, 384),       # input gradient on 289 tiles
+    # the 16x16x32 forward kernel (K a multiple of 64) with ragged rows and
+    # columns (9 x 17 tiles; the last tile's rows and weight rows past the end
+    # read as zeros by the buffers' record counts): K of three slabs (tail
+    # steps only) and of 21 slabs (four groups of five and a tail)
+    ("m16_ragged", 2100, 192, 4200),
+    ("m16_ragged_longk", 2100, 1344, 4200),
     ("generic_mid", 333, 264, 328),
     ("tiny", 7, 8, 16),
     ("one_row", 1, 64, 8),
