@@ -106,6 +106,76 @@ def traffic_summary(root: str, cmds: dict) -> str:
     return "\n".join(lines)
 
 
+COUNTER_PASSES = {
+    "a": "SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_SALU SQ_INSTS_LDS SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES "
+         "SQ_WAVE_CYCLES SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE",
+    "b": "SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAIT_INST_LDS SQ_WAIT_INST_ANY "
+         "SQ_ACTIVE_INST_LDS GRBM_GUI_ACTIVE",
+}
+COUNTER_KERNELS = [("attention forward", "fwd_bf16_kernel"), ("attention backward dQ", "dq_bf16_kernel"),
+                   ("attention backward dK/dV", "dkv_bf16_kernel"), ("GEMM forward", "gemm_k64m16_kernel"),
+                   ("GEMM input gradient", "gemm_k64_kernel"), ("GEMM weight gradient", "gemm_dma_kernel"),
+                   ("norm forward", "norm_fwd_kernel"), ("norm backward", "norm_bwd_kernel"),
+                   ("activation backward", "act_bwd_kernel")]
+
+
+def counter_summary(root: str, cmds: list) -> str:
+    """Markdown table of the instruction counters of two rocprofv3 --pmc runs
+    (root/a, root/b: COUNTER_PASSES) per kernel family, per dispatch."""
+    import glob
+    import sqlite3
+    tot = {}  # family -> counter -> [sum, dispatches]
+    for sub in COUNTER_PASSES:
+        seen = {}
+        for db in glob.glob(os.path.join(root, sub, "**", "*.db"), recursive=True):
+            c = sqlite3.connect(db)
+            for name, disp, ctr, v in c.execute("select kernel_name, dispatch_id, counter_name, value "
+                                                "from counters_collection"):
+                fam = next((f for f, key in COUNTER_KERNELS if key in name), None)
+                if fam is None:
+                    continue
+                t = tot.setdefault(fam, {}).setdefault(ctr, [0.0, set()])
+                t[0] += v
+                t[1].add((sub, disp))
+    lines = ["# Instruction counters per kernel family (Llama-GQA 4-layer stack, bf16)", "",
+             "Two counter runs over the same bench command (one kernel at a time: `--no-overlap`), from the "
+             "repository root on an MI355X:", "", "```"] + cmds + ["```", "",
+             "Per dispatch, averaged over the family's dispatches.  `VALU instr`: SQ_INSTS_VALU, which counts "
+             "the MFMA instructions too; `other VALU / MFMA`: (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA; "
+             "`SALU`, `LDS`: SQ_INSTS_SALU, SQ_INSTS_LDS per MFMA instruction.  `MFMA busy`: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024 SIMDs), "
+             "the fraction of the kernel's active cycles in which a SIMD's matrix unit is busy.  `VALU active`: "
+             "SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES, the share of a wave's cycles spent issuing VALU work.  "
+             "`MFMA TFLOP per dispatch`: 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16, the matrix work one launch "
+             "executed (recomputed products and padding included).  `LDS conflict`: SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.", "",
+             "| kernel family | dispatches | MFMA instr | VALU instr | other VALU / MFMA | SALU / MFMA | "
+             "LDS / MFMA | MFMA busy | VALU active | MFMA TFLOP per dispatch | LDS conflict |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    out = {}
+    for fam, _ in COUNTER_KERNELS:
+        t = tot.get(fam)
+        if not t:
+            continue
+        avg = {k: v[0] / max(len(v[1]), 1) for k, v in t.items()}
+        g = lambda k: avg.get(k, 0.0)
+        n = len(t.get("SQ_INSTS_MFMA", [0, set()])[1])
+        mf = g("SQ_INSTS_MFMA")
+        busy = g("SQ_VALU_MFMA_BUSY_CYCLES") / max(g("GRBM_GUI_ACTIVE") / 8 * 1024, 1.0)
+        per = lambda k: g(k) / mf if mf > 0 else None
+        row = {"dispatches": n, "mfma": mf, "valu": g("SQ_INSTS_VALU"),
+               "other_valu_per_mfma": (g("SQ_INSTS_VALU") - mf) / mf if mf > 0 else None,
+               "salu_per_mfma": per("SQ_INSTS_SALU"), "lds_per_mfma": per("SQ_INSTS_LDS"),
+               "mfma_busy": busy, "valu_active": g("SQ_ACTIVE_INST_VALU") / max(g("SQ_WAVE_CYCLES"), 1.0),
+               "mfma_tflop": 512 * g("SQ_INSTS_VALU_MFMA_MOPS_BF16") / 1e12,
+               "lds_conflict": g("SQ_LDS_BANK_CONFLICT") / max(g("SQ_LDS_IDX_ACTIVE"), 1.0)}
+        out[fam] = {k: (round(v, 4) if v is not None else None) for k, v in row.items()}
+        f2 = lambda v: "—" if v is None else f"{v:.2f}"
+        lines.append(f"| {fam} | {n} | {mf:.4g} | {row['valu']:.4g} | {f2(row['other_valu_per_mfma'])} | "
+                     f"{f2(row['salu_per_mfma'])} | {f2(row['lds_per_mfma'])} | {busy:.3f} | "
+                     f"{row['valu_active']:.3f} | {row['mfma_tflop']:.4f} | {row['lds_conflict']:.3f} |")
+    lines += ["", "```json", json.dumps(out), "```", ""]
+    return "\n".join(lines)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -130,6 +200,9 @@ def parse():
     ap.add_argument("--traffic-summary", default="",
                     help="only write the forward-GEMM traffic summary from the rocprofv3 runs under this "
                          "directory (subdirectories fetch, write, copy_fetch, copy_write) and exit")
+    ap.add_argument("--counter-summary", default="",
+                    help="only write the per-kernel instruction-counter summary from the two rocprofv3 runs "
+                         "under this directory (subdirectories a and b) and exit")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens of the oracle's bounded sample (one sequence, one layer); 0: the workload's T")
     return ap.parse_args()
@@ -591,6 +664,17 @@ def main():
             cmds.append(f"timeout -s KILL 120 rocprofv3 --pmc {ctr} -d {root}/{sub} -o p -- {prog}")
         cmds.append(f"python3 bench.py --traffic-summary {root} > profiles/gemm_fwd_llama_gqa_traffic.md")
         print(traffic_summary(root, {"workload": "llama_gqa", "copy_bytes": n, "commands": cmds}))
+        return
+    if args.counter_summary:
+        root = args.counter_summary
+        bench = "python3 bench.py --steps 2 --warmup 1 --no-cpu-baseline --no-timing --no-overlap"
+        cmds = ["cd /tmp && export TMPDIR=/tmp"]
+        for sub, ctrs in COUNTER_PASSES.items():
+            cmds.append(f"timeout -s KILL 150 rocprofv3 --pmc {ctrs} -d {root}/{sub} -o p -- "
+                        f"{bench.replace('bench.py', '/root/repo/bench.py')}")
+        cmds.append(f"cd /root/repo && python3 bench.py --counter-summary {root} > "
+                    "profiles/llama_gqa_instruction_counters.md")
+        print(counter_summary(root, cmds))
         return
     if args.workload == "oracle_table":
         oracle_table(args)
