@@ -54,7 +54,10 @@ def test_attn_long_full_size_sampled():
     del out, dq
     Q, K, V, DO = qkv[0, :, :C], qkv[0, :, C:C + KV], qkv[0, :, C + KV:], dout[0]
 
-    rows = [0, 1, 63, 64, 127, 128, 1000, 4097, 8191, 12289, T - 129, T - 1]
+    # tile edges, the first and last rows, and multiples of 97 (a stride prime to
+    # every tile size, so the sampled rows fall at every offset within a tile)
+    rows = [0, 1, 63, 64, 127, 128, 1000, 4097, 8191, 12289, T - 129, T - 1] + [97 * k for k in (1, 13, 42, 100, 168)]
+    assert max(rows) < T
     ref = [_rows_of_prefix(oracle, Q, K, V, DO, t, NH, NKV, hd) for t in rows]
     tol = TOL["bf16"]
     check("o[rows]", O[rows], np.stack([r[0] for r in ref]), tol)
